@@ -1,0 +1,220 @@
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step = one decode layer's attention step over a whole synthetic batch:
+  kv_cache_write of each sequence's current token (its K/V rewritten into its slot),
+  then the split pass of paged decode attention, then the merge pass.
+The step reads every valid K/V byte of the batch once.  Steps rotate over --layers
+separate pools (the same block tables, as the layers of one model would use), so no
+pool is re-read before the others have streamed through; with 4 layers of the Llama-3-8B
+batch that is ~2.6 GB between two reads of one pool, ten times the 256 MB MALL.
+
+Printed on stdout: one JSON line.  value = KV GB/s of the whole step (algorithmic KV bytes
+of valid tokens, sum_s L_s * Hkv * D * 2 * bytes, divided by the wall time per step);
+roofline = the split kernel alone, timed with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak (AMD public figure)
+METRIC = "paged decode attention: KV GB/s (% HBM peak) and µs/step, Llama-3-8B shape"
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llama3_8b_bf16")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--layers", type=int, default=4)
+    p.add_argument("--num-splits", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "profiles", "traffic.json"))
+    return p.parse_args()
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _cpu_baseline(case, repeats=3):
+    """The oracle, as it stands, on the full batch (median of `repeats` runs)."""
+    from oracle import attention as oatt
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oatt.decode_case(case)
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), blas_threads
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from synth import WORKLOADS, make_decode_case
+
+    wl = WORKLOADS[args.workload]
+    if wl.prefix_group:
+        raise SystemExit("bench.py times decode workloads without prefix sharing")
+    t0 = time.perf_counter()
+    case = make_decode_case(wl, args.seed)
+    _log(f"[bench] generated {wl.name} seed={args.seed} in {time.perf_counter() - t0:.1f}s; "
+         f"sum L = {int(case.lengths.sum())}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}[wl.kv_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[wl.kv_dtype]
+    B, Hq, Hkv, D, bs = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+
+    def dev_tensor(arr, storage):
+        if storage == "f32":
+            return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    store = "f32" if wl.kv_dtype == "f32" else "bf16"
+    lens32 = case.lengths.astype(np.int32)
+    t_meta = time.perf_counter()
+    all_slots = pkv.build_slot_mapping(case.block_tables, lens32, bs)
+    host_meta_us = (time.perf_counter() - t_meta) * 1e6
+    k_tok, v_tok = dev_tensor(case.k, store), dev_tensor(case.v, store)
+    slots_dev = torch.from_numpy(all_slots).to(dev)
+    pools = []
+    for _ in range(args.layers):
+        k = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)
+        v = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)
+        pkv.kv_cache_write(k_tok, v_tok, k, v, slots_dev, k_scale=float(case.k_scale), v_scale=float(case.v_scale))
+        pools.append((k, v))
+    # The step's new tokens: each sequence's last token, rewritten into its own slot.
+    last = np.cumsum(case.lengths) - 1
+    has = case.lengths > 0
+    new_idx = torch.from_numpy(last[has]).to(dev)
+    k_new = k_tok.index_select(0, new_idx).contiguous()
+    v_new = v_tok.index_select(0, new_idx).contiguous()
+    new_slots = torch.from_numpy(all_slots[last[has]]).to(dev)
+    del k_tok, v_tok, slots_dev
+    q = dev_tensor(case.q, wl.q_dtype)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(case.block_tables).to(dev)
+    lens = torch.from_numpy(lens32).to(dev)
+    qd, kd = (pkv.F32 if wl.q_dtype == "f32" else pkv.BF16), {"f32": pkv.F32, "bf16": pkv.BF16,
+                                                             "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
+    ws_bytes = pkv.paged_attention_workspace_size(B, Hq, Hkv, D, bs, qd, kd, args.num_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    splits = args.num_splits or pkv.paged_attention_default_splits(D, bs, qd, kd)
+    stream = torch.cuda.current_stream(dev)
+    ks, vs = float(case.k_scale), float(case.v_scale)
+
+    def step(i, ev=None):
+        k, v = pools[i % len(pools)]
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.kv_cache_write(k_new, v_new, k, v, new_slots, k_scale=ks, v_scale=vs)
+        if ev is not None:
+            ev[1].record(stream)
+        pkv.paged_attention_split(out, q, k, v, tables, lens, case.scale, ks, vs, args.num_splits, ws)
+        if ev is not None:
+            ev[2].record(stream)
+        pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, ks, vs, args.num_splits, ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    _log(f"[bench] warmup done; timing {args.steps} steps over {len(pools)} layer pools")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    write_us = statistics.mean(e[0].elapsed_time(e[1]) for e in events) * 1e3
+    split_us = statistics.mean(e[1].elapsed_time(e[2]) for e in events) * 1e3
+    merge_us = statistics.mean(e[2].elapsed_time(e[3]) for e in events) * 1e3
+    step_event_us = statistics.mean(e[0].elapsed_time(e[3]) for e in events) * 1e3
+
+    sum_l = int(case.lengths.sum())
+    kv_bytes = sum_l * Hkv * D * 2 * eb
+    us_per_step = elapsed / args.steps * 1e6
+    value = kv_bytes / (us_per_step * 1e-6) / 1e9
+    achieved = kv_bytes / (split_us * 1e-6) / 1e9
+
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f).get(wl.name)
+        if tj and tj.get("kernel_source_sha") == _kernel_sha():
+            traffic = tj.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
+        t_cpu, threads = _cpu_baseline(case)
+        cpu = {"value": round(kv_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"full batch ({B} sequences, sum L = {sum_l}), fp64 numpy oracle incl. decoding "
+                         f"K/V to fp64, median of 3 runs, {t_cpu * 1e3:.0f} ms per run"}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn+bf16"}[wl.kv_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, random physical block permutation)",
+        "config": {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": bs, "kv_dtype": wl.kv_dtype, "context": list(wl.length_dist),
+                   "sum_context": sum_l, "num_blocks": case.num_blocks, "seed": args.seed,
+                   "num_splits": int(splits), "layer_pools": len(pools)},
+        "us_per_step": round(us_per_step, 2),
+        "kv_bytes": kv_bytes,
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "kernel_us": {"kv_cache_write": round(write_us, 2), "paged_attention_split": round(split_us, 2),
+                      "paged_attention_merge": round(merge_us, 2), "step_events": round(step_event_us, 2)},
+        "host_metadata_us": round(host_meta_us, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "paged_attention_split_kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_329_amd", "csrc",
+                     "attention_decode.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,268 @@
+/*
+ * pagedkv.h — C ABI of the MI355X (gfx950) paged KV-cache decode library.
+ *
+ * The library implements the data-parallel hot path of PagedAttention:
+ *
+ *   - decode attention that reads every sequence's keys and values through a block
+ *     table of fixed-size, non-contiguous physical blocks and combines them with a
+ *     running softmax, so that the result is that of attention over a contiguous
+ *     layout ("PagedAttention: Optimizing KV Cache in vLLM", grasp.study, §3 "Making it
+ *     Work: The PagedAttention Kernel");
+ *   - the KV-cache write that stores new tokens' K/V into their slots ("What is
+ *     PagedAttention?", qubittool glossary, "How It Works: Map Logical to Physical
+ *     Blocks": decode appends into the partly filled last block);
+ *   - the block copy behind copy-on-write (same lesson, §4 "Advanced Benefit: Zero-Cost
+ *     Sharing with Copy-on-Write");
+ *   - a host-side block allocator (free list, reference counts, copy-on-write
+ *     decisions) that only produces block tables, slot mappings and copy lists
+ *     (glossary, "How It Works: Share Without Mutating State").
+ *
+ * Conventions for every entry point
+ *   - All pointers to tensors are device pointers unless the parameter says "host".
+ *     The caller owns every buffer, including the attention workspace; the library
+ *     never allocates or frees device memory and never synchronises a stream.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  All
+ *     kernels of one call are enqueued on that stream in order.
+ *   - Every function returns a pkv_status.  Argument checks happen on the host before
+ *     anything is enqueued; on any non-OK status nothing was enqueued and no state
+ *     changed.  pkv_last_error() returns a thread-local message for the last failure.
+ *     Launch errors are reported as PKV_HIP_ERROR; faults during execution surface at
+ *     the caller's next synchronisation, as for any asynchronous HIP work.
+ *   - No function aborts or throws across the ABI.
+ *
+ * Physical KV pool layout (one K pool and one V pool, same shape)
+ *   - Element type: float32, bfloat16 or fp8 e4m3fn (OCP E4M3: bias 7, max 448, no
+ *     infinities), b = 4, 2 or 1 bytes; x = 16 / b elements per 16-byte chunk.
+ *   - num_blocks x Hkv regions, row-major over (block, kv head); each region holds the
+ *     block_size (bs) token slots of one kv head: bs * D elements, contiguous.
+ *   - A region is bs/16 sub-tiles of 16 tokens (tokens 16u..16u+15 in sub-tile u), each
+ *     16*D elements, in order.  Inside a sub-tile, for token t (0..15) and dim d:
+ *         K element index  ((d / x) * 16 + t) * x + d % x
+ *         V element index  (((d / (4x)) * 4 + t / 4) * 16 + d % 16) * x
+ *                          + ((d / 16) % (x/4)) * 4 + t % 4
+ *     i.e. a K chunk holds x consecutive dims of one token, and a V chunk holds four
+ *     consecutive tokens for each of x/4 dims spaced 16 apart.  One wavefront load of
+ *     64 consecutive chunks then delivers exactly the operands of the gfx950 matrix
+ *     instructions the decode kernel issues, with no shuffles.
+ *   - A slot is  block * bs + offset  (offset < bs).
+ *   - Supported shapes: D in {64, 128}; bs in {16, 32}; D a multiple of 4x.
+ *
+ * Query / output layout: q and out are [num_seqs, Hq, D] row-major.  Query head h reads
+ * kv head h / G with G = Hq / Hkv (contiguous groups; G = 1 is multi-head attention).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_INVALID_ARG = 1,   /* a pointer, size or shape is invalid */
+  PKV_UNSUPPORTED = 2,   /* valid but not implemented (dtype combination, D, bs, G) */
+  PKV_OUT_OF_BLOCKS = 3, /* the allocator cannot meet the request; state unchanged */
+  PKV_UNKNOWN_SEQ = 4,   /* the allocator has no sequence with that id */
+  PKV_HIP_ERROR = 5      /* the HIP runtime reported an error */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3FN = 2
+} pkv_dtype;
+
+/* ABI version (PKV_ABI_VERSION of the built library). */
+int pkv_abi_version(void);
+
+/* Thread-local message describing the last non-OK status on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * Decode attention
+ *
+ * One query token per sequence: for sequence s, query head h (kv head g = h / G),
+ *     out[s,h,:] = sum_t w_t V_s[t,g,:] / sum_t w_t,
+ *     w_t = exp(scale * k_scale * <q[s,h,:], Kcode_s[t,g,:]> - max),  t < context_lens[s]
+ * where K_s / V_s are the sequence's tokens in logical order: token t sits in slot
+ * block_tables[s][t / bs] * bs + t % bs.  V values are v_scale * Vcode.  For f32 and
+ * bf16 caches pass k_scale = v_scale = 1.  A sequence with context_lens[s] = 0 gets a
+ * zero output.  ("PagedAttention: Optimizing KV Cache in vLLM", grasp.study, §3: the
+ * block-aware kernel walks the blocks in logical order with a running softmax and
+ * equals contiguous attention.)
+ *
+ * Arguments
+ *   out             [num_seqs, Hq, D] of q_dtype (written).
+ *   q               [num_seqs, Hq, D] of q_dtype.
+ *   k_cache, v_cache  pools as laid out above, num_blocks blocks of kv_dtype.
+ *   block_tables    int32 [num_seqs, max_blocks_per_seq]; row s lists the physical
+ *                   blocks of sequence s in logical order; entries past
+ *                   ceil(context_lens[s] / bs) are never read (pad with -1).
+ *   context_lens    int32 [num_seqs], 0 <= context_lens[s] <= max_blocks_per_seq * bs
+ *                   (larger values are clamped to that bound).
+ *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
+ *   num_splits      number of equal shares the total (sequence, kv head, block) work is
+ *                   cut into, one per wavefront; 0 = one per wavefront slot the device
+ *                   can keep resident.  Results depend only on the split count, not on
+ *                   the physical block numbering.
+ *   workspace       device scratch of at least pkv_paged_attention_workspace_size()
+ *                   bytes, owned by the caller, no initial contents required; holds the
+ *                   partial (max, sum, accumulator) of every sequence head whose work
+ *                   spans more than one share.
+ * Preconditions (not checked on the device): block table entries of used blocks lie in
+ * [0, num_blocks) — an entry outside that range is read as a block of zeros, never out
+ * of bounds; out does not alias any input.
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                              int head_dim, int block_size, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int num_splits,
+                                              size_t* bytes /* host, out */);
+
+/* The split count used when num_splits = 0: one share per wavefront slot the current
+ * device keeps resident for this kernel variant (queried once per device and cached). */
+pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int* splits /* host, out */);
+
+/* Enqueues both phases below (split pass, then reduce) on `stream`. */
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int num_seqs,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int max_blocks_per_seq,
+                                      float scale, float k_scale, float v_scale,
+                                      pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase 1 alone: every wavefront streams its share of blocks with a running softmax;
+ * sequence heads that fit in one share are written to `out` finished, the others leave
+ * partials in `workspace`.  Same arguments as pkv_paged_attention_decode. */
+pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, int num_seqs,
+                                     int num_q_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int num_blocks, int max_blocks_per_seq,
+                                     float scale, float k_scale, float v_scale,
+                                     pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase 2 alone: merges the partials of split sequence heads (rescaling each by
+ * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow
+ * phase 1 on the same stream with identical arguments. */
+pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int num_seqs,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, int max_blocks_per_seq,
+                                      float scale, float k_scale, float v_scale,
+                                      pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",
+ * glossary, "How It Works: Map Logical to Physical Blocks": a decode step appends into
+ * the sequence's partly filled last block).
+ *
+ *   k_new, v_new   [T, Hkv, D] of in_dtype, row-major.
+ *   slot_mapping   int64 [T]; token n goes to slot slot_mapping[n]; a negative slot skips
+ *                  the token; a slot >= num_blocks * bs is skipped as well (never written
+ *                  out of bounds).
+ *   in_dtype/kv_dtype  (F32, F32) and (BF16, BF16) copy bits; (F32 or BF16, FP8_E4M3FN)
+ *                  quantise: code = round-to-nearest-even(clamp(x * (1/k_scale), +-448))
+ *                  with 1/k_scale rounded to float32 once on the host and one float32
+ *                  multiply per element (v_scale for V).  The result is bit-exact.
+ * Precondition: slots are distinct within one call (duplicates race).
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                              int head_dim, int block_size, int num_blocks, pkv_dtype in_dtype,
+                              pkv_dtype kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Block copy for copy-on-write ("PagedAttention: Optimizing KV Cache in vLLM", §4: the
+ * writer gets a private block holding the shared block's contents).
+ *
+ *   block_mapping  int32 [num_pairs][2] (device) of (src, dst) block ids; for each pair
+ *                  the whole block (all kv heads, all bs slots) of K and of V is copied.
+ *                  Pairs with an id outside [0, num_blocks) are skipped.
+ * Preconditions: dst blocks are distinct and no dst is also a src in the same call.  Enqueue
+ * before the pkv_kv_cache_write that writes into the copies (same stream).
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                           int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Host block allocator (host memory only; not thread-safe — callers serialise).
+ *
+ * Hands out physical block ids from a free list, counts references per block, shares
+ * blocks between sequences and decides copy-on-write ("What is PagedAttention?",
+ * glossary, "How It Works: Map Logical to Physical Blocks" and "Share Without Mutating
+ * State"; "PagedAttention: Optimizing KV Cache in vLLM", §4).  Every call that can fail
+ * is all-or-nothing: on any non-OK status the allocator state is exactly as before.
+ * Slots follow the pool convention slot = block * bs + offset.
+ * ------------------------------------------------------------------------------------ */
+typedef struct pkv_alloc pkv_alloc;
+
+/* Creates an allocator over blocks 0..num_blocks-1.  free_order (host, nullable, a
+ * permutation of 0..num_blocks-1) fixes the order in which free blocks are first handed
+ * out; NULL means ascending.  Returns NULL on invalid arguments (see pkv_last_error). */
+pkv_alloc* pkv_alloc_create(int num_blocks, int block_size, const int32_t* free_order);
+void pkv_alloc_destroy(pkv_alloc* a);
+
+/* Prefill: a new sequence with `length` tokens takes ceil(length / bs) blocks.
+ * slots_out (host, nullable) receives the `length` slots in token order. */
+pkv_status pkv_seq_create(pkv_alloc* a, int64_t seq_id, int64_t length, int64_t* slots_out);
+
+/* Sharing: `child` (new id) gets the parent's first ceil(prefix_len / bs) blocks, each
+ * block's reference count is incremented, nothing is copied; child length = prefix_len. */
+pkv_status pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child, int64_t prefix_len);
+
+/* Appends n tokens to one sequence.  slots_out (host, [n], nullable) gets their slots.
+ * If the sequence's last block is partly filled and shared (count > 1) a private copy is
+ * taken first: its (src, dst) pair goes to cow_out (host, [1][2], nullable) and
+ * *n_cow_out (nullable) is 1, else 0. */
+pkv_status pkv_seq_extend(pkv_alloc* a, int64_t seq_id, int64_t n, int64_t* slots_out,
+                          int32_t* cow_out, int* n_cow_out);
+
+/* Decode step: appends one token to each of n distinct sequences.  slots_out (host,
+ * [n]) gets one slot per sequence; every copy-on-write taken is written to cow_out
+ * (host, [n][2], (src, dst)) and counted in *n_cow_out.  Run pkv_copy_blocks on those
+ * pairs before pkv_kv_cache_write on the slots. */
+pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int n, int64_t* slots_out,
+                          int32_t* cow_out, int* n_cow_out);
+
+/* Releases a sequence; blocks whose reference count drops to zero return to the pool. */
+pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
+
+/* Writes block tables (host int32 [n][max_blocks], padded with -1) and lengths (host
+ * int32 [n], nullable) for the listed sequences. */
+pkv_status pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int n,
+                                  int max_blocks, int32_t* tables_out, int32_t* lens_out);
+
+/* Queries (host). */
+int pkv_alloc_num_free(const pkv_alloc* a);
+int pkv_alloc_num_blocks(const pkv_alloc* a);
+int pkv_alloc_block_size(const pkv_alloc* a);
+int pkv_alloc_refcount(const pkv_alloc* a, int block); /* -1 if out of range */
+int pkv_alloc_num_seqs(const pkv_alloc* a);
+pkv_status pkv_seq_info(const pkv_alloc* a, int64_t seq_id, int64_t* length_out,
+                        int* num_blocks_out);
+/* Copies the first `cap` free block ids (host) into ids_out and returns how many exist. */
+int pkv_alloc_free_list(const pkv_alloc* a, int32_t* ids_out, int cap);
+
+/* Slot mapping for whole sequences (host): for s in order and t < lens[s], writes
+ * tables[s][t / bs] * bs + t % bs to slots_out (host, [sum lens]).  Used to place the
+ * tokens of prefilled sequences whose tables were built elsewhere. */
+pkv_status pkv_build_slot_mapping(const int32_t* tables, const int32_t* lens, int num_seqs,
+                                  int max_blocks, int block_size, int64_t* slots_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

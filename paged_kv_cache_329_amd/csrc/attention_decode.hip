@@ -1,0 +1,739 @@
+// Paged decode attention for gfx950 (MI355X): split pass + merge pass.
+//
+// What is computed ("PagedAttention: Optimizing KV Cache in vLLM", grasp.study, §3
+// "Making it Work: The PagedAttention Kernel"): the kernel looks up each request's
+// block table, visits the physical blocks in logical order and folds them into a
+// running softmax, which yields exactly attention over a contiguous K/V layout.
+//
+// How it maps onto CDNA4
+//  * Work: the total work is the list of (sequence, kv head, block) triples in
+//    sequence-major order; it is cut into `splits` equal shares, one per wavefront, so
+//    a wave's cost does not depend on how skewed the context lengths are.  A share may
+//    end inside a (sequence, kv head) unit; such a unit leaves one partial
+//    (max, sum, accumulator) per share it touches, and the merge pass combines them with
+//    the same rescaling the running softmax uses.  Units that fit in one share are
+//    finished in the split pass.
+//  * Operands: a 16-token sub-tile of a (block, kv head) is one contiguous region; wave
+//    load i, lane l reads the 16-byte chunk 64*i + l.  The pool layout makes that chunk
+//    exactly lane l's operand of the gfx950 matrix instructions:
+//      QK:  S^T[16 tokens][16 heads] = K[16 x D] . Q^T[D x 16] (heads >= G are zero),
+//           A = K chunk (token l%16, dims of chunk 4i + l/16), B = the matching q dims.
+//      PV:  O^T[16 dims][16 heads] += V^T[16 x 16 tokens] . P^T[16 tokens x 16 heads],
+//           A = V chunk (4 tokens 4(l/16).. for dim l%16), B = the probabilities that
+//           lane l already holds from QK (C layout: token 4(l/16)+j, head l%16).
+//    So the softmax needs no data movement between the two products, and the per-head
+//    statistics live in the lanes of head l%16.  No LDS is used: every K/V byte is
+//    read by exactly one wave, straight into registers.
+//  * Running softmax (base 2): m = max(m, chunk max); rescale acc and sum by 2^(m_old-m);
+//    p = 2^(s - m).  The chunk max needs two cross-row shuffles (xor 16, xor 32).
+//  * Masking: tokens at or past the context length get s = -inf (select, so garbage or
+//    NaN in unused slots cannot leak), and their V elements are zeroed before the PV
+//    product.
+//  * Types: (q, kv) = (f32, f32) uses v_mfma_f32_16x16x4_f32; (bf16, bf16) uses
+//    v_mfma_f32_16x16x32_bf16 for QK and v_mfma_f32_16x16x16_bf16 for PV with p rounded
+//    to bf16; (bf16, e4m3fn) widens each fp8 pair to bf16 with
+//    v_cvt_scalef32_pk_bf16_fp8 (exact: every e4m3fn value is a bf16 value) and folds
+//    k_scale into the logit scale and v_scale into the final normalisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <mutex>
+#include <unordered_map>
+
+#include "status.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWavesPerWG = 4;
+constexpr int kMaxGroup = 16;
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;  // [splits*2][G][D]
+  float* ws_ml;   // [splits*2][G][2]  (max in log2 units, sum)
+  int B, Hkv, G, num_blocks, max_blocks, splits;
+  float qk_scale_log2;  // scale * k_scale * log2(e)
+  float v_scale;
+};
+
+template <int KV>
+struct KvTraits;
+template <>
+struct KvTraits<PKV_F32> {
+  static constexpr int EB = 4;   // bytes per cached element
+  static constexpr int QB = 4;   // bytes per q / out element
+};
+template <>
+struct KvTraits<PKV_BF16> {
+  static constexpr int EB = 2;
+  static constexpr int QB = 2;
+};
+template <>
+struct KvTraits<PKV_FP8_E4M3FN> {
+  static constexpr int EB = 1;
+  static constexpr int QB = 2;
+};
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Two e4m3fn codes (bytes 2*sel, 2*sel+1 of w) -> two bf16 in one dword, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_k16(uint32_t a_lo, uint32_t a_hi, uint32_t b_lo,
+                                               uint32_t b_hi, f32x4 c) {
+  const uint2 a = make_uint2(a_lo, a_hi), b = make_uint2(b_lo, b_hi);
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_rows(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float wave_sum_rows(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Blocks holding a sequence's tokens (length clamped to what its table row can hold).
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int bs) {
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : L;
+  const int64_t cap = int64_t(a.max_blocks) * bs;
+  if (L > cap) L = int(cap);
+  return (L + bs - 1) / bs;
+}
+
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int bs) {
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : L;
+  const int64_t cap = int64_t(a.max_blocks) * bs;
+  return L > cap ? int(cap) : L;
+}
+
+// Total work W = Hkv * sum_s blocks(s) (wave-uniform; the host checks it fits in int).
+__device__ int total_work(const DecodeArgs& a, int bs, int lane) {
+  int acc = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int s = base + lane;
+    acc += s < a.B ? seq_blocks(a, s, bs) : 0;
+  }
+  return wave_sum(acc) * a.Hkv;
+}
+
+// Sequence whose units contain work position x (0 <= x < W), and Hkv * blocks before it.
+__device__ void locate(const DecodeArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int s = b0 + lane;
+    const int w = s < a.B ? seq_blocks(a, s, bs) * a.Hkv : 0;
+    const int incl = wave_incl_scan(w, lane);
+    const int lo = base + (incl - w), hi = base + incl;
+    const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s_out = b0 + l;
+      off_out = base + __builtin_amdgcn_readlane(incl - w, l);
+      return;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  s_out = a.B;
+  off_out = base;
+}
+
+__device__ __forceinline__ int64_t share_begin(int64_t w, int64_t W, int64_t n) { return w * W / n; }
+
+// Index of the share holding work position x.
+__device__ __forceinline__ int64_t share_of(int64_t x, int64_t W, int64_t n) {
+  return ((x + 1) * n - 1) / W;
+}
+
+template <int KV, int D>
+struct Frag {
+  using T = KvTraits<KV>;
+  static constexpr int NLOAD = D * T::EB / 64;            // 16-byte chunks per lane per sub-tile
+  static constexpr int QCH = (16 / T::EB) * T::QB / 16;   // 16-byte q chunks per K chunk
+  static constexpr int NT = D / 16;                        // 16-dim output tiles
+};
+
+// S^T for one sub-tile: c[j] = <K[token 4(l/16)+j], Q[head l%16]>.
+template <int KV, int D>
+__device__ __forceinline__ f32x4 qk_subtile(const uint4* kf, const uint4* qf) {
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
+    if constexpr (KV == PKV_F32) {
+      c = mfma_f32_k4(__uint_as_float(kf[i].x), __uint_as_float(qf[i].x), c);
+      c = mfma_f32_k4(__uint_as_float(kf[i].y), __uint_as_float(qf[i].y), c);
+      c = mfma_f32_k4(__uint_as_float(kf[i].z), __uint_as_float(qf[i].z), c);
+      c = mfma_f32_k4(__uint_as_float(kf[i].w), __uint_as_float(qf[i].w), c);
+    } else if constexpr (KV == PKV_BF16) {
+      c = mfma_bf16_k32(kf[i], qf[i], c);
+    } else {
+      const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(kf[i].x), fp8x2_to_bf16x2<true>(kf[i].x),
+                                  fp8x2_to_bf16x2<false>(kf[i].y), fp8x2_to_bf16x2<true>(kf[i].y));
+      const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(kf[i].z), fp8x2_to_bf16x2<true>(kf[i].z),
+                                  fp8x2_to_bf16x2<false>(kf[i].w), fp8x2_to_bf16x2<true>(kf[i].w));
+      c = mfma_bf16_k32(lo, qf[2 * i + 0], c);
+      c = mfma_bf16_k32(hi, qf[2 * i + 1], c);
+    }
+  }
+  return c;
+}
+
+// acc[n] += V^T tile n . P^T, p[j] = probability of token 4(l/16)+j for head l%16.
+template <int KV, int D>
+__device__ __forceinline__ void pv_subtile(f32x4* acc, const uint4* vf, const float* p) {
+  if constexpr (KV == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
+      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].x), p[0], acc[i]);
+      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].y), p[1], acc[i]);
+      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].z), p[2], acc[i]);
+      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].w), p[3], acc[i]);
+    }
+  } else {
+    const uint32_t b_lo = pack_bf16x2(p[0], p[1]), b_hi = pack_bf16x2(p[2], p[3]);
+#pragma unroll
+    for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
+      if constexpr (KV == PKV_BF16) {
+        acc[2 * i + 0] = mfma_bf16_k16(vf[i].x, vf[i].y, b_lo, b_hi, acc[2 * i + 0]);
+        acc[2 * i + 1] = mfma_bf16_k16(vf[i].z, vf[i].w, b_lo, b_hi, acc[2 * i + 1]);
+      } else {
+        const uint32_t w[4] = {vf[i].x, vf[i].y, vf[i].z, vf[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[4 * i + e] = mfma_bf16_k16(fp8x2_to_bf16x2<false>(w[e]), fp8x2_to_bf16x2<true>(w[e]),
+                                         b_lo, b_hi, acc[4 * i + e]);
+      }
+    }
+  }
+}
+
+// Zero the V elements of tokens 4(l/16)+j that are not valid (vmask bit j clear).
+template <int KV, int D>
+__device__ __forceinline__ void mask_v(uint4* vf, uint32_t vmask) {
+  uint32_t m[4];
+  if constexpr (KV == PKV_F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = (vmask >> j) & 1u ? 0xFFFFFFFFu : 0u;
+  } else if constexpr (KV == PKV_BF16) {
+    const uint32_t m01 = ((vmask & 1u) ? 0x0000FFFFu : 0u) | ((vmask & 2u) ? 0xFFFF0000u : 0u);
+    const uint32_t m23 = ((vmask & 4u) ? 0x0000FFFFu : 0u) | ((vmask & 8u) ? 0xFFFF0000u : 0u);
+    m[0] = m01; m[1] = m23; m[2] = m01; m[3] = m23;
+  } else {
+    uint32_t b = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b |= ((vmask >> j) & 1u) ? (0xFFu << (8 * j)) : 0u;
+    m[0] = m[1] = m[2] = m[3] = b;
+  }
+#pragma unroll
+  for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
+    vf[i].x &= m[0]; vf[i].y &= m[1]; vf[i].z &= m[2]; vf[i].w &= m[3];
+  }
+}
+
+template <int KV, int D, int BS, int NSUB>
+__global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArgs a) {
+  using F = Frag<KV, D>;
+  using T = KvTraits<KV>;
+  constexpr int X = 16 / T::EB;                  // cached elements per 16-byte chunk
+  constexpr int SUB_BYTES = 16 * D * T::EB;       // one 16-token sub-tile
+  constexpr int NSB = BS / 16;                    // sub-tiles per block
+  constexpr int64_t REGION = int64_t(BS) * D * T::EB;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWavesPerWG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = total_work(a, BS, lane);
+  if (W == 0) return;
+  const int nshare = std::min(a.splits, W);
+  if (wave >= nshare) return;
+  const int c_begin = int(share_begin(wave, W, nshare));
+  const int c_end = int(share_begin(wave + 1, W, nshare));
+
+  int s, seq_off;
+  locate(a, BS, lane, c_begin, s, seq_off);
+  if (s >= a.B) return;
+  int L = seq_len(a, s, BS);
+  int nb = (L + BS - 1) / BS;
+  int g = (c_begin - seq_off) / nb;
+  int unit_off = seq_off + g * nb;
+  int pos = c_begin;
+
+  const int h = lane & 15;       // head (within the group) of this lane's QK/PV column
+  const int row = lane >> 4;     // token group 4*row.. of this lane's QK/PV rows
+  const bool head_ok = h < a.G;
+
+  while (pos < c_end) {
+    const int unit_end = unit_off + nb;
+    const int seg_end = std::min(c_end, unit_end);
+    const bool full = pos == unit_off && seg_end == unit_end;
+    const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
+    const int k0 = j0 * NSB;
+    const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
+
+    // q fragments of (s, g): lane (h, row) holds q[s, g*G+h, X*(4i+row) .. +X].
+    uint4 qf[F::NLOAD * F::QCH];
+    {
+      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                            (int64_t(s) * a.Hkv * a.G + int64_t(g) * a.G + h) * D * T::QB;
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+        for (int c = 0; c < F::QCH; ++c)
+          qf[i * F::QCH + c] = head_ok ? *reinterpret_cast<const uint4*>(
+                                             qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * c)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    f32x4 acc[F::NT];
+#pragma unroll
+    for (int n = 0; n < F::NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+    int tbase = INT32_MIN / 2;
+    int tbl = -1;
+    const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
+    const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
+    const int64_t block_stride = int64_t(a.Hkv) * REGION;
+
+    for (int k = k0; k < k1; k += NSUB) {
+      const int cnt = std::min(NSUB, k1 - k);
+      const int jlast = (k + cnt - 1) / NSB;
+      if (k / NSB < tbase || jlast >= tbase + 64) {
+        tbase = k / NSB;
+        const int jj = tbase + lane;
+        tbl = jj < nb ? trow[jj] : -1;
+      }
+      // Issue every K load of the chunk, then every V load, with no branches between
+      // them, so QK can start while V is still in flight.  Sub-tiles past the chunk's
+      // end re-read its first sub-tile (a cache hit, never used).  A table entry outside
+      // [0, num_blocks) reads block 0 instead and its keys and values are replaced by
+      // zeros where they are used.
+      uint4 kf[NSUB][F::NLOAD], vf[NSUB][F::NLOAD];
+      int64_t off[NSUB];
+      bool bad[NSUB];
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        const int ku = u < cnt ? k + u : k;
+        const int phys = __builtin_amdgcn_readlane(tbl, (ku / NSB - tbase) & 63);
+        bad[u] = unsigned(phys) >= unsigned(a.num_blocks);
+        off[u] = (bad[u] ? 0 : int64_t(phys) * block_stride) + (ku % NSB) * SUB_BYTES + lane * 16;
+      }
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int i = 0; i < F::NLOAD; ++i)
+          kf[u][i] = *reinterpret_cast<const uint4*>(kbase + off[u] + i * 1024);
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u)
+#pragma unroll
+        for (int i = 0; i < F::NLOAD; ++i)
+          vf[u][i] = *reinterpret_cast<const uint4*>(vbase + off[u] + i * 1024);
+
+      float sc[NSUB][4];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        const int tok0 = (k + u) * 16 + 4 * row;
+        if (u < cnt) {
+          const f32x4 c = bad[u] ? f32x4{0.f, 0.f, 0.f, 0.f} : qk_subtile<KV, D>(kf[u], qf);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sc[u][j] = tok0 + j < L ? c[j] * a.qk_scale_log2 : -INFINITY;
+            cmax = fmaxf(cmax, sc[u][j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[u][j] = -INFINITY;
+        }
+      }
+      cmax = wave_max_rows(cmax);
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < F::NT; ++n) acc[n] *= alpha;
+#pragma unroll
+      for (int u = 0; u < NSUB; ++u) {
+        if (u < cnt) {
+          const int tok0 = (k + u) * 16 + 4 * row;
+          float p[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(sc[u][j] - m_new);
+            l_run += p[j];
+          }
+          uint32_t vm = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vm |= (tok0 + j < L && !bad[u] ? 1u : 0u) << j;
+          mask_v<KV, D>(vf[u], vm);
+          pv_subtile<KV, D>(acc, vf[u], p);
+        }
+      }
+    }
+
+    const float l_tot = wave_sum_rows(l_run);
+    if (full) {
+      if (head_ok) {
+        const float inv = a.v_scale / l_tot;
+        const int64_t orow = (int64_t(s) * a.Hkv * a.G + int64_t(g) * a.G + h) * D;
+#pragma unroll
+        for (int n = 0; n < F::NT; ++n) {
+          const int d = 16 * n + 4 * row;
+          if constexpr (KV == PKV_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) =
+                make_float4(acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) =
+                make_uint2(pack_bf16x2(acc[n][0] * inv, acc[n][1] * inv),
+                           pack_bf16x2(acc[n][2] * inv, acc[n][3] * inv));
+          }
+        }
+      }
+    } else {
+      const int slot = pos == c_begin ? 0 : 1;
+      const int64_t piece = int64_t(wave) * 2 + slot;
+      if (head_ok) {
+        float* wacc = a.ws_acc + (piece * a.G + h) * D;
+#pragma unroll
+        for (int n = 0; n < F::NT; ++n)
+          *reinterpret_cast<float4*>(wacc + 16 * n + 4 * row) =
+              make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+        if (row == 0)
+          *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = make_float2(m_run, l_tot);
+      }
+    }
+
+    pos = seg_end;
+    if (pos >= c_end) break;
+    // Next unit: next kv head of this sequence, else the next non-empty sequence.
+    unit_off = unit_end;
+    if (++g == a.Hkv) {
+      g = 0;
+      do {
+        if (++s >= a.B) return;
+        L = seq_len(a, s, BS);
+      } while (L == 0);
+      nb = (L + BS - 1) / BS;
+    }
+  }
+}
+
+// One wave per (kv head, sequence): merges the partials of a unit that spans several
+// shares, or writes zeros for an empty sequence.
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x, s = blockIdx.y;
+  // Hkv * blocks before sequence s, and the total.
+  int before = 0, all = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int ss = b0 + lane;
+    const int w = ss < a.B ? seq_blocks(a, ss, BS) : 0;
+    before += ss < s ? w : 0;
+    all += w;
+  }
+  before = wave_sum(before) * a.Hkv;
+  const int W = wave_sum(all) * a.Hkv;
+  const int nb = seq_blocks(a, s, BS);
+  const int64_t orow0 = (int64_t(s) * a.Hkv + g) * a.G * D;
+  if (nb == 0) {
+    for (int i = lane; i < a.G * D; i += 64) {
+      if constexpr (KV == PKV_F32)
+        static_cast<float*>(a.out)[orow0 + i] = 0.f;
+      else
+        static_cast<uint16_t*>(a.out)[orow0 + i] = 0;
+    }
+    return;
+  }
+  const int nshare = std::min(a.splits, W);
+  const int off = before + g * nb;
+  const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
+  if (wf == wl) return;
+  constexpr int PER = D / 64;
+  for (int h = 0; h < a.G; ++h) {
+    float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) num[r] = 0.f;
+    for (int64_t w = wf; w <= wl; ++w) {
+      const int slot = (w == wf && off != share_begin(wf, W, nshare)) ? 1 : 0;
+      const int64_t piece = w * 2 + slot;
+      const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (piece * a.G + h) * 2);
+      const float Mn = fmaxf(M, ml.x);
+      const float ca = __builtin_amdgcn_exp2f(M - Mn), cb = __builtin_amdgcn_exp2f(ml.x - Mn);
+      den = den * ca + ml.y * cb;
+      const float* pacc = a.ws_acc + (piece * a.G + h) * D;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) num[r] = num[r] * ca + pacc[lane + 64 * r] * cb;
+      M = Mn;
+    }
+    const float inv = a.v_scale / den;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int64_t o = orow0 + int64_t(h) * D + lane + 64 * r;
+      if constexpr (KV == PKV_F32)
+        static_cast<float*>(a.out)[o] = num[r] * inv;
+      else
+        static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(num[r] * inv));
+    }
+  }
+}
+
+// ---- host side --------------------------------------------------------------------------
+
+constexpr int kNsub = 2;
+
+using KernelFn = void (*)(DecodeArgs);
+
+struct KernelPair {
+  KernelFn split;
+  KernelFn merge;
+};
+
+template <int KV, int D, int BS>
+KernelPair kernels_for() {
+  return {paged_attention_split_kernel<KV, D, BS, kNsub>, paged_attention_merge_kernel<KV, D, BS>};
+}
+
+bool pick_kernels(pkv_dtype kv, int D, int bs, KernelPair* kp) {
+#define PKV_CASE(KVT, DD, BB) \
+  if (kv == KVT && D == DD && bs == BB) { *kp = kernels_for<KVT, DD, BB>(); return true; }
+  PKV_CASE(PKV_F32, 64, 16) PKV_CASE(PKV_F32, 64, 32) PKV_CASE(PKV_F32, 128, 16) PKV_CASE(PKV_F32, 128, 32)
+  PKV_CASE(PKV_BF16, 64, 16) PKV_CASE(PKV_BF16, 64, 32) PKV_CASE(PKV_BF16, 128, 16) PKV_CASE(PKV_BF16, 128, 32)
+  PKV_CASE(PKV_FP8_E4M3FN, 64, 16) PKV_CASE(PKV_FP8_E4M3FN, 64, 32)
+  PKV_CASE(PKV_FP8_E4M3FN, 128, 16) PKV_CASE(PKV_FP8_E4M3FN, 128, 32)
+#undef PKV_CASE
+  return false;
+}
+
+// Wave slots the device keeps resident for the split kernel (cached per device/kernel).
+pkv_status resident_waves(KernelFn fn, int* waves) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "hipGetDevice failed");
+  const uint64_t key = (uint64_t(reinterpret_cast<uintptr_t>(fn)) << 8) ^ uint64_t(dev);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *waves = it->second;
+      return PKV_OK;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return pkv::fail(PKV_HIP_ERROR, "hipDeviceGetAttribute(multiprocessor count) failed");
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn),
+                                                   kWavesPerWG * 64, 0) != hipSuccess)
+    return pkv::fail(PKV_HIP_ERROR, "hipOccupancyMaxActiveBlocksPerMultiprocessor failed");
+  const int w = std::max(1, cus * std::max(1, per_cu) * kWavesPerWG);
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = w;
+  *waves = w;
+  return PKV_OK;
+}
+
+int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : t == PKV_BF16 ? 2 : t == PKV_FP8_E4M3FN ? 1 : 0; }
+
+pkv_status check_shape(const char* fn, int B, int Hq, int Hkv, int D, int bs, pkv_dtype qd,
+                       pkv_dtype kd) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_seqs=%d num_q_heads=%d num_kv_heads=%d", fn, B, Hq, Hkv);
+  if (Hq % Hkv != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_q_heads=%d not a multiple of num_kv_heads=%d", fn, Hq, Hkv);
+  if (Hq / Hkv > kMaxGroup)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: group size %d > %d", fn, Hq / Hkv, kMaxGroup);
+  const bool types_ok = (qd == PKV_F32 && kd == PKV_F32) || (qd == PKV_BF16 && kd == PKV_BF16) ||
+                        (qd == PKV_BF16 && kd == PKV_FP8_E4M3FN);
+  if (!types_ok) return pkv::fail(PKV_UNSUPPORTED, "%s: q_dtype=%d kv_dtype=%d", fn, int(qd), int(kd));
+  KernelPair kp;
+  if (!pick_kernels(kd, D, bs, &kp))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: head_dim=%d block_size=%d", fn, D, bs);
+  return PKV_OK;
+}
+
+pkv_status effective_splits(KernelFn split, int requested, int* splits) {
+  if (requested < 0) return pkv::fail(PKV_INVALID_ARG, "num_splits=%d must be >= 0", requested);
+  if (requested > 0) {
+    *splits = requested;
+    return PKV_OK;
+  }
+  return resident_waves(split, splits);
+}
+
+size_t workspace_bytes_for(int splits, int G, int D) {
+  const size_t acc = size_t(splits) * 2 * G * D * sizeof(float);
+  const size_t ml = size_t(splits) * 2 * G * 2 * sizeof(float);
+  return ((acc + 255) / 256) * 256 + ml;
+}
+
+enum Phase { kBoth, kSplitOnly, kMergeOnly };
+
+pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      int B, int Hq, int Hkv, int D, int bs, int num_blocks, int max_blocks,
+                      float scale, float k_scale, float v_scale, pkv_dtype qd, pkv_dtype kd,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
+  if (st != PKV_OK) return st;
+  if (num_blocks <= 0 || max_blocks < 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_blocks=%d max_blocks_per_seq=%d", fn, num_blocks, max_blocks);
+  if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
+      k_scale == INFINITY || v_scale == INFINITY)
+    return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks > 0 && !block_tables))
+    return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
+  KernelPair kp;
+  pick_kernels(kd, D, bs, &kp);
+  int splits = 0;
+  if ((st = effective_splits(kp.split, num_splits, &splits)) != PKV_OK) return st;
+  const int G = Hq / Hkv;
+  const size_t need = workspace_bytes_for(splits, G, D);
+  if (!workspace || workspace_bytes < need)
+    return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn,
+                     workspace_bytes, need);
+  if (int64_t(B) > 65535 || Hkv > 65535)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
+  if (int64_t(B) * max_blocks * Hkv > int64_t(INT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31", fn);
+
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                     ((size_t(splits) * 2 * G * D * sizeof(float) + 255) / 256) * 256);
+  a.B = B;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks;
+  a.splits = splits;
+  a.qk_scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (phase != kMergeOnly) {
+    const unsigned wgs = unsigned((int64_t(splits) + kWavesPerWG - 1) / kWavesPerWG);
+    hipLaunchKernelGGL(kp.split, dim3(wgs), dim3(kWavesPerWG * 64), 0, hs, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
+  }
+  if (phase != kSplitOnly) {
+    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv), unsigned(B)), dim3(64), 0, hs, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                              int head_dim, int block_size, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int num_splits, size_t* bytes) {
+  pkv_status st = check_shape("pkv_paged_attention_workspace_size", num_seqs, num_q_heads,
+                              num_kv_heads, head_dim, block_size, q_dtype, kv_dtype);
+  if (st != PKV_OK) return st;
+  if (!bytes) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_attention_workspace_size: null output");
+  KernelPair kp;
+  pick_kernels(kv_dtype, head_dim, block_size, &kp);
+  int splits = 0;
+  if ((st = effective_splits(kp.split, num_splits, &splits)) != PKV_OK) return st;
+  *bytes = workspace_bytes_for(splits, num_q_heads / num_kv_heads, head_dim);
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int* splits) {
+  pkv_status st = check_shape("pkv_paged_attention_default_splits", 1, 1, 1, head_dim, block_size,
+                              q_dtype, kv_dtype);
+  if (st != PKV_OK) return st;
+  if (!splits) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_attention_default_splits: null output");
+  KernelPair kp;
+  pick_kernels(kv_dtype, head_dim, block_size, &kp);
+  return resident_waves(kp.split, splits);
+}
+
+#define PKV_DECODE_PARAMS                                                                        \
+  void *out, const void *q, const void *k_cache, const void *v_cache,                           \
+      const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
+      int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
+      float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
+      int num_splits, void *workspace, size_t workspace_bytes, void *stream
+#define PKV_DECODE_ARGS                                                                          \
+  out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,    \
+      head_dim, block_size, num_blocks, max_blocks_per_seq, scale, k_scale, v_scale, q_dtype,   \
+      kv_dtype, num_splits, workspace, workspace_bytes, stream
+
+pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
+  return run_decode("pkv_paged_attention_decode", kBoth, PKV_DECODE_ARGS);
+}
+pkv_status pkv_paged_attention_split(PKV_DECODE_PARAMS) {
+  return run_decode("pkv_paged_attention_split", kSplitOnly, PKV_DECODE_ARGS);
+}
+pkv_status pkv_paged_attention_reduce(PKV_DECODE_PARAMS) {
+  return run_decode("pkv_paged_attention_reduce", kMergeOnly, PKV_DECODE_ARGS);
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""Paged decode attention on the GPU against the fp64 oracle.
+
+Sizes here finish in seconds on the oracle yet span several 16-token sub-tiles, several
+blocks and ragged tails, with unused slots and blocks poisoned with NaN.  Tolerances:
+fp32 max |d| <= 1e-5; bf16 and fp8 |d| <= 2e-2 + 1e-2 |ref| per element.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from synth import WORKLOADS, Workload, bf16_bits_from_f32, make_decode_case
+
+from gpu_helpers import as_f64, assert_close, decode, log, pack, raw_bytes, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "llama3_8b_bf16": WORKLOADS["llama3_8b_bf16"].scaled(batch=6, length_dist=("uniform", 1, 700)),
+    "long_ctx_splitk_bf16": WORKLOADS["long_ctx_splitk_bf16"].scaled(batch=2, length_dist=("uniform", 2000, 5000)),
+    "fp8_kv": WORKLOADS["fp8_kv"].scaled(batch=4, length_dist=("uniform", 1, 1500)),
+    # Other supported shapes: D 64 / bs 32 / G 2, G 16, f32 with D 128 and bs 32, fp8 with D 64.
+    "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 5, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 300)),
+    "bf16_g16": Workload("bf16_g16", 3, 32, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 400)),
+    "f32_d128_bs32_g4": Workload("f32_d128_bs32_g4", 3, 16, 4, 128, 32, "f32", "f32", ("uniform", 1, 300)),
+    "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 500)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_parity_small(name, seed):
+    require_gpu()
+    wl = SMALL[name]
+    case = make_decode_case(wl, seed)
+    log(f"parity {name} seed={seed} lengths={case.lengths.tolist()}")
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "long_ctx_splitk_bf16", "tiny_fp32", "fp8_kv"])
+def test_split_count_does_not_change_the_result(name):
+    require_gpu()
+    wl = SMALL[name]
+    case = make_decode_case(wl, 11)
+    k, v = pack(case)
+    ref = oatt.decode_case(case)
+    outs = []
+    for n in (1, 2, 7, 64, 1000, 0):
+        log(f"splits {name} num_splits={n}")
+        got = as_f64(decode(case, k, v, num_splits=n))
+        assert_close(got, ref, wl.kv_dtype, f"{name} splits={n}")
+        outs.append(got)
+    # One share per wave is exact arithmetic order per split count; different counts only
+    # regroup the running softmax, so they agree closely with each other too.
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < (1e-5 if wl.kv_dtype == "f32" else 3e-2)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
+def test_physical_block_permutation_is_bit_identical(name):
+    """The same logical K/V under a different physical numbering gives identical bits."""
+    require_gpu()
+    wl = SMALL[name]
+    case = make_decode_case(wl, 3)
+    k, v = pack(case)
+    base = decode(case, k, v)
+    rng = np.random.default_rng(99)
+    relabel = rng.permutation(case.num_blocks).astype(np.int32)
+    tables2 = np.where(case.block_tables >= 0, relabel[np.maximum(case.block_tables, 0)], -1).astype(np.int32)
+    k2, v2 = pack(case, tables=tables2)
+    other = decode(case, k2, v2, tables=tables2)
+    assert raw_bytes(base) == raw_bytes(other)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "tiny_fp32", "fp8_kv"])
+def test_empty_and_single_token_sequences(name):
+    require_gpu()
+    wl = SMALL[name].scaled(batch=6)
+    lengths = np.array([0, 1, 17, 0, 33, 1], dtype=np.int64)
+    case = make_decode_case(wl, 4, lengths=lengths)
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    ref = oatt.decode_case(case)
+    assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    assert_close(got, ref, wl.kv_dtype, name)
+    if wl.kv_dtype != "fp8_e4m3fn":
+        # One token: the output is that token's value exactly (weight 1, sum 1).
+        G = wl.group_size
+        for s in (1, 5):
+            vals = oatt.kv_to_f64(case.seq_v(s), wl.kv_dtype)[0]
+            for h in range(wl.num_q_heads):
+                assert np.array_equal(got[s, h], vals[h // G])
+
+
+def test_all_sequences_empty():
+    require_gpu()
+    wl = SMALL["llama3_8b_bf16"].scaled(batch=3)
+    case = make_decode_case(wl, 5, lengths=np.zeros(3, dtype=np.int64))
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    assert np.all(got == 0)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "long_ctx_splitk_bf16"])
+def test_large_logits(name):
+    """q scaled by 30: nearly one-hot softmax, no overflow, parity holds."""
+    require_gpu()
+    wl = SMALL[name]
+    case = make_decode_case(wl, 6)
+    qf = (case.q.astype(np.uint32) << 16).view(np.float32) * np.float32(30.0)
+    case.q = bf16_bits_from_f32(qf)
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
+
+
+def test_unpoisoned_pool_gives_the_same_bits():
+    require_gpu()
+    wl = SMALL["llama3_8b_bf16"]
+    case = make_decode_case(wl, 7)
+    k, v = pack(case, poison=True)
+    k0, v0 = pack(case, poison=False)
+    a = raw_bytes(decode(case, k, v))
+    b = raw_bytes(decode(case, k0, v0))
+    assert a == b

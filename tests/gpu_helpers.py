@@ -96,3 +96,62 @@ def assert_close(got: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""
     assert np.all(err <= bound), (f"{what}: max err {err.max():.3g} at {worst}: got {got[worst]:.6g} "
                                   f"ref {ref[worst]:.6g}")
     return float(err.max())
+
+
+def write_tokens(k_pool, v_pool, k_vals, v_vals, slots, storage, k_scale=1.0, v_scale=1.0):
+    """kv_cache_write of host values (float32 or bf16 bits) into host-given slots."""
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    if len(slots) == 0:
+        return
+    pkv.kv_cache_write(to_dev(k_vals, storage), to_dev(v_vals, storage), k_pool, v_pool,
+                       torch.from_numpy(slots).cuda(), k_scale=k_scale, v_scale=v_scale)
+
+
+ROOT_ID_BASE = 1 << 40
+
+
+def build_prefix_batch(case, poison=True):
+    """Prefill a PrefixStepCase through the library's allocator and kv_cache_write.
+
+    Every group's root prefix is a live sequence; member i is forked from its root over
+    min(L_i, prefix_len) tokens and extended by its private tokens.  Returns
+    (allocator, k_pool, v_pool, member ids).
+    """
+    wl = case.wl
+    a = pkv.BlockAllocator(case.num_blocks, wl.block_size, free_order=case.free_order)
+    k, v = pool_pair(wl, case.num_blocks, poison)
+    P = wl.prefix_len
+    for g in range(case.groups):
+        slots = a.seq_create(ROOT_ID_BASE + g, P)
+        write_tokens(k, v, case.root_k[g], case.root_v[g], slots, "bf16")
+    priv_slots = []
+    for i in range(wl.batch):
+        g = i // wl.prefix_group
+        L = int(case.lengths[i])
+        a.fork(ROOT_ID_BASE + g, i, min(L, P))
+        if L > P:
+            slots, cow = a.extend(i, L - P)
+            assert len(cow) == 0, "a block-aligned prefix never leaves a shared partial tail"
+            priv_slots.append(slots)
+    if priv_slots:
+        write_tokens(k, v, case.priv_k, case.priv_v, np.concatenate(priv_slots), "bf16")
+    return a, k, v, list(range(wl.batch))
+
+
+def prefix_step(case, a, k, v, members, num_splits=0):
+    """One continuous-batching step: append a token to every member (allocator), copy the
+    shared partial tails it reports (copy_blocks), write the new tokens (kv_cache_write),
+    then decode.  Returns (out, cow pairs, block tables, lengths)."""
+    wl = case.wl
+    slots, cows = a.append(members)
+    if len(cows):
+        pkv.copy_blocks(k, v, torch.from_numpy(np.ascontiguousarray(cows, np.int32)).cuda(), wl.head_dim)
+    write_tokens(k, v, case.new_k, case.new_v, slots, "bf16")
+    max_blocks = int(max(a.seq_info(m)[1] for m in members))
+    tables, lens = a.block_tables(members, max_blocks)
+    qd = to_dev(case.q, wl.q_dtype)
+    out = torch.empty_like(qd)
+    pkv.paged_attention_decode(out, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               case.scale, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, cows, tables, lens

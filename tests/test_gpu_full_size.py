@@ -1,0 +1,42 @@
+"""Decode parity at the full workload sizes, in the benchmark's launch configuration.
+
+The whole batch runs on the GPU with the default split count (one share per resident
+wavefront slot, as the benchmark launches it); the fp64 oracle checks a sample of
+sequences — the shortest, the longest and a few seeded picks — element by element, and
+every output must be finite.  Workloads:
+  * Llama-3-8B-shaped bf16 layer: 64 sequences, 32 q / 8 kv heads, D 128, bs 16,
+    lengths U{512..4096};
+  * long-context split-K bf16: 8 sequences, 64 q / 8 kv heads, lengths U{32768..131072};
+  * fp8 e4m3fn KV: 128 sequences, bs 32, lengths U{2048..16384}, per-tensor scales;
+  * tiny fp32: 4 sequences, D 64, pool of 64 blocks (checked in full).
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from synth import WORKLOADS, make_decode_case
+
+from gpu_helpers import as_f64, assert_close, decode, log, pack, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(lengths, rng, extra=3):
+    idx = {int(np.argmin(lengths)), int(np.argmax(lengths))}
+    idx.update(int(i) for i in rng.choice(len(lengths), size=min(extra, len(lengths)), replace=False))
+    return sorted(idx)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_bf16", "long_ctx_splitk_bf16", "fp8_kv"])
+def test_full_size_parity(name):
+    require_gpu()
+    wl = WORKLOADS[name]
+    case = make_decode_case(wl, 0)
+    log(f"full size {name}: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks")
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    assert np.all(np.isfinite(got))
+    seqs = list(range(wl.batch)) if wl.batch <= 8 and name == "tiny_fp32" else _sample(case.lengths, np.random.default_rng(1))
+    log(f"oracle on sequences {seqs}")
+    assert_close(got[seqs], oatt.decode_case(case, seqs), wl.kv_dtype, name)

@@ -1,0 +1,111 @@
+"""The continuous-batching step with prefix sharing on the GPU, against the fp64 oracle.
+
+Groups of sequences fork a live root prefix (shared, reference-counted blocks); each step
+appends one token per sequence.  A sequence whose last block is a shared partial block
+takes a private copy first (copy-on-write), so the step runs the allocator, copy_blocks,
+kv_cache_write and decode attention in that order, as in a serving loop.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_329_amd as pkv
+from oracle import attention as oatt
+from synth import WORKLOADS, make_prefix_step_case
+
+from gpu_helpers import (ROOT_ID_BASE, as_f64, assert_close, build_prefix_batch, log, pool_pair, prefix_step,
+                         raw_bytes, require_gpu, to_dev, write_tokens)
+
+pytestmark = pytest.mark.gpu
+
+FULL = WORKLOADS["cont_batch_prefix_bf16"]
+# 16 sequences in two groups sharing a 64-token prefix; lengths below, at and above it.
+SMALL = FULL.scaled(batch=16, prefix_len=64, length_dist=("lognormal", 60.0, 1.0, 400))
+
+
+def _expected_cow(case):
+    L, P, bs = case.lengths, case.wl.prefix_len, case.wl.block_size
+    return int(np.sum((L <= P) & (L % bs != 0)))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_step_parity_small(seed):
+    require_gpu()
+    case = make_prefix_step_case(SMALL, seed)
+    log(f"prefix step small seed={seed} lengths={case.lengths.tolist()}")
+    a, k, v, members = build_prefix_batch(case)
+    out, cows, _, lens = prefix_step(case, a, k, v, members)
+    assert len(cows) == _expected_cow(case)
+    assert np.array_equal(lens, case.lengths + 1)
+    assert_close(as_f64(out), oatt.prefix_step_case(case), "bf16", "prefix step")
+
+
+def test_copy_on_write_leaves_shared_blocks_untouched():
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 3)
+    a, k, v, members = build_prefix_batch(case)
+    before_k = k.view(torch.int16).cpu().numpy().copy()
+    before_v = v.view(torch.int16).cpu().numpy().copy()
+    out, cows, tables, _ = prefix_step(case, a, k, v, members)
+    assert len(cows) > 0
+    after_k = k.view(torch.int16).cpu().numpy()
+    after_v = v.view(torch.int16).cpu().numpy()
+    srcs = np.unique(cows[:, 0])
+    assert np.array_equal(after_k[srcs], before_k[srcs])
+    assert np.array_equal(after_v[srcs], before_v[srcs])
+    # Every root still reads its own prefix: the roots' blocks are untouched by the step.
+    root_tables, _ = a.block_tables([ROOT_ID_BASE + g for g in range(case.groups)],
+                                    (case.wl.prefix_len + 15) // 16)
+    roots = np.unique(root_tables)
+    assert np.array_equal(after_k[roots], before_k[roots])
+    # Copies are private: no destination is referenced by more than one sequence.
+    for dst in cows[:, 1]:
+        assert a.refcount(int(dst)) == 1
+
+
+def test_shared_prefix_equals_unshared_copies_bitwise():
+    """Shared-prefix tables and fully private copies of the same tokens give identical bits."""
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 4)
+    a, k, v, members = build_prefix_batch(case)
+    shared_out, _, _, lens = prefix_step(case, a, k, v, members)
+    # The same logical K/V, every sequence in blocks of its own.
+    wl = case.wl
+    need = int(sum((int(L) + wl.block_size - 1) // wl.block_size for L in lens))
+    b = pkv.BlockAllocator(need + 3, wl.block_size, free_order=np.random.default_rng(5).permutation(need + 3))
+    k2, v2 = pool_pair(wl, need + 3)
+    for i in members:
+        kk, vv = case.logical_kv(i)
+        slots = b.seq_create(i, len(kk))
+        write_tokens(k2, v2, kk, vv, slots, "bf16")
+    tables, lens2 = b.block_tables(members, int(max(b.seq_info(m)[1] for m in members)))
+    assert np.array_equal(lens2, lens)
+    qd = to_dev(case.q, wl.q_dtype)
+    out2 = torch.empty_like(qd)
+    pkv.paged_attention_decode(out2, qd, k2, v2, torch.from_numpy(tables).cuda(), torch.from_numpy(lens2).cuda(),
+                               case.scale)
+    torch.cuda.synchronize()
+    assert raw_bytes(shared_out) == raw_bytes(out2)
+
+
+@pytest.mark.timeout(600)
+def test_prefix_step_parity_full_size():
+    """256 sequences in groups of 8 sharing a 1024-token prefix, lognormal lengths (median
+    1000, capped at 8192), at the launch configuration the benchmark uses; the oracle checks
+    a sample of sequences covering copy-on-write tails, prefix-only and long private parts."""
+    require_gpu()
+    case = make_prefix_step_case(FULL, 0)
+    log(f"prefix step full size: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks")
+    a, k, v, members = build_prefix_batch(case)
+    out, cows, _, lens = prefix_step(case, a, k, v, members)
+    assert len(cows) == _expected_cow(case)
+    L = case.lengths
+    cow_seq = np.flatnonzero((L <= 1024) & (L % 16 != 0))
+    long_seq = np.argsort(L)[-3:]
+    short_seq = np.argsort(L)[:2]
+    aligned = np.flatnonzero(L % 16 == 0)
+    sample = sorted(set(cow_seq[:3].tolist() + long_seq.tolist() + short_seq.tolist() + aligned[:2].tolist()))
+    log(f"sampled sequences {sample}")
+    got = as_f64(out)[sample]
+    assert_close(got, oatt.prefix_step_case(case, sample), "bf16", "prefix step full size")
+    assert np.all(np.isfinite(as_f64(out)))

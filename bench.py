@@ -37,9 +37,33 @@ def _args():
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--num-splits", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                          "profiles", "traffic.json"))
+    p.add_argument("--traffic-json", default=None,
+                   help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="instead of the benchmark, time plain device-to-device copies of MIB MiB "
+                        "(the reference kernel for scaling the HBM byte counters)")
     return p.parse_args()
+
+
+def _copy_probe(mib: int, reps: int = 10):
+    """Plain copies of a known size: what FETCH_SIZE / WRITE_SIZE read for exactly `mib` MiB
+    read and written calibrates the counters of the attention kernels."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    us = statistics.median(a.elapsed_time(b) for a, b in ev) * 1e3
+    print(json.dumps({"probe": "device copy", "bytes_read": n, "bytes_written": n, "copies": reps,
+                      "median_us": round(us, 2), "copy_GBps_read_plus_write": round(2 * n / us / 1e3, 1)}),
+          flush=True)
 
 
 def _log(msg):
@@ -68,6 +92,10 @@ def main():
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        _copy_probe(args.copy_probe)
+        return
 
     import torch
     import paged_kv_cache_329_amd as pkv
@@ -161,10 +189,14 @@ def main():
     achieved = kv_bytes / (split_us * 1e-6) / 1e9
 
     traffic = None
+    traffic_json = args.traffic_json or os.path.join(
+        os.path.dirname(os.path.abspath(__file__)), "profiles",
+        f"paged_attention_split__{wl.name}__hbm_traffic.json")
     try:
-        with open(args.traffic_json) as f:
-            tj = json.load(f).get(wl.name)
-        if tj and tj.get("kernel_source_sha") == _kernel_sha():
+        with open(traffic_json) as f:
+            tj = json.load(f)
+        # Counters taken on another version of the kernel source say nothing about this one.
+        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
             traffic = tj.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         traffic = None
@@ -202,7 +234,9 @@ def main():
         "host_metadata_us": round(host_meta_us, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "paged_attention_split_kernel"},
+                     "traffic_unit": "HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, "
+                                     "scaled by a plain copy of known size)",
+                     "algorithmic_bytes": kv_bytes, "kernel": "paged_attention_split_kernel"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -1,8 +1,9 @@
 """Benchmark of the paged decode-attention hot path on one MI355X.
 
-One step = one decode layer's attention step over a whole synthetic batch:
-  kv_cache_write of each sequence's current token (its K/V rewritten into its slot),
-  then the split pass of paged decode attention, then the merge pass.
+One step = one decode layer's attention step over a whole synthetic batch: every sequence
+appends its current token (the KV-cache write of its K/V into its slot, fused into the split
+pass of paged decode attention, which attends over the whole context including it), then the
+merge pass.
 The step reads every valid K/V byte of the batch once.  Steps rotate over --layers
 separate pools (the same block tables, as the layers of one model would use), so no
 pool is re-read before the others have streamed through; with 4 layers of the Llama-3-8B
@@ -10,7 +11,9 @@ batch that is ~2.6 GB between two reads of one pool, ten times the 256 MB MALL.
 
 Printed on stdout: one JSON line.  value = KV GB/s of the whole step (algorithmic KV bytes
 of valid tokens, sum_s L_s * Hkv * D * 2 * bytes, divided by the wall time per step);
-roofline = the split kernel alone, timed with HIP events on the launch stream.
+roofline = the split kernel alone, timed with a pair of HIP events around it on its launch
+stream in every fifth timed step (each event record costs step time, so the write and the
+merge are timed separately, after the timed region).
 """
 from __future__ import annotations
 
@@ -24,6 +27,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak (AMD public figure)
+EVENT_EVERY = 5          # timed steps per sampled split-kernel duration
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and µs/step, Llama-3-8B shape"
 
 
@@ -132,13 +136,16 @@ def main():
         v = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)
         pkv.kv_cache_write(k_tok, v_tok, k, v, slots_dev, k_scale=float(case.k_scale), v_scale=float(case.v_scale))
         pools.append((k, v))
-    # The step's new tokens: each sequence's last token, rewritten into its own slot.
+    # The step's new tokens: each sequence's last token, appended again at position L-1
+    # (its own slot) by every step.
     last = np.cumsum(case.lengths) - 1
     has = case.lengths > 0
-    new_idx = torch.from_numpy(last[has]).to(dev)
-    k_new = k_tok.index_select(0, new_idx).contiguous()
-    v_new = v_tok.index_select(0, new_idx).contiguous()
-    new_slots = torch.from_numpy(all_slots[last[has]]).to(dev)
+    rows = torch.from_numpy(np.flatnonzero(has)).to(dev)
+    src = torch.from_numpy(last[has]).to(dev)
+    k_new = torch.zeros((B, Hkv, D), dtype=k_tok.dtype, device=dev)
+    v_new = torch.zeros_like(k_new)
+    k_new[rows] = k_tok.index_select(0, src)
+    v_new[rows] = v_tok.index_select(0, src)
     del k_tok, v_tok, slots_dev
     q = dev_tensor(case.q, wl.q_dtype)
     out = torch.empty_like(q)
@@ -152,35 +159,49 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ks, vs = float(case.k_scale), float(case.v_scale)
 
-    def step(i, ev=None):
+    def step(i, ev=None, detail=False):
+        # One decode step: every sequence appends its token (stored into its slot by the
+        # split pass itself) and attends over its whole context; then the merge pass.
+        # ev: a (before, after) event pair around the split pass; detail adds an event
+        # after the merge (used only outside the timed region: every event record on the
+        # stream costs a few microseconds of step time).
         k, v = pools[i % len(pools)]
         if ev is not None:
             ev[0].record(stream)
-        pkv.kv_cache_write(k_new, v_new, k, v, new_slots, k_scale=ks, v_scale=vs)
+        pkv.paged_decode_step_split(out, q, k_new, v_new, k, v, tables, lens, case.scale, ks, vs,
+                                    args.num_splits, ws)
         if ev is not None:
             ev[1].record(stream)
-        pkv.paged_attention_split(out, q, k, v, tables, lens, case.scale, ks, vs, args.num_splits, ws)
-        if ev is not None:
-            ev[2].record(stream)
         pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, ks, vs, args.num_splits, ws)
-        if ev is not None:
-            ev[3].record(stream)
+        if detail:
+            ev[2].record(stream)
+
+    def new_events(n, per):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(n)]
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The split kernel is bracketed by events on every EVENT_EVERY-th timed step (5 is
+    # coprime with the 4 layer pools, so the sample visits every pool).
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    events = dict(zip(sampled, new_events(len(sampled), 2)))
     _log(f"[bench] warmup done; timing {args.steps} steps over {len(pools)} layer pools")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, events.get(i))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    write_us = statistics.mean(e[0].elapsed_time(e[1]) for e in events) * 1e3
-    split_us = statistics.mean(e[1].elapsed_time(e[2]) for e in events) * 1e3
-    merge_us = statistics.mean(e[2].elapsed_time(e[3]) for e in events) * 1e3
-    step_event_us = statistics.mean(e[0].elapsed_time(e[3]) for e in events) * 1e3
+    split_us = statistics.mean(e[0].elapsed_time(e[1]) for e in events.values()) * 1e3
+    # Per-kernel breakdown, outside the timed region.
+    n_detail = min(args.steps, 50)
+    detail = new_events(n_detail, 3)
+    for i in range(n_detail):
+        step(i, detail[i], detail=True)
+    torch.cuda.synchronize()
+    merge_us = statistics.mean(e[1].elapsed_time(e[2]) for e in detail) * 1e3
+    step_event_us = statistics.mean(e[0].elapsed_time(e[2]) for e in detail) * 1e3
 
     sum_l = int(case.lengths.sum())
     kv_bytes = sum_l * Hkv * D * 2 * eb
@@ -229,14 +250,15 @@ def main():
         "us_per_step": round(us_per_step, 2),
         "kv_bytes": kv_bytes,
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
-        "kernel_us": {"kv_cache_write": round(write_us, 2), "paged_attention_split": round(split_us, 2),
-                      "paged_attention_merge": round(merge_us, 2), "step_events": round(step_event_us, 2)},
+        "kernel_us": {"paged_attention_split(append)": round(split_us, 2),
+                      "detail_outside_timed_region": {"paged_attention_merge": round(merge_us, 2),
+                                                      "step_with_events": round(step_event_us, 2)}},
         "host_metadata_us": round(host_meta_us, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_unit": "HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, "
                                      "scaled by a plain copy of known size)",
-                     "algorithmic_bytes": kv_bytes, "kernel": "paged_attention_split_kernel"},
+                     "algorithmic_bytes": kv_bytes, "kernel": "paged_attention_split_kernel (decode step with append)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -163,6 +163,47 @@ pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_ca
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Decode step with append: the KV-cache write of each sequence's new token fused into the
+ * attention pass ("What is PagedAttention?", glossary, "How It Works: Map Logical to
+ * Physical Blocks": a decode step appends one token into the sequence's last block; then
+ * attention over all its tokens follows, as for pkv_paged_attention_decode).
+ *
+ * For every sequence s with L = context_lens[s] >= 1: the token at position L-1, in slot
+ * block_tables[s][(L-1)/bs] * bs + (L-1) % bs, receives k_new[s] and v_new[s] (stored
+ * exactly as pkv_kv_cache_write stores them: bit copies for f32 / bf16, the same
+ * quantisation for fp8), and out[s] is attention over tokens 0..L-1 including it.  The
+ * result equals pkv_kv_cache_write of those slots followed by pkv_paged_attention_decode.
+ *
+ *   k_new, v_new   [num_seqs, Hkv, D] of q_dtype (bf16 inputs for an fp8 cache); rows of
+ *                  sequences with L = 0 are ignored.
+ *   k_cache, v_cache  written (the appended slots only) and read.
+ *   Every other argument as for pkv_paged_attention_decode; the workspace is shared with
+ *   it and the default split count is the same.
+ * Precondition: the block receiving a sequence's token is referenced by no other sequence
+ * in the batch (the allocator's copy-on-write guarantees this); an appended slot in a
+ * block outside [0, num_blocks) is neither written nor read.
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_paged_decode_step(void* out, const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                 int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                 int max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                                 pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Phase 1 of the decode step alone (append + split pass); phase 2 is
+ * pkv_paged_attention_reduce with the same arguments and workspace. */
+pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_new,
+                                       const void* v_new, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_dim, int block_size, int num_blocks,
+                                       int max_blocks_per_seq, float scale, float k_scale,
+                                       float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                       int num_splits, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",
  * glossary, "How It Works: Map Logical to Physical Blocks": a decode step appends into
  * the sequence's partly filled last block).

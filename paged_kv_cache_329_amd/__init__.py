@@ -25,7 +25,8 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3FN",
     "allocate_kv_pool", "paged_attention_workspace_size", "paged_attention_default_splits",
     "paged_attention_decode",
-    "paged_attention_split", "paged_attention_reduce", "kv_cache_write", "copy_blocks",
+    "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
+    "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version",
 ]
 
@@ -48,6 +49,7 @@ _lock = threading.Lock()
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _DECODE_ARGS = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                 _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_p]
+_STEP_ARGS = [_c_p] * 8 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p]
 _SIGNATURES = {
     "pkv_abi_version": ([], _c_int),
     "pkv_last_error": ([], ctypes.c_char_p),
@@ -56,6 +58,8 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_split": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
+    "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
+    "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
@@ -237,6 +241,51 @@ def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens,
     """Phase 2 only (merges partials); same arguments and workspace as phase 1."""
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
                         context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+               k_scale, v_scale, num_splits, workspace, stream):
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    B, Hq, D = q.shape
+    NB, Hkv, bs = _pool_dims(k_cache, D)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    if k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim] of q's dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    qd, kd = _dtype_code(q.dtype), _dtype_code(k_cache.dtype)
+    st = _stream(stream)
+    if workspace is None:
+        nbytes = paged_attention_workspace_size(B, Hq, Hkv, D, bs, qd, kd, num_splits)
+        workspace = _workspace(nbytes, q.device, st)
+    ptrs = [_dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+            _dev(context_lens, "context_lens")]
+    _check(getattr(lib(), fn_name)(*ptrs, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                                   float(scale), float(k_scale), float(v_scale), qd, kd,
+                                   int(num_splits), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), st))
+    return out
+
+
+def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                      k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """Decode step with append (pkv_paged_decode_step): stores every sequence's new token
+    (k_new / v_new [num_seqs, Hkv, D], q's dtype) at position context_lens[s] - 1, then
+    attends over all context_lens[s] tokens; the store is fused into the split pass."""
+    return _step_call("pkv_paged_decode_step", out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def paged_decode_step_split(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                            k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """Phase 1 of the decode step (append + split pass); phase 2 is paged_attention_reduce."""
+    return _step_call("pkv_paged_decode_step_split", out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
 
 
 def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0,

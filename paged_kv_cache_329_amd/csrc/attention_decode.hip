@@ -41,6 +41,7 @@
 #include <mutex>
 #include <unordered_map>
 
+#include "kv_codec.h"
 #include "status.h"
 
 namespace {
@@ -54,6 +55,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWavesPerWG = 4;
 constexpr int kMaxGroup = 16;
+constexpr int kMergeWaves = 2;  // waves per merge workgroup
 
 struct DecodeArgs {
   void* out;
@@ -67,6 +69,13 @@ struct DecodeArgs {
   int B, Hkv, G, num_blocks, max_blocks, splits;
   float qk_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
+  // Decode step with append: each sequence's token at position L-1 is taken from
+  // k_new / v_new ([B][Hkv][D], q's dtype) and stored into its slot.
+  const void* k_new;
+  const void* v_new;
+  uint8_t* k_cache_w;
+  uint8_t* v_cache_w;
+  float k_inv, v_inv;  // float32 1/k_scale, 1/v_scale (fp8 caches)
 };
 
 template <int KV>
@@ -292,7 +301,154 @@ __device__ __forceinline__ void mask_v(uint4* vf, uint32_t vmask) {
   }
 }
 
-template <int KV, int D, int BS, int NSUB>
+
+// Stores the appended token of unit (s, g) — row (s, g) of k_new / v_new, in q's dtype —
+// as token t of the 16-token sub-tile whose K and V regions start at ksub and vsub, in the
+// cache's element format (fp8 caches quantise exactly as the KV-cache write does).  Lane l
+// writes the parts of the chunks that its own loads of that sub-tile would read:
+//  K: lanes with lane % 16 == t write the chunk of load i, dims X*(4i + lane/16) .. +X;
+//  V: lanes with lane / 16 == t / 4 write element e*4 + t%4 of the chunk of load i, which
+//     holds dim i*4X + 16e + lane%16.
+template <int KV, int D>
+__device__ __forceinline__ void store_append_token(const DecodeArgs& a, int s, int g, int t, int lane,
+                                                   uint8_t* ksub, uint8_t* vsub) {
+  using F = Frag<KV, D>;
+  constexpr int EB = KvTraits<KV>::EB;
+  constexpr int X = 16 / EB;
+  const int64_t row = (int64_t(s) * a.Hkv + g) * D;
+  const int grp = lane >> 4, col = lane & 15;
+  // All loads first, then all stores: the compiler cannot move a load above a store to a
+  // pointer it might alias, so interleaving them would cost one round trip per pair.
+  uint4 kc[F::NLOAD];
+  uint32_t ve[F::NLOAD][X / 4];
+#pragma unroll
+  for (int i = 0; i < F::NLOAD; ++i) {
+    if constexpr (KV == PKV_F32) {
+      kc[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k_new) + row + X * (4 * i + grp));
+      ve[i][0] = __float_as_uint(static_cast<const float*>(a.v_new)[row + i * 4 * X + col]);
+    } else {
+      const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + row + X * (4 * i + grp);
+      if constexpr (KV == PKV_BF16) {
+        kc[i] = *reinterpret_cast<const uint4*>(kn);
+      } else {
+        const uint4 lo = *reinterpret_cast<const uint4*>(kn);
+        const uint4 hi = *reinterpret_cast<const uint4*>(kn + 8);
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        uint32_t q[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          q[e >> 2] |= pkv::e4m3fn_from_f32(pkv::bf16_bits_to_f32(b) * a.k_inv) << (8 * (e & 3));
+        }
+        kc[i] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
+#pragma unroll
+      for (int e = 0; e < X / 4; ++e) {
+        const uint32_t b = static_cast<const uint16_t*>(a.v_new)[row + i * 4 * X + 16 * e + col];
+        ve[i][e] = KV == PKV_BF16 ? b : pkv::e4m3fn_from_f32(pkv::bf16_bits_to_f32(b) * a.v_inv);
+      }
+    }
+  }
+  if (col == t) {
+#pragma unroll
+    for (int i = 0; i < F::NLOAD; ++i) *reinterpret_cast<uint4*>(ksub + (64 * i + lane) * 16) = kc[i];
+  }
+  if (grp == (t >> 2)) {
+#pragma unroll
+    for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+      for (int e = 0; e < X / 4; ++e) {
+        uint8_t* dst = vsub + (64 * i + lane) * 16 + (e * 4 + (t & 3)) * EB;
+        if constexpr (EB == 4)
+          *reinterpret_cast<uint32_t*>(dst) = ve[i][e];
+        else if constexpr (EB == 2)
+          *reinterpret_cast<uint16_t*>(dst) = uint16_t(ve[i][e]);
+        else
+          *dst = uint8_t(ve[i][e]);
+      }
+  }
+}
+
+// Decoded value of an e4m3fn code (exact, through bf16).
+__device__ __forceinline__ float e4m3fn_value(uint32_t code) {
+  return __uint_as_float(fp8x2_to_bf16x2<false>(code) << 16);
+}
+
+// The value the cache holds for input element x (q's dtype bits or float) of k_new / v_new:
+// f32 and bf16 are stored as given; fp8 stores RNE(clamp(x * inv)) and is read back as that
+// code's value (the per-tensor scale is applied outside, as for cached tokens).
+template <int KV>
+__device__ __forceinline__ float cached_value(float x, float inv) {
+  if constexpr (KV == PKV_FP8_E4M3FN) return e4m3fn_value(pkv::e4m3fn_from_f32(x * inv));
+  return x;
+}
+
+// Folds the appended token of unit (s, g) into the running softmax of head lane % 16:
+// logit from q (this lane's fragments qf, summed over the four lane rows) and k_new, then
+// m, the sum and the accumulators as for a cached token.  `zero` stands for an appended
+// slot in a block outside the pool, which reads as zeros.  The probability is rounded to
+// bf16 for the bf16 / fp8 accumulators, as the matrix path rounds it.
+template <int KV, int D>
+__device__ __forceinline__ void fold_append_token(const DecodeArgs& a, int s, int g, const uint4* qf,
+                                                  int lane, bool zero, float& m_run, float& l_run,
+                                                  f32x4* acc) {
+  using F = Frag<KV, D>;
+  constexpr int X = 16 / KvTraits<KV>::EB;
+  const int row = lane >> 4;
+  const int64_t nrow = (int64_t(s) * a.Hkv + g) * D;
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < F::NLOAD; ++i) {
+    const int d0 = X * (4 * i + row);
+    if constexpr (KV == PKV_F32) {
+      const float4 kv = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k_new) + nrow + d0);
+      dot += __uint_as_float(qf[i].x) * kv.x + __uint_as_float(qf[i].y) * kv.y +
+             __uint_as_float(qf[i].z) * kv.z + __uint_as_float(qf[i].w) * kv.w;
+    } else {
+      const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + nrow + d0;
+#pragma unroll
+      for (int c = 0; c < F::QCH; ++c) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kn + 8 * c);
+        const uint4 qw = qf[i * F::QCH + c];
+        const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, qq[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kx = pkv::bf16_bits_to_f32((kk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          const float qx = pkv::bf16_bits_to_f32((qq[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+          dot += qx * cached_value<KV>(kx, a.k_inv);
+        }
+      }
+    }
+  }
+  dot += __shfl_xor(dot, 16);
+  dot += __shfl_xor(dot, 32);
+  const float sc = zero ? 0.f : dot * a.qk_scale_log2;
+  const float m_new = fmaxf(m_run, sc);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  const float pr = __builtin_amdgcn_exp2f(sc - m_new);
+  l_run = l_run * alpha + (row == 0 ? pr : 0.f);
+  const float pm = zero ? 0.f : (KV == PKV_F32 ? pr : __uint_as_float(bf16_rne(pr) << 16));
+#pragma unroll
+  for (int n = 0; n < F::NT; ++n) {
+    const int d = 16 * n + 4 * row;
+    float v[4];
+    if constexpr (KV == PKV_F32) {
+      const float4 vv = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v_new) + nrow + d);
+      v[0] = vv.x; v[1] = vv.y; v[2] = vv.z; v[3] = vv.w;
+    } else {
+      const uint2 vw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v_new) + nrow + d);
+      v[0] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.x & 0xFFFFu), a.v_inv);
+      v[1] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.x >> 16), a.v_inv);
+      v[2] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.y & 0xFFFFu), a.v_inv);
+      v[3] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.y >> 16), a.v_inv);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[n][j] = acc[n][j] * alpha + pm * v[j];
+  }
+  m_run = m_new;
+}
+
+template <int KV, int D, int BS, int NSUB, bool APPEND>
 __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
@@ -323,13 +479,20 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   const int row = lane >> 4;     // token group 4*row.. of this lane's QK/PV rows
   const bool head_ok = h < a.G;
 
+  // With APPEND, token L-1 of every sequence is the appended one: the block walk masks its
+  // slot (Lc = L - 1 cached tokens are read), the segment holding it folds it in from
+  // k_new / v_new after the walk, and its stores into the pool are issued last (below the
+  // loop), because a store ahead of the remaining loads would delay them: loads and stores
+  // of a wave complete in issue order.
+  bool done = false;
   while (pos < c_end) {
+    const int Lc = APPEND ? L - 1 : L;
     const int unit_end = unit_off + nb;
     const int seg_end = std::min(c_end, unit_end);
     const bool full = pos == unit_off && seg_end == unit_end;
     const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
     const int k0 = j0 * NSB;
-    const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
+    const int k1 = (std::min(j1 * BS, Lc) + 15) / 16;                   // sub-tiles [k0, k1)
 
     // q fragments of (s, g): lane (h, row) holds q[s, g*G+h, X*(4i+row) .. +X].
     uint4 qf[F::NLOAD * F::QCH];
@@ -345,14 +508,16 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
                                        : make_uint4(0u, 0u, 0u, 0u);
     }
 
+    // The first window of block-table entries is requested together with q, so that both
+    // arrive in one round trip.
+    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+    int tbase = k0 / NSB;
+    int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
     f32x4 acc[F::NT];
 #pragma unroll
     for (int n = 0; n < F::NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-    int tbase = INT32_MIN / 2;
-    int tbl = -1;
     const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
     const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
     const int64_t block_stride = int64_t(a.Hkv) * REGION;
@@ -390,22 +555,26 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i)
           vf[u][i] = load_stream(vbase + off[u] + i * 1024);
-
+      // Everything below is branch-free on the loaded data: a branch around QK or PV
+      // would let the compiler sink the chunk loads into it and wait on them one by one.
+      // Sub-tiles past the chunk's end and out-of-range blocks are masked instead: their
+      // K chunks are zeroed (a block outside the pool reads as zeros), their scores are
+      // -inf past the context or the chunk, and their V elements are zeroed.
       float sc[NSUB][4];
       float cmax = -INFINITY;
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         const int tok0 = (k + u) * 16 + 4 * row;
-        if (u < cnt) {
-          const f32x4 c = bad[u] ? f32x4{0.f, 0.f, 0.f, 0.f} : qk_subtile<KV, D>(kf[u], qf);
+        const uint32_t km = bad[u] ? 0u : 0xFFFFFFFFu;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sc[u][j] = tok0 + j < L ? c[j] * a.qk_scale_log2 : -INFINITY;
-            cmax = fmaxf(cmax, sc[u][j]);
-          }
-        } else {
+        for (int i = 0; i < F::NLOAD; ++i) {
+          kf[u][i].x &= km; kf[u][i].y &= km; kf[u][i].z &= km; kf[u][i].w &= km;
+        }
+        const f32x4 c = qk_subtile<KV, D>(kf[u], qf);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sc[u][j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+          sc[u][j] = (u < cnt && tok0 + j < Lc) ? c[j] * a.qk_scale_log2 : -INFINITY;
+          cmax = fmaxf(cmax, sc[u][j]);
         }
       }
       cmax = wave_max_rows(cmax);
@@ -417,23 +586,27 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
       for (int n = 0; n < F::NT; ++n) acc[n] *= alpha;
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
-        if (u < cnt) {
-          const int tok0 = (k + u) * 16 + 4 * row;
-          float p[4];
+        const int tok0 = (k + u) * 16 + 4 * row;
+        float p[4];
+        uint32_t vm = 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(sc[u][j] - m_new);
-            l_run += p[j];
-          }
-          uint32_t vm = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vm |= (tok0 + j < L && !bad[u] ? 1u : 0u) << j;
-          mask_v<KV, D>(vf[u], vm);
-          pv_subtile<KV, D>(acc, vf[u], p);
+        for (int j = 0; j < 4; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(sc[u][j] - m_new);   // 0 where masked
+          l_run += p[j];
+          vm |= (u < cnt && tok0 + j < Lc && !bad[u] ? 1u : 0u) << j;
         }
+        mask_v<KV, D>(vf[u], vm);
+        pv_subtile<KV, D>(acc, vf[u], p);
       }
     }
 
+    if constexpr (APPEND) {
+      if (seg_end == unit_end) {
+        const int phys = trow[(L - 1) / BS];
+        fold_append_token<KV, D>(a, s, g, qf, lane, unsigned(phys) >= unsigned(a.num_blocks), m_run,
+                                 l_run, acc);
+      }
+    }
     const float l_tot = wave_sum_rows(l_run);
     if (full) {
       if (head_ok) {
@@ -473,26 +646,59 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     if (++g == a.Hkv) {
       g = 0;
       do {
-        if (++s >= a.B) return;
-        L = seq_len(a, s, BS);
-      } while (L == 0);
+        done = ++s >= a.B;
+      } while (!done && (L = seq_len(a, s, BS)) == 0);
+      if (done) break;
       nb = (L + BS - 1) / BS;
+    }
+  }
+
+  if constexpr (APPEND) {
+    // Store the appended token of every unit whose last block lies in this share.
+    locate(a, BS, lane, c_begin, s, seq_off);
+    L = seq_len(a, s, BS);
+    nb = (L + BS - 1) / BS;
+    g = (c_begin - seq_off) / nb;
+    for (unit_off = seq_off + g * nb; unit_off < c_end;) {
+      const int last = unit_off + nb - 1;   // the unit's last block, appended into
+      if (last >= c_begin && last < c_end) {
+        const int knew = (L - 1) / 16;
+        const int phys = a.block_tables[int64_t(s) * a.max_blocks + knew / NSB];
+        if (unsigned(phys) < unsigned(a.num_blocks)) {
+          const int64_t sub = int64_t(phys) * a.Hkv * REGION + int64_t(g) * REGION + (knew % NSB) * SUB_BYTES;
+          store_append_token<KV, D>(a, s, g, (L - 1) & 15, lane, a.k_cache_w + sub, a.v_cache_w + sub);
+        }
+      }
+      unit_off += nb;
+      if (++g == a.Hkv) {
+        g = 0;
+        do {
+          done = ++s >= a.B;
+        } while (!done && (L = seq_len(a, s, BS)) == 0);
+        if (done) break;
+        nb = (L + BS - 1) / BS;
+      }
     }
   }
 }
 
-// One workgroup per (kv head, sequence): merges the partials of a unit that spans several
-// shares, or writes zeros for an empty sequence.  Wave w handles heads w, w + 4, ...  The
-// loads are batched so that a unit's partials arrive in about two memory round trips: the
-// (max, sum) of up to 64 partials with one load per lane, then the accumulators eight
-// partials at a time, each scaled by 2^(m_p - max m) as in the running softmax.
+// One workgroup per (query head, sequence): merges the partials of a (sequence, kv head)
+// unit that spans several shares, or writes zeros for an empty sequence.  The unit's
+// partials are dealt round-robin to the workgroup's waves; each wave folds its partials in
+// batches of sixteen with the running-softmax rule (load a batch's (max, sum) and
+// accumulators together, raise the running max, rescale, add), so a batch costs one memory
+// round trip.  The waves' results are then combined through LDS the same way.  Two waves
+// per workgroup keep a whole batch of workgroups resident at once even for 128 sequences
+// x 32 heads, while a unit with ~100 partials (long contexts) needs only 3-4 batches.
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(256) void paged_attention_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void paged_attention_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;   // output dims per lane
-  constexpr int BATCH = 8;      // partial accumulators loaded together
+  constexpr int BATCH = 16;     // partials loaded together
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
+  __shared__ float s_acc[kMergeWaves][D];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.x, s = blockIdx.y;
+  const int g = blockIdx.x / a.G, h = blockIdx.x % a.G, s = blockIdx.y;
   // Hkv * blocks before sequence s, and the total.
   int before = 0, all = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
@@ -504,13 +710,13 @@ __global__ __launch_bounds__(256) void paged_attention_merge_kernel(DecodeArgs a
   before = wave_sum(before) * a.Hkv;
   const int W = wave_sum(all) * a.Hkv;
   const int nb = seq_blocks(a, s, BS);
-  const int64_t orow0 = (int64_t(s) * a.Hkv + g) * a.G * D;
+  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D;
   if (nb == 0) {
-    for (int i = threadIdx.x; i < a.G * D; i += kWavesPerWG * 64) {
+    for (int i = threadIdx.x; i < D; i += kMergeWaves * 64) {
       if constexpr (KV == PKV_F32)
-        static_cast<float*>(a.out)[orow0 + i] = 0.f;
+        static_cast<float*>(a.out)[orow + i] = 0.f;
       else
-        static_cast<uint16_t*>(a.out)[orow0 + i] = 0;
+        static_cast<uint16_t*>(a.out)[orow + i] = 0;
     }
     return;
   }
@@ -522,55 +728,69 @@ __global__ __launch_bounds__(256) void paged_attention_merge_kernel(DecodeArgs a
   // The unit's piece in share wf is that share's first segment (slot 0) only if the unit
   // begins exactly where the share does; in every later share it is the first segment.
   const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
-  auto piece = [&](int j) -> int64_t { return j == 0 ? piece0 : (wf + j) * 2; };
 
-  for (int h = wv; h < a.G; h += kWavesPerWG) {
-    float M = -INFINITY;
-    for (int j0 = 0; j0 < np; j0 += 64) {
-      const int j = j0 + lane;
-      if (j < np) M = fmaxf(M, a.ws_ml[(piece(j) * a.G + h) * 2]);
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) num[r] = 0.f;
+  for (int j0 = wv; j0 < np; j0 += kMergeWaves * BATCH) {
+    float2 ml[BATCH];
+    float x[BATCH][PER];
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      const int j = std::min(j0 + t * kMergeWaves, np - 1);
+      const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
+      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + (pc * a.G + h) * 2);
+      const float* pacc = a.ws_acc + (pc * a.G + h) * D + lane;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) x[t][r] = pacc[64 * r];
     }
+    float mb = M;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float den = 0.f, num[PER];
+    for (int t = 0; t < BATCH; ++t)
+      if (j0 + t * kMergeWaves < np) mb = fmaxf(mb, ml[t].x);
+    const float alpha = __builtin_amdgcn_exp2f(M - mb);
+    den *= alpha;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) num[r] = 0.f;
-    for (int j0 = 0; j0 < np; j0 += 64) {
-      const int j = j0 + lane;
-      float c = 0.f;
-      if (j < np) {
-        const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (piece(j) * a.G + h) * 2);
-        c = __builtin_amdgcn_exp2f(ml.x - M);
-        den += ml.y * c;
-      }
-      const int cnt = std::min(64, np - j0);
-      for (int t0 = 0; t0 < cnt; t0 += BATCH) {
-        float x[BATCH][PER];
+    for (int r = 0; r < PER; ++r) num[r] *= alpha;
 #pragma unroll
-        for (int t = 0; t < BATCH; ++t) {
-          const int jj = j0 + std::min(t0 + t, cnt - 1);
-          const float* pacc = a.ws_acc + (piece(jj) * a.G + h) * D + lane;
+    for (int t = 0; t < BATCH; ++t) {
+      const float c = j0 + t * kMergeWaves < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
+      den += ml[t].y * c;
 #pragma unroll
-          for (int r = 0; r < PER; ++r) x[t][r] = pacc[64 * r];
-        }
-#pragma unroll
-        for (int t = 0; t < BATCH; ++t) {
-          const float ct = t0 + t < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), (t0 + t) & 63)) : 0.f;
-#pragma unroll
-          for (int r = 0; r < PER; ++r) num[r] += x[t][r] * ct;
-        }
-      }
+      for (int r = 0; r < PER; ++r) num[r] += x[t][r] * c;
     }
+    M = mb;
+  }
+  if (lane == 0) {
+    s_m[wv] = M;
+    s_l[wv] = den;
+  }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
-    const float inv = a.v_scale / den;
+  for (int r = 0; r < PER; ++r) s_acc[wv][lane + 64 * r] = num[r];
+  __syncthreads();
+  if (wv == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, s_m[w]);
+    float dt = 0.f, nt[PER];
+#pragma unroll
+    for (int r = 0; r < PER; ++r) nt[r] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      // A wave with no partials holds M = -inf and zero sums; its weight is 0.
+      const float c = s_m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w] - Mt);
+      dt += s_l[w] * c;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) nt[r] += s_acc[w][lane + 64 * r] * c;
+    }
+    const float inv = a.v_scale / dt;
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int64_t o = orow0 + int64_t(h) * D + lane + 64 * r;
+      const int64_t o = orow + lane + 64 * r;
       if constexpr (KV == PKV_F32)
-        static_cast<float*>(a.out)[o] = num[r] * inv;
+        static_cast<float*>(a.out)[o] = nt[r] * inv;
       else
-        static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(num[r] * inv));
+        static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(nt[r] * inv));
     }
   }
 }
@@ -587,13 +807,15 @@ constexpr int subtiles_per_step() {
 using KernelFn = void (*)(DecodeArgs);
 
 struct KernelPair {
-  KernelFn split;
+  KernelFn split;         // plain decode
+  KernelFn split_append;  // decode step that stores each sequence's appended token first
   KernelFn merge;
 };
 
 template <int KV, int D, int BS>
 KernelPair kernels_for() {
-  return {paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>()>,
+  return {paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), false>,
+          paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), true>,
           paged_attention_merge_kernel<KV, D, BS>};
 }
 
@@ -655,13 +877,25 @@ pkv_status check_shape(const char* fn, int B, int Hq, int Hkv, int D, int bs, pk
   return PKV_OK;
 }
 
-pkv_status effective_splits(KernelFn split, int requested, int* splits) {
+// Default split count of a kernel variant: the resident wave slots of the plain and the
+// appending split kernels, whichever is fewer, so that both entry points (and the merge,
+// which recomputes the shares) agree on it.
+pkv_status default_splits(const KernelPair& kp, int* splits) {
+  int a = 0, b = 0;
+  pkv_status st = resident_waves(kp.split, &a);
+  if (st != PKV_OK) return st;
+  if ((st = resident_waves(kp.split_append, &b)) != PKV_OK) return st;
+  *splits = std::min(a, b);
+  return PKV_OK;
+}
+
+pkv_status effective_splits(const KernelPair& kp, int requested, int* splits) {
   if (requested < 0) return pkv::fail(PKV_INVALID_ARG, "num_splits=%d must be >= 0", requested);
   if (requested > 0) {
     *splits = requested;
     return PKV_OK;
   }
-  return resident_waves(split, splits);
+  return default_splits(kp, splits);
 }
 
 size_t workspace_bytes_for(int splits, int G, int D) {
@@ -672,11 +906,16 @@ size_t workspace_bytes_for(int splits, int G, int D) {
 
 enum Phase { kBoth, kSplitOnly, kMergeOnly };
 
-pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, const void* k_cache,
-                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                      int B, int Hq, int Hkv, int D, int bs, int num_blocks, int max_blocks,
-                      float scale, float k_scale, float v_scale, pkv_dtype qd, pkv_dtype kd,
-                      int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+// k_new / v_new non-null: the decode step with append (the split pass stores each
+// sequence's token at position L-1 from k_new / v_new into the writable caches).
+pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, const void* k_new,
+                      const void* v_new, const void* k_cache, const void* v_cache,
+                      void* k_cache_w, void* v_cache_w, const int32_t* block_tables,
+                      const int32_t* context_lens, int B, int Hq, int Hkv, int D, int bs,
+                      int num_blocks, int max_blocks, float scale, float k_scale, float v_scale,
+                      pkv_dtype qd, pkv_dtype kd, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const bool append = k_new != nullptr || v_new != nullptr;
   pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
   if (st != PKV_OK) return st;
   if (num_blocks <= 0 || max_blocks < 0)
@@ -687,10 +926,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks > 0 && !block_tables))
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
+  if (append && (!k_new || !v_new || !k_cache_w || !v_cache_w))
+    return pkv::fail(PKV_INVALID_ARG, "%s: k_new and v_new must both be given", fn);
   KernelPair kp;
   pick_kernels(kd, D, bs, &kp);
   int splits = 0;
-  if ((st = effective_splits(kp.split, num_splits, &splits)) != PKV_OK) return st;
+  if ((st = effective_splits(kp, num_splits, &splits)) != PKV_OK) return st;
   const int G = Hq / Hkv;
   const size_t need = workspace_bytes_for(splits, G, D);
   if (!workspace || workspace_bytes < need)
@@ -716,18 +957,26 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.G = G;
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
-  a.splits = splits;
+  // More shares than (sequence, kv head, block) triples would only launch idle waves; the
+  // table width bounds the triples without reading the device-side lengths.
+  a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * max_blocks)));
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache_w = static_cast<uint8_t*>(k_cache_w);
+  a.v_cache_w = static_cast<uint8_t*>(v_cache_w);
+  a.k_inv = 1.0f / k_scale;
+  a.v_inv = 1.0f / v_scale;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {
-    const unsigned wgs = unsigned((int64_t(splits) + kWavesPerWG - 1) / kWavesPerWG);
-    hipLaunchKernelGGL(kp.split, dim3(wgs), dim3(kWavesPerWG * 64), 0, hs, a);
+    const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
+    hipLaunchKernelGGL(append ? kp.split_append : kp.split, dim3(wgs), dim3(kWavesPerWG * 64), 0, hs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
   }
   if (phase != kSplitOnly) {
-    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv), unsigned(B)), dim3(kWavesPerWG * 64), 0, hs, a);
+    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv * G), unsigned(B)), dim3(kMergeWaves * 64), 0, hs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
   }
@@ -748,7 +997,7 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
   KernelPair kp;
   pick_kernels(kv_dtype, head_dim, block_size, &kp);
   int splits = 0;
-  if ((st = effective_splits(kp.split, num_splits, &splits)) != PKV_OK) return st;
+  if ((st = effective_splits(kp, num_splits, &splits)) != PKV_OK) return st;
   *bytes = workspace_bytes_for(splits, num_q_heads / num_kv_heads, head_dim);
   return PKV_OK;
 }
@@ -761,7 +1010,7 @@ pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_
   if (!splits) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_attention_default_splits: null output");
   KernelPair kp;
   pick_kernels(kv_dtype, head_dim, block_size, &kp);
-  return resident_waves(kp.split, splits);
+  return default_splits(kp, splits);
 }
 
 #define PKV_DECODE_PARAMS                                                                        \
@@ -771,9 +1020,9 @@ pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_
       float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
       int num_splits, void *workspace, size_t workspace_bytes, void *stream
 #define PKV_DECODE_ARGS                                                                          \
-  out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,    \
-      head_dim, block_size, num_blocks, max_blocks_per_seq, scale, k_scale, v_scale, q_dtype,   \
-      kv_dtype, num_splits, workspace, workspace_bytes, stream
+  out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,     \
+      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
+      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes, stream
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_decode", kBoth, PKV_DECODE_ARGS);
@@ -783,6 +1032,27 @@ pkv_status pkv_paged_attention_split(PKV_DECODE_PARAMS) {
 }
 pkv_status pkv_paged_attention_reduce(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_reduce", kMergeOnly, PKV_DECODE_ARGS);
+}
+
+#define PKV_STEP_PARAMS                                                                          \
+  void *out, const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache, \
+      const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
+      int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
+      float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
+      int num_splits, void *workspace, size_t workspace_bytes, void *stream
+#define PKV_STEP_ARGS                                                                            \
+  out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables, context_lens,         \
+      num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
+      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes, stream
+
+pkv_status pkv_paged_decode_step(PKV_STEP_PARAMS) {
+  if (!k_new || !v_new) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step: null k_new / v_new");
+  return run_decode("pkv_paged_decode_step", kBoth, PKV_STEP_ARGS);
+}
+pkv_status pkv_paged_decode_step_split(PKV_STEP_PARAMS) {
+  if (!k_new || !v_new)
+    return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step_split: null k_new / v_new");
+  return run_decode("pkv_paged_decode_step_split", kSplitOnly, PKV_STEP_ARGS);
 }
 
 }  // extern "C"

@@ -1,0 +1,146 @@
+"""The decode step with append (KV write fused into the attention pass) on the GPU.
+
+Each sequence's last token is withheld from the pool (its slot keeps the NaN poison) and
+handed to the step as k_new / v_new.  After the step:
+  * the output matches the fp64 oracle over all tokens, and matches kv_cache_write of those
+    tokens followed by plain decode (same split count) to within one rounding of the
+    output dtype: the step folds the new token's logit in from k_new with vector
+    arithmetic, the plain decode reads it back through the matrix cores, so the two sum in
+    different orders;
+  * the whole pool is bit-identical to the pool that kv_cache_write produces.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_329_amd as pkv
+from oracle import attention as oatt
+from synth import WORKLOADS, Workload, make_decode_case
+
+from gpu_helpers import (INT_VIEW, as_f64, assert_close, decode, kv_storage, log, pack, pool_pair,
+                         raw_bytes, require_gpu, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "llama3_8b_bf16": WORKLOADS["llama3_8b_bf16"].scaled(batch=6, length_dist=("uniform", 1, 700)),
+    "long_ctx_splitk_bf16": WORKLOADS["long_ctx_splitk_bf16"].scaled(batch=2, length_dist=("uniform", 2000, 5000)),
+    "fp8_kv": WORKLOADS["fp8_kv"].scaled(batch=4, length_dist=("uniform", 1, 1500)),
+    "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 5, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 300)),
+    "f32_d128_bs32_g4": Workload("f32_d128_bs32_g4", 3, 16, 4, 128, 32, "f32", "f32", ("uniform", 1, 300)),
+    "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 500)),
+}
+
+
+def _withheld(case):
+    """Pools holding every token but each sequence's last, and that last token as [B, Hkv, D]."""
+    wl = case.wl
+    k, v = pool_pair(wl, case.num_blocks, poison=True)
+    slots = pkv.build_slot_mapping(case.block_tables, case.lengths.astype(np.int32), wl.block_size)
+    last = case.offsets[1:] - 1
+    has = case.lengths > 0
+    slots[last[has]] = -1                     # skipped by kv_cache_write
+    st = kv_storage(wl)
+    if len(slots):
+        pkv.kv_cache_write(to_dev(case.k, st), to_dev(case.v, st), k, v, torch.from_numpy(slots).cuda(),
+                           k_scale=float(case.k_scale), v_scale=float(case.v_scale))
+    shape = (wl.batch, wl.num_kv_heads, wl.head_dim)
+    kn = np.zeros(shape, dtype=case.k.dtype)
+    vn = np.zeros(shape, dtype=case.v.dtype)
+    kn[has] = case.k[last[has]]
+    vn[has] = case.v[last[has]]
+    return k, v, to_dev(kn, wl.q_dtype), to_dev(vn, wl.q_dtype)
+
+
+def _step(case, k, v, kn, vn, num_splits=0, split_only=False):
+    wl = case.wl
+    q = to_dev(case.q, wl.q_dtype)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).cuda()
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
+    if split_only:
+        pkv.paged_decode_step_split(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
+                                    float(case.v_scale), num_splits=num_splits)
+        pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, float(case.k_scale),
+                                   float(case.v_scale), num_splits=num_splits)
+    else:
+        pkv.paged_decode_step(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
+                              float(case.v_scale), num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+def _pool_bytes(t):
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def _assert_same_up_to_rounding(got, ref, kv_dtype):
+    """Equal up to the rounding of the bf16 probabilities and outputs: the step applies the
+    new token's weight at another point of the running softmax, so its probabilities are
+    rounded to bf16 at another scale; in a short sequence that moves an output by a few
+    thousandths of the value scale, so the bound is absolute plus relative."""
+    a, b = as_f64(got), as_f64(ref)
+    bound = 1e-5 if kv_dtype == "f32" else 2.0 ** -6 * (1.0 + np.abs(b))
+    assert np.all(np.abs(a - b) <= bound), float(np.max(np.abs(a - b)))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_decode_step_matches_oracle_and_write_then_decode(name, seed):
+    require_gpu()
+    case = make_decode_case(CASES[name], seed)
+    log(f"decode step {name} seed={seed} lengths={case.lengths.tolist()}")
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn)
+    assert_close(as_f64(out), oatt.decode_case(case), case.wl.kv_dtype, name)
+    k_ref, v_ref = pack(case)                  # every token written by kv_cache_write
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k_ref))
+    assert np.array_equal(_pool_bytes(v), _pool_bytes(v_ref))
+    _assert_same_up_to_rounding(out, decode(case, k_ref, v_ref), case.wl.kv_dtype)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
+def test_decode_step_edge_lengths(name):
+    """Empty sequences, one token, and new tokens on the first / last slot of a sub-tile
+    and of a block."""
+    require_gpu()
+    wl = CASES[name].scaled(batch=9)
+    lengths = np.array([0, 1, 16, 17, 32, 33, 15, 31, 64], dtype=np.int64)
+    case = make_decode_case(wl, 5, lengths=lengths)
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn)
+    got = as_f64(out)
+    assert np.all(got[0] == 0)
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
+    k_ref, v_ref = pack(case)
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k_ref))
+    assert np.array_equal(_pool_bytes(v), _pool_bytes(v_ref))
+
+
+@pytest.mark.parametrize("n", [1, 7, 1000])
+def test_decode_step_phases_and_split_counts(n):
+    require_gpu()
+    case = make_decode_case(CASES["llama3_8b_bf16"], 8)
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn, num_splits=n, split_only=True)
+    k_ref, v_ref = pack(case)
+    _assert_same_up_to_rounding(out, decode(case, k_ref, v_ref, num_splits=n), "bf16")
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k_ref))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv"])
+def test_decode_step_full_size(name):
+    """Full workload sizes in the benchmark's launch configuration, sampled against the oracle."""
+    require_gpu()
+    case = make_decode_case(WORKLOADS[name], 0)
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn)
+    rng = np.random.default_rng(2)
+    seqs = sorted({int(np.argmin(case.lengths)), int(np.argmax(case.lengths)),
+                   *rng.choice(len(case.lengths), 3, replace=False).tolist()})
+    log(f"decode step full size {name}: oracle on {seqs}")
+    got = as_f64(out)
+    assert np.all(np.isfinite(got))
+    assert_close(got[seqs], oatt.decode_case(case, seqs), case.wl.kv_dtype, name)

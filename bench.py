@@ -11,9 +11,9 @@ batch that is ~2.6 GB between two reads of one pool, ten times the 256 MB MALL.
 
 Printed on stdout: one JSON line.  value = KV GB/s of the whole step (algorithmic KV bytes
 of valid tokens, sum_s L_s * Hkv * D * 2 * bytes, divided by the wall time per step);
-roofline = the split kernel alone, timed with a pair of HIP events around it on its launch
-stream in every fifth timed step (each event record costs step time, so the write and the
-merge are timed separately, after the timed region).
+roofline = the split kernel alone, timed in every fifth timed step by a pair of HIP events
+that its own dispatch records (hipExtLaunchKernel) on its launch stream; the merge is timed
+separately, after the timed region.
 """
 from __future__ import annotations
 
@@ -162,22 +162,26 @@ def main():
     def step(i, ev=None, detail=False):
         # One decode step: every sequence appends its token (stored into its slot by the
         # split pass itself) and attends over its whole context; then the merge pass.
-        # ev: a (before, after) event pair around the split pass; detail adds an event
-        # after the merge (used only outside the timed region: every event record on the
-        # stream costs a few microseconds of step time).
+        # ev: an event pair that the split kernel's own dispatch records at its start and
+        # end (pkv_set_launch_events), so it times the kernel alone and adds no packets to
+        # the stream; detail adds a stream event after the merge (used only outside the
+        # timed region).
         k, v = pools[i % len(pools)]
         if ev is not None:
-            ev[0].record(stream)
+            pkv.set_launch_events(ev[0], ev[1])
         pkv.paged_decode_step_split(out, q, k_new, v_new, k, v, tables, lens, case.scale, ks, vs,
                                     args.num_splits, ws)
-        if ev is not None:
-            ev[1].record(stream)
         pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, ks, vs, args.num_splits, ws)
         if detail:
             ev[2].record(stream)
 
     def new_events(n, per):
-        return [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(n)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(per)] for _ in range(n)]
+        for pair in evs:            # create them on the device before they are handed over
+            for e in pair:
+                e.record(stream)
+        torch.cuda.synchronize()
+        return evs
 
     for i in range(args.warmup):
         step(i)
@@ -200,7 +204,7 @@ def main():
     for i in range(n_detail):
         step(i, detail[i], detail=True)
     torch.cuda.synchronize()
-    merge_us = statistics.mean(e[1].elapsed_time(e[2]) for e in detail) * 1e3
+    merge_us = statistics.mean(e[1].elapsed_time(e[2]) for e in detail) * 1e3  # incl. the launch gap
     step_event_us = statistics.mean(e[0].elapsed_time(e[2]) for e in detail) * 1e3
 
     sum_l = int(case.lengths.sum())

@@ -203,6 +203,13 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
                                        int num_splits, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/* Measurement aid: the next split pass launched on the calling thread (by any attention or
+ * decode-step entry point) records start_event when its kernel begins and stop_event when
+ * it ends, as part of its own dispatch (hipExtLaunchKernel), so that the events time the
+ * kernel alone; the setting then clears.  start_event / stop_event are hipEvent_t handles
+ * created with timing enabled (either may be NULL).  Always returns PKV_OK. */
+pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",
  * glossary, "How It Works: Map Logical to Physical Blocks": a decode step appends into

@@ -27,7 +27,7 @@ __all__ = [
     "paged_attention_decode",
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
-    "build_slot_mapping", "BlockAllocator", "abi_version",
+    "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -59,6 +59,7 @@ _SIGNATURES = {
     "pkv_paged_attention_split": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
     "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
+    "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
@@ -286,6 +287,14 @@ def paged_decode_step_split(out, q, k_new, v_new, k_cache, v_cache, block_tables
     """Phase 1 of the decode step (append + split pass); phase 2 is paged_attention_reduce."""
     return _step_call("pkv_paged_decode_step_split", out, q, k_new, v_new, k_cache, v_cache, block_tables,
                       context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def set_launch_events(start, stop):
+    """The next split pass launched on this thread records these torch.cuda.Event objects
+    around its own kernel (pkv_set_launch_events).  The events must already exist on the
+    device: record each of them once beforehand."""
+    _check(lib().pkv_set_launch_events(start.cuda_event if start is not None else None,
+                                       stop.cuda_event if stop is not None else None))
 
 
 def kv_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0,

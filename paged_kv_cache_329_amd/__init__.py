@@ -375,23 +375,40 @@ class BlockAllocator:
                                     cow.ctypes.data, ctypes.byref(ncow)))
         return slots, cow[:ncow.value].copy()
 
-    def append(self, seq_ids):
+    def append(self, seq_ids, slots_out=None, cow_out=None):
+        """One token for each listed sequence -> (slots, copy-on-write pairs).
+
+        slots_out (int64 [n]) and cow_out (int32 [>= n, 2]), if given, are filled in place
+        (for example numpy views of pinned host tensors) and views of them are returned.
+        """
         ids = _np(seq_ids, np.int64)
         n = len(ids)
-        slots = np.empty(n, dtype=np.int64)
-        cow = np.empty((max(n, 1), 2), dtype=np.int32)
+        slots = np.empty(n, dtype=np.int64) if slots_out is None else slots_out
+        cow = np.empty((max(n, 1), 2), dtype=np.int32) if cow_out is None else cow_out
+        if slots.dtype != np.int64 or slots.shape[0] < n or not slots.flags.c_contiguous:
+            raise ValueError("slots_out must be a contiguous int64 array of at least n entries")
+        if cow.dtype != np.int32 or cow.shape[0] < max(n, 1) or not cow.flags.c_contiguous:
+            raise ValueError("cow_out must be a contiguous int32 [>= n, 2] array")
         ncow = ctypes.c_int(0)
         _check(lib().pkv_seq_append(self._h, ids.ctypes.data, n, slots.ctypes.data, cow.ctypes.data,
                                     ctypes.byref(ncow)))
-        return slots, cow[:ncow.value].copy()
+        if cow_out is None:
+            return slots, cow[:ncow.value].copy()
+        return slots[:n], cow[:ncow.value]
 
     def free(self, seq_id: int):
         _check(lib().pkv_seq_free(self._h, seq_id))
 
-    def block_tables(self, seq_ids, max_blocks: int):
+    def block_tables(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
+        """Block tables [n, max_blocks] (padded with -1) and lengths [n], int32; filled into
+        tables_out / lens_out when given (contiguous int32 arrays of those shapes)."""
         ids = _np(seq_ids, np.int64)
-        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
-        lens = np.empty(len(ids), dtype=np.int32)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32) if tables_out is None else tables_out
+        lens = np.empty(len(ids), dtype=np.int32) if lens_out is None else lens_out
+        if tables.dtype != np.int32 or tables.shape != (len(ids), max_blocks) or not tables.flags.c_contiguous:
+            raise ValueError("tables_out must be a contiguous int32 [n, max_blocks] array")
+        if lens.dtype != np.int32 or lens.shape != (len(ids),):
+            raise ValueError("lens_out must be an int32 [n] array")
         _check(lib().pkv_alloc_block_tables(self._h, ids.ctypes.data, len(ids), max_blocks,
                                             tables.ctypes.data, lens.ctypes.data))
         return tables, lens

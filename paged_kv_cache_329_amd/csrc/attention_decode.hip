@@ -56,7 +56,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWavesPerWG = 4;
 constexpr int kMaxGroup = 16;
-constexpr int kMergeWaves = 2;  // waves per merge workgroup
 
 struct DecodeArgs {
   void* out;
@@ -67,6 +66,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_acc;  // [splits*2][G][D]
   float* ws_ml;   // [splits*2][G][2]  (max in log2 units, sum)
+  int* ws_seq;    // [B+1]: Hkv * blocks of the sequences before s; [B] = total work W
   int B, Hkv, G, num_blocks, max_blocks, splits;
   float qk_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
@@ -461,6 +461,18 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWavesPerWG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = total_work(a, BS, lane);
+  if (wave == 0) {
+    // Work offset of every sequence, for the merge pass.
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int sq = b0 + lane;
+      const int w = sq < a.B ? seq_blocks(a, sq, BS) * a.Hkv : 0;
+      const int incl = wave_incl_scan(w, lane);
+      if (sq < a.B) a.ws_seq[sq] = base + incl - w;
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) a.ws_seq[a.B] = base;
+  }
   if (W == 0) return;
   const int nshare = std::min(a.splits, W);
   if (wave >= nshare) return;
@@ -683,41 +695,30 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   }
 }
 
-// One workgroup per (query head, sequence): merges the partials of a (sequence, kv head)
-// unit that spans several shares, or writes zeros for an empty sequence.  The unit's
-// partials are dealt round-robin to the workgroup's waves; each wave folds its partials in
-// batches of sixteen with the running-softmax rule (load a batch's (max, sum) and
-// accumulators together, raise the running max, rescale, add), so a batch costs one memory
-// round trip.  The waves' results are then combined through LDS the same way.  Two waves
-// per workgroup keep a whole batch of workgroups resident at once even for 128 sequences
-// x 32 heads, while a unit with ~100 partials (long contexts) needs only 3-4 batches.
+// One wave per (query head, sequence): merges the partials of a (sequence, kv head) unit
+// that spans several shares, or writes zeros for an empty sequence.  The unit's place in the
+// work list comes from the offsets the split pass left in the workspace.  Partials are
+// folded eight at a time with the running-softmax rule (load a batch's (max, sum) and
+// accumulators together, raise the running max, rescale, add), and the next batch's loads
+// are issued before the current batch is folded, so a unit with many partials (long
+// contexts) keeps two batches in flight.
 template <int KV, int D, int BS>
-__global__ __launch_bounds__(kMergeWaves * 64) void paged_attention_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;   // output dims per lane
-  constexpr int BATCH = 16;     // partials loaded together
-  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
-  __shared__ float s_acc[kMergeWaves][D];
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int BATCH = 8;      // partials per batch
+  const int lane = threadIdx.x;
   const int g = blockIdx.x / a.G, h = blockIdx.x % a.G, s = blockIdx.y;
-  // Hkv * blocks before sequence s, and the total.
-  int before = 0, all = 0;
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int ss = b0 + lane;
-    const int w = ss < a.B ? seq_blocks(a, ss, BS) : 0;
-    before += ss < s ? w : 0;
-    all += w;
-  }
-  before = wave_sum(before) * a.Hkv;
-  const int W = wave_sum(all) * a.Hkv;
-  const int nb = seq_blocks(a, s, BS);
+  const int before = a.ws_seq[s];
+  const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
+  const int W = a.ws_seq[a.B];
   const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D;
   if (nb == 0) {
-    for (int i = threadIdx.x; i < D; i += kMergeWaves * 64) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
       if constexpr (KV == PKV_F32)
-        static_cast<float*>(a.out)[orow + i] = 0.f;
+        static_cast<float*>(a.out)[orow + lane + 64 * r] = 0.f;
       else
-        static_cast<uint16_t*>(a.out)[orow + i] = 0;
+        static_cast<uint16_t*>(a.out)[orow + lane + 64 * r] = 0;
     }
     return;
   }
@@ -730,69 +731,56 @@ __global__ __launch_bounds__(kMergeWaves * 64) void paged_attention_merge_kernel
   // begins exactly where the share does; in every later share it is the first segment.
   const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
 
-  float M = -INFINITY, den = 0.f, num[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) num[r] = 0.f;
-  for (int j0 = wv; j0 < np; j0 += kMergeWaves * BATCH) {
-    float2 ml[BATCH];
-    float x[BATCH][PER];
+  auto load = [&](int j0, float2* ml, float (*x)[PER]) {
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
-      const int j = std::min(j0 + t * kMergeWaves, np - 1);
+      const int j = std::min(j0 + t, np - 1);
       const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
       ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + (pc * a.G + h) * 2);
       const float* pacc = a.ws_acc + (pc * a.G + h) * D + lane;
 #pragma unroll
       for (int r = 0; r < PER; ++r) x[t][r] = pacc[64 * r];
     }
+  };
+  float M = -INFINITY, den = 0.f, num[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) num[r] = 0.f;
+  auto fold = [&](int j0, const float2* ml, const float (*x)[PER]) {
     float mb = M;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t)
-      if (j0 + t * kMergeWaves < np) mb = fmaxf(mb, ml[t].x);
+      if (j0 + t < np) mb = fmaxf(mb, ml[t].x);
     const float alpha = __builtin_amdgcn_exp2f(M - mb);
     den *= alpha;
 #pragma unroll
     for (int r = 0; r < PER; ++r) num[r] *= alpha;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
-      const float c = j0 + t * kMergeWaves < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
+      const float c = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
       den += ml[t].y * c;
 #pragma unroll
       for (int r = 0; r < PER; ++r) num[r] += x[t][r] * c;
     }
     M = mb;
+  };
+  float2 mlA[BATCH], mlB[BATCH];
+  float xA[BATCH][PER], xB[BATCH][PER];
+  load(0, mlA, xA);
+  for (int j0 = 0; j0 < np; j0 += 2 * BATCH) {
+    if (j0 + BATCH < np) load(j0 + BATCH, mlB, xB);
+    fold(j0, mlA, xA);
+    if (j0 + BATCH >= np) break;
+    if (j0 + 2 * BATCH < np) load(j0 + 2 * BATCH, mlA, xA);
+    fold(j0 + BATCH, mlB, xB);
   }
-  if (lane == 0) {
-    s_m[wv] = M;
-    s_l[wv] = den;
-  }
+  const float inv = a.v_scale / den;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) s_acc[wv][lane + 64 * r] = num[r];
-  __syncthreads();
-  if (wv == 0) {
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, s_m[w]);
-    float dt = 0.f, nt[PER];
-#pragma unroll
-    for (int r = 0; r < PER; ++r) nt[r] = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
-      // A wave with no partials holds M = -inf and zero sums; its weight is 0.
-      const float c = s_m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[w] - Mt);
-      dt += s_l[w] * c;
-#pragma unroll
-      for (int r = 0; r < PER; ++r) nt[r] += s_acc[w][lane + 64 * r] * c;
-    }
-    const float inv = a.v_scale / dt;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int64_t o = orow + lane + 64 * r;
-      if constexpr (KV == PKV_F32)
-        static_cast<float*>(a.out)[o] = nt[r] * inv;
-      else
-        static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(nt[r] * inv));
-    }
+  for (int r = 0; r < PER; ++r) {
+    const int64_t o = orow + lane + 64 * r;
+    if constexpr (KV == PKV_F32)
+      static_cast<float*>(a.out)[o] = num[r] * inv;
+    else
+      static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(num[r] * inv));
   }
 }
 
@@ -899,10 +887,13 @@ pkv_status effective_splits(const KernelPair& kp, int requested, int* splits) {
   return default_splits(kp, splits);
 }
 
-size_t workspace_bytes_for(int splits, int G, int D) {
-  const size_t acc = size_t(splits) * 2 * G * D * sizeof(float);
-  const size_t ml = size_t(splits) * 2 * G * 2 * sizeof(float);
-  return ((acc + 255) / 256) * 256 + ml;
+// Workspace: partial accumulators, partial (max, sum) pairs, per-sequence work offsets.
+size_t ws_acc_bytes(int splits, int G, int D) {
+  return ((size_t(splits) * 2 * G * D * sizeof(float) + 255) / 256) * 256;
+}
+size_t ws_ml_bytes(int splits, int G) { return ((size_t(splits) * 2 * G * 2 * sizeof(float) + 255) / 256) * 256; }
+size_t workspace_bytes_for(int splits, int B, int G, int D) {
+  return ws_acc_bytes(splits, G, D) + ws_ml_bytes(splits, G) + (size_t(B) + 1) * sizeof(int);
 }
 
 enum Phase { kBoth, kSplitOnly, kMergeOnly };
@@ -937,7 +928,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   int splits = 0;
   if ((st = effective_splits(kp, num_splits, &splits)) != PKV_OK) return st;
   const int G = Hq / Hkv;
-  const size_t need = workspace_bytes_for(splits, G, D);
+  const size_t need = workspace_bytes_for(splits, B, G, D);
   if (!workspace || workspace_bytes < need)
     return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn,
                      workspace_bytes, need);
@@ -954,8 +945,9 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
-                                     ((size_t(splits) * 2 * G * D * sizeof(float) + 255) / 256) * 256);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_acc_bytes(splits, G, D));
+  a.ws_seq = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_acc_bytes(splits, G, D) +
+                                    ws_ml_bytes(splits, G));
   a.B = B;
   a.Hkv = Hkv;
   a.G = G;
@@ -991,7 +983,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
   }
   if (phase != kSplitOnly) {
-    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv * G), unsigned(B)), dim3(kMergeWaves * 64), 0, hs, a);
+    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv * G), unsigned(B)), dim3(64), 0, hs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
   }
@@ -1013,7 +1005,7 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
   pick_kernels(kv_dtype, head_dim, block_size, &kp);
   int splits = 0;
   if ((st = effective_splits(kp, num_splits, &splits)) != PKV_OK) return st;
-  *bytes = workspace_bytes_for(splits, num_q_heads / num_kv_heads, head_dim);
+  *bytes = workspace_bytes_for(splits, num_seqs, num_q_heads / num_kv_heads, head_dim);
   return PKV_OK;
 }
 

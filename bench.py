@@ -272,11 +272,12 @@ def _prefix_step_bench(args, wl):
     """Continuous-batching steps over prefix-sharing groups (one pool; timed steps follow
     one another, each appending one token to every sequence).
 
-    A step: the C++ allocator appends a token to every sequence (copy-on-write pairs for
-    shared partial tails) and writes the block tables into a pinned host buffer; the tables,
-    lengths and copy pairs go to the device asynchronously; then copy_blocks, the decode step
-    (the KV write of each token fused into the split pass) and the merge.  Host buffers are
-    double-buffered so the host prepares step i+1 while the GPU runs step i.
+    A step: the C++ allocator appends a token to every sequence (slots, and copy-on-write
+    pairs for shared partial tails) into a pinned host buffer; only the slots (and pairs) go
+    to the device, asynchronously; then copy_blocks, pkv_apply_append (the device copies of
+    the block tables and lengths take the step's change), the decode step (the KV write of
+    each token fused into the split pass) and the merge.  Host buffers are double-buffered
+    so the host prepares step i+1 while the GPU runs step i.
     """
     import math
 
@@ -329,13 +330,14 @@ def _prefix_step_bench(args, wl):
         def __init__(self):
             self.slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
             self.cow = torch.empty((B, 2), dtype=torch.int32, pin_memory=True)
-            self.tables = torch.empty((B, max_blocks), dtype=torch.int32, pin_memory=True)
-            self.lens = torch.empty(B, dtype=torch.int32, pin_memory=True)
             self.done = torch.cuda.Event()
 
     bufs = [HostBuf(), HostBuf()]
-    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
-    lens_d = torch.empty(B, dtype=torch.int32, device=dev)
+    tables0, lens0 = a.block_tables(members, max_blocks)
+    tables_d = torch.from_numpy(tables0).to(dev)      # uploaded once; each step updates it
+    lens_d = torch.from_numpy(lens0).to(dev)          # on the device (pkv_apply_append)
+    lens_host = lens0.astype(np.int64)
+    slots_d = torch.empty(B, dtype=torch.int64, device=dev)
     cow_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
     host_s = [0.0]
     logical_bytes = []
@@ -346,13 +348,12 @@ def _prefix_step_bench(args, wl):
         hb.done.synchronize()                  # its previous copies have been consumed
         th = time.perf_counter()
         _, cows = a.append(members, hb.slots.numpy(), hb.cow.numpy())
-        a.block_tables(members, max_blocks, hb.tables.numpy(), hb.lens.numpy())
         host_s[0] += time.perf_counter() - th
         n_cow = len(cows)
         cows_seen.append(n_cow)
-        logical_bytes.append(int(hb.lens.numpy().astype(np.int64).sum()) * Hkv * D * 2 * 2)
-        tables_d.copy_(hb.tables, non_blocking=True)
-        lens_d.copy_(hb.lens, non_blocking=True)
+        lens_host[:] += 1
+        logical_bytes.append(int(lens_host.sum()) * Hkv * D * 2 * 2)
+        slots_d.copy_(hb.slots, non_blocking=True)
         if n_cow:
             cow_d[:n_cow].copy_(hb.cow[:n_cow], non_blocking=True)
         hb.done.record(stream)
@@ -360,6 +361,7 @@ def _prefix_step_bench(args, wl):
             after_copy.record(stream)
         if n_cow:
             pkv.copy_blocks(k, v, cow_d[:n_cow], D)
+        pkv.apply_append(tables_d, lens_d, slots_d, bs, nb)
         if ev is not None:
             pkv.set_launch_events(ev[0], ev[1])
         pkv.paged_decode_step_split(out, q, k_new, v_new, k, v, tables_d, lens_d, case.scale,
@@ -375,6 +377,8 @@ def _prefix_step_bench(args, wl):
     one = torch.ones(B, dtype=torch.int32, device=dev)
     st = torch.zeros((B, 1), dtype=torch.int32, device=dev)
     pkv.copy_blocks(sk, sv, torch.tensor([[0, 1]], dtype=torch.int32, device=dev), D)
+    pkv.apply_append(torch.zeros((1, 1), dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
+                     torch.full((1,), -1, dtype=torch.int64, device=dev), bs, 4)
     pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, workspace=ws)
     pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, workspace=ws)
     del sk, sv, one, st
@@ -383,8 +387,7 @@ def _prefix_step_bench(args, wl):
     for e in e_first:
         e.record(stream)
     torch.cuda.synchronize()
-    e_first[0].record(stream)
-    step(0)
+    step(0, after_copy=e_first[0])             # GPU time from the metadata copies' end
     e_first[1].record(stream)
     torch.cuda.synchronize()
     first_us = e_first[0].elapsed_time(e_first[1]) * 1e3
@@ -428,8 +431,9 @@ def _prefix_step_bench(args, wl):
     gpu_step_us = statistics.mean(d[0].elapsed_time(d[4]) for d in det) * 1e3
     # Unique physical KV bytes of the last step: each referenced block once, with the
     # largest number of valid tokens any referencing sequence reads in it.
-    tables = bufs[(n_steps + n_detail - 1) % 2].tables.numpy()
-    lens = bufs[(n_steps + n_detail - 1) % 2].lens.numpy().astype(np.int64)
+    tables, lens = a.block_tables(members, max_blocks)
+    lens = lens.astype(np.int64)
+    assert np.array_equal(tables, tables_d.cpu().numpy()) and np.array_equal(lens, lens_d.cpu().numpy().astype(np.int64))
     used = {}
     for si in range(B):
         for j in range(int(math.ceil(lens[si] / bs))):
@@ -458,7 +462,8 @@ def _prefix_step_bench(args, wl):
                           "merge_incl_gap": round(merge_us, 2),
                           "gpu_step": round(gpu_step_us, 2)}},
         "host_allocator_us_per_step": round(host_s[0] / args.steps * 1e6, 1),
-        "first_step": {"copy_on_write_pairs": int(first_cow), "gpu_us_incl_copy_blocks": round(first_us, 2)},
+        "first_step": {"copy_on_write_pairs": int(first_cow),
+                       "gpu_us_copy_blocks_to_merge_end": round(first_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
                      "note": "logical KV bytes (shared prefix blocks counted once per reader)",

@@ -245,6 +245,29 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_ma
                            int num_blocks, pkv_dtype kv_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Device-side mirror of a decode step's table update ("What is PagedAttention?", glossary,
+ * "How It Works: Map Logical to Physical Blocks": a decode step appends one token into the
+ * sequence's last block and takes a new block only when that one is full).
+ *
+ * After pkv_seq_append gave each of num_seqs sequences one token (slot_mapping[s], the slots
+ * it returned, copied to the device), this applies the same change to device copies of the
+ * block tables and lengths, so that only the slots cross to the device each step: for every
+ * s with 0 <= slot < num_blocks * bs, position p = context_lens[s] gets
+ * block_tables[s][p / bs] = slot / bs (a new block, a copy-on-write copy or the unchanged
+ * tail) and context_lens[s] becomes p + 1.
+ *
+ *   block_tables   int32 [num_seqs, max_blocks_per_seq] (device, updated in place); row s
+ *                  belongs to the s-th sequence passed to pkv_seq_append.
+ *   context_lens   int32 [num_seqs] (device, updated in place).
+ *   slot_mapping   int64 [num_seqs] (device); a negative slot leaves row s unchanged.
+ * Rows whose slot does not match their length (slot % bs != p % bs) or whose new position
+ * lies past max_blocks_per_seq blocks are left unchanged (a caller error, never a fault).
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_apply_append(int32_t* block_tables, int32_t* context_lens, const int64_t* slot_mapping,
+                            int num_seqs, int max_blocks_per_seq, int block_size, int num_blocks,
+                            void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Host block allocator (host memory only; not thread-safe — callers serialise).
  *
  * Hands out physical block ids from a free list, counts references per block, shares

@@ -27,7 +27,7 @@ __all__ = [
     "paged_attention_decode",
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
-    "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events",
+    "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -60,6 +60,7 @@ _SIGNATURES = {
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
     "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
+    "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
@@ -323,6 +324,18 @@ def copy_blocks(k_cache, v_cache, block_mapping, head_dim: int, stream=None):
     _check(lib().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                                  _dev(block_mapping, "block_mapping") if n else None, n, Hkv,
                                  head_dim, bs, NB, _dtype_code(k_cache.dtype), _stream(stream)))
+
+
+def apply_append(block_tables, context_lens, slot_mapping, block_size: int, num_blocks: int, stream=None):
+    """Mirror a decode step's append on device tables / lengths (pkv_apply_append)."""
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or slot_mapping.dtype != torch.int64:
+        raise TypeError("block_tables / context_lens must be int32 and slot_mapping int64")
+    n = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != n or slot_mapping.shape != (n,):
+        raise ValueError("block_tables [n, max_blocks], context_lens [n], slot_mapping [n]")
+    _check(lib().pkv_apply_append(_dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+                                  _dev(slot_mapping, "slot_mapping"), n, block_tables.shape[1], block_size,
+                                  num_blocks, _stream(stream)))
 
 
 def build_slot_mapping(block_tables, lens, block_size: int) -> np.ndarray:

@@ -101,6 +101,25 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
   }
 }
 
+
+// One thread per sequence: the device-side mirror of a decode step's allocator update.  The
+// step gave sequence s one token at position lens[s] in slot slots[s]; that position's block
+// table entry becomes the slot's block (a new block, a copy-on-write copy, or the same tail
+// block again) and the length grows by one.  A negative slot means no token for s.
+__global__ __launch_bounds__(256) void apply_append_kernel(int32_t* __restrict__ tables,
+                                                           int32_t* __restrict__ lens,
+                                                           const int64_t* __restrict__ slots, int n,
+                                                           int max_blocks, int bs, int64_t num_slots) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n) return;
+  const int64_t slot = slots[s];
+  if (slot < 0 || slot >= num_slots) return;
+  const int pos = lens[s];
+  if (pos < 0 || pos / bs >= max_blocks || pos % bs != int(slot % bs)) return;
+  tables[int64_t(s) * max_blocks + pos / bs] = int32_t(slot / bs);
+  lens[s] = pos + 1;
+}
+
 int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : t == PKV_BF16 ? 2 : t == PKV_FP8_E4M3FN ? 1 : 0; }
 
 bool shape_ok(int D, int bs, pkv_dtype kv) {
@@ -194,4 +213,21 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_
                      reinterpret_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
                      static_cast<uint4*>(v_cache), block_mapping, num_blocks, chunks);
   return launch_status("pkv_copy_blocks");
+}
+
+extern "C" pkv_status pkv_apply_append(int32_t* block_tables, int32_t* context_lens,
+                                       const int64_t* slot_mapping, int num_seqs,
+                                       int max_blocks_per_seq, int block_size, int num_blocks,
+                                       void* stream) {
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || block_size <= 0 || num_blocks <= 0)
+    return pkv::fail(PKV_INVALID_ARG,
+                     "pkv_apply_append: num_seqs=%d max_blocks_per_seq=%d block_size=%d num_blocks=%d",
+                     num_seqs, max_blocks_per_seq, block_size, num_blocks);
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !slot_mapping)
+    return pkv::fail(PKV_INVALID_ARG, "pkv_apply_append: null pointer");
+  hipLaunchKernelGGL(apply_append_kernel, dim3(unsigned((num_seqs + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), block_tables, context_lens, slot_mapping,
+                     num_seqs, max_blocks_per_seq, block_size, int64_t(num_blocks) * block_size);
+  return launch_status("pkv_apply_append");
 }

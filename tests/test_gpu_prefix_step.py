@@ -109,3 +109,40 @@ def test_prefix_step_parity_full_size():
     got = as_f64(out)[sample]
     assert_close(got, oatt.prefix_step_case(case, sample), "bf16", "prefix step full size")
     assert np.all(np.isfinite(as_f64(out)))
+
+
+def test_apply_append_mirrors_the_allocator_tables():
+    """Forty decode steps: only each step's slots cross to the device, and apply_append keeps
+    the device tables and lengths equal to the allocator's after every step (copy-on-write
+    tails, new blocks and unchanged tails all occur)."""
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 9)
+    wl = case.wl
+    a, k, v, members = build_prefix_batch(case)
+    steps = 40
+    max_blocks = int((case.lengths.max() + steps + wl.block_size) // wl.block_size) + 1
+    tables, lens = a.block_tables(members, max_blocks)
+    t_dev = torch.from_numpy(tables).cuda()
+    l_dev = torch.from_numpy(lens).cuda()
+    n_cow = 0
+    for i in range(steps):
+        slots, cows = a.append(members)
+        n_cow += len(cows)
+        pkv.apply_append(t_dev, l_dev, torch.from_numpy(slots).cuda(), wl.block_size, case.num_blocks)
+        want_t, want_l = a.block_tables(members, max_blocks)
+        torch.cuda.synchronize()
+        assert np.array_equal(t_dev.cpu().numpy(), want_t), f"step {i}"
+        assert np.array_equal(l_dev.cpu().numpy(), want_l), f"step {i}"
+    assert n_cow == _expected_cow(case)
+
+
+def test_apply_append_skips_negative_and_inconsistent_slots():
+    require_gpu()
+    tables = torch.full((3, 4), -1, dtype=torch.int32, device="cuda")
+    lens = torch.tensor([0, 5, 16], dtype=torch.int32, device="cuda")
+    slots = torch.tensor([-1, 7 * 16 + 5, 9 * 16 + 3], dtype=torch.int64, device="cuda")  # row 2: offset 3 != 16 % 16
+    pkv.apply_append(tables, lens, slots, 16, 64)
+    torch.cuda.synchronize()
+    assert lens.cpu().tolist() == [0, 6, 16]
+    t = tables.cpu().numpy()
+    assert t[1, 0] == 7 and (t[0] == -1).all() and (t[2] == -1).all()

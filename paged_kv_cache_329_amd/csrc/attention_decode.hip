@@ -303,124 +303,109 @@ __device__ __forceinline__ void mask_v(uint4* vf, uint32_t vmask) {
 }
 
 
-// Stores the appended token of unit (s, g) — row (s, g) of k_new / v_new, in q's dtype —
-// as token t of the 16-token sub-tile whose K and V regions start at ksub and vsub, in the
-// cache's element format (fp8 caches quantise exactly as the KV-cache write does).  Lane l
-// writes the parts of the chunks that its own loads of that sub-tile would read:
-//  K: lanes with lane % 16 == t write the chunk of load i, dims X*(4i + lane/16) .. +X;
-//  V: lanes with lane / 16 == t / 4 write element e*4 + t%4 of the chunk of load i, which
-//     holds dim i*4X + 16e + lane%16.
-template <int KV, int D>
-__device__ __forceinline__ void store_append_token(const DecodeArgs& a, int s, int g, int t, int lane,
-                                                   uint8_t* ksub, uint8_t* vsub) {
-  using F = Frag<KV, D>;
-  constexpr int EB = KvTraits<KV>::EB;
-  constexpr int X = 16 / EB;
-  const int64_t row = (int64_t(s) * a.Hkv + g) * D;
-  const int grp = lane >> 4, col = lane & 15;
-  // All loads first, then all stores: the compiler cannot move a load above a store to a
-  // pointer it might alias, so interleaving them would cost one round trip per pair.
-  uint4 kc[F::NLOAD];
-  uint32_t ve[F::NLOAD][X / 4];
-#pragma unroll
-  for (int i = 0; i < F::NLOAD; ++i) {
-    if constexpr (KV == PKV_F32) {
-      kc[i] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.k_new) + row + X * (4 * i + grp));
-      ve[i][0] = __float_as_uint(static_cast<const float*>(a.v_new)[row + i * 4 * X + col]);
-    } else {
-      const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + row + X * (4 * i + grp);
-      if constexpr (KV == PKV_BF16) {
-        kc[i] = *reinterpret_cast<const uint4*>(kn);
-      } else {
-        const uint4 lo = *reinterpret_cast<const uint4*>(kn);
-        const uint4 hi = *reinterpret_cast<const uint4*>(kn + 8);
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        uint32_t q[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          q[e >> 2] |= pkv::e4m3fn_from_f32(pkv::bf16_bits_to_f32(b) * a.k_inv) << (8 * (e & 3));
-        }
-        kc[i] = make_uint4(q[0], q[1], q[2], q[3]);
-      }
-#pragma unroll
-      for (int e = 0; e < X / 4; ++e) {
-        const uint32_t b = static_cast<const uint16_t*>(a.v_new)[row + i * 4 * X + 16 * e + col];
-        ve[i][e] = KV == PKV_BF16 ? b : pkv::e4m3fn_from_f32(pkv::bf16_bits_to_f32(b) * a.v_inv);
-      }
-    }
-  }
-  if (col == t) {
-#pragma unroll
-    for (int i = 0; i < F::NLOAD; ++i) *reinterpret_cast<uint4*>(ksub + (64 * i + lane) * 16) = kc[i];
-  }
-  if (grp == (t >> 2)) {
-#pragma unroll
-    for (int i = 0; i < F::NLOAD; ++i)
-#pragma unroll
-      for (int e = 0; e < X / 4; ++e) {
-        uint8_t* dst = vsub + (64 * i + lane) * 16 + (e * 4 + (t & 3)) * EB;
-        if constexpr (EB == 4)
-          *reinterpret_cast<uint32_t*>(dst) = ve[i][e];
-        else if constexpr (EB == 2)
-          *reinterpret_cast<uint16_t*>(dst) = uint16_t(ve[i][e]);
-        else
-          *dst = uint8_t(ve[i][e]);
-      }
-  }
-}
-
 // Decoded value of an e4m3fn code (exact, through bf16).
 __device__ __forceinline__ float e4m3fn_value(uint32_t code) {
   return __uint_as_float(fp8x2_to_bf16x2<false>(code) << 16);
 }
 
-// The value the cache holds for input element x (q's dtype bits or float) of k_new / v_new:
-// f32 and bf16 are stored as given; fp8 stores RNE(clamp(x * inv)) and is read back as that
-// code's value (the per-tensor scale is applied outside, as for cached tokens).
+// Element bits the cache stores for input element bits x (q's dtype) of k_new / v_new: f32
+// and bf16 are stored as given; fp8 stores RNE(clamp(x * inv)), as the KV-cache write does.
 template <int KV>
-__device__ __forceinline__ float cached_value(float x, float inv) {
-  if constexpr (KV == PKV_FP8_E4M3FN) return e4m3fn_value(pkv::e4m3fn_from_f32(x * inv));
+__device__ __forceinline__ uint32_t cache_bits(uint32_t x, float inv) {
+  if constexpr (KV == PKV_FP8_E4M3FN) return pkv::e4m3fn_from_f32(pkv::bf16_bits_to_f32(x) * inv);
   return x;
 }
 
-// Folds the appended token of unit (s, g) into the running softmax of head lane % 16:
-// logit from q (this lane's fragments qf, summed over the four lane rows) and k_new, then
-// m, the sum and the accumulators as for a cached token.  `zero` stands for an appended
-// slot in a block outside the pool, which reads as zeros.  The probability is rounded to
-// bf16 for the bf16 / fp8 accumulators, as the matrix path rounds it.
+// The value attention uses for cached element bits c (per-tensor scales applied outside).
+template <int KV>
+__device__ __forceinline__ float cache_value(uint32_t c) {
+  if constexpr (KV == PKV_F32) return __uint_as_float(c);
+  else if constexpr (KV == PKV_BF16) return pkv::bf16_bits_to_f32(c);
+  else return e4m3fn_value(c);
+}
+
+// Input element e (q's dtype: 4 or 2 bytes) of a run of 16-byte words.
+template <int QB>
+__device__ __forceinline__ uint32_t input_element(const uint4* w, int e) {
+  const uint4 c = w[(e * QB) / 16];
+  const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+  const int k = e % (16 / QB);
+  if constexpr (QB == 4) return d[k];
+  else return (d[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+}
+
+// The appended token of one unit, as this lane needs it, loaded when the segment that ends
+// the unit starts (so that neither the fold nor the stores wait for memory):
+//  k[i*QCH ..]: k_new dims X*(4i + lane/16) .. +X (the dims of this lane's q fragments,
+//               and of its K chunk of load i),
+//  vf[n][..]:   v_new dims 16n + 4*(lane/16) .. +3 (this lane's accumulator dims),
+//  vs[i][e]:    v_new dim i*4X + 16e + lane%16 (its element of the V chunk of load i).
 template <int KV, int D>
-__device__ __forceinline__ void fold_append_token(const DecodeArgs& a, int s, int g, const uint4* qf,
-                                                  int lane, bool zero, float& m_run, float& l_run,
-                                                  f32x4* acc) {
+struct AppendRegs {
+  static constexpr int QB = KvTraits<KV>::QB;
+  static constexpr int X = 16 / KvTraits<KV>::EB;
+  uint4 k[Frag<KV, D>::NLOAD * Frag<KV, D>::QCH];
+  uint32_t vf[Frag<KV, D>::NT][QB];
+  uint32_t vs[Frag<KV, D>::NLOAD][X / 4];
+};
+
+template <int KV, int D>
+__device__ __forceinline__ void load_append_regs(const DecodeArgs& a, int s, int g, int lane,
+                                                 AppendRegs<KV, D>& r) {
   using F = Frag<KV, D>;
+  constexpr int QB = KvTraits<KV>::QB;
   constexpr int X = 16 / KvTraits<KV>::EB;
-  const int row = lane >> 4;
-  const int64_t nrow = (int64_t(s) * a.Hkv + g) * D;
-  float dot = 0.f;
+  const int row = lane >> 4, col = lane & 15;
+  const uint8_t* kn = static_cast<const uint8_t*>(a.k_new) + (int64_t(s) * a.Hkv + g) * D * QB;
+  const uint8_t* vn = static_cast<const uint8_t*>(a.v_new) + (int64_t(s) * a.Hkv + g) * D * QB;
 #pragma unroll
-  for (int i = 0; i < F::NLOAD; ++i) {
-    const int d0 = X * (4 * i + row);
-    if constexpr (KV == PKV_F32) {
-      const float4 kv = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k_new) + nrow + d0);
-      dot += __uint_as_float(qf[i].x) * kv.x + __uint_as_float(qf[i].y) * kv.y +
-             __uint_as_float(qf[i].z) * kv.z + __uint_as_float(qf[i].w) * kv.w;
+  for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+    for (int c = 0; c < F::QCH; ++c)
+      r.k[i * F::QCH + c] = *reinterpret_cast<const uint4*>(kn + (X * (4 * i + row)) * QB + 16 * c);
+#pragma unroll
+  for (int n = 0; n < F::NT; ++n) {
+    const uint8_t* src = vn + (16 * n + 4 * row) * QB;
+    if constexpr (QB == 4) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src);
+      r.vf[n][0] = w.x; r.vf[n][1] = w.y; r.vf[n][2] = w.z; r.vf[n][3] = w.w;
     } else {
-      const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + nrow + d0;
-#pragma unroll
-      for (int c = 0; c < F::QCH; ++c) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(kn + 8 * c);
-        const uint4 qw = qf[i * F::QCH + c];
-        const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, qq[4] = {qw.x, qw.y, qw.z, qw.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kx = pkv::bf16_bits_to_f32((kk[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          const float qx = pkv::bf16_bits_to_f32((qq[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          dot += qx * cached_value<KV>(kx, a.k_inv);
-        }
-      }
+      const uint2 w = *reinterpret_cast<const uint2*>(src);
+      r.vf[n][0] = w.x; r.vf[n][1] = w.y;
     }
   }
+#pragma unroll
+  for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+    for (int e = 0; e < X / 4; ++e) {
+      const int d = i * 4 * X + 16 * e + col;
+      r.vs[i][e] = QB == 4 ? reinterpret_cast<const uint32_t*>(vn)[d] : reinterpret_cast<const uint16_t*>(vn)[d];
+    }
+}
+
+// Folds the appended token into the running softmax of head lane % 16: its logit from this
+// lane's q fragments and the key as the cache holds it (summed over the four lane rows),
+// then m, the sum and the accumulators as for a cached token; the probability is rounded
+// to bf16 for the bf16 / fp8 accumulators, as the matrix path rounds it.  `zero` stands for
+// an appended slot in a block outside the pool, which reads as zeros.
+template <int KV, int D>
+__device__ __forceinline__ void fold_append_token(const DecodeArgs& a, const AppendRegs<KV, D>& r,
+                                                  const uint4* qf, int lane, bool zero, float& m_run,
+                                                  float& l_run, f32x4* acc) {
+  using F = Frag<KV, D>;
+  constexpr int QB = KvTraits<KV>::QB;
+  constexpr int X = 16 / KvTraits<KV>::EB;
+  const int row = lane >> 4;
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+      const uint32_t kx = input_element<QB>(r.k + i * F::QCH, e);
+      const uint32_t qx = input_element<QB>(qf + i * F::QCH, e);
+      const float qv = QB == 4 ? __uint_as_float(qx) : pkv::bf16_bits_to_f32(qx);
+      dot += qv * cache_value<KV>(cache_bits<KV>(kx, a.k_inv));
+    }
   dot += __shfl_xor(dot, 16);
   dot += __shfl_xor(dot, 32);
   const float sc = zero ? 0.f : dot * a.qk_scale_log2;
@@ -430,23 +415,73 @@ __device__ __forceinline__ void fold_append_token(const DecodeArgs& a, int s, in
   l_run = l_run * alpha + (row == 0 ? pr : 0.f);
   const float pm = zero ? 0.f : (KV == PKV_F32 ? pr : __uint_as_float(bf16_rne(pr) << 16));
 #pragma unroll
-  for (int n = 0; n < F::NT; ++n) {
-    const int d = 16 * n + 4 * row;
-    float v[4];
-    if constexpr (KV == PKV_F32) {
-      const float4 vv = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v_new) + nrow + d);
-      v[0] = vv.x; v[1] = vv.y; v[2] = vv.z; v[3] = vv.w;
-    } else {
-      const uint2 vw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v_new) + nrow + d);
-      v[0] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.x & 0xFFFFu), a.v_inv);
-      v[1] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.x >> 16), a.v_inv);
-      v[2] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.y & 0xFFFFu), a.v_inv);
-      v[3] = cached_value<KV>(pkv::bf16_bits_to_f32(vw.y >> 16), a.v_inv);
-    }
+  for (int n = 0; n < F::NT; ++n)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[n][j] = acc[n][j] * alpha + pm * v[j];
-  }
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t x = QB == 4 ? r.vf[n][j] : (r.vf[n][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      acc[n][j] = acc[n][j] * alpha + pm * cache_value<KV>(cache_bits<KV>(x, a.v_inv));
+    }
   m_run = m_new;
+}
+
+// The appended token's bytes this lane stores, in the cache's format: the K chunk of load
+// i (lanes with lane % 16 == t) and its element of the V chunk of load i (lanes with
+// lane / 16 == t / 4, at position e*4 + t%4).
+template <int KV, int D>
+struct AppendStore {
+  uint4 k[Frag<KV, D>::NLOAD];
+  uint32_t v[Frag<KV, D>::NLOAD][16 / KvTraits<KV>::EB / 4];
+  int64_t sub = -1;  // byte offset of the sub-tile's K / V region in the pools; -1 = none
+  int t = 0;         // token within the sub-tile
+};
+
+template <int KV, int D>
+__device__ __forceinline__ void make_append_store(const DecodeArgs& a, const AppendRegs<KV, D>& r,
+                                                  int64_t sub, int t, AppendStore<KV, D>& st) {
+  using F = Frag<KV, D>;
+  constexpr int EB = KvTraits<KV>::EB;
+  constexpr int QB = KvTraits<KV>::QB;
+  constexpr int X = 16 / EB;
+#pragma unroll
+  for (int i = 0; i < F::NLOAD; ++i) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < X; ++e)
+      w[(e * EB) >> 2] |= cache_bits<KV>(input_element<QB>(r.k + i * F::QCH, e), a.k_inv) << (8 * ((e * EB) & 3));
+    st.k[i] = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+    for (int e = 0; e < X / 4; ++e) st.v[i][e] = cache_bits<KV>(r.vs[i][e], a.v_inv);
+  }
+  st.sub = sub;
+  st.t = t;
+}
+
+template <int KV, int D>
+__device__ __forceinline__ void issue_append_store(const DecodeArgs& a, const AppendStore<KV, D>& st,
+                                                   int lane) {
+  using F = Frag<KV, D>;
+  constexpr int EB = KvTraits<KV>::EB;
+  constexpr int X = 16 / EB;
+  uint8_t* ksub = a.k_cache_w + st.sub;
+  uint8_t* vsub = a.v_cache_w + st.sub;
+  if ((lane & 15) == st.t) {
+#pragma unroll
+    for (int i = 0; i < F::NLOAD; ++i) *reinterpret_cast<uint4*>(ksub + (64 * i + lane) * 16) = st.k[i];
+  }
+  if ((lane >> 4) == (st.t >> 2)) {
+#pragma unroll
+    for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+      for (int e = 0; e < X / 4; ++e) {
+        uint8_t* dst = vsub + (64 * i + lane) * 16 + (e * 4 + (st.t & 3)) * EB;
+        if constexpr (EB == 4)
+          *reinterpret_cast<uint32_t*>(dst) = st.v[i][e];
+        else if constexpr (EB == 2)
+          *reinterpret_cast<uint16_t*>(dst) = uint16_t(st.v[i][e]);
+        else
+          *dst = uint8_t(st.v[i][e]);
+      }
+  }
 }
 
 template <int KV, int D, int BS, int NSUB, bool APPEND>
@@ -492,11 +527,12 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   const int row = lane >> 4;     // token group 4*row.. of this lane's QK/PV rows
   const bool head_ok = h < a.G;
 
-  // With APPEND, token L-1 of every sequence is the appended one: the block walk masks its
-  // slot (Lc = L - 1 cached tokens are read), the segment holding it folds it in from
-  // k_new / v_new after the walk, and its stores into the pool are issued last (below the
-  // loop), because a store ahead of the remaining loads would delay them: loads and stores
-  // of a wave complete in issue order.
+  // With APPEND, token L-1 of every sequence is the appended one.  The block walk masks its
+  // slot (Lc = L - 1 cached tokens are read); the segment that ends the unit loads the
+  // token's k_new / v_new values when it starts, folds the token in after the walk and keeps
+  // its pool stores in registers until the wave has issued its last load: a wave's loads and
+  // stores complete in issue order, so a store ahead of the remaining loads would delay them.
+  AppendStore<KV, D> held;
   bool done = false;
   while (pos < c_end) {
     const int Lc = APPEND ? L - 1 : L;
@@ -526,6 +562,11 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
     int tbase = k0 / NSB;
     int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+    const bool ends_unit = APPEND && seg_end == unit_end;
+    AppendRegs<KV, D> app;
+    if constexpr (APPEND) {
+      if (ends_unit) load_append_regs<KV, D>(a, s, g, lane, app);
+    }
     f32x4 acc[F::NT];
 #pragma unroll
     for (int n = 0; n < F::NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -614,10 +655,18 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     }
 
     if constexpr (APPEND) {
-      if (seg_end == unit_end) {
-        const int phys = trow[(L - 1) / BS];
-        fold_append_token<KV, D>(a, s, g, qf, lane, unsigned(phys) >= unsigned(a.num_blocks), m_run,
-                                 l_run, acc);
+      if (ends_unit) {
+        const int knew = (L - 1) / 16;
+        const int jb = knew / NSB;   // usually inside the walk's last table window
+        const int phys = jb >= tbase && jb < tbase + 64 ? __builtin_amdgcn_readlane(tbl, jb - tbase) : trow[jb];
+        const bool zero = unsigned(phys) >= unsigned(a.num_blocks);
+        fold_append_token<KV, D>(a, app, qf, lane, zero, m_run, l_run, acc);
+        if (held.sub >= 0) issue_append_store<KV, D>(a, held, lane);   // a second unit end
+        held.sub = -1;
+        if (!zero)
+          make_append_store<KV, D>(a, app, int64_t(phys) * block_stride + int64_t(g) * REGION +
+                                               (knew % NSB) * SUB_BYTES,
+                                   (L - 1) & 15, held);
       }
     }
     const float l_tot = wave_sum_rows(l_run);
@@ -667,31 +716,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   }
 
   if constexpr (APPEND) {
-    // Store the appended token of every unit whose last block lies in this share.
-    locate(a, BS, lane, c_begin, s, seq_off);
-    L = seq_len(a, s, BS);
-    nb = (L + BS - 1) / BS;
-    g = (c_begin - seq_off) / nb;
-    for (unit_off = seq_off + g * nb; unit_off < c_end;) {
-      const int last = unit_off + nb - 1;   // the unit's last block, appended into
-      if (last >= c_begin && last < c_end) {
-        const int knew = (L - 1) / 16;
-        const int phys = a.block_tables[int64_t(s) * a.max_blocks + knew / NSB];
-        if (unsigned(phys) < unsigned(a.num_blocks)) {
-          const int64_t sub = int64_t(phys) * a.Hkv * REGION + int64_t(g) * REGION + (knew % NSB) * SUB_BYTES;
-          store_append_token<KV, D>(a, s, g, (L - 1) & 15, lane, a.k_cache_w + sub, a.v_cache_w + sub);
-        }
-      }
-      unit_off += nb;
-      if (++g == a.Hkv) {
-        g = 0;
-        do {
-          done = ++s >= a.B;
-        } while (!done && (L = seq_len(a, s, BS)) == 0);
-        if (done) break;
-        nb = (L + BS - 1) / BS;
-      }
-    }
+    if (held.sub >= 0) issue_append_store<KV, D>(a, held, lane);
   }
 }
 

@@ -107,13 +107,14 @@ const char* pkv_last_error(void);
  *                   (larger values are clamped to that bound).
  *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
  *   num_splits      number of equal shares the total (sequence, kv head, block) work is
- *                   cut into, one per wavefront; 0 = one per wavefront slot the device
- *                   can keep resident.  Results depend only on the split count, not on
- *                   the physical block numbering.
+ *                   cut into, one per wavefront; 0 = pkv_paged_attention_default_splits.
+ *                   Results depend only on the split count, not on the physical block
+ *                   numbering.
  *   workspace       device scratch of at least pkv_paged_attention_workspace_size()
  *                   bytes, owned by the caller, no initial contents required; holds the
  *                   partial (max, sum, accumulator) of every sequence head whose work
- *                   spans more than one share.
+ *                   spans more than one share and every sequence's offset in the work
+ *                   list (written by the split pass, read by the reduce pass).
  * Preconditions (not checked on the device): block table entries of used blocks lie in
  * [0, num_blocks) — an entry outside that range is read as a block of zeros, never out
  * of bounds; out does not alias any input.
@@ -123,8 +124,10 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
                                               pkv_dtype kv_dtype, int num_splits,
                                               size_t* bytes /* host, out */);
 
-/* The split count used when num_splits = 0: one share per wavefront slot the current
- * device keeps resident for this kernel variant (queried once per device and cached). */
+/* The split count used when num_splits = 0: one share per wave of 2 workgroups (of 4 waves)
+ * per CU for f32 / bf16 caches and 4 for fp8 caches (the fastest counts measured on
+ * MI355X), capped by what the current device keeps resident of the plain and the appending
+ * split kernels (queried once per device and cached). */
 pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_dtype q_dtype,
                                               pkv_dtype kv_dtype, int* splits /* host, out */);
 

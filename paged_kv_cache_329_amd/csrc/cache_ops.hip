@@ -32,42 +32,28 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) {
   return __uint_as_float(uint32_t(*p) << 16);
 }
 
-// One thread per (token, kv head, group of x consecutive dims).  K: the group is one
-// 16-byte chunk of the token's sub-tile; V: the group's x elements land in x chunks that
-// are 16 bytes apart (same position inside each).
+// Writes dims d0 .. d0+X of token n, kv head h, into slot `slot` (one thread's share of the
+// per-token path).  K: the dims are one 16-byte chunk of the token's sub-tile; V: the X
+// elements land in X chunks that are 16 bytes apart (same position inside each).
 template <int EB, typename InT, bool QUANT>
-__global__ __launch_bounds__(256) void kv_cache_write_kernel(
-    const InT* __restrict__ k_new, const InT* __restrict__ v_new, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slots, int T, int Hkv, int D,
-    int bs, int64_t num_slots, float k_inv, float v_inv) {
+__device__ __forceinline__ void write_token_group(const InT* __restrict__ k_new, const InT* __restrict__ v_new,
+                                                  uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                  int64_t n, int h, int grp, int64_t slot, int Hkv, int D,
+                                                  int bs, float k_inv, float v_inv) {
   constexpr int X = 16 / EB;
-  const int groups = D / X;
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = int64_t(T) * Hkv * groups;
-  if (gid >= total) return;
-  const int grp = int(gid % groups);
-  const int h = int((gid / groups) % Hkv);
-  const int64_t n = gid / (int64_t(groups) * Hkv);
-  const int64_t slot = slots[n];
-  if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / bs;
   const int off = int(slot % bs);
   const int u = off >> 4, t = off & 15;
   const int d0 = grp * X;
-  const int64_t region = (blk * Hkv + h) * int64_t(bs) * D;  // element index of the region
-  const int64_t sub = region + int64_t(u) * 16 * D;
+  const int64_t sub = ((blk * Hkv + h) * int64_t(bs) + int64_t(u) * 16) * D;  // element index
   const int64_t src = (n * Hkv + h) * D + d0;
-
-  // K: one 16-byte chunk.
   const int64_t kel = sub + (int64_t(grp) * 16 + t) * X;
-  // V: element (t, d0 + e) for e < X; all share i = d0/(4X), tile e4 = (d0/16)%(X/4).
+  // V element (t, d0 + e) for e < X: all share i = d0/(4X) and position group (d0/16)%(X/4).
   const int vi = d0 / (4 * X), ve = (d0 / 16) % (X / 4), vc0 = d0 % 16;
   const int64_t vel0 = sub + ((int64_t(vi) * 4 + (t >> 2)) * 16 + vc0) * X + ve * 4 + (t & 3);
-
   if constexpr (!QUANT) {
     // Bit copies: EB == sizeof(InT).
-    const uint4 kv = *reinterpret_cast<const uint4*>(k_new + src);
-    *reinterpret_cast<uint4*>(k_cache + kel * EB) = kv;
+    *reinterpret_cast<uint4*>(k_cache + kel * EB) = *reinterpret_cast<const uint4*>(k_new + src);
     const InT* vs = v_new + src;
     InT* vd = reinterpret_cast<InT*>(v_cache) + vel0;
 #pragma unroll
@@ -82,6 +68,91 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
 #pragma unroll
     for (int e = 0; e < X; ++e)
       vd[int64_t(e) * X] = uint8_t(e4m3fn_from_f32(load_as_f32(v_new + src + e) * v_inv));
+  }
+}
+
+template <typename InT, bool QUANT>
+__device__ __forceinline__ uint32_t cache_element(InT x, float inv) {
+  if constexpr (QUANT) return e4m3fn_from_f32(load_as_f32(&x) * inv);
+  else if constexpr (sizeof(InT) == 4) return __float_as_uint(x);
+  else return uint32_t(x);
+}
+
+// One workgroup per (16 consecutive tokens, kv head).  When the 16 tokens go to the 16 slots
+// of one sub-tile in order (a prefill, or any run of appends that fills a sub-tile), the
+// workgroup writes that sub-tile's K and V regions whole: every thread stores complete
+// 16-byte chunks (K from one token's row, V assembled from the token rows staged in LDS),
+// so the stores are contiguous instead of scattered 2-byte writes.  Any other slot pattern
+// (decode appends, skipped or out-of-range slots, runs that cross sub-tiles) takes the
+// per-token path.
+template <int EB, typename InT, bool QUANT>
+__global__ __launch_bounds__(256) void kv_cache_write_kernel(
+    const InT* __restrict__ k_new, const InT* __restrict__ v_new, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slots, int T, int Hkv, int D,
+    int bs, int64_t num_slots, float k_inv, float v_inv) {
+  constexpr int X = 16 / EB;
+  __shared__ int64_t s_slot[16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * 128 * sizeof(InT)];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int64_t n0 = int64_t(blockIdx.x) * 16;
+  const int cnt = int(T - n0 < 16 ? T - n0 : 16);
+  if (tid < 16) s_slot[tid] = tid < cnt ? slots[n0 + tid] : -1;
+  __syncthreads();
+  const int64_t s0 = s_slot[0];
+  bool whole = cnt == 16 && s0 >= 0 && s0 % 16 == 0 && s0 + 15 < num_slots;
+#pragma unroll
+  for (int i = 1; i < 16; ++i) whole = whole && s_slot[i] == s0 + i;
+
+  if (whole) {
+    const int64_t blk = s0 / bs;
+    const int64_t sub = ((blk * Hkv + h) * int64_t(bs) + (s0 % bs)) * D;   // element index
+    // Stage the 16 tokens' V rows (row-major [16][D] of InT) in LDS.
+    const int row_chunks = D * int(sizeof(InT)) / 16;
+    for (int c = tid; c < 16 * row_chunks; c += 256) {
+      const int t = c / row_chunks, w = c % row_chunks;
+      reinterpret_cast<uint4*>(s_v)[c] =
+          reinterpret_cast<const uint4*>(v_new + ((n0 + t) * Hkv + h) * D)[w];
+    }
+    __syncthreads();
+    const InT* sv = reinterpret_cast<const InT*>(s_v);
+    for (int c = tid; c < D * EB; c += 256) {          // 16-byte chunks of the sub-tile
+      // K chunk c: token c % 16, dims X*(c/16) .. +X.
+      const int t = c & 15, d0 = X * (c >> 4);
+      const InT* ks = k_new + ((n0 + t) * Hkv + h) * D + d0;
+      uint4 kc;
+      if constexpr (!QUANT) {
+        kc = *reinterpret_cast<const uint4*>(ks);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < X; ++e) w[e >> 2] |= e4m3fn_from_f32(load_as_f32(ks + e) * k_inv) << (8 * (e & 3));
+        kc = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      *reinterpret_cast<uint4*>(k_cache + (sub + int64_t(c) * X) * EB) = kc;
+      // V chunk c: tokens 4*((c/16)%4) + j (j < 4), dims (c/64)*4X + 16e + c%16 (e < X/4);
+      // element e*4 + j.
+      const int tg = ((c >> 4) & 3) * 4, vd0 = (c >> 6) * 4 * X + (c & 15);
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < X / 4; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = e * 4 + j;   // element index within the chunk
+          const uint32_t bits = cache_element<InT, QUANT>(sv[(tg + j) * D + vd0 + 16 * e], v_inv);
+          w[(p * EB) >> 2] |= (EB == 4 ? bits : bits & ((1u << (8 * EB)) - 1u)) << (8 * ((p * EB) & 3));
+        }
+      *reinterpret_cast<uint4*>(v_cache + (sub + int64_t(c) * X) * EB) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return;
+  }
+  const int groups = D / X;
+  for (int idx = tid; idx < cnt * groups; idx += 256) {
+    const int t = idx / groups, grp = idx % groups;
+    const int64_t slot = s_slot[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    write_token_group<EB, InT, QUANT>(k_new, v_new, k_cache, v_cache, n0 + t, h, grp, slot, Hkv, D, bs,
+                                      k_inv, v_inv);
   }
 }
 
@@ -157,16 +228,14 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
     return pkv::fail(PKV_INVALID_ARG, "pkv_kv_cache_write: null pointer");
-  const int x = 16 / elem_bytes(kv_dtype);
-  const int64_t total = int64_t(num_tokens) * num_kv_heads * (head_dim / x);
-  const int64_t nwg = (total + 255) / 256;
-  if (nwg > INT32_MAX) return pkv::fail(PKV_INVALID_ARG, "pkv_kv_cache_write: too many tokens");
+  if (num_kv_heads > 65535) return pkv::fail(PKV_UNSUPPORTED, "pkv_kv_cache_write: num_kv_heads > 65535");
+  const int64_t nwg = (int64_t(num_tokens) + 15) / 16;
   const int64_t num_slots = int64_t(num_blocks) * block_size;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
   auto* kc = static_cast<uint8_t*>(k_cache);
   auto* vc = static_cast<uint8_t*>(v_cache);
-  const dim3 grid{unsigned(nwg)}, block{256u};
+  const dim3 grid{unsigned(nwg), unsigned(num_kv_heads)}, block{256u};
   if (kv_dtype == PKV_F32) {
     hipLaunchKernelGGL((kv_cache_write_kernel<4, float, false>), grid, block, 0, st,
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new), kc, vc,

@@ -125,3 +125,46 @@ def test_copy_on_write_step_leaves_the_shared_block_untouched():
     got = _pool_bits(dk, "bf16")
     assert np.array_equal(got[src], shared_before)
     assert np.array_equal(got, hk) and np.array_equal(_pool_bits(dv, "bf16"), hv)
+
+
+@pytest.mark.parametrize("in_dt,kv", COMBOS)
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 16), (128, 32)])
+def test_kv_cache_write_whole_subtiles_bit_exact(in_dt, kv, D, bs):
+    """Runs of 16 tokens that fill whole sub-tiles (the prefill pattern, written as whole
+    16-byte chunks), next to a misaligned run, a run with a skipped slot and scattered
+    single slots (the per-token path), all bit-exact against the oracle's pool model."""
+    require_gpu()
+    log(f"kv_cache_write whole sub-tiles {in_dt}->{kv} D={D} bs={bs}")
+    rng = np.random.default_rng(3 * D + bs)
+    NB, Hkv = 24, 3
+    hk, dk = _random_pool(rng, NB, Hkv, bs, D, kv)
+    hv, dv = _random_pool(rng, NB, Hkv, bs, D, kv)
+    sub_per_block = bs // 16
+    subtiles = rng.permutation(NB * sub_per_block)
+    runs = [np.arange(16) + 16 * int(st) for st in subtiles[:6]]        # whole sub-tiles
+    # A misaligned run covers the end of one sub-tile and the start of the next: take a
+    # pair of adjacent sub-tiles that no other run uses (slots must be distinct).
+    taken = set(subtiles[:6].tolist()) | set(subtiles[7:14].tolist())
+    mis = next(int(st) for st in subtiles[6:] if int(st) not in taken and int(st) + 1 not in taken
+               and int(st) + 1 < NB * sub_per_block and int(st) not in subtiles[7:14])
+    runs.append(np.arange(16) + 16 * mis + 3)                           # misaligned run
+    skipped = np.arange(16) + 16 * int(subtiles[7])
+    skipped[5] = -1                                                     # one token skipped
+    runs.append(skipped)
+    runs.append(16 * subtiles[8:14].astype(np.int64) + rng.integers(0, 16, 6))   # scattered
+    slots = np.concatenate(runs).astype(np.int64)
+    slots[(slots >= NB * bs)] = -1
+    used = slots[slots >= 0]
+    assert len(np.unique(used)) == len(used)
+    T = len(slots)
+    x = (rng.standard_normal((T, Hkv, D)) * 2).astype(np.float32)
+    y = (rng.standard_normal((T, Hkv, D)) * 0.7).astype(np.float32)
+    kn = x if in_dt == "f32" else bf16_bits_from_f32(x)
+    vn = y if in_dt == "f32" else bf16_bits_from_f32(y)
+    ks, vs = (np.float32(0.0117), np.float32(0.0049)) if kv == "fp8_e4m3fn" else (1.0, 1.0)
+    pkv.kv_cache_write(to_dev(kn, in_dt), to_dev(vn, in_dt), dk, dv, torch.from_numpy(slots).cuda(),
+                       k_scale=float(ks), v_scale=float(vs))
+    torch.cuda.synchronize()
+    opool.write(hk, hv, kn, vn, slots, in_dt, kv, bs, ks, vs)
+    assert np.array_equal(_pool_bits(dk, kv), hk)
+    assert np.array_equal(_pool_bits(dv, kv), hv)

@@ -43,6 +43,11 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=None,
                    help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
+    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks"], default=None,
+                   help="instead of the decode step, time one pool-maintenance kernel on the "
+                        "workload's pool: the KV-cache write of the whole batch (the prefill "
+                        "pattern) or copy_blocks of --pairs random block pairs")
+    p.add_argument("--pairs", type=int, default=1024)
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, time plain device-to-device copies of MIB MiB "
                         "(the reference kernel for scaling the HBM byte counters)")
@@ -99,6 +104,9 @@ def main():
 
     if args.copy_probe:
         _copy_probe(args.copy_probe)
+        return
+    if args.op:
+        _op_bench(args)
         return
 
     import torch
@@ -266,6 +274,67 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def _op_bench(args):
+    """Bandwidth of one pool-maintenance kernel (its own JSON line, not the headline)."""
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from synth import WORKLOADS, make_decode_case
+
+    wl = WORKLOADS[args.workload]
+    if wl.prefix_group:
+        raise SystemExit("--op runs on the decode workloads")
+    case = make_decode_case(wl, args.seed)
+    dev = torch.device("cuda:0")
+    kvt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}[wl.kv_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[wl.kv_dtype]
+    inb = 4 if wl.kv_dtype == "f32" else 2
+    Hkv, D, bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+    pools = [(pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev),
+              pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)) for _ in range(max(1, args.layers))]
+
+    def dev_tensor(arr):
+        if wl.kv_dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ks, vs = float(case.k_scale), float(case.v_scale)
+    if args.op == "kv_cache_write":
+        slots = torch.from_numpy(pkv.build_slot_mapping(case.block_tables, case.lengths.astype(np.int32), bs)).to(dev)
+        kt, vt = dev_tensor(case.k), dev_tensor(case.v)
+        T = int(slots.numel())
+        nbytes = T * Hkv * D * 2 * (inb + eb)           # read K, V in; write K, V out
+
+        def run(i):
+            k, v = pools[i % len(pools)]
+            pkv.kv_cache_write(kt, vt, k, v, slots, k_scale=ks, v_scale=vs)
+        what = f"{T} tokens x {Hkv} kv heads into their slots (prefill pattern)"
+    else:
+        rng = np.random.default_rng(args.seed)
+        ids = rng.permutation(case.num_blocks)
+        n = min(args.pairs, case.num_blocks // 2)
+        pairs = torch.from_numpy(np.stack([ids[:n], ids[n:2 * n]], 1).astype(np.int32)).to(dev)
+        nbytes = n * 2 * Hkv * bs * D * eb * 2          # K and V blocks, read + write
+
+        def run(i):
+            k, v = pools[i % len(pools)]
+            pkv.copy_blocks(k, v, pairs, D)
+        what = f"{n} random (src, dst) block pairs, whole blocks of K and V"
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    gbps = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"op": args.op, "workload": wl.name, "what": what, "us_per_call": round(us, 2),
+                      "bytes_read_plus_written": int(nbytes), "GBps": round(gbps, 1),
+                      "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
 def _prefix_step_bench(args, wl):

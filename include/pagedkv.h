@@ -29,6 +29,8 @@
  *     Launch errors are reported as PKV_HIP_ERROR; faults during execution surface at
  *     the caller's next synchronisation, as for any asynchronous HIP work.
  *   - No function aborts or throws across the ABI.
+ *   - Tensor pointers (q, out, k_new, v_new, the pools, the workspace) must be 16-byte
+ *     aligned; a misaligned one is rejected with PKV_INVALID_ARG.
  *
  * Physical KV pool layout (one K pool and one V pool, same shape)
  *   - Element type: float32, bfloat16 or fp8 e4m3fn (OCP E4M3: bias 7, max 448, no

@@ -955,6 +955,8 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
   if (append && (!k_new || !v_new || !k_cache_w || !v_cache_w))
     return pkv::fail(PKV_INVALID_ARG, "%s: k_new and v_new must both be given", fn);
+  if (!pkv::aligned16({out, q, k_cache, v_cache, k_new, v_new, workspace}))
+    return pkv::fail(PKV_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   KernelPair kp;
   pick_kernels(kd, D, bs, &kp);
   int splits = 0;

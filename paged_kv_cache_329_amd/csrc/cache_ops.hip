@@ -32,6 +32,37 @@ __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) {
   return __uint_as_float(uint32_t(*p) << 16);
 }
 
+// The 16 fp8 codes of 16 consecutive input elements held in `raw` (sizeof(InT) 16-byte
+// words, elements in memory order), packed into one 16-byte chunk.
+template <typename InT>
+__device__ __forceinline__ uint4 quantize16_regs(const uint4* raw, float inv) {
+  constexpr int PER = 16 / int(sizeof(InT));   // elements per 16-byte word
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int l = 0; l < 16 / PER; ++l) {
+    const uint32_t r[4] = {raw[l].x, raw[l].y, raw[l].z, raw[l].w};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = l * PER + i;
+      float f;
+      if constexpr (sizeof(InT) == 4) f = __uint_as_float(r[i]);
+      else f = __uint_as_float((i & 1) ? (r[i >> 1] & 0xFFFF0000u) : (r[i >> 1] << 16));
+      w[e >> 2] |= e4m3fn_from_f32(f * inv) << (8 * (e & 3));
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The same for 16 consecutive input elements at p (16-byte aligned).
+template <typename InT>
+__device__ __forceinline__ uint4 quantize16(const InT* p, float inv) {
+  constexpr int WORDS = int(sizeof(InT));      // 16 elements = sizeof(InT) 16-byte words
+  uint4 raw[WORDS];
+#pragma unroll
+  for (int l = 0; l < WORDS; ++l) raw[l] = reinterpret_cast<const uint4*>(p)[l];
+  return quantize16_regs<InT>(raw, inv);
+}
+
 // Writes dims d0 .. d0+X of token n, kv head h, into slot `slot` (one thread's share of the
 // per-token path).  K: the dims are one 16-byte chunk of the token's sub-tile; V: the X
 // elements land in X chunks that are 16 bytes apart (same position inside each).
@@ -59,11 +90,7 @@ __device__ __forceinline__ void write_token_group(const InT* __restrict__ k_new,
 #pragma unroll
     for (int e = 0; e < X; ++e) vd[int64_t(e) * X] = vs[e];
   } else {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < X; ++e)
-      w[e >> 2] |= e4m3fn_from_f32(load_as_f32(k_new + src + e) * k_inv) << (8 * (e & 3));
-    *reinterpret_cast<uint4*>(k_cache + kel) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(k_cache + kel) = quantize16(k_new + src, k_inv);
     uint8_t* vd = v_cache + vel0;
 #pragma unroll
     for (int e = 0; e < X; ++e)
@@ -78,57 +105,84 @@ __device__ __forceinline__ uint32_t cache_element(InT x, float inv) {
   else return uint32_t(x);
 }
 
-// One workgroup per (16 consecutive tokens, kv head).  When the 16 tokens go to the 16 slots
-// of one sub-tile in order (a prefill, or any run of appends that fills a sub-tile), the
-// workgroup writes that sub-tile's K and V regions whole: every thread stores complete
-// 16-byte chunks (K from one token's row, V assembled from the token rows staged in LDS),
-// so the stores are contiguous instead of scattered 2-byte writes.  Any other slot pattern
-// (decode appends, skipped or out-of-range slots, runs that cross sub-tiles) takes the
-// per-token path.
-template <int EB, typename InT, bool QUANT>
-__global__ __launch_bounds__(256) void kv_cache_write_kernel(
-    const InT* __restrict__ k_new, const InT* __restrict__ v_new, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slots, int T, int Hkv, int D,
-    int bs, int64_t num_slots, float k_inv, float v_inv) {
-  constexpr int X = 16 / EB;
-  __shared__ int64_t s_slot[16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[16 * 128 * sizeof(InT)];
-  const int tid = threadIdx.x;
-  const int h = blockIdx.y;
-  const int64_t n0 = int64_t(blockIdx.x) * 16;
-  const int cnt = int(T - n0 < 16 ? T - n0 : 16);
-  if (tid < 16) s_slot[tid] = tid < cnt ? slots[n0 + tid] : -1;
-  __syncthreads();
-  const int64_t s0 = s_slot[0];
-  bool whole = cnt == 16 && s0 >= 0 && s0 % 16 == 0 && s0 + 15 < num_slots;
-#pragma unroll
-  for (int i = 1; i < 16; ++i) whole = whole && s_slot[i] == s0 + i;
+// Threads per workgroup of the write kernel: one per 16-byte chunk of a sub-tile (D * b),
+// kept within [64, 256].
+constexpr int write_threads(int D, int EB) { return D * EB < 64 ? 64 : D * EB > 256 ? 256 : D * EB; }
 
-  if (whole) {
+// One workgroup per (16 consecutive tokens, kv head), the head varying fastest across
+// workgroups so that neighbouring workgroups read neighbouring input rows and write
+// neighbouring pool regions.  The workgroup owns tokens n0 .. n0+15.
+//
+// A run is 16 consecutive tokens whose slots are the 16 slots of one sub-tile in order (a
+// prefill writes its sequences' full sub-tiles this way, and so does any run of appends that
+// fills one).  Runs need not start at a multiple of 16 in the token list (sequences of a
+// prefill have arbitrary lengths), and two runs never overlap (slots are distinct).  The
+// workgroup that owns a run's first token writes the run's sub-tile whole: every thread
+// stores complete 16-byte chunks (K from one token's row, V assembled from the token rows
+// staged in LDS), so the stores are contiguous instead of scattered element writes.  Each
+// workgroup therefore looks at the slots of tokens n0-15 .. n0+30: at most one run starts
+// among its own tokens, and at most one run that started among the previous 15 tokens
+// reaches into them.  Its own tokens that no run covers (decode appends, partial sub-tiles,
+// skipped or out-of-range slots) take the per-token path.
+template <int EB, typename InT, bool QUANT, int D>
+__global__ __launch_bounds__(write_threads(D, EB)) void kv_cache_write_kernel(
+    const InT* __restrict__ k_new, const InT* __restrict__ v_new, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slots, int T, int Hkv, int bs,
+    int64_t num_slots, float k_inv, float v_inv) {
+  constexpr int X = 16 / EB;
+  constexpr int NT = write_threads(D, EB);
+  constexpr int ROW = D * int(sizeof(InT)) / 16;        // 16-byte words per token row
+  __shared__ int64_t s_slot[48];                        // entry k: slot of token n0 - 16 + k
+  __shared__ int s_run[2];
+  __shared__ __attribute__((aligned(16))) uint4 s_v[16 * ROW];
+  const int tid = threadIdx.x;
+  const int h = int(blockIdx.x % unsigned(Hkv));
+  const int64_t n0 = int64_t(blockIdx.x / unsigned(Hkv)) * 16;
+  const int cnt = int(T - n0 < 16 ? T - n0 : 16);
+  for (int k = tid; k < 48; k += NT) {
+    const int64_t n = n0 - 16 + k;
+    s_slot[k] = n >= 0 && n < T ? slots[n] : -1;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // Lane i < 31 tests whether a run starts at token n0 - 15 + i (entry i + 1).
+    bool ok = false;
+    if (tid < 31) {
+      const int64_t s0 = s_slot[tid + 1];
+      ok = s0 >= 0 && s0 % 16 == 0 && s0 + 15 < num_slots;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) ok = ok && s_slot[tid + 1 + i] == s0 + i;
+    }
+    const uint64_t m = __ballot(ok);
+    if (tid == 0) {
+      const uint64_t own = (m >> 15) & 0xFFFFu;   // starts at n0 .. n0+15
+      const uint64_t prev = m & 0x7FFFu;           // starts at n0-15 .. n0-1
+      // Offset of the run starting among the own tokens, or -1.
+      s_run[0] = own ? int(__builtin_ctzll(own)) : -1;
+      // A run starting at n0-15+b covers own tokens 0 .. b.
+      s_run[1] = prev ? 64 - int(__builtin_clzll(prev)) : 0;
+    }
+  }
+  __syncthreads();
+  const int r = s_run[0], covered = s_run[1];
+
+  if (r >= 0) {
+    const int64_t nr = n0 + r;                    // first token of the run
+    const int64_t s0 = s_slot[r + 16];
     const int64_t blk = s0 / bs;
     const int64_t sub = ((blk * Hkv + h) * int64_t(bs) + (s0 % bs)) * D;   // element index
-    // Stage the 16 tokens' V rows (row-major [16][D] of InT) in LDS.
-    const int row_chunks = D * int(sizeof(InT)) / 16;
-    for (int c = tid; c < 16 * row_chunks; c += 256) {
-      const int t = c / row_chunks, w = c % row_chunks;
-      reinterpret_cast<uint4*>(s_v)[c] =
-          reinterpret_cast<const uint4*>(v_new + ((n0 + t) * Hkv + h) * D)[w];
-    }
+    // Stage the run's V rows (row-major [16][D] of InT) in LDS.
+    for (int c = tid; c < 16 * ROW; c += NT)
+      s_v[c] = reinterpret_cast<const uint4*>(v_new + ((nr + c / ROW) * Hkv + h) * D)[c % ROW];
     __syncthreads();
     const InT* sv = reinterpret_cast<const InT*>(s_v);
-    for (int c = tid; c < D * EB; c += 256) {          // 16-byte chunks of the sub-tile
+    for (int c = tid; c < D * EB; c += NT) {           // 16-byte chunks of the sub-tile
       // K chunk c: token c % 16, dims X*(c/16) .. +X.
       const int t = c & 15, d0 = X * (c >> 4);
-      const InT* ks = k_new + ((n0 + t) * Hkv + h) * D + d0;
+      const InT* ks = k_new + ((nr + t) * Hkv + h) * D + d0;
       uint4 kc;
-      if constexpr (!QUANT) {
-        kc = *reinterpret_cast<const uint4*>(ks);
-      } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < X; ++e) w[e >> 2] |= e4m3fn_from_f32(load_as_f32(ks + e) * k_inv) << (8 * (e & 3));
-        kc = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      if constexpr (!QUANT) kc = *reinterpret_cast<const uint4*>(ks);
+      else kc = quantize16(ks, k_inv);
       *reinterpret_cast<uint4*>(k_cache + (sub + int64_t(c) * X) * EB) = kc;
       // V chunk c: tokens 4*((c/16)%4) + j (j < 4), dims (c/64)*4X + 16e + c%16 (e < X/4);
       // element e*4 + j.
@@ -144,16 +198,31 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
         }
       *reinterpret_cast<uint4*>(v_cache + (sub + int64_t(c) * X) * EB) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    return;
   }
-  const int groups = D / X;
-  for (int idx = tid; idx < cnt * groups; idx += 256) {
+  // Own tokens outside both runs: [covered, r) when a run starts here, else [covered, cnt).
+  const int lo = covered, hi = r >= 0 ? r : cnt;
+  constexpr int groups = D / X;
+  for (int idx = lo * groups + tid; idx < hi * groups; idx += NT) {
     const int t = idx / groups, grp = idx % groups;
-    const int64_t slot = s_slot[t];
+    const int64_t slot = s_slot[t + 16];
     if (slot < 0 || slot >= num_slots) continue;
     write_token_group<EB, InT, QUANT>(k_new, v_new, k_cache, v_cache, n0 + t, h, grp, slot, Hkv, D, bs,
                                       k_inv, v_inv);
   }
+}
+
+template <int EB, typename InT, bool QUANT>
+void launch_write(int D, unsigned nwg, hipStream_t st, const void* k_new, const void* v_new,
+                  uint8_t* kc, uint8_t* vc, const int64_t* slots, int T, int Hkv, int bs,
+                  int64_t num_slots, float k_inv, float v_inv) {
+  const auto* k = static_cast<const InT*>(k_new);
+  const auto* v = static_cast<const InT*>(v_new);
+  if (D == 64)
+    hipLaunchKernelGGL((kv_cache_write_kernel<EB, InT, QUANT, 64>), dim3(nwg), dim3(write_threads(64, EB)),
+                       0, st, k, v, kc, vc, slots, T, Hkv, bs, num_slots, k_inv, v_inv);
+  else
+    hipLaunchKernelGGL((kv_cache_write_kernel<EB, InT, QUANT, 128>), dim3(nwg), dim3(write_threads(128, EB)),
+                       0, st, k, v, kc, vc, slots, T, Hkv, bs, num_slots, k_inv, v_inv);
 }
 
 // grid.y = pair; each workgroup copies a strided share of the K and V block regions.
@@ -228,35 +297,29 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
     return pkv::fail(PKV_INVALID_ARG, "pkv_kv_cache_write: null pointer");
-  if (num_kv_heads > 65535) return pkv::fail(PKV_UNSUPPORTED, "pkv_kv_cache_write: num_kv_heads > 65535");
+  if (!pkv::aligned16({k_new, v_new, k_cache, v_cache}))
+    return pkv::fail(PKV_INVALID_ARG, "pkv_kv_cache_write: tensor pointers must be 16-byte aligned");
+  if ((int64_t(num_tokens) + 15) / 16 * num_kv_heads > int64_t(UINT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "pkv_kv_cache_write: too many tokens x kv heads");
   const int64_t nwg = (int64_t(num_tokens) + 15) / 16;
   const int64_t num_slots = int64_t(num_blocks) * block_size;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
   auto* kc = static_cast<uint8_t*>(k_cache);
   auto* vc = static_cast<uint8_t*>(v_cache);
-  const dim3 grid{unsigned(nwg), unsigned(num_kv_heads)}, block{256u};
-  if (kv_dtype == PKV_F32) {
-    hipLaunchKernelGGL((kv_cache_write_kernel<4, float, false>), grid, block, 0, st,
-                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), kc, vc,
-                       slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_slots,
-                       1.0f, 1.0f);
-  } else if (kv_dtype == PKV_BF16) {
-    hipLaunchKernelGGL((kv_cache_write_kernel<2, uint16_t, false>), grid, block, 0, st,
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       kc, vc, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
-                       num_slots, 1.0f, 1.0f);
-  } else if (in_dtype == PKV_BF16) {
-    hipLaunchKernelGGL((kv_cache_write_kernel<1, uint16_t, true>), grid, block, 0, st,
-                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                       kc, vc, slot_mapping, num_tokens, num_kv_heads, head_dim, block_size,
-                       num_slots, k_inv, v_inv);
-  } else {
-    hipLaunchKernelGGL((kv_cache_write_kernel<1, float, true>), grid, block, 0, st,
-                       static_cast<const float*>(k_new), static_cast<const float*>(v_new), kc, vc,
-                       slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_slots,
-                       k_inv, v_inv);
-  }
+  const unsigned grid = unsigned(nwg * num_kv_heads);   // token groups x kv heads
+  if (kv_dtype == PKV_F32)
+    launch_write<4, float, false>(head_dim, grid, st, k_new, v_new, kc, vc, slot_mapping, num_tokens,
+                                  num_kv_heads, block_size, num_slots, 1.0f, 1.0f);
+  else if (kv_dtype == PKV_BF16)
+    launch_write<2, uint16_t, false>(head_dim, grid, st, k_new, v_new, kc, vc, slot_mapping, num_tokens,
+                                     num_kv_heads, block_size, num_slots, 1.0f, 1.0f);
+  else if (in_dtype == PKV_BF16)
+    launch_write<1, uint16_t, true>(head_dim, grid, st, k_new, v_new, kc, vc, slot_mapping, num_tokens,
+                                    num_kv_heads, block_size, num_slots, k_inv, v_inv);
+  else
+    launch_write<1, float, true>(head_dim, grid, st, k_new, v_new, kc, vc, slot_mapping, num_tokens,
+                                 num_kv_heads, block_size, num_slots, k_inv, v_inv);
   return launch_status("pkv_kv_cache_write");
 }
 
@@ -273,6 +336,8 @@ extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_
   if (num_pairs == 0) return PKV_OK;
   if (!k_cache || !v_cache || !block_mapping)
     return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: null pointer");
+  if (!pkv::aligned16({k_cache, v_cache}))
+    return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: pools must be 16-byte aligned");
   if (num_pairs > 65535) return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: more than 65535 pairs");
   const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(kv_dtype);
   const int64_t chunks = block_bytes / 16;

@@ -101,6 +101,19 @@ def test_cache_ops_reject_on_host():
     assert lib.pkv_copy_blocks(None, None, None, 2, 8, 128, 24, 10, pkv.BF16, None) == 2
 
 
+def test_misaligned_tensors_are_rejected_on_host():
+    lib = pkv.lib()
+    a, m = ctypes.c_void_p(256), ctypes.c_void_p(264)   # 16-byte aligned / not
+    assert lib.pkv_kv_cache_write(a, m, a, a, a, 3, 8, 128, 16, 10, pkv.BF16, pkv.BF16,
+                                  1.0, 1.0, None) == 1
+    assert b"aligned" in lib.pkv_last_error()
+    assert lib.pkv_copy_blocks(a, m, a, 2, 8, 128, 16, 10, pkv.BF16, None) == 1
+    assert b"aligned" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_decode(a, m, a, a, a, a, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
+                                        pkv.F32, pkv.F32, 8, a, 1 << 30, None)
+    assert st == 1 and b"aligned" in lib.pkv_last_error()
+
+
 def test_build_slot_mapping_matches_definition():
     import numpy as np
     tables = np.array([[5, 2, -1], [7, -1, -1], [0, 0, 0]], dtype=np.int32)

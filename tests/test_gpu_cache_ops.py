@@ -128,7 +128,7 @@ def test_copy_on_write_step_leaves_the_shared_block_untouched():
 
 
 @pytest.mark.parametrize("in_dt,kv", COMBOS)
-@pytest.mark.parametrize("D,bs", [(64, 16), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 16), (128, 32), (64, 32)])
 def test_kv_cache_write_whole_subtiles_bit_exact(in_dt, kv, D, bs):
     """Runs of 16 tokens that fill whole sub-tiles (the prefill pattern, written as whole
     16-byte chunks), next to a misaligned run, a run with a skipped slot and scattered
@@ -156,6 +156,44 @@ def test_kv_cache_write_whole_subtiles_bit_exact(in_dt, kv, D, bs):
     slots[(slots >= NB * bs)] = -1
     used = slots[slots >= 0]
     assert len(np.unique(used)) == len(used)
+    T = len(slots)
+    x = (rng.standard_normal((T, Hkv, D)) * 2).astype(np.float32)
+    y = (rng.standard_normal((T, Hkv, D)) * 0.7).astype(np.float32)
+    kn = x if in_dt == "f32" else bf16_bits_from_f32(x)
+    vn = y if in_dt == "f32" else bf16_bits_from_f32(y)
+    ks, vs = (np.float32(0.0117), np.float32(0.0049)) if kv == "fp8_e4m3fn" else (1.0, 1.0)
+    pkv.kv_cache_write(to_dev(kn, in_dt), to_dev(vn, in_dt), dk, dv, torch.from_numpy(slots).cuda(),
+                       k_scale=float(ks), v_scale=float(vs))
+    torch.cuda.synchronize()
+    opool.write(hk, hv, kn, vn, slots, in_dt, kv, bs, ks, vs)
+    assert np.array_equal(_pool_bits(dk, kv), hk)
+    assert np.array_equal(_pool_bits(dv, kv), hv)
+
+
+@pytest.mark.parametrize("in_dt,kv", COMBOS)
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
+def test_kv_cache_write_ragged_prefill_bit_exact(in_dt, kv, D, bs):
+    """A prefill of sequences with ragged lengths into randomly placed blocks: full
+    sub-tiles start at every offset within the 16-token groups of the token list, runs
+    reach across group boundaries, and partial tail sub-tiles take the per-token path."""
+    require_gpu()
+    log(f"kv_cache_write ragged prefill {in_dt}->{kv} D={D} bs={bs}")
+    rng = np.random.default_rng(11 * D + bs)
+    lens = [1, 15, 16, 17, 33, 50, 64, 7, 31, 2, 48, 29, 16, 5, 95, 3]
+    Hkv = 2
+    need = sum((L + bs - 1) // bs for L in lens)
+    NB = need + 5
+    hk, dk = _random_pool(rng, NB, Hkv, bs, D, kv)
+    hv, dv = _random_pool(rng, NB, Hkv, bs, D, kv)
+    ids = rng.permutation(NB)
+    slots, used = [], 0
+    for L in lens:
+        nblk = (L + bs - 1) // bs
+        blocks = ids[used:used + nblk]
+        used += nblk
+        i = np.arange(L)
+        slots.append(blocks[i // bs].astype(np.int64) * bs + i % bs)
+    slots = np.concatenate(slots)
     T = len(slots)
     x = (rng.standard_normal((T, Hkv, D)) * 2).astype(np.float32)
     y = (rng.standard_normal((T, Hkv, D)) * 0.7).astype(np.float32)

@@ -22,6 +22,17 @@ Pinned by ``tests/test_oracle_attention.py``: a scalar brute force with math.fsu
 a hand-worked fixture (tests/golden/attention_hand_example.json), closed forms
 (L = 1, q = 0, L = 2), torch's float64 scaled_dot_product_attention and the
 shift / affine / permutation invariants of softmax attention.
+
+Several query tokens per sequence (``prefill_attention``): "What is PagedAttention?"
+(qubittool glossary), "How It Works: Map Logical to Physical Blocks", has a prefill
+allocate blocks for the whole input, and "PagedAttention: Optimizing KV Cache in vLLM"
+(grasp.study), "Conclusion", points at speculative decoding, where a target model checks
+several drafted tokens at once.  Neither page writes out the attention of those query
+tokens; the plainest reading, and the one decode already follows (the new token attends
+to every cached token and to itself), is causal attention: the sequence's last n_s tokens
+are the queries, and the query at position P attends to tokens 0..P.  A prefill is
+n_s = L_s, a prefill chunk or a verification is n_s < L_s, and n_s = 1 is decode.
+Pinned by ``tests/test_oracle_prefill.py``.
 """
 from __future__ import annotations
 
@@ -105,3 +116,76 @@ def prefix_step_case(case, seqs=None) -> np.ndarray:
         ks.append(kv_to_f64(k, wl.kv_dtype))
         vs.append(kv_to_f64(v, wl.kv_dtype))
     return decode_attention(q, ks, vs, case.scale, wl.group_size)
+
+
+def causal_query(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, P: int, scale: float,
+                 group_size: int) -> np.ndarray:
+    """One query token at position P over tokens 0..P of K / V ([L, Hkv, D] float64).
+
+    q_row: [Hq, D] float64.  Returns [Hq, D]; zero when P < 0.
+    """
+    Hq, D = q_row.shape
+    G = int(group_size)
+    out = np.zeros((Hq, D), dtype=np.float64)
+    if P < 0:
+        return out
+    Kp, Vp = K[:P + 1], V[:P + 1]
+    for g in range(Hq // G):
+        Qg = q_row[g * G:(g + 1) * G]                    # [G, D]
+        X = scale * (Qg @ Kp[:, g, :].T)                  # [G, P+1]
+        W = np.exp(X - X.max(axis=1, keepdims=True))
+        out[g * G:(g + 1) * G] = (W @ Vp[:, g, :]) / W.sum(axis=1, keepdims=True)
+    return out
+
+
+def prefill_attention(q: np.ndarray, ks, vs, q_lens, scale: float, group_size: int) -> np.ndarray:
+    """Causal softmax attention of the last n_s tokens of every sequence, in float64.
+
+    q:       [sum n_s, Hq, D] float64; sequence s's queries are rows
+             sum(n_0..n_{s-1}) .. + n_s, in position order.
+    ks, vs:  sequences of [L_s, Hkv, D] float64 arrays (logical token order), holding every
+             token of the sequence, the queries' own tokens included.
+    q_lens:  n_s per sequence.  Query i of sequence s sits at position P = L_s - n_s + i and
+             attends to tokens 0..P; a query with P < 0 (n_s > L_s) attends to nothing and
+             its output is zero.
+    Returns [sum n_s, Hq, D] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    T, Hq, D = q.shape
+    G = int(group_size)
+    assert Hq % G == 0
+    q_lens = [int(n) for n in q_lens]
+    assert sum(q_lens) == T
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    row = 0
+    for s, n in enumerate(q_lens):
+        K = np.asarray(ks[s], dtype=np.float64)
+        V = np.asarray(vs[s], dtype=np.float64)
+        L = K.shape[0]
+        assert V.shape == K.shape and (L == 0 or K.shape[1:] == (Hq // G, D))
+        for i in range(n):
+            out[row + i] = causal_query(q[row + i], K, V, L - n + i, scale, G)
+        row += n
+    return out
+
+
+def prefill_case(case, rows=None) -> np.ndarray:
+    """Oracle output for a ``synth.PrefillCase``, for all query rows or the listed ones.
+
+    Returns [len(rows), Hq, D] float64 in the order of ``rows`` (global query-row indices).
+    """
+    wl = case.wl
+    qs = np.asarray(case.query_start, dtype=np.int64)
+    rows = list(range(int(qs[-1]))) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(rows), wl.num_q_heads, wl.head_dim), dtype=np.float64)
+    decoded = {}
+    for k, r in enumerate(rows):
+        s = int(np.searchsorted(qs, r, side="right") - 1)
+        if s not in decoded:
+            decoded[s] = (kv_to_f64(case.seq_k(s), wl.kv_dtype, case.k_scale),
+                          kv_to_f64(case.seq_v(s), wl.kv_dtype, case.v_scale))
+        K, V = decoded[s]
+        n = int(qs[s + 1] - qs[s])
+        P = int(case.lengths[s]) - n + (r - int(qs[s]))
+        out[k] = causal_query(q_to_f64(case.q[r], wl.q_dtype), K, V, P, case.scale, wl.group_size)
+    return out

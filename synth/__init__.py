@@ -31,7 +31,10 @@ __all__ = [
     "WORKLOADS",
     "DecodeCase",
     "PrefixStepCase",
+    "PrefillCase",
     "make_decode_case",
+    "make_prefill_case",
+    "query_lengths",
     "make_prefix_step_case",
     "draw_lengths",
     "bf16_bits_from_f32",
@@ -54,6 +57,8 @@ class Workload:
     pool_blocks: int | None = None   # fixed pool size; None = ceil(1.1 * blocks in use)
     prefix_group: int = 0            # sequences per shared-prefix group (0 = no sharing)
     prefix_len: int = 0              # tokens in each group's shared prefix
+    query_dist: tuple = ("one",)     # query tokens per sequence: ("one",) | ("all",) = every
+                                     # token (a prefill) | ("fixed", n) = the last min(n, L)
 
     @property
     def group_size(self) -> int:
@@ -79,6 +84,23 @@ WORKLOADS: dict[str, Workload] = {
     # fp8 e4m3fn KV cache with per-tensor scales, bs 32, lengths U{2048..16384}.
     "fp8_kv": Workload("fp8_kv", 128, 32, 8, 128, 32, "bf16", "fp8_e4m3fn",
                        ("uniform", 2048, 16384)),
+    # Several query tokens per sequence, causal over the same pool.
+    # Small fp32 case with grouped heads, every token a query (a prefill).
+    "prefill_tiny_fp32": Workload("prefill_tiny_fp32", 4, 8, 4, 64, 16, "f32", "f32",
+                                  ("uniform", 1, 100), 64, query_dist=("all",)),
+    # Llama-3-8B prefill: 16 prompts of U{512..4096} tokens.
+    "prefill_llama3_8b_bf16": Workload("prefill_llama3_8b_bf16", 16, 32, 8, 128, 16, "bf16", "bf16",
+                                       ("uniform", 512, 4096), query_dist=("all",)),
+    # Chunked prefill: the last 512 tokens of contexts of U{1024..8192} tokens.
+    "chunked_prefill_llama3_8b_bf16": Workload("chunked_prefill_llama3_8b_bf16", 16, 32, 8, 128, 16,
+                                               "bf16", "bf16", ("uniform", 1024, 8192),
+                                               query_dist=("fixed", 512)),
+    # Speculative verification: 4 drafted tokens + 1 checked per sequence, decode-sized batch.
+    "spec_verify_llama3_8b_bf16": Workload("spec_verify_llama3_8b_bf16", 64, 32, 8, 128, 16, "bf16",
+                                           "bf16", ("uniform", 512, 4096), query_dist=("fixed", 5)),
+    # Prefill over an fp8 e4m3fn cache (bs 32).
+    "prefill_fp8_kv": Workload("prefill_fp8_kv", 16, 32, 8, 128, 32, "bf16", "fp8_e4m3fn",
+                               ("uniform", 512, 4096), query_dist=("all",)),
 }
 
 _N_STREAMS = 6  # lengths, permutation, q, K, V, extra
@@ -293,3 +315,48 @@ def make_prefix_step_case(wl: Workload, seed: int = 0, lengths=None) -> PrefixSt
     q = _draw_values(ss[2], (wl.batch, wl.num_q_heads, wl.head_dim), wl.q_dtype)
     return PrefixStepCase(wl, seed, lengths, num_blocks, free_order, root_k, root_v,
                           priv_k, priv_v, poffs, new_k, new_v, q)
+
+
+def query_lengths(wl: Workload, lengths: np.ndarray) -> np.ndarray:
+    """Query tokens per sequence (the last n_s of its L_s tokens) under ``wl.query_dist``."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    kind = wl.query_dist[0]
+    if kind == "one":
+        return np.minimum(lengths, 1)
+    if kind == "all":
+        return lengths.copy()
+    if kind == "fixed":
+        return np.minimum(lengths, int(wl.query_dist[1]))
+    raise ValueError(f"unknown query distribution {wl.query_dist!r}")
+
+
+@dataclass
+class PrefillCase(DecodeCase):
+    """A batch whose sequences each have n_s query tokens: the last n_s of their L_s tokens.
+
+    K / V hold every token, the queries' own included (a prefill writes them into the pool
+    before attention reads them).  ``q`` is [sum n_s, Hq, D]; ``query_start`` is the int32
+    prefix sum [B+1] of ``q_lens``.
+    """
+
+    q_lens: np.ndarray = None        # int64 [B]
+    query_start: np.ndarray = None   # int32 [B+1]
+
+    @property
+    def num_q_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def make_prefill_case(wl: Workload, seed: int = 0, lengths=None, q_lens=None) -> PrefillCase:
+    """Draw a multi-query batch: the decode case's lengths, pool and K/V, and a query
+    tensor of sum n_s rows drawn from the extra stream."""
+    base = make_decode_case(wl, seed, lengths)
+    q_lens = query_lengths(wl, base.lengths) if q_lens is None else np.asarray(q_lens, dtype=np.int64)
+    assert q_lens.shape == (wl.batch,) and np.all(q_lens >= 0)
+    qs = np.zeros(wl.batch + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(q_lens)
+    extra = np.random.SeedSequence(seed).spawn(_N_STREAMS)[5]
+    q = _draw_values(extra.spawn(1)[0], (int(qs[-1]), wl.num_q_heads, wl.head_dim), wl.q_dtype)
+    fields = {f.name: getattr(base, f.name) for f in dataclasses.fields(DecodeCase)}
+    fields["q"] = q
+    return PrefillCase(**fields, q_lens=q_lens, query_start=qs)

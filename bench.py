@@ -542,12 +542,16 @@ def _prefix_step_bench(args, wl):
     print(json.dumps(result), flush=True)
 
 
-def _kernel_sha() -> str:
+def _kernel_sha(files=("attention_decode.hip", "attention_tile.h")) -> str:
+    """Hash of the sources a profiled kernel is built from (traffic figures are reported
+    only while it matches)."""
     import hashlib
-    p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_329_amd", "csrc",
-                     "attention_decode.hip")
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in files:
+        p = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_329_amd", "csrc", name)
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

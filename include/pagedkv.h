@@ -216,6 +216,40 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
 pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
 
 /* ------------------------------------------------------------------------------------
+ * Multi-query attention with a causal mask over the same pool: a prefill, a chunk of a
+ * prefill, or the check of drafted tokens in speculative decoding.  "What is
+ * PagedAttention?" (glossary), "How It Works: Map Logical to Physical Blocks": a prefill
+ * allocates blocks for the whole input; "PagedAttention: Optimizing KV Cache in vLLM", §3:
+ * walking the blocks in logical order gives attention over contiguous K/V, and
+ * "Conclusion": speculative decoding checks drafted tokens against the cache.  The pages do
+ * not write out this attention; it is read as causal attention:
+ *
+ *   Sequence s has n_s = query_start[s+1] - query_start[s] query tokens, the last n_s of its
+ *   L_s = context_lens[s] tokens; query i (0 <= i < n_s) sits at position
+ *   P = L_s - n_s + i and attends to tokens 0..P.  All L_s tokens, the queries' own included,
+ *   must already be in the pool (pkv_kv_cache_write first).  A query with P < 0 gets zeros.
+ *
+ *   out, q         [num_q_tokens, Hq, D] of q_dtype, row-major; sequence s's queries are
+ *                  rows query_start[s] .. query_start[s+1]-1 in position order.
+ *   query_start    int32 [num_seqs + 1] (device), non-decreasing, from 0 to num_q_tokens;
+ *                  entries are clamped to [0, num_q_tokens].
+ *   max_query_len  host bound on every n_s: query rows past it in a sequence are neither
+ *                  computed nor written.
+ *   Every other argument as for pkv_paged_attention_decode.  No workspace; out is written
+ *   once per query row and head, nothing else is written.
+ * Limits: max_blocks_per_seq <= 16384 (the sequence's table entries are staged on chip);
+ * num_q_tokens * Hq < 2^31.
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, const int32_t* query_start,
+                                       int num_seqs, int num_q_tokens, int num_q_heads,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int num_blocks, int max_blocks_per_seq, int max_query_len,
+                                       float scale, float k_scale, float v_scale,
+                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",
  * glossary, "How It Works: Map Logical to Physical Blocks": a decode step appends into
  * the sequence's partly filled last block).

@@ -28,6 +28,7 @@ __all__ = [
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
+    "paged_attention_prefill",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -62,6 +63,7 @@ _SIGNATURES = {
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
+    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 2 + [_c_p], _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
@@ -243,6 +245,32 @@ def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens,
     """Phase 2 only (merges partials); same arguments and workspace as phase 1."""
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
                         context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            max_query_len, scale, k_scale=1.0, v_scale=1.0, stream=None):
+    """Causal multi-query attention (pkv_paged_attention_prefill): sequence s's queries are
+    q rows query_start[s] .. query_start[s+1]-1, its last tokens, each attending to every
+    token up to its own position.  q / out are [num_q_tokens, Hq, D]."""
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_q_tokens, num_q_heads, head_dim] of one dtype")
+    T, Hq, D = q.shape
+    NB, Hkv, bs = _pool_dims(k_cache, D)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and query_start must be int32")
+    B = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.dim() != 1 or query_start.shape != (B + 1,):
+        raise ValueError("block_tables [num_seqs, max_blocks], context_lens [num_seqs], query_start [num_seqs+1]")
+    ptrs = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+            _dev(query_start, "query_start")]
+    _check(lib().pkv_paged_attention_prefill(*ptrs, B, T, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                                             int(max_query_len), float(scale), float(k_scale),
+                                             float(v_scale), _dtype_code(q.dtype),
+                                             _dtype_code(k_cache.dtype), _stream(stream)))
+    return out
 
 
 def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,

@@ -22,7 +22,7 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "allocator.cpp", "cache_ops.hip", "attention_decode.hip"]
+SOURCES = ["status.cpp", "allocator.cpp", "cache_ops.hip", "attention_decode.hip", "attention_prefill.hip"]
 
 
 def _hipcc() -> str:

@@ -42,18 +42,14 @@
 #include <mutex>
 #include <unordered_map>
 
+#include "attention_tile.h"
 #include "kv_codec.h"
 #include "status.h"
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+using namespace pkv::tile;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWavesPerWG = 4;
 constexpr int kMaxGroup = 16;
 
@@ -78,74 +74,6 @@ struct DecodeArgs {
   uint8_t* v_cache_w;
   float k_inv, v_inv;  // float32 1/k_scale, 1/v_scale (fp8 caches)
 };
-
-template <int KV>
-struct KvTraits;
-template <>
-struct KvTraits<PKV_F32> {
-  static constexpr int EB = 4;   // bytes per cached element
-  static constexpr int QB = 4;   // bytes per q / out element
-};
-template <>
-struct KvTraits<PKV_BF16> {
-  static constexpr int EB = 2;
-  static constexpr int QB = 2;
-};
-template <>
-struct KvTraits<PKV_FP8_E4M3FN> {
-  static constexpr int EB = 1;
-  static constexpr int QB = 2;
-};
-
-// Cached K/V bytes are read exactly once per call, so they are loaded with the
-// non-temporal hint: on MI355X this lifts a random 4 KiB-chunk gather from about
-// 5.9 to 6.5 TB/s, because streaming data no longer displaces cache lines.
-__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
-}
-
-// Two e4m3fn codes (bytes 2*sel, 2*sel+1 of w) -> two bf16 in one dword, exactly.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16_k32(uint4 a, uint4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_bf16_k16(uint32_t a_lo, uint32_t a_hi, uint32_t b_lo,
-                                               uint32_t b_hi, f32x4 c) {
-  const uint2 a = make_uint2(a_lo, a_hi), b = make_uint2(b_lo, b_hi);
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float wave_max_rows(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
-}
-
-__device__ __forceinline__ float wave_sum_rows(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
 
 // Sum over the wave, returned as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_sum(int v) {
@@ -215,97 +143,6 @@ __device__ __forceinline__ int64_t share_begin(int64_t w, int64_t W, int64_t n) 
 // Index of the share holding work position x.
 __device__ __forceinline__ int64_t share_of(int64_t x, int64_t W, int64_t n) {
   return ((x + 1) * n - 1) / W;
-}
-
-template <int KV, int D>
-struct Frag {
-  using T = KvTraits<KV>;
-  static constexpr int NLOAD = D * T::EB / 64;            // 16-byte chunks per lane per sub-tile
-  static constexpr int QCH = (16 / T::EB) * T::QB / 16;   // 16-byte q chunks per K chunk
-  static constexpr int NT = D / 16;                        // 16-dim output tiles
-};
-
-// S^T for one sub-tile: c[j] = <K[token 4(l/16)+j], Q[head l%16]>.
-template <int KV, int D>
-__device__ __forceinline__ f32x4 qk_subtile(const uint4* kf, const uint4* qf) {
-  f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
-    if constexpr (KV == PKV_F32) {
-      c = mfma_f32_k4(__uint_as_float(kf[i].x), __uint_as_float(qf[i].x), c);
-      c = mfma_f32_k4(__uint_as_float(kf[i].y), __uint_as_float(qf[i].y), c);
-      c = mfma_f32_k4(__uint_as_float(kf[i].z), __uint_as_float(qf[i].z), c);
-      c = mfma_f32_k4(__uint_as_float(kf[i].w), __uint_as_float(qf[i].w), c);
-    } else if constexpr (KV == PKV_BF16) {
-      c = mfma_bf16_k32(kf[i], qf[i], c);
-    } else {
-      const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(kf[i].x), fp8x2_to_bf16x2<true>(kf[i].x),
-                                  fp8x2_to_bf16x2<false>(kf[i].y), fp8x2_to_bf16x2<true>(kf[i].y));
-      const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(kf[i].z), fp8x2_to_bf16x2<true>(kf[i].z),
-                                  fp8x2_to_bf16x2<false>(kf[i].w), fp8x2_to_bf16x2<true>(kf[i].w));
-      c = mfma_bf16_k32(lo, qf[2 * i + 0], c);
-      c = mfma_bf16_k32(hi, qf[2 * i + 1], c);
-    }
-  }
-  return c;
-}
-
-// acc[n] += V^T tile n . P^T, p[j] = probability of token 4(l/16)+j for head l%16.
-template <int KV, int D>
-__device__ __forceinline__ void pv_subtile(f32x4* acc, const uint4* vf, const float* p) {
-  if constexpr (KV == PKV_F32) {
-#pragma unroll
-    for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
-      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].x), p[0], acc[i]);
-      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].y), p[1], acc[i]);
-      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].z), p[2], acc[i]);
-      acc[i] = mfma_f32_k4(__uint_as_float(vf[i].w), p[3], acc[i]);
-    }
-  } else {
-    const uint32_t b_lo = pack_bf16x2(p[0], p[1]), b_hi = pack_bf16x2(p[2], p[3]);
-#pragma unroll
-    for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
-      if constexpr (KV == PKV_BF16) {
-        acc[2 * i + 0] = mfma_bf16_k16(vf[i].x, vf[i].y, b_lo, b_hi, acc[2 * i + 0]);
-        acc[2 * i + 1] = mfma_bf16_k16(vf[i].z, vf[i].w, b_lo, b_hi, acc[2 * i + 1]);
-      } else {
-        const uint32_t w[4] = {vf[i].x, vf[i].y, vf[i].z, vf[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[4 * i + e] = mfma_bf16_k16(fp8x2_to_bf16x2<false>(w[e]), fp8x2_to_bf16x2<true>(w[e]),
-                                         b_lo, b_hi, acc[4 * i + e]);
-      }
-    }
-  }
-}
-
-// Zero the V elements of tokens 4(l/16)+j that are not valid (vmask bit j clear).
-template <int KV, int D>
-__device__ __forceinline__ void mask_v(uint4* vf, uint32_t vmask) {
-  uint32_t m[4];
-  if constexpr (KV == PKV_F32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m[j] = (vmask >> j) & 1u ? 0xFFFFFFFFu : 0u;
-  } else if constexpr (KV == PKV_BF16) {
-    const uint32_t m01 = ((vmask & 1u) ? 0x0000FFFFu : 0u) | ((vmask & 2u) ? 0xFFFF0000u : 0u);
-    const uint32_t m23 = ((vmask & 4u) ? 0x0000FFFFu : 0u) | ((vmask & 8u) ? 0xFFFF0000u : 0u);
-    m[0] = m01; m[1] = m23; m[2] = m01; m[3] = m23;
-  } else {
-    uint32_t b = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b |= ((vmask >> j) & 1u) ? (0xFFu << (8 * j)) : 0u;
-    m[0] = m[1] = m[2] = m[3] = b;
-  }
-#pragma unroll
-  for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
-    vf[i].x &= m[0]; vf[i].y &= m[1]; vf[i].z &= m[2]; vf[i].w &= m[3];
-  }
-}
-
-
-// Decoded value of an e4m3fn code (exact, through bf16).
-__device__ __forceinline__ float e4m3fn_value(uint32_t code) {
-  return __uint_as_float(fp8x2_to_bf16x2<false>(code) << 16);
 }
 
 // Element bits the cache stores for input element bits x (q's dtype) of k_new / v_new: f32

@@ -1,0 +1,365 @@
+// Multi-query paged attention for gfx950 (MI355X): several query tokens per sequence with a
+// causal mask, over the same block tables and pool as decode.  This covers a prefill (every
+// token of the prompt is a query), a chunk of a prefill (the last n tokens of a longer
+// context) and the check of drafted tokens in speculative decoding.
+//
+// What is computed:
+//  * "What is PagedAttention?" (qubittool glossary), "How It Works: Map Logical to Physical
+//    Blocks": a prefill allocates blocks for the whole input, so the prompt's K/V sit in the
+//    pool behind the sequence's block table before its attention runs.
+//  * "PagedAttention: Optimizing KV Cache in vLLM" (grasp.study), §3 "Making it Work: The
+//    PagedAttention Kernel": the kernel walks the blocks in logical order with a running
+//    softmax and reaches attention over a contiguous layout; "Conclusion": speculative
+//    decoding, where several drafted tokens are checked against the cache in one pass.
+//  * Neither page writes out the attention of several query tokens; the reading taken is
+//    causal attention: sequence s's n_s queries are its last n_s tokens, and the query at
+//    position P = L_s - n_s + i attends to tokens 0..P.  n_s = 1 is decode.
+//
+// How it maps onto CDNA4
+//  * Columns: a column is one (query token, query head) pair of one kv head; a workgroup
+//    of 4 waves owns 64*CT consecutive columns of one (sequence, kv head), each wave 16*CT
+//    (CT matrix-instruction column tiles).  With G query heads per kv head the columns of
+//    one query token are adjacent, so every K/V byte a workgroup stages serves all of them.
+//  * Staging: each step the workgroup copies SUBS 16-token sub-tiles of K and of V (32 KiB
+//    for bf16, D 128) from the pool into LDS, one 16-byte chunk per thread per load, with the
+//    next step's loads in flight while the current step computes (two LDS buffers, one
+//    barrier per step).  The sequence's block-table entries are staged in LDS once, so a
+//    chunk's address depends on an LDS read, not on a global load.
+//  * Matrix products: the pool layout makes chunk 64*i + lane of a sub-tile exactly lane's
+//    operand (attention_tile.h): QK^T with K as the A operand and q (held in registers) as B,
+//    then PV with the probabilities reused in place as B.  Each K/V operand read from LDS
+//    feeds CT products.
+//  * Causal mask and running softmax (base 2): token t is kept for a column iff t <= P of
+//    that column; the rest get -inf by select.  A step that lies entirely past a wave's last
+//    position is skipped by that wave (it still stages its share of the loads).  V elements
+//    of slots at or past L_s are zeroed (an unwritten tail slot may hold NaN).
+//  * Order: the workgroups of one (sequence, kv head) are launched last tile first, so the
+//    tiles with the most keys start earliest.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "attention_tile.h"
+#include "status.h"
+
+namespace {
+
+using namespace pkv::tile;
+
+constexpr int kWaves = 4;
+constexpr int kMaxTableBytes = 64 * 1024;   // block-table entries staged in LDS, at most
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int B, Hkv, G, num_blocks, max_blocks, num_q_tokens;
+  float qk_scale_log2;  // scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// Sub-tiles staged per step: 16 KiB of K plus 16 KiB of V, at most 8 sub-tiles.
+template <int KV, int D>
+constexpr int step_subtiles() {
+  constexpr int sub = 16 * D * KvTraits<KV>::EB;
+  return 16384 / sub > 8 ? 8 : 16384 / sub;
+}
+
+template <int KV, int D, int BS, int CT>
+__global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(PrefillArgs a) {
+  using F = Frag<KV, D>;
+  using T = KvTraits<KV>;
+  constexpr int X = 16 / T::EB;
+  constexpr int SUB_BYTES = 16 * D * T::EB;
+  constexpr int SUB_CHUNKS = SUB_BYTES / 16;
+  constexpr int NSB = BS / 16;
+  constexpr int64_t REGION = int64_t(BS) * D * T::EB;
+  constexpr int SUBS = step_subtiles<KV, D>();
+  constexpr int STEP_TOK = 16 * SUBS;
+  constexpr int COLS = kWaves * 16 * CT;
+  constexpr int STAGE_CHUNKS = 2 * SUBS * SUB_CHUNKS;      // K then V
+  constexpr int PER_THREAD = STAGE_CHUNKS / 256;
+  static_assert(STAGE_CHUNKS % 256 == 0, "staging tiling");
+  __shared__ __attribute__((aligned(16))) uint4 stage[2][STAGE_CHUNKS];
+  extern __shared__ int32_t s_tbl[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.z, g = blockIdx.y;
+  const int tile = int(gridDim.x) - 1 - int(blockIdx.x);
+
+  int q0 = a.query_start[s], q1 = a.query_start[s + 1];
+  q0 = std::min(std::max(q0, 0), a.num_q_tokens);
+  q1 = std::min(std::max(q1, q0), a.num_q_tokens);
+  const int n = q1 - q0;
+  const int col0 = tile * COLS;
+  if (col0 >= n * a.G) return;
+  int L = a.context_lens[s];
+  L = std::max(L, 0);
+  if (int64_t(L) > int64_t(a.max_blocks) * BS) L = a.max_blocks * BS;
+  const int last_q = std::min(n - 1, (col0 + COLS - 1) / a.G);
+  const int ntok = std::max(L - n + last_q + 1, 0);      // keys the workgroup reads
+  const int nsub = (ntok + 15) / 16;
+  const int nsteps = (nsub + SUBS - 1) / SUBS;
+  const int nblk = (ntok + BS - 1) / BS;
+
+  const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+  for (int j = tid; j < nblk; j += 256) s_tbl[j] = trow[j];
+
+  // This lane's columns: (query qi, head hh) for column col0 + 16*(wave*CT + ct) + lane%16.
+  const int row = lane >> 4;
+  int pos[CT];
+  int wave_pmax = -1;
+  uint4 qf[CT][F::NLOAD * F::QCH];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int c = col0 + 16 * (wave * CT + ct) + (lane & 15);
+    const int qi = c / a.G, hh = c % a.G;
+    const bool ok = qi < n;
+    pos[ct] = ok ? L - n + qi : -1;
+    wave_pmax = std::max(wave_pmax, pos[ct]);
+    const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                          ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
+#pragma unroll
+    for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+      for (int cc = 0; cc < F::QCH; ++cc)
+        qf[ct][i * F::QCH + cc] =
+            ok ? *reinterpret_cast<const uint4*>(qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * cc)
+               : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wave_pmax = std::max(wave_pmax, __shfl_xor(wave_pmax, o));
+  wave_pmax = __builtin_amdgcn_readfirstlane(wave_pmax);
+
+  f32x4 acc[CT][F::NT];
+  float m_run[CT], l_run[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+    for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
+
+  const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
+  const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
+  const int64_t block_stride = int64_t(a.Hkv) * REGION;
+  __syncthreads();   // s_tbl
+
+  // Chunk tid + 256*r of a step: K or V, sub-tile u, chunk w.  Sub-tiles past the keys the
+  // workgroup reads and blocks outside [0, num_blocks) stage zeros.
+  uint4 pre[PER_THREAD];
+  auto fetch = [&](int step) {
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + 256 * r;
+      const int which = ci / (SUBS * SUB_CHUNKS);
+      const int u = (ci / SUB_CHUNKS) % SUBS;
+      const int w = ci % SUB_CHUNKS;
+      const int k = step * SUBS + u;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k < nsub) {
+        const int phys = s_tbl[k / NSB];
+        if (unsigned(phys) < unsigned(a.num_blocks))
+          v = *reinterpret_cast<const uint4*>((which ? vbase : kbase) + int64_t(phys) * block_stride +
+                                              (k % NSB) * SUB_BYTES + w * 16);
+      }
+      pre[r] = v;
+    }
+  };
+
+  if (nsteps > 0) fetch(0);
+  for (int step = 0; step < nsteps; ++step) {
+    uint4* buf = stage[step & 1];
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) buf[tid + 256 * r] = pre[r];
+    if (step + 1 < nsteps) fetch(step + 1);
+    __syncthreads();
+    const int tok_step = step * STEP_TOK;
+    if (tok_step <= wave_pmax) {
+#pragma unroll
+      for (int u0 = 0; u0 < SUBS; u0 += 2) {
+        // Two sub-tiles per running-softmax update.
+        float sc[CT][2][4];
+        uint4 kf[F::NLOAD];
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const int u = u0 + uu;
+#pragma unroll
+          for (int i = 0; i < F::NLOAD; ++i) kf[i] = buf[u * SUB_CHUNKS + 64 * i + lane];
+          const int t0 = tok_step + 16 * u + 4 * row;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[ct][uu][j] = t0 + j <= pos[ct] ? c[j] * a.qk_scale_log2 : -INFINITY;
+          }
+        }
+        float p[CT][2][4];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          float cmax = -INFINITY;
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sc[ct][uu][j]);
+          cmax = wave_max_rows(cmax);
+          const float m_new = fmaxf(m_run[ct], cmax);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;   // column with nothing yet
+          const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+          m_run[ct] = m_new;
+          l_run[ct] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              p[ct][uu][j] = __builtin_amdgcn_exp2f(sc[ct][uu][j] - m_use);   // 0 where masked
+              l_run[ct] += p[ct][uu][j];
+            }
+        }
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const int u = u0 + uu;
+          uint4 vf[F::NLOAD];
+#pragma unroll
+          for (int i = 0; i < F::NLOAD; ++i) vf[i] = buf[(SUBS + u) * SUB_CHUNKS + 64 * i + lane];
+          const int t0 = tok_step + 16 * u + 4 * row;
+          uint32_t vm = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vm |= (t0 + j < L ? 1u : 0u) << j;
+          mask_v<KV, D>(vf, vm);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct][uu]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const float l_tot = wave_sum_rows(l_run[ct]);
+    const int c = col0 + 16 * (wave * CT + ct) + (lane & 15);
+    const int qi = c / a.G, hh = c % a.G;
+    if (qi >= n) continue;
+    const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
+    const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+#pragma unroll
+    for (int nn = 0; nn < F::NT; ++nn) {
+      const int d = 16 * nn + 4 * row;
+      if constexpr (KV == PKV_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) =
+            make_float4(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv, acc[ct][nn][2] * inv, acc[ct][nn][3] * inv);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) =
+            make_uint2(pack_bf16x2(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv),
+                       pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
+      }
+    }
+  }
+}
+
+using PrefillFn = void (*)(PrefillArgs);
+
+template <int KV, int D, int BS>
+constexpr int prefill_col_tiles() {
+  return KV == PKV_F32 ? 1 : 2;
+}
+
+template <int KV, int D, int BS>
+PrefillFn prefill_fn() {
+  return paged_attention_prefill_kernel<KV, D, BS, prefill_col_tiles<KV, D, BS>()>;
+}
+
+template <int KV>
+bool pick_prefill(int D, int bs, PrefillFn* fn, int* cols) {
+  const int ct = KV == PKV_F32 ? 1 : 2;
+  *cols = kWaves * 16 * ct;
+  if (D == 64 && bs == 16) *fn = prefill_fn<KV, 64, 16>();
+  else if (D == 64 && bs == 32) *fn = prefill_fn<KV, 64, 32>();
+  else if (D == 128 && bs == 16) *fn = prefill_fn<KV, 128, 16>();
+  else if (D == 128 && bs == 32) *fn = prefill_fn<KV, 128, 32>();
+  else return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attention_prefill(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_q_tokens,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    int max_blocks_per_seq, int max_query_len, float scale, float k_scale, float v_scale,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, void* stream) {
+  const char* fn = "pkv_paged_attention_prefill";
+  const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads;
+  if (B < 0 || num_q_tokens < 0 || max_query_len < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_seqs=%d num_q_tokens=%d max_query_len=%d Hq=%d Hkv=%d", fn,
+                     B, num_q_tokens, max_query_len, Hq, Hkv);
+  const bool combo_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) ||
+                        (q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3FN));
+  if (!combo_ok)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: q_dtype=%d kv_dtype=%d", fn, int(q_dtype), int(kv_dtype));
+  if (!((head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32)))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: head_dim=%d block_size=%d", fn, head_dim, block_size);
+  if (num_blocks <= 0 || max_blocks_per_seq < 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_blocks=%d max_blocks_per_seq=%d", fn, num_blocks,
+                     max_blocks_per_seq);
+  if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
+      k_scale == INFINITY || v_scale == INFINITY)
+    return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (B == 0 || num_q_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || !query_start ||
+      (max_blocks_per_seq > 0 && !block_tables))
+    return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
+  if (!pkv::aligned16({out, q, k_cache, v_cache}))
+    return pkv::fail(PKV_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (B > 65535 || Hkv > 65535)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
+  if (int64_t(num_q_tokens) * Hq > int64_t(INT32_MAX) || int64_t(max_query_len) * (Hq / Hkv) > int64_t(INT32_MAX) / 2)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tokens", fn);
+  const int64_t tbl_bytes = int64_t(max_blocks_per_seq) * 4;
+  if (tbl_bytes > kMaxTableBytes)
+    return pkv::fail(PKV_UNSUPPORTED, "%s: max_blocks_per_seq=%d exceeds %d", fn, max_blocks_per_seq,
+                     kMaxTableBytes / 4);
+
+  PrefillFn kfn = nullptr;
+  int cols = 0;
+  bool ok = kv_dtype == PKV_F32    ? pick_prefill<PKV_F32>(head_dim, block_size, &kfn, &cols)
+            : kv_dtype == PKV_BF16 ? pick_prefill<PKV_BF16>(head_dim, block_size, &kfn, &cols)
+                                   : pick_prefill<PKV_FP8_E4M3FN>(head_dim, block_size, &kfn, &cols);
+  if (!ok) return pkv::fail(PKV_UNSUPPORTED, "%s: no kernel for this shape", fn);
+  const int G = Hq / Hkv;
+  const int64_t tiles = (int64_t(max_query_len) * G + cols - 1) / cols;
+  if (tiles > int64_t(INT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tiles", fn);
+
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_q_tokens = num_q_tokens;
+  a.qk_scale_log2 = scale * k_scale * kLog2e;
+  a.v_scale = v_scale;
+  hipLaunchKernelGGL(kfn, dim3(unsigned(tiles), unsigned(Hkv), unsigned(B)), dim3(kWaves * 64),
+                     size_t(std::max<int64_t>(tbl_bytes, 4)), reinterpret_cast<hipStream_t>(stream), a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
+  return PKV_OK;
+}

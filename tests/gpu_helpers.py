@@ -155,3 +155,21 @@ def prefix_step(case, a, k, v, members, num_splits=0):
                                case.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return out, cows, tables, lens
+
+
+def prefill(case, k, v, tables=None, lengths=None, query_start=None, q=None, max_query_len=None):
+    """Multi-query attention of a PrefillCase through pkv.paged_attention_prefill."""
+    wl = case.wl
+    tables = case.block_tables if tables is None else tables
+    lengths = case.lengths if lengths is None else lengths
+    qs = case.query_start if query_start is None else query_start
+    qd = to_dev(case.q if q is None else q, wl.q_dtype)
+    if max_query_len is None:
+        max_query_len = int(np.max(np.diff(qs))) if len(qs) > 1 else 0
+    out = torch.empty_like(qd)
+    pkv.paged_attention_prefill(out, qd, k, v, torch.from_numpy(np.ascontiguousarray(tables, np.int32)).cuda(),
+                                torch.from_numpy(np.asarray(lengths, np.int32)).cuda(),
+                                torch.from_numpy(np.asarray(qs, np.int32)).cuda(), max_query_len,
+                                case.scale, float(case.k_scale), float(case.v_scale))
+    torch.cuda.synchronize()
+    return out

@@ -1,0 +1,140 @@
+"""Causal multi-query paged attention (prefill, prefill chunks, drafted-token checks) on the
+GPU against the fp64 oracle.
+
+Small cases finish in seconds on the oracle yet span several 16-token sub-tiles, several
+staging steps and query tiles, ragged tails and partial column tiles, with unused slots and
+blocks poisoned with NaN.  Tolerances as for decode: fp32 max |d| <= 1e-5; bf16 and fp8
+|d| <= 2e-2 + 1e-2 |ref| per element.
+"""
+import numpy as np
+import pytest
+
+from oracle import attention as oatt
+from synth import WORKLOADS, Workload, make_prefill_case
+
+from gpu_helpers import as_f64, assert_close, decode, log, pack, prefill, raw_bytes, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "prefill_tiny_fp32": WORKLOADS["prefill_tiny_fp32"],
+    "prefill_bf16": WORKLOADS["prefill_llama3_8b_bf16"].scaled(batch=3, length_dist=("uniform", 1, 300)),
+    "chunk_bf16": WORKLOADS["chunked_prefill_llama3_8b_bf16"].scaled(
+        batch=4, length_dist=("uniform", 1, 400), query_dist=("fixed", 70)),
+    "verify_bf16": WORKLOADS["spec_verify_llama3_8b_bf16"].scaled(batch=6, length_dist=("uniform", 1, 500)),
+    "prefill_fp8": WORKLOADS["prefill_fp8_kv"].scaled(batch=3, length_dist=("uniform", 1, 300)),
+    # Other shapes: D 64 / bs 32 / G 2, G 16, G 1, G 3 (column tiles cross query tokens),
+    # f32 with D 128 and bs 32, fp8 with D 64.
+    "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 3, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 200),
+                                 query_dist=("fixed", 50)),
+    "bf16_g16": Workload("bf16_g16", 2, 32, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 150),
+                         query_dist=("all",)),
+    "bf16_g1": Workload("bf16_g1", 2, 4, 4, 128, 16, "bf16", "bf16", ("uniform", 60, 260),
+                        query_dist=("all",)),
+    "bf16_g3": Workload("bf16_g3", 3, 6, 2, 64, 16, "bf16", "bf16", ("uniform", 1, 120),
+                        query_dist=("fixed", 33)),
+    "f32_d128_bs32_g4": Workload("f32_d128_bs32_g4", 2, 16, 4, 128, 32, "f32", "f32", ("uniform", 1, 150),
+                                 query_dist=("all",)),
+    "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 200),
+                                query_dist=("fixed", 40)),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("seed", [0, 1])
+def test_parity_small(name, seed):
+    require_gpu()
+    wl = SMALL[name]
+    case = make_prefill_case(wl, seed)
+    log(f"prefill parity {name} seed={seed} lengths={case.lengths.tolist()} q_lens={case.q_lens.tolist()}")
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v))
+    assert_close(got, oatt.prefill_case(case), wl.kv_dtype, name)
+
+
+def test_edge_query_counts():
+    """n_s = 0, n_s = L_s, n_s > L_s (the first queries sit before position 0: zeros),
+    L_s = 0, a single token, and lengths on sub-tile and step boundaries."""
+    require_gpu()
+    wl = SMALL["prefill_bf16"].scaled(batch=9)
+    lengths = np.array([5, 16, 64, 65, 1, 0, 31, 128, 3])
+    q_lens = np.array([0, 16, 10, 65, 1, 2, 40, 1, 7])
+    case = make_prefill_case(wl, 3, lengths=lengths, q_lens=q_lens)
+    log(f"prefill edges lengths={lengths.tolist()} q_lens={q_lens.tolist()}")
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v))
+    ref = oatt.prefill_case(case)
+    assert_close(got, ref, wl.kv_dtype, "edges")
+    qs = case.query_start
+    assert np.all(got[qs[5]:qs[6]] == 0)            # L = 0: no keys at all
+    assert np.all(got[qs[6]:qs[6] + 9] == 0)        # n = 40 > L = 31: first 9 queries see nothing
+
+
+def test_max_query_len_bounds_the_rows_written():
+    require_gpu()
+    wl = SMALL["chunk_bf16"]
+    case = make_prefill_case(wl, 4)
+    k, v = pack(case)
+    cap = 20
+    got = prefill(case, k, v, max_query_len=cap)
+    full = prefill(case, k, v)
+    qs = case.query_start
+    for s in range(wl.batch):
+        a, b = int(qs[s]), int(qs[s + 1])
+        m = min(b - a, cap)
+        assert raw_bytes(got[a:a + m]) == raw_bytes(full[a:a + m])
+
+
+def test_one_query_per_sequence_matches_decode():
+    require_gpu()
+    wl = SMALL["verify_bf16"].scaled(query_dist=("one",), length_dist=("uniform", 1, 900))
+    case = make_prefill_case(wl, 5)
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v))
+    dec = as_f64(decode(case, k, v, q=case.q))
+    assert_close(got, oatt.prefill_case(case), wl.kv_dtype, "prefill n=1")
+    assert np.max(np.abs(got - dec)) <= 2e-2
+
+
+def test_chunks_and_block_placement_do_not_change_bits():
+    """Each output column runs the same arithmetic whatever the other queries of its tile
+    and wherever the blocks sit: the queries computed in two chunks (the first over the
+    tokens that exist when it runs) and over a permuted pool give the same bytes."""
+    require_gpu()
+    wl = SMALL["prefill_bf16"].scaled(batch=2, length_dist=("uniform", 150, 300))
+    case = make_prefill_case(wl, 6)
+    k, v = pack(case)
+    whole = prefill(case, k, v)
+    qs = case.query_start
+    for s in range(wl.batch):
+        L = int(case.lengths[s])
+        a = int(qs[s])
+        split = 37 + 20 * s
+        one = make_prefill_case(wl.scaled(batch=1), 6, lengths=[L], q_lens=[L])
+        one.q = case.q[a:a + L]
+        one.k, one.v = case.seq_k(s), case.seq_v(s)
+        one.offsets = np.array([0, L])
+        ko, vo = pack(one)
+        first = prefill(one, ko, vo, lengths=[split], query_start=[0, split], q=one.q[:split])
+        second = prefill(one, ko, vo, query_start=[0, L - split], q=one.q[split:])
+        assert raw_bytes(first) == raw_bytes(whole[a:a + split])
+        assert raw_bytes(second) == raw_bytes(whole[a + split:a + L])
+    # A different physical placement of the same logical blocks.
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(case.num_blocks)
+    tables = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1).astype(np.int32)
+    k2, v2 = pack(case, tables=tables)
+    assert raw_bytes(prefill(case, k2, v2, tables=tables)) == raw_bytes(whole)
+
+
+def test_large_logits_stay_finite():
+    require_gpu()
+    wl = SMALL["prefill_bf16"]
+    case = make_prefill_case(wl, 7)
+    q32 = case.q.view(np.uint16).astype(np.uint32) << 16
+    big = (q32.view(np.float32) * 30.0).astype(np.float32)
+    import torch
+    case.q = torch.from_numpy(big).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v))
+    assert_close(got, oatt.prefill_case(case), wl.kv_dtype, "large logits")

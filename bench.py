@@ -27,6 +27,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E peak (AMD public figure)
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (AMD public figure)
 EVENT_EVERY = 5          # timed steps per sampled split-kernel duration
 METRIC = "paged decode attention: KV GB/s (% HBM peak) and µs/step, Llama-3-8B shape"
 
@@ -116,6 +117,8 @@ def main():
     wl = WORKLOADS[args.workload]
     if wl.prefix_group:
         return _prefix_step_bench(args, wl)
+    if wl.query_dist[0] != "one":
+        return _multi_query_bench(args, wl)
     t0 = time.perf_counter()
     case = make_decode_case(wl, args.seed)
     _log(f"[bench] generated {wl.name} seed={args.seed} in {time.perf_counter() - t0:.1f}s; "
@@ -271,6 +274,168 @@ def main():
                      "traffic_unit": "HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, "
                                      "scaled by a plain copy of known size)",
                      "algorithmic_bytes": kv_bytes, "kernel": "paged_attention_split_kernel (decode step with append)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def _multi_query_bench(args, wl):
+    """Causal multi-query attention (prefill, prefill chunk, drafted-token check): one step is
+    one pkv_paged_attention_prefill call over the whole batch, on one of `layers` pools.
+
+    Algorithmic work: every query at position P attends to P + 1 keys, 4 * D flops per key and
+    query head (QK^T and PV), and every K/V byte of the batch is read at least once per kv
+    head.  The roofline is the one the arithmetic intensity puts the workload under: MFMA
+    (bf16, 2.5 PFLOP/s) above the ridge of 2.5e15 / 8e12 flop/B, HBM below it.
+    """
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from synth import make_prefill_case
+
+    t0 = time.perf_counter()
+    case = make_prefill_case(wl, args.seed)
+    _log(f"[bench] generated {wl.name} seed={args.seed} in {time.perf_counter() - t0:.1f}s; "
+         f"sum L = {int(case.lengths.sum())}, query tokens = {case.num_q_tokens}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}[wl.kv_dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[wl.kv_dtype]
+    B, Hq, Hkv, D, bs = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+
+    def dev_tensor(arr, storage):
+        if storage == "f32":
+            return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    store = "f32" if wl.kv_dtype == "f32" else "bf16"
+    lens32 = case.lengths.astype(np.int32)
+    slots_dev = torch.from_numpy(pkv.build_slot_mapping(case.block_tables, lens32, bs)).to(dev)
+    k_tok, v_tok = dev_tensor(case.k, store), dev_tensor(case.v, store)
+    pools = []
+    for _ in range(args.layers):
+        k = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)
+        v = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, kvt, dev)
+        pkv.kv_cache_write(k_tok, v_tok, k, v, slots_dev, k_scale=float(case.k_scale), v_scale=float(case.v_scale))
+        pools.append((k, v))
+    del k_tok, v_tok, slots_dev
+    q = dev_tensor(case.q, wl.q_dtype)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(case.block_tables).to(dev)
+    lens = torch.from_numpy(lens32).to(dev)
+    qstart = torch.from_numpy(case.query_start.astype(np.int32)).to(dev)
+    max_q = int(case.q_lens.max())
+    stream = torch.cuda.current_stream(dev)
+    ks, vs = float(case.k_scale), float(case.v_scale)
+
+    def step(i, ev=None):
+        k, v = pools[i % len(pools)]
+        if ev is not None:
+            pkv.set_launch_events(ev[0], ev[1])
+        pkv.paged_attention_prefill(out, q, k, v, tables, lens, qstart, max_q, case.scale, ks, vs)
+
+    def new_events(n):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for pair in evs:
+            for e in pair:
+                e.record(stream)
+        torch.cuda.synchronize()
+        return evs
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    events = dict(zip(sampled, new_events(len(sampled))))
+    _log(f"[bench] warmup done; timing {args.steps} steps over {len(pools)} layer pools")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events.get(i))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    kernel_us = statistics.mean(e[0].elapsed_time(e[1]) for e in events.values()) * 1e3
+
+    # Keys per query: P + 1 for P = L - n + i >= 0.
+    keys = 0
+    for L, n in zip(case.lengths.tolist(), case.q_lens.tolist()):
+        first = L - n + 1                       # keys of query 0
+        lo = max(first, 1)
+        hi = L                                  # keys of the last query
+        if hi >= lo:
+            keys += (lo + hi) * (hi - lo + 1) // 2
+    flops = keys * Hq * 4 * D
+    sum_l = int(case.lengths.sum())
+    kv_bytes = sum_l * Hkv * D * 2 * eb
+    us_per_step = elapsed / args.steps * 1e6
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = flops / kv_bytes > ridge
+    if mfma_bound:
+        metric, unit = "attention TFLOP/s", "TFLOP/s"
+        value = flops / (us_per_step * 1e-6) / 1e12
+        achieved = flops / (kernel_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops": flops}
+    else:
+        metric, unit = "KV GB/s", "GB/s"
+        value = kv_bytes / (us_per_step * 1e-6) / 1e9
+        achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes": kv_bytes}
+    roof["kernel"] = "paged_attention_prefill_kernel"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attention as oatt
+        _log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
+        nrows = min(case.num_q_tokens, 512)
+        rows = np.linspace(0, case.num_q_tokens - 1, nrows).astype(np.int64)
+        qs = case.query_start.astype(np.int64)
+        t_cpu0 = time.perf_counter()
+        oatt.prefill_case(case, rows)
+        t_cpu = time.perf_counter() - t_cpu0
+        sample_keys = 0
+        for r in rows.tolist():
+            s_ = int(np.searchsorted(qs, r, side="right") - 1)
+            P = int(case.lengths[s_]) - int(case.q_lens[s_]) + (r - int(qs[s_]))
+            sample_keys += max(P + 1, 0)
+        sflops = sample_keys * Hq * 4 * D
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = 1
+        if mfma_bound:
+            cval, cunit = sflops / t_cpu / 1e12, "TFLOP/s"
+        else:
+            # The sample's share of the batch's work, in the metric's bytes.
+            cval, cunit = kv_bytes * (sample_keys / max(keys, 1)) / t_cpu / 1e9, "GB/s"
+        cpu = {"value": round(cval, 6), "unit": cunit, "cores": threads, "kind": "oracle",
+               "sample": f"{nrows} query rows spread evenly over the batch ({sample_keys} keys in all), fp64 "
+                         f"numpy oracle incl. decoding each touched sequence's K/V to fp64, {t_cpu:.1f} s"}
+
+    result = {
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_step / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8_e4m3fn": "fp8_e4m3fn+bf16"}[wl.kv_dtype],
+        "data": "synthetic (seeded N(0,1) q/K/V, random physical block permutation)",
+        "config": {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "block_size": bs, "kv_dtype": wl.kv_dtype, "context": list(wl.length_dist),
+                   "queries": list(wl.query_dist), "sum_context": sum_l, "query_tokens": case.num_q_tokens,
+                   "num_blocks": case.num_blocks, "seed": args.seed, "layer_pools": len(pools)},
+        "us_per_step": round(us_per_step, 2),
+        "flops": flops,
+        "kv_bytes": kv_bytes,
+        "kernel_us": {"paged_attention_prefill": round(kernel_us, 2)},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

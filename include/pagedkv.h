@@ -208,9 +208,10 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
                                        int num_splits, void* workspace, size_t workspace_bytes,
                                        void* stream);
 
-/* Measurement aid: the next split pass launched on the calling thread (by any attention or
- * decode-step entry point) records start_event when its kernel begins and stop_event when
- * it ends, as part of its own dispatch (hipExtLaunchKernel), so that the events time the
+/* Measurement aid: the next split pass launched on the calling thread (by any decode or
+ * decode-step entry point), or the next multi-query attention kernel
+ * (pkv_paged_attention_prefill), records start_event when its kernel begins and stop_event
+ * when it ends, as part of its own dispatch (hipExtLaunchKernel), so that the events time the
  * kernel alone; the setting then clears.  start_event / stop_event are hipEvent_t handles
  * created with timing enabled (either may be NULL).  Always returns PKV_OK. */
 pkv_status pkv_set_launch_events(void* start_event, void* stop_event);

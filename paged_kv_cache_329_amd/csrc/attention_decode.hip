@@ -767,9 +767,6 @@ size_t workspace_bytes_for(int splits, int B, int G, int D) {
 
 enum Phase { kBoth, kSplitOnly, kMergeOnly };
 
-// Events the next split-pass launch on this thread records at its start and end.
-thread_local hipEvent_t t_launch_start = nullptr, t_launch_stop = nullptr;
-
 // k_new / v_new non-null: the decode step with append (the split pass stores each
 // sequence's token at position L-1 from k_new / v_new into the writable caches).
 pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, const void* k_new,
@@ -839,13 +836,13 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   if (phase != kMergeOnly) {
     const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
     KernelFn kfn = append ? kp.split_append : kp.split;
-    if (t_launch_start || t_launch_stop) {
+    void *ev0 = nullptr, *ev1 = nullptr;
+    if (pkv::take_launch_events(&ev0, &ev1)) {
       // The dispatch itself records the events, so they time the kernel alone.
       void* kargs[] = {&a};
-      hipEvent_t e0 = t_launch_start, e1 = t_launch_stop;
-      t_launch_start = t_launch_stop = nullptr;
       hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kfn), dim3(wgs),
-                                        dim3(kWavesPerWG * 64), kargs, 0, hs, e0, e1, 0);
+                                        dim3(kWavesPerWG * 64), kargs, 0, hs,
+                                        static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
       if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
     } else {
       hipLaunchKernelGGL(kfn, dim3(wgs), dim3(kWavesPerWG * 64), 0, hs, a);
@@ -901,12 +898,6 @@ pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_
   out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,     \
       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
       scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes, stream
-
-pkv_status pkv_set_launch_events(void* start_event, void* stop_event) {
-  t_launch_start = static_cast<hipEvent_t>(start_event);
-  t_launch_stop = static_cast<hipEvent_t>(stop_event);
-  return PKV_OK;
-}
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_decode", kBoth, PKV_DECODE_ARGS);

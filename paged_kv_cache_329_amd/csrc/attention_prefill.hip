@@ -35,6 +35,7 @@
 //    of slots at or past L_s are zeroed (an unwritten tail slot may hold NaN).
 //  * Order: the workgroups of one (sequence, kv head) are launched last tile first, so the
 //    tiles with the most keys start earliest.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -357,8 +358,19 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.num_q_tokens = num_q_tokens;
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
-  hipLaunchKernelGGL(kfn, dim3(unsigned(tiles), unsigned(Hkv), unsigned(B)), dim3(kWaves * 64),
-                     size_t(std::max<int64_t>(tbl_bytes, 4)), reinterpret_cast<hipStream_t>(stream), a);
+  const dim3 grid{unsigned(tiles), unsigned(Hkv), unsigned(B)}, block{unsigned(kWaves * 64)};
+  const size_t lds = size_t(std::max<int64_t>(tbl_bytes, 4));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void *ev0 = nullptr, *ev1 = nullptr;
+  if (pkv::take_launch_events(&ev0, &ev1)) {
+    // The dispatch itself records the events, so they time the kernel alone.
+    void* kargs[] = {&a};
+    hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kfn), grid, block, kargs, lds, hs,
+                                      static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
+  } else {
+    hipLaunchKernelGGL(kfn, grid, block, lds, hs, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
   return PKV_OK;

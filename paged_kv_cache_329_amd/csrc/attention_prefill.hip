@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   // This lane's columns: (query qi, head hh) for column col0 + 16*(wave*CT + ct) + lane%16.
   const int row = lane >> 4;
   int pos[CT];
-  int wave_pmax = -1;
+  int wave_pmax = -1, wave_pmin = INT32_MAX;
   uint4 qf[CT][F::NLOAD * F::QCH];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -124,6 +124,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
     const bool ok = qi < n;
     pos[ct] = ok ? L - n + qi : -1;
     wave_pmax = std::max(wave_pmax, pos[ct]);
+    wave_pmin = std::min(wave_pmin, pos[ct]);
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
                           ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
 #pragma unroll
@@ -135,9 +136,14 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
                : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) wave_pmax = std::max(wave_pmax, __shfl_xor(wave_pmax, o));
+  for (int o = 32; o > 0; o >>= 1) {
+    wave_pmax = std::max(wave_pmax, __shfl_xor(wave_pmax, o));
+    wave_pmin = std::min(wave_pmin, __shfl_xor(wave_pmin, o));
+  }
   wave_pmax = __builtin_amdgcn_readfirstlane(wave_pmax);
+  wave_pmin = __builtin_amdgcn_readfirstlane(wave_pmin);
 
+  // Running max in raw logit units (before the scale), sum and accumulators per column.
   f32x4 acc[CT][F::NT];
   float m_run[CT], l_run[CT];
 #pragma unroll
@@ -184,14 +190,19 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
     __syncthreads();
     const int tok_step = step * STEP_TOK;
     if (tok_step <= wave_pmax) {
+      // Masks only where they can bite: the causal mask on steps that reach past the wave's
+      // lowest position, the V mask on steps that reach the slots at or past L.
+      const bool causal = tok_step + STEP_TOK - 1 > wave_pmin;
+      const bool tail = tok_step + STEP_TOK > L;
+      const float sl2 = a.qk_scale_log2;
 #pragma unroll
       for (int u0 = 0; u0 < SUBS; u0 += 2) {
-        // Two sub-tiles per running-softmax update.
-        float sc[CT][2][4];
-        uint4 kf[F::NLOAD];
+        // Two sub-tiles (32 tokens) per running-softmax update and per PV product.
+        float sc[CT][2][4];   // raw logits; -inf where masked
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
           const int u = u0 + uu;
+          uint4 kf[F::NLOAD];
 #pragma unroll
           for (int i = 0; i < F::NLOAD; ++i) kf[i] = buf[u * SUB_CHUNKS + 64 * i + lane];
           const int t0 = tok_step + 16 * u + 4 * row;
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
           for (int ct = 0; ct < CT; ++ct) {
             const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sc[ct][uu][j] = t0 + j <= pos[ct] ? c[j] * a.qk_scale_log2 : -INFINITY;
+            for (int j = 0; j < 4; ++j) sc[ct][uu][j] = !causal || t0 + j <= pos[ct] ? c[j] : -INFINITY;
           }
         }
         float p[CT][2][4];
@@ -211,35 +222,45 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
 #pragma unroll
             for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sc[ct][uu][j]);
           cmax = wave_max_rows(cmax);
-          const float m_new = fmaxf(m_run[ct], cmax);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;   // column with nothing yet
-          const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
-          m_run[ct] = m_new;
-          l_run[ct] *= alpha;
+          // The accumulators are rescaled only when some column's max grew by more than
+          // 2^8 in probability: until then p = 2^(s - m) stays below 256, which float32 sums
+          // and bf16 operands hold without loss of relative precision.
+          if (__any((cmax - m_run[ct]) * sl2 > 8.f)) {
+            const float m_new = fmaxf(m_run[ct], cmax);
+            const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
+            m_run[ct] = m_new;
+            l_run[ct] *= alpha;
 #pragma unroll
-          for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+            for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+          }
+          const float m_off = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
 #pragma unroll
           for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              p[ct][uu][j] = __builtin_amdgcn_exp2f(sc[ct][uu][j] - m_use);   // 0 where masked
+              p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][uu][j], sl2, m_off));   // 0 where masked
               l_run[ct] += p[ct][uu][j];
             }
         }
+        uint4 vf0[F::NLOAD], vf1[F::NLOAD];
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const int u = u0 + uu;
-          uint4 vf[F::NLOAD];
-#pragma unroll
-          for (int i = 0; i < F::NLOAD; ++i) vf[i] = buf[(SUBS + u) * SUB_CHUNKS + 64 * i + lane];
-          const int t0 = tok_step + 16 * u + 4 * row;
-          uint32_t vm = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vm |= (t0 + j < L ? 1u : 0u) << j;
-          mask_v<KV, D>(vf, vm);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct][uu]);
+        for (int i = 0; i < F::NLOAD; ++i) {
+          vf0[i] = buf[(SUBS + u0) * SUB_CHUNKS + 64 * i + lane];
+          vf1[i] = buf[(SUBS + u0 + 1) * SUB_CHUNKS + 64 * i + lane];
         }
+        if (tail) {
+          const int t0 = tok_step + 16 * u0 + 4 * row;
+          uint32_t vm0 = 0, vm1 = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            vm0 |= (t0 + j < L ? 1u : 0u) << j;
+            vm1 |= (t0 + 16 + j < L ? 1u : 0u) << j;
+          }
+          mask_v<KV, D>(vf0, vm0);
+          mask_v<KV, D>(vf1, vm1);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) pv_pair<KV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
       }
     }
   }

@@ -61,8 +61,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> two bf16 (round to nearest even) in one dword, lo in the low half
+// (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Two e4m3fn codes (bytes 2*sel, 2*sel+1 of w) -> two bf16 in one dword, exactly.
@@ -88,14 +92,22 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48 hold one
+// column).  v_permlane16_swap exchanges the odd rows of one register with the even rows of
+// the other and v_permlane32_swap the upper half of one with the lower half of the other, so
+// applied to two copies of v they leave each lane holding v at l and at l^16 (then l^32).
 __device__ __forceinline__ float wave_max_rows(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float wave_sum_rows(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int KV, int D>
@@ -183,6 +195,38 @@ __device__ __forceinline__ void mask_v(uint4* vf, uint32_t vmask) {
   }
 }
 
+
+// acc[n] += V^T tile n . P^T over two sub-tiles at once (32 tokens, one k = 32 product per
+// tile for bf16 and fp8).  The product's k index 8r + j (j < 4) is token 4r + j of the first
+// sub-tile and 8r + 4 + j token 4r + j of the second, for both operands: lane l (r = l/16)
+// holds, for its dim, the first sub-tile's V chunk half next to the second's, and the
+// probabilities p0[j], p1[j] it already has from QK.
+template <int KV, int D>
+__device__ __forceinline__ void pv_pair(f32x4* acc, const uint4* vf0, const uint4* vf1, const float* p0,
+                                        const float* p1) {
+  if constexpr (KV == PKV_F32) {
+    pv_subtile<KV, D>(acc, vf0, p0);
+    pv_subtile<KV, D>(acc, vf1, p1);
+  } else {
+    const uint4 b = make_uint4(pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                               pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3]));
+#pragma unroll
+    for (int i = 0; i < Frag<KV, D>::NLOAD; ++i) {
+      if constexpr (KV == PKV_BF16) {
+        acc[2 * i + 0] = mfma_bf16_k32(make_uint4(vf0[i].x, vf0[i].y, vf1[i].x, vf1[i].y), b, acc[2 * i + 0]);
+        acc[2 * i + 1] = mfma_bf16_k32(make_uint4(vf0[i].z, vf0[i].w, vf1[i].z, vf1[i].w), b, acc[2 * i + 1]);
+      } else {
+        const uint32_t w0[4] = {vf0[i].x, vf0[i].y, vf0[i].z, vf0[i].w};
+        const uint32_t w1[4] = {vf1[i].x, vf1[i].y, vf1[i].z, vf1[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[4 * i + e] = mfma_bf16_k32(make_uint4(fp8x2_to_bf16x2<false>(w0[e]), fp8x2_to_bf16x2<true>(w0[e]),
+                                                    fp8x2_to_bf16x2<false>(w1[e]), fp8x2_to_bf16x2<true>(w1[e])),
+                                         b, acc[4 * i + e]);
+      }
+    }
+  }
+}
 
 // Decoded value of an e4m3fn code (exact, through bf16).
 __device__ __forceinline__ float e4m3fn_value(uint32_t code) {

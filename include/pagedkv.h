@@ -238,7 +238,7 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *                  computed nor written.
  *   Every other argument as for pkv_paged_attention_decode.  No workspace; out is written
  *   once per query row and head, nothing else is written.
- * Limits: max_blocks_per_seq <= 16384 (the sequence's table entries are staged on chip);
+ * Limits: max_blocks_per_seq <= 16376 (the sequence's table entries are staged on chip);
  * num_q_tokens * Hq < 2^31.
  * ------------------------------------------------------------------------------------ */
 pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,

@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "attention_tile.h"
 #include "status.h"
@@ -50,6 +51,7 @@ using namespace pkv::tile;
 
 constexpr int kWaves = 4;
 constexpr int kMaxTableBytes = 64 * 1024;   // block-table entries staged in LDS, at most
+constexpr int kTblPad = 8;                  // -1 entries after them (a step reads at most 7 past)
 
 struct PrefillArgs {
   void* out;
@@ -109,22 +111,25 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   const int nsteps = (nsub + SUBS - 1) / SUBS;
   const int nblk = (ntok + BS - 1) / BS;
 
+  // The table entries the workgroup reads, then kTblPad entries of -1: a step's lookups
+  // past the last block land there instead of outside the array.
   const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-  for (int j = tid; j < nblk; j += 256) s_tbl[j] = trow[j];
+  for (int j = tid; j < nblk + kTblPad; j += 256) s_tbl[j] = j < nblk ? trow[j] : -1;
 
   // This lane's columns: (query qi, head hh) for column col0 + 16*(wave*CT + ct) + lane%16.
   const int row = lane >> 4;
   int pos[CT];
-  int wave_pmax = -1, wave_pmin = INT32_MAX;
+  int wave_pmax = -1;
   uint4 qf[CT][F::NLOAD * F::QCH];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int c = col0 + 16 * (wave * CT + ct) + (lane & 15);
     const int qi = c / a.G, hh = c % a.G;
     const bool ok = qi < n;
-    pos[ct] = ok ? L - n + qi : -1;
-    wave_pmax = std::max(wave_pmax, pos[ct]);
-    wave_pmin = std::min(wave_pmin, pos[ct]);
+    // A column past the sequence's queries is computed unmasked (over q = 0, finite) and
+    // never written; it does not extend the wave's key range.
+    pos[ct] = ok ? L - n + qi : INT32_MAX;
+    wave_pmax = std::max(wave_pmax, ok ? pos[ct] : -1);
     const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
                           ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
 #pragma unroll
@@ -136,12 +141,8 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
                : make_uint4(0u, 0u, 0u, 0u);
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    wave_pmax = std::max(wave_pmax, __shfl_xor(wave_pmax, o));
-    wave_pmin = std::min(wave_pmin, __shfl_xor(wave_pmin, o));
-  }
+  for (int o = 32; o > 0; o >>= 1) wave_pmax = std::max(wave_pmax, __shfl_xor(wave_pmax, o));
   wave_pmax = __builtin_amdgcn_readfirstlane(wave_pmax);
-  wave_pmin = __builtin_amdgcn_readfirstlane(wave_pmin);
 
   // Running max in raw logit units (before the scale), sum and accumulators per column.
   f32x4 acc[CT][F::NT];
@@ -160,9 +161,19 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   __syncthreads();   // s_tbl
 
   // Chunk tid + 256*r of a step: K or V, sub-tile u, chunk w.  Sub-tiles past the keys the
-  // workgroup reads and blocks outside [0, num_blocks) stage zeros.
+  // workgroup reads and blocks outside [0, num_blocks) are read from block 0 (always in
+  // bounds) and staged as zeros; zmask marks them (rare: the last step, or a bad table entry).
+  //
+  // LDS layout of a step: K sub-tiles in pool order, then V.  For bf16 the V chunks of each
+  // pair of sub-tiles (2p, 2p+1) are interleaved by 8-byte halves, [pair][half e][chunk w]
+  // [sub-tile parity]: one 16-byte read of (p, e, w) is then exactly the k = 32 PV operand
+  // {sub-tile 2p half e, sub-tile 2p+1 half e} of output tile 2i+e, with no register moves.
+  constexpr bool VPAIR = KV == PKV_BF16;
+  __builtin_assume(tid < 256);
   uint4 pre[PER_THREAD];
+  uint32_t zmask = 0;
   auto fetch = [&](int step) {
+    zmask = 0;
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
       const int ci = tid + 256 * r;
@@ -170,85 +181,138 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
       const int u = (ci / SUB_CHUNKS) % SUBS;
       const int w = ci % SUB_CHUNKS;
       const int k = step * SUBS + u;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (k < nsub) {
-        const int phys = s_tbl[k / NSB];
-        if (unsigned(phys) < unsigned(a.num_blocks))
-          v = *reinterpret_cast<const uint4*>((which ? vbase : kbase) + int64_t(phys) * block_stride +
-                                              (k % NSB) * SUB_BYTES + w * 16);
+      // k / NSB < nblk + 7 (a step starts below nsub), inside the padded table.
+      const int phys = s_tbl[k / NSB];
+      const bool ok = k < nsub && unsigned(phys) < unsigned(a.num_blocks);
+      zmask |= ok ? 0u : 1u << r;
+      pre[r] = *reinterpret_cast<const uint4*>((which ? vbase : kbase) +
+                                               (ok ? int64_t(phys) * block_stride + (k % NSB) * SUB_BYTES : 0) +
+                                               w * 16);
+    }
+  };
+  auto stage_write = [&](uint4* buf) {
+    if (__any(zmask != 0)) {
+#pragma unroll
+      for (int r = 0; r < PER_THREAD; ++r)
+        if ((zmask >> r) & 1u) pre[r] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < PER_THREAD; ++r) {
+      const int ci = tid + 256 * r;
+      if (!VPAIR || ci < SUBS * SUB_CHUNKS) {
+        buf[ci] = pre[r];
+      } else {
+        const int u = (ci / SUB_CHUNKS) % SUBS, w = ci % SUB_CHUNKS;
+        uint2* vb = reinterpret_cast<uint2*>(buf + SUBS * SUB_CHUNKS);
+        const int base = (u >> 1) * 2 * SUB_CHUNKS;
+        vb[2 * (base + w) + (u & 1)] = make_uint2(pre[r].x, pre[r].y);
+        vb[2 * (base + SUB_CHUNKS + w) + (u & 1)] = make_uint2(pre[r].z, pre[r].w);
       }
-      pre[r] = v;
     }
   };
 
-  if (nsteps > 0) fetch(0);
-  for (int step = 0; step < nsteps; ++step) {
-    uint4* buf = stage[step & 1];
+  // One step's work for this wave; MASK: apply the causal mask and zero V of slots at or
+  // past L (the steps on the diagonal and the last ones).
+  const float sl2 = a.qk_scale_log2;
+  auto compute = [&](const uint4* buf, int tok_step, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool TAIL = MASK;
 #pragma unroll
-    for (int r = 0; r < PER_THREAD; ++r) buf[tid + 256 * r] = pre[r];
-    if (step + 1 < nsteps) fetch(step + 1);
-    __syncthreads();
-    const int tok_step = step * STEP_TOK;
-    if (tok_step <= wave_pmax) {
-      // Masks only where they can bite: the causal mask on steps that reach past the wave's
-      // lowest position, the V mask on steps that reach the slots at or past L.
-      const bool causal = tok_step + STEP_TOK - 1 > wave_pmin;
-      const bool tail = tok_step + STEP_TOK > L;
-      const float sl2 = a.qk_scale_log2;
+    for (int u0 = 0; u0 < SUBS; u0 += 2) {
+      // Two sub-tiles (32 tokens) per running-softmax update and per PV product.
+      float sc[CT][2][4];   // raw logits; -inf where masked
 #pragma unroll
-      for (int u0 = 0; u0 < SUBS; u0 += 2) {
-        // Two sub-tiles (32 tokens) per running-softmax update and per PV product.
-        float sc[CT][2][4];   // raw logits; -inf where masked
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = u0 + uu;
+        uint4 kf[F::NLOAD];
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const int u = u0 + uu;
-          uint4 kf[F::NLOAD];
-#pragma unroll
-          for (int i = 0; i < F::NLOAD; ++i) kf[i] = buf[u * SUB_CHUNKS + 64 * i + lane];
-          const int t0 = tok_step + 16 * u + 4 * row;
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[ct][uu][j] = !causal || t0 + j <= pos[ct] ? c[j] : -INFINITY;
-          }
-        }
-        float p[CT][2][4];
+        for (int i = 0; i < F::NLOAD; ++i) kf[i] = buf[u * SUB_CHUNKS + 64 * i + lane];
+        const int t0 = tok_step + 16 * u + 4 * row;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          float cmax = -INFINITY;
+          const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
 #pragma unroll
-          for (int uu = 0; uu < 2; ++uu)
+          for (int j = 0; j < 4; ++j) sc[ct][uu][j] = !MASK || t0 + j <= pos[ct] ? c[j] : -INFINITY;
+        }
+      }
+      float p[CT][2][4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sc[ct][uu][j]);
-          cmax = wave_max_rows(cmax);
-          // The accumulators are rescaled only when some column's max grew by more than
-          // 2^8 in probability: until then p = 2^(s - m) stays below 256, which float32 sums
-          // and bf16 operands hold without loss of relative precision.
-          if (__any((cmax - m_run[ct]) * sl2 > 8.f)) {
-            const float m_new = fmaxf(m_run[ct], cmax);
-            const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
-            m_run[ct] = m_new;
-            l_run[ct] *= alpha;
+      for (int ct = 0; ct < CT; ++ct) {
+        float cmax = -INFINITY;
 #pragma unroll
-            for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sc[ct][uu][j]);
+        cmax = wave_max_rows(cmax);
+        // The accumulators are rescaled only when some column's max grew by more than 2^8 in
+        // probability: until then p = 2^(s - m) stays below 256, which float32 sums and bf16
+        // operands hold without loss of relative precision.
+        if (__any((cmax - m_run[ct]) * sl2 > 8.f)) {
+          const float m_new = fmaxf(m_run[ct], cmax);
+          const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
+          m_run[ct] = m_new;
+          l_run[ct] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+        }
+        const float m_off = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][uu][j], sl2, m_off));   // 0 where masked
+            l_run[ct] += p[ct][uu][j];
           }
-          const float m_off = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
+      }
+      const uint4* vsrc = buf + SUBS * SUB_CHUNKS;
+      if constexpr (VPAIR) {
+        // vp[e][i]: the paired operand of output tile 2i+e.
+        uint4 vp[2][F::NLOAD];
 #pragma unroll
-          for (int uu = 0; uu < 2; ++uu)
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][uu][j], sl2, m_off));   // 0 where masked
-              l_run[ct] += p[ct][uu][j];
+          for (int i = 0; i < F::NLOAD; ++i) vp[e][i] = vsrc[(u0 + e) * SUB_CHUNKS + 64 * i + lane];
+        if constexpr (TAIL) {
+          // Element order within a paired operand: tokens 4r..4r+3 of the first sub-tile,
+          // then of the second.
+          const int t0 = tok_step + 16 * u0 + 4 * row;
+          uint32_t lo = 0, hi = 0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            lo |= (t0 + j < L ? 0xFFFFu : 0u) << (16 * j);
+            hi |= (t0 + 2 + j < L ? 0xFFFFu : 0u) << (16 * j);
+          }
+          uint32_t lo1 = 0, hi1 = 0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            lo1 |= (t0 + 16 + j < L ? 0xFFFFu : 0u) << (16 * j);
+            hi1 |= (t0 + 18 + j < L ? 0xFFFFu : 0u) << (16 * j);
+          }
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int i = 0; i < F::NLOAD; ++i) {
+              vp[e][i].x &= lo; vp[e][i].y &= hi; vp[e][i].z &= lo1; vp[e][i].w &= hi1;
             }
         }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const uint4 bop = make_uint4(pack_bf16x2(p[ct][0][0], p[ct][0][1]), pack_bf16x2(p[ct][0][2], p[ct][0][3]),
+                                       pack_bf16x2(p[ct][1][0], p[ct][1][1]), pack_bf16x2(p[ct][1][2], p[ct][1][3]));
+#pragma unroll
+          for (int i = 0; i < F::NLOAD; ++i) {
+            acc[ct][2 * i + 0] = mfma_bf16_k32(vp[0][i], bop, acc[ct][2 * i + 0]);
+            acc[ct][2 * i + 1] = mfma_bf16_k32(vp[1][i], bop, acc[ct][2 * i + 1]);
+          }
+        }
+      } else {
         uint4 vf0[F::NLOAD], vf1[F::NLOAD];
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i) {
-          vf0[i] = buf[(SUBS + u0) * SUB_CHUNKS + 64 * i + lane];
-          vf1[i] = buf[(SUBS + u0 + 1) * SUB_CHUNKS + 64 * i + lane];
+          vf0[i] = vsrc[u0 * SUB_CHUNKS + 64 * i + lane];
+          vf1[i] = vsrc[(u0 + 1) * SUB_CHUNKS + 64 * i + lane];
         }
-        if (tail) {
+        if constexpr (TAIL) {
           const int t0 = tok_step + 16 * u0 + 4 * row;
           uint32_t vm0 = 0, vm1 = 0;
 #pragma unroll
@@ -263,7 +327,27 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
         for (int ct = 0; ct < CT; ++ct) pv_pair<KV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
       }
     }
-  }
+  };
+
+  // Steps [0, s_free) lie below every column's position in the workgroup and need no mask;
+  // the rest (the diagonal and the tail) are masked.  Two loops keep the two variants'
+  // registers apart.  Each step: stage the loaded chunks, issue the next step's loads,
+  // barrier, compute.
+  const int pmin_wg = L - n + col0 / a.G;
+  const int s_free = pmin_wg < 0 ? 0 : std::min(nsteps, (pmin_wg + 1) / STEP_TOK);
+  auto run_steps = [&](int s_begin, int s_end, auto mask_c) {
+    for (int step = s_begin; step < s_end; ++step) {
+      uint4* buf = stage[step & 1];
+      stage_write(buf);
+      if (step + 1 < nsteps) fetch(step + 1);
+      __syncthreads();
+      const int tok_step = step * STEP_TOK;
+      if (tok_step <= wave_pmax) compute(buf, tok_step, mask_c);
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  run_steps(0, s_free, std::integral_constant<bool, false>());
+  run_steps(s_free, nsteps, std::integral_constant<bool, true>());
 
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -347,10 +431,10 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
   if (int64_t(num_q_tokens) * Hq > int64_t(INT32_MAX) || int64_t(max_query_len) * (Hq / Hkv) > int64_t(INT32_MAX) / 2)
     return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tokens", fn);
-  const int64_t tbl_bytes = int64_t(max_blocks_per_seq) * 4;
+  const int64_t tbl_bytes = (int64_t(max_blocks_per_seq) + kTblPad) * 4;
   if (tbl_bytes > kMaxTableBytes)
     return pkv::fail(PKV_UNSUPPORTED, "%s: max_blocks_per_seq=%d exceeds %d", fn, max_blocks_per_seq,
-                     kMaxTableBytes / 4);
+                     kMaxTableBytes / 4 - kTblPad);
 
   PrefillFn kfn = nullptr;
   int cols = 0;
@@ -380,7 +464,7 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
   const dim3 grid{unsigned(tiles), unsigned(Hkv), unsigned(B)}, block{unsigned(kWaves * 64)};
-  const size_t lds = size_t(std::max<int64_t>(tbl_bytes, 4));
+  const size_t lds = size_t(tbl_bytes);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   void *ev0 = nullptr, *ev1 = nullptr;
   if (pkv::take_launch_events(&ev0, &ev1)) {

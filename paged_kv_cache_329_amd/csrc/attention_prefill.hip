@@ -17,8 +17,9 @@
 //
 // How it maps onto CDNA4
 //  * Columns: a column is one (query token, query head) pair of one kv head; a workgroup
-//    of 4 waves owns 64*CT consecutive columns of one (sequence, kv head), each wave 16*CT
-//    (CT matrix-instruction column tiles).  With G query heads per kv head the columns of
+//    of 8 waves owns 128*CT consecutive columns of one (sequence, kv head), each wave 16*CT
+//    (CT matrix-instruction column tiles).  Every tile re-reads its unit's K/V, so wide
+//    tiles keep that traffic down.  With G query heads per kv head the columns of
 //    one query token are adjacent, so every K/V byte a workgroup stages serves all of them.
 //  * Staging: each step the workgroup copies SUBS 16-token sub-tiles of K and of V (32 KiB
 //    for bf16, D 128) from the pool into LDS, one 16-byte chunk per thread per load, with the
@@ -33,8 +34,8 @@
 //    that column; the rest get -inf by select.  A step that lies entirely past a wave's last
 //    position is skipped by that wave (it still stages its share of the loads).  V elements
 //    of slots at or past L_s are zeroed (an unwritten tail slot may hold NaN).
-//  * Order: the workgroups of one (sequence, kv head) are launched last tile first, so the
-//    tiles with the most keys start earliest.
+//  * Order: all tiles of one (sequence, kv head) run on one XCD (sharing its L2), launched
+//    last tile first, so the tiles with the most keys start earliest.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -49,7 +50,9 @@ namespace {
 
 using namespace pkv::tile;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                   // waves per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kMaxTableBytes = 64 * 1024;   // block-table entries staged in LDS, at most
 constexpr int kTblPad = 8;                  // -1 entries after them (a step reads at most 7 past)
 
@@ -62,6 +65,8 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* query_start;
   int B, Hkv, G, num_blocks, max_blocks, num_q_tokens;
+  int tiles;            // query tiles per (sequence, kv head)
+  int units_per_xcd;    // ceil(B * Hkv / kXcds)
   float qk_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
 };
@@ -74,7 +79,7 @@ constexpr int step_subtiles() {
 }
 
 template <int KV, int D, int BS, int CT>
-__global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(PrefillArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;
@@ -86,15 +91,21 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   constexpr int STEP_TOK = 16 * SUBS;
   constexpr int COLS = kWaves * 16 * CT;
   constexpr int STAGE_CHUNKS = 2 * SUBS * SUB_CHUNKS;      // K then V
-  constexpr int PER_THREAD = STAGE_CHUNKS / 256;
-  static_assert(STAGE_CHUNKS % 256 == 0, "staging tiling");
+  constexpr int PER_THREAD = STAGE_CHUNKS / kThreads;
+  static_assert(STAGE_CHUNKS % kThreads == 0, "staging tiling");
   __shared__ __attribute__((aligned(16))) uint4 stage[2][STAGE_CHUNKS];
   extern __shared__ int32_t s_tbl[];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = blockIdx.z, g = blockIdx.y;
-  const int tile = int(gridDim.x) - 1 - int(blockIdx.x);
+  // Workgroup b runs on XCD b % kXcds.  The (sequence, kv head) units are dealt to the XCDs
+  // round-robin (unit u on XCD u % kXcds), and every query tile of a unit goes to the unit's
+  // XCD, last tile first, so the unit's K/V stays in that XCD's L2 while its tiles run.
+  const int xcd = int(blockIdx.x) % kXcds, j = int(blockIdx.x) / kXcds;
+  const int unit = xcd + kXcds * (j / a.tiles);
+  if (unit >= a.B * a.Hkv) return;
+  const int s = unit / a.Hkv, g = unit % a.Hkv;
+  const int tile = a.tiles - 1 - j % a.tiles;
 
   int q0 = a.query_start[s], q1 = a.query_start[s + 1];
   q0 = std::min(std::max(q0, 0), a.num_q_tokens);
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   // The table entries the workgroup reads, then kTblPad entries of -1: a step's lookups
   // past the last block land there instead of outside the array.
   const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-  for (int j = tid; j < nblk + kTblPad; j += 256) s_tbl[j] = j < nblk ? trow[j] : -1;
+  for (int e = tid; e < nblk + kTblPad; e += kThreads) s_tbl[e] = e < nblk ? trow[e] : -1;
 
   // This lane's columns: (query qi, head hh) for column col0 + 16*(wave*CT + ct) + lane%16.
   const int row = lane >> 4;
@@ -169,14 +180,14 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
   // [sub-tile parity]: one 16-byte read of (p, e, w) is then exactly the k = 32 PV operand
   // {sub-tile 2p half e, sub-tile 2p+1 half e} of output tile 2i+e, with no register moves.
   constexpr bool VPAIR = KV == PKV_BF16;
-  __builtin_assume(tid < 256);
+  __builtin_assume(tid < kThreads);
   uint4 pre[PER_THREAD];
   uint32_t zmask = 0;
   auto fetch = [&](int step) {
     zmask = 0;
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
-      const int ci = tid + 256 * r;
+      const int ci = tid + kThreads * r;
       const int which = ci / (SUBS * SUB_CHUNKS);
       const int u = (ci / SUB_CHUNKS) % SUBS;
       const int w = ci % SUB_CHUNKS;
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_prefill_kernel(Prefill
     }
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
-      const int ci = tid + 256 * r;
+      const int ci = tid + kThreads * r;
       if (!VPAIR || ci < SUBS * SUB_CHUNKS) {
         buf[ci] = pre[r];
       } else {
@@ -427,8 +438,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
   if (!pkv::aligned16({out, q, k_cache, v_cache}))
     return pkv::fail(PKV_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
-  if (B > 65535 || Hkv > 65535)
-    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
+  if (int64_t(B) * Hkv > int64_t(INT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * num_kv_heads exceeds 2^31", fn);
   if (int64_t(num_q_tokens) * Hq > int64_t(INT32_MAX) || int64_t(max_query_len) * (Hq / Hkv) > int64_t(INT32_MAX) / 2)
     return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tokens", fn);
   const int64_t tbl_bytes = (int64_t(max_blocks_per_seq) + kTblPad) * 4;
@@ -463,7 +474,12 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.num_q_tokens = num_q_tokens;
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
-  const dim3 grid{unsigned(tiles), unsigned(Hkv), unsigned(B)}, block{unsigned(kWaves * 64)};
+  a.tiles = int(tiles);
+  a.units_per_xcd = (B * Hkv + kXcds - 1) / kXcds;
+  const int64_t wgs = int64_t(kXcds) * a.units_per_xcd * tiles;
+  if (wgs > int64_t(UINT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: too many workgroups", fn);
+  const dim3 grid{unsigned(wgs)}, block{unsigned(kThreads)};
   const size_t lds = size_t(tbl_bytes);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   void *ev0 = nullptr, *ev1 = nullptr;

@@ -383,6 +383,20 @@ def _multi_query_bench(args, wl):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes": kv_bytes}
     roof["kernel"] = "paged_attention_prefill_kernel"
+    roof["traffic_unit"] = ("HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, scaled by a plain "
+                            "copy of known size)")
+    qb = 4 if wl.q_dtype == "f32" else 2
+    roof["q_out_bytes"] = 2 * case.num_q_tokens * Hq * D * qb
+    try:
+        tpath = args.traffic_json or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                                  f"paged_attention_prefill__{wl.name}__hbm_traffic.json")
+        with open(tpath) as f:
+            tj = json.load(f)
+        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha(
+                ("attention_prefill.hip", "attention_tile.h")):
+            roof["traffic"] = tj.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -44,7 +44,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=None,
                    help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
-    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks"], default=None,
+    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks", "swap"], default=None,
                    help="instead of the decode step, time one pool-maintenance kernel on the "
                         "workload's pool: the KV-cache write of the whole batch (the prefill "
                         "pattern) or copy_blocks of --pairs random block pairs")
@@ -498,7 +498,7 @@ def _op_bench(args):
             k, v = pools[i % len(pools)]
             pkv.kv_cache_write(kt, vt, k, v, slots, k_scale=ks, v_scale=vs)
         what = f"{T} tokens x {Hkv} kv heads into their slots (prefill pattern)"
-    else:
+    elif args.op == "copy_blocks":
         rng = np.random.default_rng(args.seed)
         ids = rng.permutation(case.num_blocks)
         n = min(args.pairs, case.num_blocks // 2)
@@ -509,6 +509,8 @@ def _op_bench(args):
             k, v = pools[i % len(pools)]
             pkv.copy_blocks(k, v, pairs, D)
         what = f"{n} random (src, dst) block pairs, whole blocks of K and V"
+    if args.op == "swap":
+        return _swap_bench(args, wl, case, pools[0], kvt, eb)
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
@@ -523,6 +525,50 @@ def _op_bench(args):
     print(json.dumps({"op": args.op, "workload": wl.name, "what": what, "us_per_call": round(us, 2),
                       "bytes_read_plus_written": int(nbytes), "GBps": round(gbps, 1),
                       "frac_of_8TBps": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
+def _swap_bench(args, wl, case, pool, kvt, eb):
+    """Swap-out (device pool -> pinned host pool) and swap-in (back into other device blocks)
+    of --pairs random blocks with pkv_swap_blocks, against torch's contiguous copy of the same
+    number of bytes between device memory and pinned host memory."""
+    import torch
+    import paged_kv_cache_329_amd as pkv
+
+    dev = torch.device("cuda:0")
+    k, v = pool
+    Hkv, D, bs = wl.num_kv_heads, wl.head_dim, wl.block_size
+    n = min(args.pairs, case.num_blocks // 2)
+    rng = np.random.default_rng(args.seed)
+    ids = rng.permutation(case.num_blocks)
+    hk = pkv.allocate_host_pool(n, Hkv, bs, D, kvt)
+    hv = pkv.allocate_host_pool(n, Hkv, bs, D, kvt)
+    out_pairs = torch.from_numpy(np.stack([ids[:n], np.arange(n)], 1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), ids[n:2 * n]], 1).astype(np.int32)).to(dev)
+    nbytes = n * 2 * Hkv * bs * D * eb                  # K and V blocks moved one way
+    flat_d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    flat_h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    res = {"out": timed(lambda: pkv.swap_blocks(hk, hv, k, v, out_pairs, D)),
+           "in": timed(lambda: pkv.swap_blocks(k, v, hk, hv, in_pairs, D)),
+           "copy_d2h": timed(lambda: flat_h.copy_(flat_d, non_blocking=True)),
+           "copy_h2d": timed(lambda: flat_d.copy_(flat_h, non_blocking=True))}
+    gb = {key: round(nbytes / (us * 1e-6) / 1e9, 2) for key, us in res.items()}
+    print(json.dumps({"op": "swap", "workload": wl.name,
+                      "what": f"{n} random blocks (K and V, {nbytes} bytes) device -> pinned host and back",
+                      "us_per_call": {key: round(us, 2) for key, us in res.items()}, "bytes_one_way": nbytes,
+                      "GBps": gb}), flush=True)
 
 
 def _prefix_step_bench(args, wl):

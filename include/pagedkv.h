@@ -285,6 +285,26 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_ma
                            int num_blocks, pkv_dtype kv_dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Block copy between two pools of the same layout, for swap ("What is PagedAttention?",
+ * glossary, "How It Works: Map Logical to Physical Blocks": swap is one of the explicit
+ * responses to an allocation that cannot be met).
+ *
+ *   dst_k, dst_v / src_k, src_v  K and V pools of dst_num_blocks / src_num_blocks blocks,
+ *                  each device memory or pinned host memory the device can access
+ *                  (hipHostMalloc); one side is typically the device pool and the other a
+ *                  host pool.
+ *   block_mapping  int32 [num_pairs][2] of (src, dst) block ids, device-accessible; the
+ *                  whole block (all kv heads, all bs slots) of K and of V is copied.  Pairs
+ *                  with an id outside its pool are skipped.  pkv_seq_swap produces them.
+ * Preconditions: dst blocks distinct; the pools do not overlap.  Other arguments as for
+ * pkv_copy_blocks.
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k,
+                           const void* src_v, int src_num_blocks, const int32_t* block_mapping,
+                           int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                           pkv_dtype kv_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Device-side mirror of a decode step's table update ("What is PagedAttention?", glossary,
  * "How It Works: Map Logical to Physical Blocks": a decode step appends one token into the
  * sequence's last block and takes a new block only when that one is full).
@@ -349,6 +369,22 @@ pkv_status pkv_seq_append(pkv_alloc* a, const int64_t* seq_ids, int n, int64_t* 
 
 /* Releases a sequence; blocks whose reference count drops to zero return to the pool. */
 pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
+
+/* Swap (the pages' named response to an allocation that cannot be met: "What is
+ * PagedAttention?", glossary, "How It Works: Map Logical to Physical Blocks").  Moves
+ * sequence seq_id from allocator `from` to allocator `to` -- typically the device pool's
+ * and a pinned host pool's, in either direction -- all-or-nothing:
+ *   - `to` takes one fresh block per logical block of the sequence (PKV_OUT_OF_BLOCKS if
+ *     it has too few free; nothing changes then); sharing does not survive a swap;
+ *   - pairs_out[2j], pairs_out[2j+1] = (block in `from`, block in `to`) of logical block j,
+ *     for j < *n_pairs_out (the sequence's block count, pkv_seq_info); host memory;
+ *   - the sequence leaves `from`: its blocks' reference counts drop, and blocks no other
+ *     sequence holds return to `from`'s free list.
+ * The caller copies the pairs with pkv_swap_blocks before anything writes the blocks freed
+ * in `from` (enqueue the copy first on the stream that later writes them).  Both
+ * allocators need the same block size; seq_id must not exist in `to`. */
+pkv_status pkv_seq_swap(pkv_alloc* from, pkv_alloc* to, int64_t seq_id, int32_t* pairs_out,
+                        int* n_pairs_out);
 
 /* Writes block tables (host int32 [n][max_blocks], padded with -1) and lengths (host
  * int32 [n], nullable) for the listed sequences. */

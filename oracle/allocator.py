@@ -140,6 +140,27 @@ class AllocatorModel:
             raise
         return slots, cows
 
+    def swap_to(self, other: "AllocatorModel", sid: int):
+        """Moves sequence `sid` into `other` ("What is PagedAttention?", "How It Works: Map
+        Logical to Physical Blocks": swap is one of the explicit responses to an allocation
+        that cannot be met).  Reading taken (the pages do not detail it): `other` gives
+        every logical block a fresh block of its own, so sharing does not survive the
+        move; the sequence then leaves this allocator as by free_seq.  All-or-nothing.
+        Returns the (block here, block in other) pair of each logical block, in order."""
+        if other is self or other.bs != self.bs:
+            raise AllocError(INVALID_ARG)
+        if sid not in self.seqs:
+            raise AllocError(UNKNOWN_SEQ)
+        if sid in other.seqs:
+            raise AllocError(INVALID_ARG)
+        blocks, length = self.seqs[sid]
+        if len(blocks) > len(other.free):
+            raise AllocError(OUT_OF_BLOCKS)
+        fresh = [other._pop() for _ in blocks]
+        other.seqs[sid] = [fresh, length]
+        self.free_seq(sid)
+        return list(zip(blocks, fresh))
+
     def free_seq(self, sid: int):
         if sid not in self.seqs:
             raise AllocError(UNKNOWN_SEQ)

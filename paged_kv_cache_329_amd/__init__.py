@@ -28,7 +28,7 @@ __all__ = [
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
-    "paged_attention_prefill",
+    "paged_attention_prefill", "allocate_host_pool", "swap_blocks",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -67,6 +67,8 @@ _SIGNATURES = {
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
+    "pkv_swap_blocks": ([_c_p, _c_p, _c_int, _c_p, _c_p, _c_int, _c_p] + [_c_int] * 5 + [_c_p], _c_int),
+    "pkv_seq_swap": ([_c_p, _c_p, _c_i64, _c_p, _c_p], _c_int),
     "pkv_alloc_create": ([_c_int, _c_int, _c_p], _c_p),
     "pkv_alloc_destroy": ([_c_p], None),
     "pkv_seq_create": ([_c_p, _c_i64, _c_i64, _c_p], _c_int),
@@ -354,6 +356,42 @@ def copy_blocks(k_cache, v_cache, block_mapping, head_dim: int, stream=None):
                                  head_dim, bs, NB, _dtype_code(k_cache.dtype), _stream(stream)))
 
 
+def allocate_host_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                       dtype: torch.dtype) -> torch.Tensor:
+    """Pinned host pool [num_blocks, num_kv_heads, block_size * head_dim] (same layout as the
+    device pool), for swapped-out sequences; the device reads and writes it directly."""
+    return torch.empty((num_blocks, num_kv_heads, block_size * head_dim), dtype=dtype, pin_memory=True)
+
+
+def _pool_ptr(t: torch.Tensor, name: str) -> int:
+    # A device tensor, or a pinned host tensor (device-accessible at the same address).
+    if isinstance(t, torch.Tensor) and not t.is_cuda:
+        if not t.is_pinned():
+            raise ValueError(f"{name} must be a device tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t.data_ptr()
+    return _dev(t, name)
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, head_dim: int, stream=None):
+    """Copy whole blocks between two pools of the same layout (pkv_swap_blocks): device <->
+    pinned host for a swap.  block_mapping is int32 [n, 2] of (src, dst) on the device."""
+    SNB, Hkv, bs = _pool_dims(src_k, head_dim)
+    DNB, Hkv2, bs2 = _pool_dims(dst_k, head_dim)
+    if (Hkv, bs) != (Hkv2, bs2) or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools must share kv heads, block size and dtype")
+    if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape:
+        raise ValueError("V pools must match their K pools")
+    if block_mapping.dtype != torch.int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int32 [num_pairs, 2]")
+    n = block_mapping.shape[0]
+    _check(lib().pkv_swap_blocks(_pool_ptr(dst_k, "dst_k"), _pool_ptr(dst_v, "dst_v"), DNB,
+                                 _pool_ptr(src_k, "src_k"), _pool_ptr(src_v, "src_v"), SNB,
+                                 _dev(block_mapping, "block_mapping") if n else None, n, Hkv, head_dim, bs,
+                                 _dtype_code(src_k.dtype), _stream(stream)))
+
+
 def apply_append(block_tables, context_lens, slot_mapping, block_size: int, num_blocks: int, stream=None):
     """Mirror a decode step's append on device tables / lengths (pkv_apply_append)."""
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or slot_mapping.dtype != torch.int64:
@@ -439,6 +477,15 @@ class BlockAllocator:
 
     def free(self, seq_id: int):
         _check(lib().pkv_seq_free(self._h, seq_id))
+
+    def swap_to(self, other: "BlockAllocator", seq_id: int) -> np.ndarray:
+        """Move a sequence into `other` (pkv_seq_swap); returns int32 [n, 2] of (block here,
+        block in other) to copy with swap_blocks before the freed blocks are written."""
+        _, nb = self.seq_info(seq_id)
+        pairs = np.zeros((max(nb, 1), 2), dtype=np.int32)
+        n = ctypes.c_int(0)
+        _check(lib().pkv_seq_swap(self._h, other._h, seq_id, pairs.ctypes.data, ctypes.byref(n)))
+        return pairs[:n.value]
 
     def block_tables(self, seq_ids, max_blocks: int, tables_out=None, lens_out=None):
         """Block tables [n, max_blocks] (padded with -1) and lengths [n], int32; filled into

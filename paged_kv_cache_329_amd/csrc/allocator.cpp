@@ -15,6 +15,10 @@
 //    block whose count exceeds one first takes a private block with a copy of it,
 //    repoints only the writer's table entry and drops the old block's count; a block
 //    whose count reaches zero returns to the free list.
+//  * "What is PagedAttention?", "How It Works: Map Logical to Physical Blocks": an
+//    allocation that cannot be met must lead to admission control, preemption, swap or
+//    rejection.  pkv_seq_swap moves a sequence between two allocators (the device pool's
+//    and a host pool's), returning the block copies the move needs.
 #include <algorithm>
 #include <cstring>
 #include <unordered_map>
@@ -228,6 +232,41 @@ pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
     return fail(PKV_UNKNOWN_SEQ, "pkv_seq_free: unknown sequence %lld", (long long)seq_id);
   for (int32_t b : it->second.blocks) release_block(a, b);
   a->seqs.erase(it);
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_swap(pkv_alloc* from, pkv_alloc* to, int64_t seq_id, int32_t* pairs_out,
+                        int* n_pairs_out) {
+  if (!from || !to || from == to)
+    return fail(PKV_INVALID_ARG, "pkv_seq_swap: needs two distinct allocators");
+  if (from->block_size != to->block_size)
+    return fail(PKV_INVALID_ARG, "pkv_seq_swap: block sizes differ (%d, %d)", from->block_size,
+                to->block_size);
+  auto it = from->seqs.find(seq_id);
+  if (it == from->seqs.end())
+    return fail(PKV_UNKNOWN_SEQ, "pkv_seq_swap: unknown sequence %lld", (long long)seq_id);
+  if (to->seqs.count(seq_id))
+    return fail(PKV_INVALID_ARG, "pkv_seq_swap: sequence %lld already in the destination",
+                (long long)seq_id);
+  const size_t n = it->second.blocks.size();
+  if (n > 0 && !pairs_out) return fail(PKV_INVALID_ARG, "pkv_seq_swap: null pairs_out");
+  if (n > to->free_stack.size())
+    return fail(PKV_OUT_OF_BLOCKS, "pkv_seq_swap: needs %zu blocks, %zu free in the destination", n,
+                to->free_stack.size());
+  // Every logical block gets a private destination block: sharing does not survive a swap.
+  pkv_alloc::Seq moved;
+  moved.length = it->second.length;
+  moved.blocks.reserve(n);
+  for (size_t j = 0; j < n; ++j) {
+    const int32_t tb = take_block(to);
+    pairs_out[2 * j + 0] = it->second.blocks[j];
+    pairs_out[2 * j + 1] = tb;
+    moved.blocks.push_back(tb);
+  }
+  for (int32_t b : it->second.blocks) release_block(from, b);
+  from->seqs.erase(it);
+  to->seqs.emplace(seq_id, std::move(moved));
+  if (n_pairs_out) *n_pairs_out = int(n);
   return PKV_OK;
 }
 

@@ -225,22 +225,28 @@ void launch_write(int D, unsigned nwg, hipStream_t st, const void* k_new, const 
                        0, st, k, v, kc, vc, slots, T, Hkv, bs, num_slots, k_inv, v_inv);
 }
 
-// grid.y = pair; each workgroup copies a strided share of the K and V block regions.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
-                                                          uint4* __restrict__ v_cache,
-                                                          const int32_t* __restrict__ pairs,
-                                                          int num_blocks, int64_t chunks_per_block) {
-  const int32_t src = pairs[2 * blockIdx.y + 0];
-  const int32_t dst = pairs[2 * blockIdx.y + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const int64_t s0 = int64_t(src) * chunks_per_block, d0 = int64_t(dst) * chunks_per_block;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks_per_block;
-       i += int64_t(gridDim.x) * blockDim.x) {
-    k_cache[d0 + i] = k_cache[s0 + i];
-    v_cache[d0 + i] = v_cache[s0 + i];
+// Whole-block copies from a source pool to a destination pool (the same pool for
+// copy-on-write; a device pool and a pinned host pool for a swap).  grid.y strides over the
+// pairs, grid.x over each block's 16-byte chunks.  A pair with an id outside its pool is
+// skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* dst_k, uint4* dst_v, const uint4* src_k,
+                                                          const uint4* src_v, const int32_t* __restrict__ pairs,
+                                                          int num_pairs, int src_blocks, int dst_blocks,
+                                                          int64_t chunks_per_block) {
+  for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
+    const int32_t src = pairs[2 * p + 0];
+    const int32_t dst = pairs[2 * p + 1];
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) continue;
+    const int64_t s0 = int64_t(src) * chunks_per_block, d0 = int64_t(dst) * chunks_per_block;
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < chunks_per_block;
+         i += int64_t(gridDim.x) * blockDim.x) {
+      const uint4 k = src_k[s0 + i];
+      const uint4 v = src_v[s0 + i];
+      dst_k[d0 + i] = k;
+      dst_v[d0 + i] = v;
+    }
   }
 }
-
 
 // One thread per sequence: the device-side mirror of a decode step's allocator update.  The
 // step gave sequence s one token at position lens[s] in slot slots[s]; that position's block
@@ -323,30 +329,94 @@ extern "C" pkv_status pkv_kv_cache_write(const void* k_new, const void* v_new, v
   return launch_status("pkv_kv_cache_write");
 }
 
-extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
-                                      int num_pairs, int num_kv_heads, int head_dim,
-                                      int block_size, int num_blocks, pkv_dtype kv_dtype,
-                                      void* stream) {
-  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
-    return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: num_pairs=%d num_kv_heads=%d num_blocks=%d",
-                     num_pairs, num_kv_heads, num_blocks);
+namespace {
+
+// Host-side checks shared by the block copies (nothing touches the device).
+pkv_status check_copy(const char* fn, const void* dst_k, const void* dst_v, int dst_blocks, const void* src_k,
+                      const void* src_v, int src_blocks, const int32_t* pairs, int num_pairs, int num_kv_heads,
+                      int head_dim, int block_size, pkv_dtype kv_dtype) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || src_blocks <= 0 || dst_blocks <= 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: num_pairs=%d num_kv_heads=%d pools of %d and %d blocks", fn,
+                     num_pairs, num_kv_heads, src_blocks, dst_blocks);
   if (!shape_ok(head_dim, block_size, kv_dtype))
-    return pkv::fail(PKV_UNSUPPORTED, "pkv_copy_blocks: head_dim=%d block_size=%d kv_dtype=%d",
-                     head_dim, block_size, int(kv_dtype));
+    return pkv::fail(PKV_UNSUPPORTED, "%s: head_dim=%d block_size=%d kv_dtype=%d", fn, head_dim,
+                     block_size, int(kv_dtype));
   if (num_pairs == 0) return PKV_OK;
-  if (!k_cache || !v_cache || !block_mapping)
-    return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: null pointer");
-  if (!pkv::aligned16({k_cache, v_cache}))
-    return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: pools must be 16-byte aligned");
-  if (num_pairs > 65535) return pkv::fail(PKV_INVALID_ARG, "pkv_copy_blocks: more than 65535 pairs");
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
+  if (!pkv::aligned16({dst_k, dst_v, src_k, src_v}))
+    return pkv::fail(PKV_INVALID_ARG, "%s: pools must be 16-byte aligned", fn);
+  return PKV_OK;
+}
+
+pkv_status launch_copy(const char* fn, void* dst_k, void* dst_v, int dst_blocks, const void* src_k,
+                       const void* src_v, int src_blocks, const int32_t* pairs, int num_pairs,
+                       int num_kv_heads, int head_dim, int block_size, pkv_dtype kv_dtype, void* stream) {
   const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(kv_dtype);
   const int64_t chunks = block_bytes / 16;
   const int64_t per_wg = 256 * 4;
   const unsigned gx = unsigned(std::min<int64_t>((chunks + per_wg - 1) / per_wg, 1024));
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, unsigned(num_pairs)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<uint4*>(k_cache),
-                     static_cast<uint4*>(v_cache), block_mapping, num_blocks, chunks);
-  return launch_status("pkv_copy_blocks");
+  const unsigned gy = unsigned(std::min(num_pairs, 65535));
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, gy), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), static_cast<const uint4*>(src_k),
+                     static_cast<const uint4*>(src_v), pairs, num_pairs, src_blocks, dst_blocks, chunks);
+  return launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                                      int num_pairs, int num_kv_heads, int head_dim,
+                                      int block_size, int num_blocks, pkv_dtype kv_dtype,
+                                      void* stream) {
+  const char* fn = "pkv_copy_blocks";
+  pkv_status st = check_copy(fn, k_cache, v_cache, num_blocks, k_cache, v_cache, num_blocks, block_mapping,
+                             num_pairs, num_kv_heads, head_dim, block_size, kv_dtype);
+  if (st != PKV_OK || num_pairs == 0) return st;
+  return launch_copy(fn, k_cache, v_cache, num_blocks, k_cache, v_cache, num_blocks, block_mapping, num_pairs,
+                     num_kv_heads, head_dim, block_size, kv_dtype, stream);
+}
+
+namespace {
+
+// The address at which the device reaches `p`: device memory as it is, pinned host memory
+// (hipHostMalloc) at the device address the runtime reports.  Anything else (pageable host
+// memory, an unknown pointer) is rejected before any kernel could touch it.
+pkv_status device_view(const char* fn, const char* name, const void* p, void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return pkv::fail(PKV_INVALID_ARG, "%s: %s is neither device memory nor pinned host memory", fn, name);
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = const_cast<void*>(p);
+    return PKV_OK;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer && attr.hostPointer) {
+    // Offset from the host address the runtime reports (the allocation's, or p itself).
+    *out = static_cast<char*>(attr.devicePointer) +
+           (static_cast<const char*>(p) - static_cast<const char*>(attr.hostPointer));
+    return PKV_OK;
+  }
+  return pkv::fail(PKV_INVALID_ARG, "%s: %s is not device-accessible memory", fn, name);
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const void* src_k,
+                                      const void* src_v, int src_num_blocks, const int32_t* block_mapping,
+                                      int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                                      pkv_dtype kv_dtype, void* stream) {
+  const char* fn = "pkv_swap_blocks";
+  pkv_status st = check_copy(fn, dst_k, dst_v, dst_num_blocks, src_k, src_v, src_num_blocks, block_mapping,
+                             num_pairs, num_kv_heads, head_dim, block_size, kv_dtype);
+  if (st != PKV_OK || num_pairs == 0) return st;
+  void *dk, *dv, *sk, *sv, *map;
+  if ((st = device_view(fn, "dst_k", dst_k, &dk)) != PKV_OK || (st = device_view(fn, "dst_v", dst_v, &dv)) != PKV_OK ||
+      (st = device_view(fn, "src_k", src_k, &sk)) != PKV_OK || (st = device_view(fn, "src_v", src_v, &sv)) != PKV_OK ||
+      (st = device_view(fn, "block_mapping", block_mapping, &map)) != PKV_OK)
+    return st;
+  return launch_copy(fn, dk, dv, dst_num_blocks, sk, sv, src_num_blocks, static_cast<const int32_t*>(map),
+                     num_pairs, num_kv_heads, head_dim, block_size, kv_dtype, stream);
 }
 
 extern "C" pkv_status pkv_apply_append(int32_t* block_tables, int32_t* context_lens,

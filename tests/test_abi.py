@@ -123,3 +123,13 @@ def test_build_slot_mapping_matches_definition():
     assert got.tolist() == want
     with pytest.raises(pkv.PagedKVError):
         pkv.build_slot_mapping(tables, np.array([49, 0, 0], dtype=np.int32), 16)
+
+
+def test_swap_blocks_rejects_on_host():
+    lib = pkv.lib()
+    a = ctypes.c_void_p(256)
+    # Unsupported shape, bad counts and null pointers are rejected before any HIP call.
+    assert lib.pkv_swap_blocks(a, a, 4, a, a, 4, a, 2, 8, 96, 16, pkv.BF16, None) == 2
+    assert lib.pkv_swap_blocks(a, a, 0, a, a, 4, a, 2, 8, 128, 16, pkv.BF16, None) == 1
+    assert lib.pkv_swap_blocks(None, a, 4, a, a, 4, a, 2, 8, 128, 16, pkv.BF16, None) == 1
+    assert lib.pkv_swap_blocks(a, a, 4, a, a, 4, None, 0, 8, 128, 16, pkv.BF16, None) == 0

@@ -55,10 +55,14 @@ class AllocatorMachine(RuleBasedStateMachine):
         order = np.random.default_rng(0).permutation(self.nb).astype(np.int32)
         self.a = pkv.BlockAllocator(self.nb, self.bs, order)
         self.m = AllocatorModel(self.nb, self.bs, order)
+        # A smaller host pool that swapped-out sequences move to.
+        self.ah = pkv.BlockAllocator(10, self.bs)
+        self.mh = AllocatorModel(10, self.bs)
         self.next_id = 0
 
     def teardown(self):
         self.a.close()
+        self.ah.close()
 
     def _ids(self):
         return sorted(self.m.seqs)
@@ -128,10 +132,34 @@ class AllocatorMachine(RuleBasedStateMachine):
         s2, _ = _status(self.m.free_seq, sid)
         assert s1 == s2 == 0
 
+    def _swap(self, src_l, dst_l, src_m, dst_m, sid):
+        before = _compare(src_l, src_m)
+        s1, r1 = _status(src_l.swap_to, dst_l, sid)
+        s2, r2 = _status(src_m.swap_to, dst_m, sid)
+        assert s1 == s2
+        if s1 == 0:
+            after = _compare(dst_l, dst_m)
+            assert len(r1) == len(r2)
+            for (ls, ld), (ms, md) in zip(r1.tolist(), r2):
+                assert before[ls] == ms and after[ld] == md
+                assert dst_l.refcount(ld) == 1
+
+    @precondition(lambda self: self.m.seqs)
+    @rule(data=st.data())
+    def swap_out(self, data):
+        self._swap(self.a, self.ah, self.m, self.mh, data.draw(st.sampled_from(self._ids())))
+
+    @precondition(lambda self: self.mh.seqs)
+    @rule(data=st.data())
+    def swap_in(self, data):
+        self._swap(self.ah, self.a, self.mh, self.m, data.draw(st.sampled_from(sorted(self.mh.seqs))))
+
     @invariant()
     def states_agree(self):
         _compare(self.a, self.m)
+        _compare(self.ah, self.mh)
         self.m.check_invariants()
+        self.mh.check_invariants()
 
 
 TestAllocatorMachine = AllocatorMachine.TestCase
@@ -189,3 +217,21 @@ def test_invalid_create_arguments():
         pkv.BlockAllocator(0, 16)
     with pytest.raises(pkv.PagedKVError):
         pkv.BlockAllocator(4, 16, free_order=[0, 1, 1, 2])
+
+
+def test_swap_errors_leave_both_allocators_unchanged():
+    dev, host = pkv.BlockAllocator(8, 16), pkv.BlockAllocator(2, 16)
+    dev.seq_create(0, 40)                       # 3 blocks; the host pool holds only 2
+    with pytest.raises(pkv.PagedKVError) as e:
+        dev.swap_to(host, 0)
+    assert e.value.status_name == "OUT_OF_BLOCKS"
+    assert dev.num_free == 5 and host.num_free == 2 and dev.seq_info(0) == (40, 3)
+    with pytest.raises(pkv.PagedKVError) as e:
+        dev.swap_to(host, 7)
+    assert e.value.status_name == "UNKNOWN_SEQ"
+    other = pkv.BlockAllocator(8, 32)
+    with pytest.raises(pkv.PagedKVError) as e:
+        dev.swap_to(other, 0)
+    assert e.value.status_name == "INVALID_ARG"
+    with pytest.raises(pkv.PagedKVError):
+        dev.swap_to(dev, 0)

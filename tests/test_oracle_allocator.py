@@ -113,3 +113,34 @@ def test_waste_stays_under_one_block():
         blocks, n = m.seqs[sid]
         assert 0 <= len(blocks) * 16 - n < 16
     _check(m)
+
+
+def test_swap_out_and_back_keeps_length_and_unshares_blocks():
+    dev, host = AllocatorModel(10, 4), AllocatorModel(6, 4)
+    dev.seq_create(1, 10)          # blocks for tokens 0-3, 4-7, 8-9
+    dev.fork(1, 2, 8)              # child shares the two full blocks
+    free0 = len(dev.free)
+    pairs = dev.swap_to(host, 1)
+    assert len(pairs) == 3 and host.seqs[1][1] == 10
+    assert [d for _, d in pairs] == host.seqs[1][0]
+    assert all(host.ref[d] == 1 for _, d in pairs)
+    # Only the block no one else holds returned to the device's free list.
+    assert len(dev.free) == free0 + 1 and all(dev.ref[s] == 1 for s, _ in pairs[:2])
+    back = host.swap_to(dev, 1)
+    assert dev.seqs[1][1] == 10 and len(dev.seqs[1][0]) == 3
+    # The swapped-in sequence owns fresh blocks; the child still holds the old shared ones.
+    assert not set(dev.seqs[1][0]) & set(dev.seqs[2][0])
+    assert [s for s, _ in back] == [d for _, d in pairs]     # read back from where it went
+    _check(dev)
+    _check(host)
+
+
+def test_swap_exhaustion_fails_and_leaves_both_unchanged():
+    dev, host = AllocatorModel(10, 4), AllocatorModel(2, 4)
+    dev.seq_create(1, 9)
+    snap = (list(dev.free), list(dev.ref), {k: (list(v[0]), v[1]) for k, v in dev.seqs.items()})
+    with pytest.raises(AllocError) as e:
+        dev.swap_to(host, 1)
+    assert e.value.status == OUT_OF_BLOCKS
+    assert (dev.free, dev.ref) == (snap[0], snap[1]) and dev.seqs[1] == [snap[2][1][0], 9]
+    assert len(host.free) == 2 and not host.seqs

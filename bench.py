@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import statistics
 import sys
@@ -44,7 +45,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=None,
                    help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
-    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks", "swap"], default=None,
+    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks", "swap", "waste"], default=None,
                    help="instead of the decode step, time one pool-maintenance kernel on the "
                         "workload's pool: the KV-cache write of the whole batch (the prefill "
                         "pattern) or copy_blocks of --pairs random block pairs")
@@ -105,6 +106,9 @@ def main():
 
     if args.copy_probe:
         _copy_probe(args.copy_probe)
+        return
+    if args.op == "waste":
+        _waste_report(args)
         return
     if args.op:
         _op_bench(args)
@@ -462,6 +466,75 @@ def _multi_query_bench(args, wl):
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+def _waste_report(args):
+    """Allocation waste and capacity on the synthetic length distributions (host only).
+
+    For each workload's drawn lengths: the share of allocated KV slots that hold no token under
+    paging with blocks of 16 and 32 (the real allocator, pkv_alloc_stats_get) and under a
+    contiguous reservation of the distribution's maximum length per sequence; and how many
+    sequences drawn from the same distribution fit in a fixed budget (the paged pool the
+    workload sizes at 16-token blocks) either way.  For the prefix-sharing workload the
+    allocator also forks each group from its root, and shared blocks count once.
+    """
+    import paged_kv_cache_329_amd as pkv
+    from synth import WORKLOADS, draw_lengths
+
+    names = [args.workload] if args.workload != "llama3_8b_bf16" else \
+        ["llama3_8b_bf16", "cont_batch_prefix_bf16", "long_ctx_splitk_bf16", "fp8_kv"]
+    for name in names:
+        wl = WORKLOADS[name]
+        rng = np.random.default_rng(np.random.SeedSequence(args.seed).spawn(6)[0])
+        lengths = draw_lengths(wl, rng)
+        max_len = int(wl.length_dist[2] if wl.length_dist[0] == "uniform" else wl.length_dist[3])
+        if wl.prefix_group:
+            max_len = max(max_len, wl.prefix_len)
+        row = {"op": "waste", "workload": name, "sequences": int(len(lengths)), "sum_tokens": int(lengths.sum()),
+               "max_len": max_len}
+        budget_slots = None
+        for bs in (16, 32):
+            need = int(sum((int(L) + bs - 1) // bs for L in lengths))
+            groups = wl.batch // wl.prefix_group if wl.prefix_group else 0
+            nb = need + groups * ((wl.prefix_len + bs - 1) // bs) + 1
+            a = pkv.BlockAllocator(nb, bs)
+            if groups:
+                for gi in range(groups):
+                    a.seq_create(1_000_000 + gi, wl.prefix_len)
+                for i, L in enumerate(lengths.tolist()):
+                    root = 1_000_000 + i // wl.prefix_group
+                    a.fork(root, i, min(L, wl.prefix_len))
+                    if L > wl.prefix_len:
+                        a.extend(i, L - wl.prefix_len)
+                for gi in range(groups):
+                    a.free(1_000_000 + gi)
+            else:
+                for i, L in enumerate(lengths.tolist()):
+                    a.seq_create(i, L)
+            st = a.stats()
+            a.close()
+            held = st["used_blocks"] * bs
+            row[f"paged_bs{bs}"] = {"blocks_used": st["used_blocks"], "shared_blocks": st["shared_blocks"],
+                                    "logical_blocks": st["logical_blocks"], "slots_held": held,
+                                    "stored_tokens": st["stored_tokens"],
+                                    "waste_frac": round(1 - st["stored_tokens"] / held, 5)}
+            if bs == 16:
+                budget_slots = int(math.ceil(1.1 * held))
+        row["contiguous_max_len"] = {"slots_held": int(len(lengths)) * max_len,
+                                     "waste_frac": round(1 - int(lengths.sum()) / (len(lengths) * max_len), 5)}
+        # Capacity in the same budget: sequences from the same distribution until one does not fit.
+        cap_rng = np.random.default_rng(args.seed + 1)
+        more = draw_lengths(wl.scaled(batch=200_000), cap_rng)
+        fits_paged, used = 0, 0
+        for L in more.tolist():
+            blocks = (L + 15) // 16
+            if used + blocks * 16 > budget_slots:
+                break
+            used += blocks * 16
+            fits_paged += 1
+        row["budget_slots"] = budget_slots
+        row["sequences_that_fit"] = {"paged_bs16": fits_paged, "contiguous_max_len": budget_slots // max_len}
+        print(json.dumps(row), flush=True)
 
 
 def _op_bench(args):

@@ -391,6 +391,22 @@ pkv_status pkv_seq_swap(pkv_alloc* from, pkv_alloc* to, int64_t seq_id, int32_t*
 pkv_status pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int n,
                                   int max_blocks, int32_t* tables_out, int32_t* lens_out);
 
+/* Occupancy of an allocator's pool, for waste accounting ("PagedAttention: Optimizing KV
+ * Cache in vLLM", §2 "The Solution": paging leaves at most the last block of a sequence
+ * partly empty; §4: shared blocks are stored once).  All counts are over the current state:
+ *   used_blocks     physical blocks with a reference count > 0 (free_blocks the rest);
+ *   shared_blocks   physical blocks with a reference count > 1;
+ *   logical_blocks  sum over sequences of their block-table lengths;
+ *   tokens          sum over sequences of their lengths (a shared token once per holder);
+ *   stored_tokens   slots of used blocks that hold a token of at least one holder, so
+ *                   used_blocks * block_size - stored_tokens is the unused space in held
+ *                   blocks. */
+typedef struct pkv_alloc_stats {
+  int64_t num_blocks, free_blocks, used_blocks, shared_blocks;
+  int64_t logical_blocks, tokens, stored_tokens, num_seqs;
+} pkv_alloc_stats;
+pkv_status pkv_alloc_stats_get(const pkv_alloc* a, pkv_alloc_stats* out);
+
 /* Queries (host). */
 int pkv_alloc_num_free(const pkv_alloc* a);
 int pkv_alloc_num_blocks(const pkv_alloc* a);

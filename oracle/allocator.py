@@ -186,6 +186,20 @@ class AllocatorModel:
     def num_free(self) -> int:
         return len(self.free)
 
+    def stats(self) -> dict:
+        """Pool occupancy: blocks in use and shared, and how many of their slots hold a token
+        ("PagedAttention: Optimizing KV Cache in vLLM", §2: only a sequence's last block can be
+        partly empty; §4: a shared block is stored once however many tables point at it)."""
+        holders = {}
+        for blocks, n in self.seqs.values():
+            for j, b in enumerate(blocks):
+                holders.setdefault(b, []).append(min(self.bs, n - j * self.bs))
+        return {"num_blocks": self.num_blocks, "free_blocks": len(self.free),
+                "used_blocks": len(holders), "shared_blocks": sum(1 for h in holders.values() if len(h) > 1),
+                "logical_blocks": sum(len(b) for b, _ in self.seqs.values()),
+                "tokens": sum(n for _, n in self.seqs.values()),
+                "stored_tokens": sum(max(h) for h in holders.values()), "num_seqs": len(self.seqs)}
+
     # ---- invariants ----------------------------------------------------------------
     def check_invariants(self):
         check_allocator_state(self.num_blocks, self.bs, set(self.free), self.ref,

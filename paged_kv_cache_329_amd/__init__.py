@@ -69,6 +69,7 @@ _SIGNATURES = {
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_swap_blocks": ([_c_p, _c_p, _c_int, _c_p, _c_p, _c_int, _c_p] + [_c_int] * 5 + [_c_p], _c_int),
     "pkv_seq_swap": ([_c_p, _c_p, _c_i64, _c_p, _c_p], _c_int),
+    "pkv_alloc_stats_get": ([_c_p, _c_p], _c_int),
     "pkv_alloc_create": ([_c_int, _c_int, _c_p], _c_p),
     "pkv_alloc_destroy": ([_c_p], None),
     "pkv_seq_create": ([_c_p, _c_i64, _c_i64, _c_p], _c_int),
@@ -414,6 +415,11 @@ def build_slot_mapping(block_tables, lens, block_size: int) -> np.ndarray:
     return out
 
 
+class _AllocStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("num_blocks", "free_blocks", "used_blocks", "shared_blocks",
+                                              "logical_blocks", "tokens", "stored_tokens", "num_seqs")]
+
+
 class BlockAllocator:
     """Host block allocator (pkv_alloc_*): free list, refcounts, copy-on-write decisions."""
 
@@ -477,6 +483,12 @@ class BlockAllocator:
 
     def free(self, seq_id: int):
         _check(lib().pkv_seq_free(self._h, seq_id))
+
+    def stats(self) -> dict:
+        """Pool occupancy (pkv_alloc_stats_get) as a dict of the struct's fields."""
+        st = _AllocStats()
+        _check(lib().pkv_alloc_stats_get(self._h, ctypes.byref(st)))
+        return {name: int(getattr(st, name)) for name, _ in _AllocStats._fields_}
 
     def swap_to(self, other: "BlockAllocator", seq_id: int) -> np.ndarray:
         """Move a sequence into `other` (pkv_seq_swap); returns int32 [n, 2] of (block here,

@@ -318,6 +318,33 @@ pkv_status pkv_seq_info(const pkv_alloc* a, int64_t seq_id, int64_t* length_out,
   return PKV_OK;
 }
 
+pkv_status pkv_alloc_stats_get(const pkv_alloc* a, pkv_alloc_stats* out) {
+  if (!a || !out) return fail(PKV_INVALID_ARG, "pkv_alloc_stats_get: null argument");
+  pkv_alloc_stats st{};
+  st.num_blocks = a->num_blocks;
+  st.free_blocks = int64_t(a->free_stack.size());
+  st.num_seqs = int64_t(a->seqs.size());
+  // Slots of each physical block that hold a token of at least one holder.
+  std::vector<int32_t> filled(a->num_blocks, 0);
+  const int bs = a->block_size;
+  for (const auto& kv : a->seqs) {
+    const pkv_alloc::Seq& q = kv.second;
+    st.tokens += q.length;
+    st.logical_blocks += int64_t(q.blocks.size());
+    for (size_t j = 0; j < q.blocks.size(); ++j) {
+      const int64_t in_block = std::min<int64_t>(bs, q.length - int64_t(j) * bs);
+      filled[q.blocks[j]] = std::max<int32_t>(filled[q.blocks[j]], int32_t(in_block));
+    }
+  }
+  for (int b = 0; b < a->num_blocks; ++b) {
+    if (a->refcount[b] > 0) ++st.used_blocks;
+    if (a->refcount[b] > 1) ++st.shared_blocks;
+    st.stored_tokens += filled[b];
+  }
+  *out = st;
+  return PKV_OK;
+}
+
 int pkv_alloc_free_list(const pkv_alloc* a, int32_t* ids_out, int cap) {
   if (!a) return -1;
   int n = int(a->free_stack.size());

@@ -158,6 +158,7 @@ class AllocatorMachine(RuleBasedStateMachine):
     def states_agree(self):
         _compare(self.a, self.m)
         _compare(self.ah, self.mh)
+        assert self.a.stats() == self.m.stats() and self.ah.stats() == self.mh.stats()
         self.m.check_invariants()
         self.mh.check_invariants()
 

@@ -144,3 +144,24 @@ def test_swap_exhaustion_fails_and_leaves_both_unchanged():
     assert e.value.status == OUT_OF_BLOCKS
     assert (dev.free, dev.ref) == (snap[0], snap[1]) and dev.seqs[1] == [snap[2][1][0], 9]
     assert len(host.free) == 2 and not host.seqs
+
+
+def test_stats_match_the_waste_closed_form():
+    """Paged waste is sum over sequences of ceil(L/bs)*bs - L (each under one block); a
+    fork adds logical blocks and tokens but no stored ones."""
+    m = AllocatorModel(40, 16)
+    lens = [1, 16, 17, 40]
+    for i, L in enumerate(lens):
+        m.seq_create(i, L)
+    st = m.stats()
+    assert st["used_blocks"] == 1 + 1 + 2 + 3 == st["logical_blocks"]
+    assert st["tokens"] == st["stored_tokens"] == 74
+    assert st["used_blocks"] * 16 - st["stored_tokens"] == 15 + 0 + 15 + 8
+    m.fork(3, 9, 32)                       # shares the two full blocks of sequence 3
+    st2 = m.stats()
+    assert st2["used_blocks"] == 7 and st2["shared_blocks"] == 2 and st2["logical_blocks"] == 9
+    assert st2["tokens"] == 74 + 32 and st2["stored_tokens"] == 74
+    m.extend(9, 3)                         # the child writes past its shared prefix
+    st3 = m.stats()
+    assert st3["used_blocks"] == 8 and st3["stored_tokens"] == 77 and st3["free_blocks"] == 32
+    _check(m)

@@ -45,11 +45,13 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=None,
                    help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
-    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks", "swap", "waste"], default=None,
+    p.add_argument("--op", choices=["kv_cache_write", "copy_blocks", "swap", "waste", "vmm"], default=None,
                    help="instead of the decode step, time one pool-maintenance kernel on the "
                         "workload's pool: the KV-cache write of the whole batch (the prefill "
                         "pattern) or copy_blocks of --pairs random block pairs")
     p.add_argument("--pairs", type=int, default=1024)
+    p.add_argument("--vmm-page-kib", type=int, default=0,
+                   help="--op vmm: page size in KiB of the virtual-memory pool (0: the paged pool)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="instead of the benchmark, time plain device-to-device copies of MIB MiB "
                         "(the reference kernel for scaling the HBM byte counters)")
@@ -109,6 +111,9 @@ def main():
         return
     if args.op == "waste":
         _waste_report(args)
+        return
+    if args.op == "vmm":
+        _vmm_bench(args)
         return
     if args.op:
         _op_bench(args)
@@ -535,6 +540,105 @@ def _waste_report(args):
         row["budget_slots"] = budget_slots
         row["sequences_that_fit"] = {"paged_bs16": fits_paged, "contiguous_max_len": budget_slots // max_len}
         print(json.dumps(row), flush=True)
+
+
+def _vmm_bench(args):
+    """Decode over the same K/V in three placements: the paged pool with blocks in random
+    order, and contiguous per-sequence slices of virtual memory mapped on demand (pkv_vmm_*)
+    with one-block pages and with 2 MiB pages.  Each uses --layers copies so that a step reads
+    from HBM; the split kernel is timed by its dispatch-recorded events on every step."""
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from synth import WORKLOADS, make_decode_case
+
+    wl = WORKLOADS[args.workload]
+    if wl.prefix_group or wl.kv_dtype != "bf16":
+        raise SystemExit("--op vmm runs on the bf16 decode workloads")
+    case = make_decode_case(wl, args.seed)
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, D, bs = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size
+    lens32 = case.lengths.astype(np.int32)
+    nbs = [(int(L) + bs - 1) // bs for L in case.lengths]
+    max_blocks = max(1, max(nbs))
+    kt = torch.from_numpy(np.ascontiguousarray(case.k, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    vt = torch.from_numpy(np.ascontiguousarray(case.v, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = torch.from_numpy(np.ascontiguousarray(case.q, np.uint16).view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty_like(q)
+    lens = torch.from_numpy(lens32).to(dev)
+    kv_bytes = int(case.lengths.sum()) * Hkv * D * 2 * 2
+    layouts, failed = {}, {}
+    if args.vmm_page_kib == 0:
+        paged = []
+        ptab = torch.from_numpy(case.block_tables).to(dev)
+        pslots = torch.from_numpy(pkv.build_slot_mapping(case.block_tables, lens32, bs)).to(dev)
+        for _ in range(args.layers):
+            k = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, torch.bfloat16, dev)
+            v = pkv.allocate_kv_pool(case.num_blocks, Hkv, bs, D, torch.bfloat16, dev)
+            pkv.kv_cache_write(kt, vt, k, v, pslots)
+            paged.append((k, v, ptab))
+        layouts["paged_random_blocks"] = (paged, case.num_blocks * Hkv * bs * D * 2 * 2 * args.layers, None)
+    else:
+        page = args.vmm_page_kib << 10
+        name = f"vmm_{args.vmm_page_kib}KiB_pages"
+        pools, mapped = [], 0
+        t0 = time.perf_counter()
+        n_pages = 0
+        try:
+            for _ in range(args.layers):
+                vmm = pkv.VmmPool(B, max_blocks, Hkv, bs, D, torch.bfloat16, page_bytes=page)
+                pools.append((vmm.k, vmm.v, None, vmm))
+                tables = np.full((B, max_blocks), -1, dtype=np.int32)
+                for s_, nb in enumerate(nbs):
+                    vmm.reserve(s_, nb)
+                    tables[s_, :nb] = vmm.first_block(s_) + np.arange(nb)
+                n_pages += (vmm.mapped_bytes // vmm.page_bytes) - 2
+                pools[-1] = (vmm.k, vmm.v, torch.from_numpy(tables).to(dev), vmm)
+                mapped += vmm.mapped_bytes
+        except pkv.PagedKVError as e:
+            # Record how far the mapping got: the driver caps the number of allocations.
+            last = pools[-1][3] if pools else None
+            if last is not None and pools[-1][2] is None:
+                n_pages += (last.mapped_bytes // last.page_bytes) - 2
+            failed[name] = {"page_bytes": page, "error": str(e), "pages_mapped_before_failure": int(n_pages)}
+            for p_ in pools:
+                p_[3].close()
+            pools = []
+        if pools:
+            map_s = time.perf_counter() - t0
+            for k, v, t, _ in pools:
+                slots = torch.from_numpy(pkv.build_slot_mapping(t.cpu().numpy(), lens32, bs)).to(dev)
+                pkv.kv_cache_write(kt, vt, k, v, slots)
+            layouts[name] = (pools, mapped, {"page_bytes": pools[0][3].page_bytes,
+                                             "map_us_per_page": round(map_s * 1e6 / max(1, n_pages), 2),
+                                             "pages_mapped": int(n_pages)})
+    del kt, vt
+    qd, kd = pkv.BF16, pkv.BF16
+    ws = torch.empty(pkv.paged_attention_workspace_size(B, Hq, Hkv, D, bs, qd, kd, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rows = {}
+    for name, (pools, mapped, extra) in layouts.items():
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for pair in evs:
+            for e in pair:
+                e.record(stream)
+        torch.cuda.synchronize()
+        for i in range(args.warmup + args.steps):
+            k, v, t = pools[i % len(pools)][:3]
+            if i >= args.warmup:
+                pkv.set_launch_events(*evs[i - args.warmup])
+            pkv.paged_attention_decode(out, q, k, v, t, lens, case.scale, num_splits=0, workspace=ws)
+        torch.cuda.synchronize()
+        us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
+        rows[name] = {"split_kernel_us": round(us, 2), "GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+                      "device_bytes_backing_kv": int(mapped)}
+        if extra:
+            rows[name].update(extra)
+    print(json.dumps({"op": "vmm", "workload": wl.name, "kv_bytes": kv_bytes, "layers": args.layers,
+                      "layouts": rows, "could_not_map": failed}), flush=True)
+    for pools, _, _ in layouts.values():
+        for entry in pools:
+            if len(entry) > 3:
+                entry[3].close()
 
 
 def _op_bench(args):

@@ -20,7 +20,9 @@
  * Conventions for every entry point
  *   - All pointers to tensors are device pointers unless the parameter says "host".
  *     The caller owns every buffer, including the attention workspace; the library
- *     never allocates or frees device memory and never synchronises a stream.
+ *     never allocates or frees device memory and never synchronises a stream -- except
+ *     the virtual-memory pool object (pkv_vmm_*), whose purpose is to map and unmap
+ *     device memory, and only in its own calls.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.  All
  *     kernels of one call are enqueued on that stream in order.
  *   - Every function returns a pkv_status.  Argument checks happen on the host before
@@ -423,6 +425,47 @@ int pkv_alloc_free_list(const pkv_alloc* a, int32_t* ids_out, int cap);
  * tokens of prefilled sequences whose tables were built elsewhere. */
 pkv_status pkv_build_slot_mapping(const int32_t* tables, const int32_t* lens, int num_seqs,
                                   int max_blocks, int block_size, int64_t* slots_out);
+
+/* ------------------------------------------------------------------------------------
+ * KV pool in contiguous virtual memory, backed on demand (the alternative the pages set
+ * against paging: "What is PagedAttention?", glossary, "Frequently Asked Questions" and
+ * "Common Use Cases": contiguous virtual memory whose physical pages are mapped as a
+ * sequence grows, versus paged blocks).  For comparing placements; the attention kernels
+ * read it unchanged.
+ *
+ * pkv_vmm_create reserves, for K and for V, a virtual range of the pool layout with one
+ * contiguous slice of max_blocks_per_seq blocks per sequence after a first page that stays
+ * mapped, zeroed, for the pool's lifetime (block 0 lives there; the kernels read block 0 in
+ * place of a table entry outside the pool).  Physical memory is mapped in pages: a page
+ * holds whole blocks and whole device granules, and is the smallest such size at least
+ * page_bytes (0: the runtime's recommended granule).  Each slice starts on a page.
+ * block_bytes is one block of one pool (Hkv * bs * D * element bytes).  Returns NULL on
+ * failure (see pkv_last_error; PKV_UNSUPPORTED where the device has no virtual memory
+ * management).
+ *
+ * pkv_vmm_reserve maps physical memory (page by page, K and V) so that blocks
+ * [0, num_blocks) of seq's slice are backed; all-or-nothing.  pkv_vmm_release unmaps and
+ * frees all of seq's pages.  Both synchronise with the device as the HIP virtual-memory
+ * calls do; no kernel may read a slice beyond its mapped blocks.
+ *
+ * Sequence seq's logical block j is pool block pkv_vmm_seq_first_block(seq) + j of the
+ * pools at pkv_vmm_k_base / pkv_vmm_v_base, which hold pkv_vmm_num_blocks blocks (most of
+ * them unmapped).  pkv_vmm_mapped_bytes counts the physical bytes mapped, both pools and the
+ * base pages included; pkv_vmm_page_bytes is the page size.
+ * ------------------------------------------------------------------------------------ */
+typedef struct pkv_vmm pkv_vmm;
+pkv_vmm* pkv_vmm_create(int device, int max_seqs, int max_blocks_per_seq, size_t block_bytes,
+                        size_t page_bytes);
+void pkv_vmm_destroy(pkv_vmm* v);
+pkv_status pkv_vmm_reserve(pkv_vmm* v, int seq, int num_blocks);
+pkv_status pkv_vmm_release(pkv_vmm* v, int seq);
+void* pkv_vmm_k_base(const pkv_vmm* v);
+void* pkv_vmm_v_base(const pkv_vmm* v);
+int pkv_vmm_num_blocks(const pkv_vmm* v);
+int pkv_vmm_seq_first_block(const pkv_vmm* v, int seq);
+int pkv_vmm_mapped_blocks(const pkv_vmm* v, int seq);
+size_t pkv_vmm_mapped_bytes(const pkv_vmm* v);
+size_t pkv_vmm_page_bytes(const pkv_vmm* v);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ __all__ = [
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
-    "paged_attention_prefill", "allocate_host_pool", "swap_blocks",
+    "paged_attention_prefill", "allocate_host_pool", "swap_blocks", "VmmPool",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -70,6 +70,17 @@ _SIGNATURES = {
     "pkv_swap_blocks": ([_c_p, _c_p, _c_int, _c_p, _c_p, _c_int, _c_p] + [_c_int] * 5 + [_c_p], _c_int),
     "pkv_seq_swap": ([_c_p, _c_p, _c_i64, _c_p, _c_p], _c_int),
     "pkv_alloc_stats_get": ([_c_p, _c_p], _c_int),
+    "pkv_vmm_create": ([_c_int, _c_int, _c_int, _c_sz, _c_sz], _c_p),
+    "pkv_vmm_destroy": ([_c_p], None),
+    "pkv_vmm_reserve": ([_c_p, _c_int, _c_int], _c_int),
+    "pkv_vmm_release": ([_c_p, _c_int], _c_int),
+    "pkv_vmm_k_base": ([_c_p], _c_p),
+    "pkv_vmm_v_base": ([_c_p], _c_p),
+    "pkv_vmm_num_blocks": ([_c_p], _c_int),
+    "pkv_vmm_seq_first_block": ([_c_p, _c_int], _c_int),
+    "pkv_vmm_mapped_blocks": ([_c_p, _c_int], _c_int),
+    "pkv_vmm_mapped_bytes": ([_c_p], _c_sz),
+    "pkv_vmm_page_bytes": ([_c_p], _c_sz),
     "pkv_alloc_create": ([_c_int, _c_int, _c_p], _c_p),
     "pkv_alloc_destroy": ([_c_p], None),
     "pkv_seq_create": ([_c_p, _c_i64, _c_i64, _c_p], _c_int),
@@ -413,6 +424,75 @@ def build_slot_mapping(block_tables, lens, block_size: int) -> np.ndarray:
     _check(lib().pkv_build_slot_mapping(t.ctypes.data, ln.ctypes.data, len(ln), t.shape[1],
                                         block_size, out.ctypes.data))
     return out
+
+
+class _DeviceArray:
+    """A device address range described through __cuda_array_interface__, so that torch can
+    view memory the library mapped (the tensor does not own it)."""
+
+    def __init__(self, ptr: int, shape, typestr: str):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (int(ptr), False),
+                                         "version": 2, "strides": None}
+
+
+_RAW = {torch.float32: ("<f4", torch.float32), torch.bfloat16: ("<i2", torch.bfloat16),
+        torch.float8_e4m3fn: ("|u1", torch.float8_e4m3fn)}
+
+
+class VmmPool:
+    """K/V pools in contiguous virtual memory mapped on demand (pkv_vmm_*).
+
+    ``k`` and ``v`` are [num_blocks, Hkv, bs * D] views of the reserved ranges, in the pool
+    layout; sequence ``seq``'s logical block j is block ``first_block(seq) + j``.  Only the
+    blocks made resident with ``reserve`` (and block 0) may be read or written.
+    """
+
+    def __init__(self, max_seqs: int, max_blocks_per_seq: int, num_kv_heads: int, block_size: int,
+                 head_dim: int, dtype: torch.dtype, device: int = 0, page_bytes: int = 0):
+        eb = torch.empty((), dtype=dtype).element_size()
+        self.block_bytes = num_kv_heads * block_size * head_dim * eb
+        h = lib().pkv_vmm_create(device, max_seqs, max_blocks_per_seq, self.block_bytes, page_bytes)
+        if not h:
+            raise PagedKVError(2, lib().pkv_last_error().decode(errors="replace"))
+        self._h = h
+        nb = lib().pkv_vmm_num_blocks(h)
+        typestr, tdt = _RAW[dtype]
+        shape = (nb, num_kv_heads, block_size * head_dim)
+        with torch.cuda.device(device):
+            self.k = torch.as_tensor(_DeviceArray(lib().pkv_vmm_k_base(h), shape, typestr), device=f"cuda:{device}").view(tdt)
+            self.v = torch.as_tensor(_DeviceArray(lib().pkv_vmm_v_base(h), shape, typestr), device=f"cuda:{device}").view(tdt)
+
+    def reserve(self, seq: int, num_blocks: int):
+        _check(lib().pkv_vmm_reserve(self._h, seq, num_blocks))
+
+    def release(self, seq: int):
+        _check(lib().pkv_vmm_release(self._h, seq))
+
+    def first_block(self, seq: int) -> int:
+        return lib().pkv_vmm_seq_first_block(self._h, seq)
+
+    def mapped_blocks(self, seq: int) -> int:
+        return lib().pkv_vmm_mapped_blocks(self._h, seq)
+
+    @property
+    def mapped_bytes(self) -> int:
+        return lib().pkv_vmm_mapped_bytes(self._h)
+
+    @property
+    def page_bytes(self) -> int:
+        return lib().pkv_vmm_page_bytes(self._h)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.k = self.v = None
+            lib().pkv_vmm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover
+            pass
 
 
 class _AllocStats(ctypes.Structure):

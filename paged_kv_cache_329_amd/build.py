@@ -22,7 +22,7 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "allocator.cpp", "cache_ops.hip", "attention_decode.hip", "attention_prefill.hip"]
+SOURCES = ["status.cpp", "allocator.cpp", "vmm.cpp", "cache_ops.hip", "attention_decode.hip", "attention_prefill.hip"]
 
 
 def _hipcc() -> str:
@@ -42,7 +42,9 @@ def _compile(src: str, verbose: bool) -> str:
     if src.endswith(".hip"):
         cmd = [_hipcc(), *COMMON_FLAGS, *HIP_FLAGS, "-c", path, "-o", obj]
     else:
-        cmd = [_hipcc(), "-x", "c++", *COMMON_FLAGS, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
+        rocm = os.path.dirname(os.path.dirname(os.path.realpath(_hipcc())))
+        cmd = [_hipcc(), "-x", "c++", *COMMON_FLAGS, "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include", "-c", path,
+               "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -133,3 +133,11 @@ def test_swap_blocks_rejects_on_host():
     assert lib.pkv_swap_blocks(a, a, 0, a, a, 4, a, 2, 8, 128, 16, pkv.BF16, None) == 1
     assert lib.pkv_swap_blocks(None, a, 4, a, a, 4, a, 2, 8, 128, 16, pkv.BF16, None) == 1
     assert lib.pkv_swap_blocks(a, a, 4, a, a, 4, None, 0, 8, 128, 16, pkv.BF16, None) == 0
+
+
+def test_vmm_create_rejects_bad_sizes_without_a_device_call():
+    lib = pkv.lib()
+    assert not lib.pkv_vmm_create(0, 0, 1, 32768, 0)
+    assert b"max_seqs" in lib.pkv_last_error()
+    assert not lib.pkv_vmm_create(0, 4, 16, 100, 0)        # block bytes not a multiple of 16
+    assert lib.pkv_vmm_num_blocks(None) == -1 and lib.pkv_vmm_mapped_bytes(None) == 0

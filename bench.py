@@ -335,12 +335,18 @@ def _multi_query_bench(args, wl):
     max_q = int(case.q_lens.max())
     stream = torch.cuda.current_stream(dev)
     ks, vs = float(case.k_scale), float(case.v_scale)
+    qd = pkv.F32 if wl.q_dtype == "f32" else pkv.BF16
+    kd = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
+    ws_bytes = pkv.paged_attention_prefill_workspace_size(B, Hq, Hkv, D, bs, qd, kd, max_q, args.num_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    path = "split over keys + merge (few queries)" if ws_bytes else "query tiles through LDS"
 
     def step(i, ev=None):
         k, v = pools[i % len(pools)]
         if ev is not None:
             pkv.set_launch_events(ev[0], ev[1])
-        pkv.paged_attention_prefill(out, q, k, v, tables, lens, qstart, max_q, case.scale, ks, vs)
+        pkv.paged_attention_prefill(out, q, k, v, tables, lens, qstart, max_q, case.scale, ks, vs,
+                                    num_splits=args.num_splits, workspace=ws)
 
     def new_events(n):
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
@@ -391,7 +397,8 @@ def _multi_query_bench(args, wl):
         achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes": kv_bytes}
-    roof["kernel"] = "paged_attention_prefill_kernel"
+    roof["kernel"] = "paged_attention_mq_split_kernel" if ws_bytes else "paged_attention_prefill_kernel"
+    roof["path"] = path
     roof["traffic_unit"] = ("HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, scaled by a plain "
                             "copy of known size)")
     qb = 4 if wl.q_dtype == "f32" else 2

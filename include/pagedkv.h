@@ -237,12 +237,26 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *   query_start    int32 [num_seqs + 1] (device), non-decreasing, from 0 to num_q_tokens;
  *                  entries are clamped to [0, num_q_tokens].
  *   max_query_len  host bound on every n_s: query rows past it in a sequence are neither
- *                  computed nor written.
- *   Every other argument as for pkv_paged_attention_decode.  No workspace; out is written
- *   once per query row and head, nothing else is written.
- * Limits: max_blocks_per_seq <= 16376 (the sequence's table entries are staged on chip);
- * num_q_tokens * Hq < 2^31.
+ *                  computed nor written.  It also picks the kernel: with max_query_len * G
+ *                  <= 32 (a few drafted tokens, short chunks) the work is cut like decode's
+ *                  into num_splits equal shares of the (sequence, kv head, block) list with a
+ *                  merge pass, which needs the workspace; otherwise query tiles of 256
+ *                  (query, head) columns each stream their sequence's K/V through LDS, with no
+ *                  workspace.
+ *   num_splits     shares for the few-query path (0 = a default like decode's); ignored
+ *                  otherwise.
+ *   workspace      device scratch of pkv_paged_attention_prefill_workspace_size bytes (0 on
+ *                  the tile path, where it may be NULL); no initial contents needed.
+ *   Every other argument as for pkv_paged_attention_decode.  out is written once per
+ *   query row and head.
+ * Limits: on the tile path max_blocks_per_seq <= 16376 (the sequence's table entries are
+ * staged on chip); num_q_tokens * Hq < 2^31.
  * ------------------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_prefill_workspace_size(int num_seqs, int num_q_heads,
+                                                      int num_kv_heads, int head_dim,
+                                                      int block_size, pkv_dtype q_dtype,
+                                                      pkv_dtype kv_dtype, int max_query_len,
+                                                      int num_splits, size_t* bytes /* host, out */);
 pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_cache,
                                        const void* v_cache, const int32_t* block_tables,
                                        const int32_t* context_lens, const int32_t* query_start,
@@ -250,7 +264,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        int num_kv_heads, int head_dim, int block_size,
                                        int num_blocks, int max_blocks_per_seq, int max_query_len,
                                        float scale, float k_scale, float v_scale,
-                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, void* stream);
+                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",

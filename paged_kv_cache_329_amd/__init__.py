@@ -28,7 +28,7 @@ __all__ = [
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
-    "paged_attention_prefill", "allocate_host_pool", "swap_blocks", "VmmPool",
+    "paged_attention_prefill", "paged_attention_prefill_workspace_size", "allocate_host_pool", "swap_blocks", "VmmPool",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -63,7 +63,9 @@ _SIGNATURES = {
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
-    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 2 + [_c_p], _c_int),
+    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
+                                    _c_int),
+    "pkv_paged_attention_prefill_workspace_size": ([_c_int] * 9 + [ctypes.POINTER(_c_sz)], _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                             _c_int, _c_int, _c_f, _c_f, _c_p], _c_int),
     "pkv_copy_blocks": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
@@ -261,11 +263,22 @@ def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens,
                         context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
 
 
+def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                           q_dtype, kv_dtype, max_query_len, num_splits=0) -> int:
+    n = _c_sz(0)
+    _check(lib().pkv_paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                            block_size, q_dtype, kv_dtype, int(max_query_len),
+                                                            int(num_splits), ctypes.byref(n)))
+    return n.value
+
+
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
-                            max_query_len, scale, k_scale=1.0, v_scale=1.0, stream=None):
+                            max_query_len, scale, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None,
+                            stream=None):
     """Causal multi-query attention (pkv_paged_attention_prefill): sequence s's queries are
     q rows query_start[s] .. query_start[s+1]-1, its last tokens, each attending to every
-    token up to its own position.  q / out are [num_q_tokens, Hq, D]."""
+    token up to its own position.  q / out are [num_q_tokens, Hq, D].  A workspace is made
+    (and cached per stream) when the few-query path needs one and none is given."""
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_q_tokens, num_q_heads, head_dim] of one dtype")
     T, Hq, D = q.shape
@@ -277,14 +290,33 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     B = context_lens.shape[0]
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.dim() != 1 or query_start.shape != (B + 1,):
         raise ValueError("block_tables [num_seqs, max_blocks], context_lens [num_seqs], query_start [num_seqs+1]")
+    qd, kd = _dtype_code(q.dtype), _dtype_code(k_cache.dtype)
+    st = _stream(stream)
+    if workspace is None:
+        nbytes = paged_attention_prefill_workspace_size(B, Hq, Hkv, D, bs, qd, kd, max_query_len, num_splits)
+        workspace = _mq_workspace(nbytes, q.device, st) if nbytes else None
     ptrs = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
             _dev(query_start, "query_start")]
     _check(lib().pkv_paged_attention_prefill(*ptrs, B, T, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                                              int(max_query_len), float(scale), float(k_scale),
-                                             float(v_scale), _dtype_code(q.dtype),
-                                             _dtype_code(k_cache.dtype), _stream(stream)))
+                                             float(v_scale), qd, kd, int(num_splits),
+                                             _dev(workspace, "workspace") if workspace is not None else None,
+                                             workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                             st))
     return out
+
+
+_mq_ws_cache: dict = {}
+
+
+def _mq_workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
+    key = (str(device), stream_handle)
+    ws = _mq_ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _mq_ws_cache[key] = ws
+    return ws
 
 
 def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,

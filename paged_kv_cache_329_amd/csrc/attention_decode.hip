@@ -75,21 +75,6 @@ struct DecodeArgs {
   float k_inv, v_inv;  // float32 1/k_scale, 1/v_scale (fp8 caches)
 };
 
-// Sum over the wave, returned as a wave-uniform (scalar) value.
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return __builtin_amdgcn_readfirstlane(v);
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
 
 // Blocks holding a sequence's tokens (length clamped to what its table row can hold).
 __device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s, int bs) {
@@ -138,12 +123,6 @@ __device__ void locate(const DecodeArgs& a, int bs, int lane, int x, int& s_out,
   off_out = base;
 }
 
-__device__ __forceinline__ int64_t share_begin(int64_t w, int64_t W, int64_t n) { return w * W / n; }
-
-// Index of the share holding work position x.
-__device__ __forceinline__ int64_t share_of(int64_t x, int64_t W, int64_t n) {
-  return ((x + 1) * n - 1) / W;
-}
 
 // Element bits the cache stores for input element bits x (q's dtype) of k_new / v_new: f32
 // and bf16 are stored as given; fp8 stores RNE(clamp(x * inv)), as the KV-cache write does.

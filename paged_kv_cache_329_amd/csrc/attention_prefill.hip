@@ -41,7 +41,10 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "attention_tile.h"
 #include "status.h"
@@ -383,6 +386,424 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   }
 }
 
+// ---- few query tokens per sequence: split over the keys ---------------------------------
+//
+// With n_s * G <= 32 columns per (sequence, kv head) -- checking a few drafted tokens, or
+// short prefill chunks -- a query tile would leave most of a workgroup idle and put one
+// workgroup on each long (sequence, kv head).  This path is decode's: the flattened
+// (sequence, kv head, block) list is cut into equal shares, one per wavefront; each wave
+// streams its blocks straight from the pool (no LDS) with two 16-column matrix tiles
+// covering all of the unit's (query, head) columns, the causal mask per column, and leaves
+// a finished result or a partial (max, sum, accumulator) per column; a merge pass folds the
+// partials of units that span several shares.
+
+constexpr int kMqWaves = 4;
+constexpr int kMqCols = 32;   // columns per (sequence, kv head) this path takes
+
+struct MqArgs {
+  void* out;
+  const void* q;
+  const uint8_t* k_cache;
+  const uint8_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  float* ws_acc;  // [splits*2][kMqCols][D]
+  float* ws_ml;   // [splits*2][kMqCols][2]  (max in log2 units, sum)
+  int* ws_seq;    // [B+1]: Hkv * blocks of the sequences before s; [B] = total work W
+  int B, Hkv, G, num_blocks, max_blocks, num_q_tokens, splits;
+  float qk_scale_log2;
+  float v_scale;
+};
+
+__device__ __forceinline__ int mq_len(const MqArgs& a, int s, int bs) {
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : L;
+  const int64_t cap = int64_t(a.max_blocks) * bs;
+  return L > cap ? int(cap) : L;
+}
+
+__device__ __forceinline__ void mq_queries(const MqArgs& a, int s, int& q0, int& n) {
+  int lo = a.query_start[s], hi = a.query_start[s + 1];
+  lo = std::min(std::max(lo, 0), a.num_q_tokens);
+  hi = std::min(std::max(hi, lo), a.num_q_tokens);
+  q0 = lo;
+  n = hi - lo;
+}
+
+// Total work W = Hkv * sum_s blocks(s) (wave-uniform).
+__device__ int mq_total(const MqArgs& a, int bs, int lane) {
+  int acc = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int s = base + lane;
+    acc += s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs : 0;
+  }
+  return wave_sum(acc) * a.Hkv;
+}
+
+// Sequence whose units contain work position x, and Hkv * blocks before it.
+__device__ void mq_locate(const MqArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int s = b0 + lane;
+    const int w = s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs * a.Hkv : 0;
+    const int incl = wave_incl_scan(w, lane);
+    const int lo = base + (incl - w), hi = base + incl;
+    const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      s_out = b0 + l;
+      off_out = base + __builtin_amdgcn_readlane(incl - w, l);
+      return;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  s_out = a.B;
+  off_out = base;
+}
+
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs a) {
+  using F = Frag<KV, D>;
+  using T = KvTraits<KV>;
+  constexpr int X = 16 / T::EB;
+  constexpr int SUB_BYTES = 16 * D * T::EB;
+  constexpr int NSB = BS / 16;
+  constexpr int64_t REGION = int64_t(BS) * D * T::EB;
+  constexpr int CT = kMqCols / 16;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kMqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = mq_total(a, BS, lane);
+  if (wave == 0) {
+    int base = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int sq = b0 + lane;
+      const int w = sq < a.B ? (mq_len(a, sq, BS) + BS - 1) / BS * a.Hkv : 0;
+      const int incl = wave_incl_scan(w, lane);
+      if (sq < a.B) a.ws_seq[sq] = base + incl - w;
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) a.ws_seq[a.B] = base;
+  }
+  if (W == 0) return;
+  const int nshare = std::min(a.splits, W);
+  if (wave >= nshare) return;
+  const int c_begin = int(share_begin(wave, W, nshare));
+  const int c_end = int(share_begin(wave + 1, W, nshare));
+
+  int s, seq_off;
+  mq_locate(a, BS, lane, c_begin, s, seq_off);
+  if (s >= a.B) return;
+  int L = mq_len(a, s, BS);
+  int nb = (L + BS - 1) / BS;
+  int g = (c_begin - seq_off) / nb;
+  int unit_off = seq_off + g * nb;
+  int pos = c_begin;
+  const int row = lane >> 4;
+  const float sl2 = a.qk_scale_log2;
+
+  while (pos < c_end) {
+    const int unit_end = unit_off + nb;
+    const int seg_end = std::min(c_end, unit_end);
+    const bool full = pos == unit_off && seg_end == unit_end;
+    const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
+    const int k0 = j0 * NSB;
+    const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
+
+    int q0, n;
+    mq_queries(a, s, q0, n);
+    // Column c = 16*ct + lane%16 is (query c / G, head c % G); query i sits at L - n + i.
+    int posc[CT];
+    uint4 qf[CT][F::NLOAD * F::QCH];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + (lane & 15);
+      const int qi = c / a.G, hh = c % a.G;
+      const bool ok = qi < n;
+      posc[ct] = ok ? L - n + qi : -1;
+      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                            ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+        for (int cc = 0; cc < F::QCH; ++cc)
+          qf[ct][i * F::QCH + cc] =
+              ok ? *reinterpret_cast<const uint4*>(qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * cc)
+                 : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+    int tbase = k0 / NSB;
+    int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+    f32x4 acc[CT][F::NT];
+    float m_run[CT], l_run[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[ct] = -INFINITY;
+      l_run[ct] = 0.f;
+    }
+    const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
+    const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
+    const int64_t block_stride = int64_t(a.Hkv) * REGION;
+
+    for (int k = k0; k < k1; ++k) {
+      if (k / NSB >= tbase + 64) {
+        tbase = k / NSB;
+        tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+      }
+      // K and V of the sub-tile are loaded together, with no branch before their use: a
+      // table entry outside [0, num_blocks) reads block 0 and its keys and values are
+      // replaced by zeros.
+      const int phys = __builtin_amdgcn_readlane(tbl, k / NSB - tbase);
+      const bool bad = unsigned(phys) >= unsigned(a.num_blocks);
+      const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
+      uint4 kf[F::NLOAD], vf[F::NLOAD];
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_stream(kbase + off + i * 1024);
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_stream(vbase + off + i * 1024);
+      const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) {
+        kf[i].x &= km; kf[i].y &= km; kf[i].z &= km; kf[i].w &= km;
+      }
+      const int t0 = k * 16 + 4 * row;
+      float p[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
+        float sc[4];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[j] = t0 + j <= posc[ct] ? c[j] * sl2 : -INFINITY;   // posc < L: the tail is masked too
+          cmax = fmaxf(cmax, sc[j]);
+        }
+        cmax = wave_max_rows(cmax);
+        const float m_new = fmaxf(m_run[ct], cmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;      // column with nothing yet
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+        m_run[ct] = m_new;
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[ct][j] = __builtin_amdgcn_exp2f(sc[j] - m_use);          // 0 where masked
+          l_run[ct] += p[ct][j];
+        }
+      }
+      uint32_t vm = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vm |= (t0 + j < L && !bad ? 1u : 0u) << j;
+      mask_v<KV, D>(vf, vm);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct]);
+    }
+
+    const int slot = pos == c_begin ? 0 : 1;
+    const int64_t piece = int64_t(wave) * 2 + slot;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float l_tot = wave_sum_rows(l_run[ct]);
+      const int c = 16 * ct + (lane & 15);
+      const int qi = c / a.G, hh = c % a.G;
+      if (qi >= n) continue;
+      if (full) {
+        const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
+        const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+#pragma unroll
+        for (int nn = 0; nn < F::NT; ++nn) {
+          const int d = 16 * nn + 4 * row;
+          if constexpr (KV == PKV_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) =
+                make_float4(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv, acc[ct][nn][2] * inv, acc[ct][nn][3] * inv);
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) =
+                make_uint2(pack_bf16x2(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv),
+                           pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
+          }
+        }
+      } else {
+        float* wacc = a.ws_acc + (piece * kMqCols + c) * D;
+#pragma unroll
+        for (int nn = 0; nn < F::NT; ++nn)
+          *reinterpret_cast<float4*>(wacc + 16 * nn + 4 * row) =
+              make_float4(acc[ct][nn][0], acc[ct][nn][1], acc[ct][nn][2], acc[ct][nn][3]);
+        if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = make_float2(m_run[ct], l_tot);
+      }
+    }
+
+    pos = seg_end;
+    if (pos >= c_end) break;
+    // Next unit: next kv head of this sequence, else the next non-empty sequence.
+    unit_off = unit_end;
+    if (++g == a.Hkv) {
+      g = 0;
+      bool done;
+      do {
+        done = ++s >= a.B;
+      } while (!done && (L = mq_len(a, s, BS)) == 0);
+      if (done) break;
+      nb = (L + BS - 1) / BS;
+    }
+  }
+}
+
+// One wave per (four columns, kv head, sequence), four waves per workgroup: merges the
+// partials of a split unit's columns, or writes zeros for the queries of a sequence without
+// keys.  The four columns' partials of a batch of pieces are all requested before any is
+// folded.
+constexpr int kMqMergeCols = 4;
+constexpr int kMqMergeWaves = 4;
+
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_kernel(MqArgs a) {
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 8;     // pieces per round of loads: a unit rarely spans more shares
+  constexpr int C4 = kMqMergeCols;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c0 = (blockIdx.x * kMqMergeWaves + wave) * C4, g = blockIdx.y, s = blockIdx.z;
+  int q0, n;
+  mq_queries(a, s, q0, n);
+  const int ncols = std::min(C4, n * a.G - c0);     // valid columns of this wave
+  if (ncols <= 0) return;
+  const int before = a.ws_seq[s];
+  const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
+  const int W = a.ws_seq[a.B];
+  auto write = [&](int c, const float* v, float inv) {
+    const int qi = c / a.G, hh = c % a.G;
+    const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int64_t o = orow + lane + 64 * r;
+      if constexpr (KV == PKV_F32) static_cast<float*>(a.out)[o] = v[r] * inv;
+      else static_cast<uint16_t*>(a.out)[o] = uint16_t(pack_bf16x2(v[r] * inv, 0.f) & 0xFFFFu);
+    }
+  };
+  float num[C4][PER];
+#pragma unroll
+  for (int cc = 0; cc < C4; ++cc)
+#pragma unroll
+    for (int r = 0; r < PER; ++r) num[cc][r] = 0.f;
+  if (nb == 0) {
+    for (int cc = 0; cc < ncols; ++cc) write(c0 + cc, num[cc], 0.f);
+    return;
+  }
+  const int nshare = std::min(a.splits, W);
+  const int off = before + g * nb;
+  const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
+  if (wf == wl) return;
+  const int np = int(wl - wf + 1);
+  const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  float M[C4], den[C4];
+#pragma unroll
+  for (int cc = 0; cc < C4; ++cc) {
+    M[cc] = -INFINITY;
+    den[cc] = 0.f;
+  }
+  for (int j0 = 0; j0 < np; j0 += BATCH) {
+    float2 ml[BATCH][C4];
+    float x[BATCH][C4][PER];
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      const int j = std::min(j0 + t, np - 1);
+      const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
+#pragma unroll
+      for (int cc = 0; cc < C4; ++cc) {
+        const int c = c0 + std::min(cc, ncols - 1);
+        ml[t][cc] = *reinterpret_cast<const float2*>(a.ws_ml + (pc * kMqCols + c) * 2);
+        const float* pacc = a.ws_acc + (pc * kMqCols + c) * D + lane;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) x[t][cc][r] = pacc[64 * r];
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < C4; ++cc) {
+      float mb = M[cc];
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t)
+        if (j0 + t < np) mb = fmaxf(mb, ml[t][cc].x);
+      if (mb == -INFINITY) continue;                   // nothing attended yet
+      const float alpha = __builtin_amdgcn_exp2f(M[cc] - mb);
+      den[cc] *= alpha;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) num[cc][r] *= alpha;
+#pragma unroll
+      for (int t = 0; t < BATCH; ++t) {
+        const float w = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t][cc].x - mb) : 0.f;
+        den[cc] += ml[t][cc].y * w;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) num[cc][r] += x[t][cc][r] * w;
+      }
+      M[cc] = mb;
+    }
+  }
+  for (int cc = 0; cc < ncols; ++cc) write(c0 + cc, num[cc], den[cc] > 0.f ? a.v_scale / den[cc] : 0.f);
+}
+
+using MqFn = void (*)(MqArgs);
+struct MqPair {
+  MqFn split, merge;
+};
+
+template <int KV, int D, int BS>
+MqPair mq_kernels() {
+  return {paged_attention_mq_split_kernel<KV, D, BS>, paged_attention_mq_merge_kernel<KV, D, BS>};
+}
+
+bool pick_mq(pkv_dtype kv, int D, int bs, MqPair* kp) {
+#define PKV_MQ(KVT, DD, BB) \
+  if (kv == KVT && D == DD && bs == BB) { *kp = mq_kernels<KVT, DD, BB>(); return true; }
+  PKV_MQ(PKV_F32, 64, 16) PKV_MQ(PKV_F32, 64, 32) PKV_MQ(PKV_F32, 128, 16) PKV_MQ(PKV_F32, 128, 32)
+  PKV_MQ(PKV_BF16, 64, 16) PKV_MQ(PKV_BF16, 64, 32) PKV_MQ(PKV_BF16, 128, 16) PKV_MQ(PKV_BF16, 128, 32)
+  PKV_MQ(PKV_FP8_E4M3FN, 64, 16) PKV_MQ(PKV_FP8_E4M3FN, 64, 32)
+  PKV_MQ(PKV_FP8_E4M3FN, 128, 16) PKV_MQ(PKV_FP8_E4M3FN, 128, 32)
+#undef PKV_MQ
+  return false;
+}
+
+size_t mq_round(size_t b) { return (b + 255) / 256 * 256; }
+size_t mq_workspace_bytes(int splits, int B, int D) {
+  return mq_round(size_t(splits) * 2 * kMqCols * D * sizeof(float)) +
+         mq_round(size_t(splits) * 2 * kMqCols * 2 * sizeof(float)) + (size_t(B) + 1) * sizeof(int);
+}
+
+// Default share count of the few-query path: as decode's, 2 workgroups of 4 waves per CU
+// (4 for fp8 caches), capped by what the device keeps resident of the split kernel.
+pkv_status mq_default_splits(const MqPair& kp, pkv_dtype kv, int* splits) {
+  // The device queries are made once per (device, kernel) and cached.
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, std::pair<int, int>> cache;   // -> (CUs, resident)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return pkv::fail(PKV_HIP_ERROR, "pkv_paged_attention_prefill: no current device");
+  }
+  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(kp.split));
+  std::pair<int, int> cu_res;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it == cache.end()) {
+      int cus = 0, per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, key.second, kMqWaves * 64, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return pkv::fail(PKV_HIP_ERROR, "pkv_paged_attention_prefill: device query failed");
+      }
+      it = cache.emplace(key, std::make_pair(cus, per_cu)).first;
+    }
+    cu_res = it->second;
+  }
+  const int target = kv == PKV_FP8_E4M3FN ? 4 : 2;
+  *splits = std::max(1, cu_res.first * std::min(target, std::max(cu_res.second, 1)) * kMqWaves);
+  return PKV_OK;
+}
+
 using PrefillFn = void (*)(PrefillArgs);
 
 template <int KV, int D, int BS>
@@ -409,14 +830,10 @@ bool pick_prefill(int D, int bs, PrefillFn* fn, int* cols) {
 
 }  // namespace
 
-extern "C" pkv_status pkv_paged_attention_prefill(
-    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
-    const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_q_tokens,
-    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-    int max_blocks_per_seq, int max_query_len, float scale, float k_scale, float v_scale,
-    pkv_dtype q_dtype, pkv_dtype kv_dtype, void* stream) {
-  const char* fn = "pkv_paged_attention_prefill";
-  const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads;
+namespace {
+
+pkv_status check_mq_shape(const char* fn, int B, int num_q_tokens, int max_query_len, int Hq, int Hkv,
+                          int head_dim, int block_size, pkv_dtype q_dtype, pkv_dtype kv_dtype) {
   if (B < 0 || num_q_tokens < 0 || max_query_len < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
     return pkv::fail(PKV_INVALID_ARG, "%s: num_seqs=%d num_q_tokens=%d max_query_len=%d Hq=%d Hkv=%d", fn,
                      B, num_q_tokens, max_query_len, Hq, Hkv);
@@ -426,6 +843,55 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return pkv::fail(PKV_UNSUPPORTED, "%s: q_dtype=%d kv_dtype=%d", fn, int(q_dtype), int(kv_dtype));
   if (!((head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32)))
     return pkv::fail(PKV_UNSUPPORTED, "%s: head_dim=%d block_size=%d", fn, head_dim, block_size);
+  return PKV_OK;
+}
+
+// The few-query path takes batches whose (query, head) columns per (sequence, kv head) fit
+// two matrix tiles.
+bool few_queries(int max_query_len, int G) { return int64_t(max_query_len) * G <= kMqCols; }
+
+pkv_status mq_splits(const char* fn, pkv_dtype kv, int D, int bs, int requested, MqPair* kp, int* splits) {
+  if (!pick_mq(kv, D, bs, kp)) return pkv::fail(PKV_UNSUPPORTED, "%s: no kernel for this shape", fn);
+  if (requested < 0) return pkv::fail(PKV_INVALID_ARG, "%s: num_splits=%d", fn, requested);
+  if (requested > 0) {
+    *splits = requested;
+    return PKV_OK;
+  }
+  return mq_default_splits(*kp, kv, splits);
+}
+
+}  // namespace
+
+extern "C" pkv_status pkv_paged_attention_prefill_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                                                 int head_dim, int block_size, pkv_dtype q_dtype,
+                                                                 pkv_dtype kv_dtype, int max_query_len,
+                                                                 int num_splits, size_t* bytes) {
+  const char* fn = "pkv_paged_attention_prefill_workspace_size";
+  if (!bytes) return pkv::fail(PKV_INVALID_ARG, "%s: null output", fn);
+  pkv_status st = check_mq_shape(fn, num_seqs, 0, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, q_dtype, kv_dtype);
+  if (st != PKV_OK) return st;
+  *bytes = 0;
+  if (!few_queries(max_query_len, num_q_heads / num_kv_heads)) return PKV_OK;
+  MqPair kp;
+  int splits = 0;
+  if ((st = mq_splits(fn, kv_dtype, head_dim, block_size, num_splits, &kp, &splits)) != PKV_OK) return st;
+  *bytes = mq_workspace_bytes(splits, num_seqs, head_dim);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_attention_prefill(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_q_tokens,
+    int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+    int max_blocks_per_seq, int max_query_len, float scale, float k_scale, float v_scale,
+    pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  const char* fn = "pkv_paged_attention_prefill";
+  const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads;
+  pkv_status cst = check_mq_shape(fn, B, num_q_tokens, max_query_len, Hq, Hkv, head_dim, block_size, q_dtype,
+                                  kv_dtype);
+  if (cst != PKV_OK) return cst;
   if (num_blocks <= 0 || max_blocks_per_seq < 0)
     return pkv::fail(PKV_INVALID_ARG, "%s: num_blocks=%d max_blocks_per_seq=%d", fn, num_blocks,
                      max_blocks_per_seq);
@@ -436,12 +902,67 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   if (!out || !q || !k_cache || !v_cache || !context_lens || !query_start ||
       (max_blocks_per_seq > 0 && !block_tables))
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
-  if (!pkv::aligned16({out, q, k_cache, v_cache}))
+  if (!pkv::aligned16({out, q, k_cache, v_cache, workspace}))
     return pkv::fail(PKV_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
   if (int64_t(B) * Hkv > int64_t(INT32_MAX))
     return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * num_kv_heads exceeds 2^31", fn);
   if (int64_t(num_q_tokens) * Hq > int64_t(INT32_MAX) || int64_t(max_query_len) * (Hq / Hkv) > int64_t(INT32_MAX) / 2)
     return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tokens", fn);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (few_queries(max_query_len, Hq / Hkv)) {
+    // Few query tokens per sequence: shares of the (sequence, kv head, block) list, then merge.
+    MqPair kp;
+    int splits = 0;
+    pkv_status st = mq_splits(fn, kv_dtype, head_dim, block_size, num_splits, &kp, &splits);
+    if (st != PKV_OK) return st;
+    const size_t need = mq_workspace_bytes(splits, B, head_dim);
+    if (!workspace || workspace_bytes < need)
+      return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
+    if (B > 65535 || Hkv > 65535)
+      return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535 here", fn);
+    if (int64_t(B) * max_blocks_per_seq * Hkv > int64_t(INT32_MAX))
+      return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31", fn);
+    MqArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.query_start = query_start;
+    uint8_t* wsb = static_cast<uint8_t*>(workspace);
+    a.ws_acc = reinterpret_cast<float*>(wsb);
+    a.ws_ml = reinterpret_cast<float*>(wsb + mq_round(size_t(splits) * 2 * kMqCols * head_dim * sizeof(float)));
+    a.ws_seq = reinterpret_cast<int*>(wsb + mq_round(size_t(splits) * 2 * kMqCols * head_dim * sizeof(float)) +
+                                      mq_round(size_t(splits) * 2 * kMqCols * 2 * sizeof(float)));
+    a.B = B;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.num_blocks = num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_q_tokens = num_q_tokens;
+    a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * std::max(1, max_blocks_per_seq))));
+    a.qk_scale_log2 = scale * k_scale * kLog2e;
+    a.v_scale = v_scale;
+    const unsigned wgs = unsigned((int64_t(a.splits) + kMqWaves - 1) / kMqWaves);
+    void *ev0 = nullptr, *ev1 = nullptr;
+    if (pkv::take_launch_events(&ev0, &ev1)) {
+      void* kargs[] = {&a};
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kp.split), dim3(wgs), dim3(kMqWaves * 64),
+                                        kargs, 0, hs, static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
+      if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
+    } else {
+      hipLaunchKernelGGL(kp.split, dim3(wgs), dim3(kMqWaves * 64), 0, hs, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
+    static_assert(kMqCols % (kMqMergeCols * kMqMergeWaves) == 0, "merge tiling");
+    hipLaunchKernelGGL(kp.merge, dim3(unsigned(kMqCols / (kMqMergeCols * kMqMergeWaves)), unsigned(Hkv), unsigned(B)),
+                       dim3(64 * kMqMergeWaves), 0, hs, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
+    return PKV_OK;
+  }
   const int64_t tbl_bytes = (int64_t(max_blocks_per_seq) + kTblPad) * 4;
   if (tbl_bytes > kMaxTableBytes)
     return pkv::fail(PKV_UNSUPPORTED, "%s: max_blocks_per_seq=%d exceeds %d", fn, max_blocks_per_seq,
@@ -481,7 +1002,6 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return pkv::fail(PKV_UNSUPPORTED, "%s: too many workgroups", fn);
   const dim3 grid{unsigned(wgs)}, block{unsigned(kThreads)};
   const size_t lds = size_t(tbl_bytes);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   void *ev0 = nullptr, *ev1 = nullptr;
   if (pkv::take_launch_events(&ev0, &ev1)) {
     // The dispatch itself records the events, so they time the kernel alone.

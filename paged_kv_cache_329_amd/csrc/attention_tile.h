@@ -110,6 +110,30 @@ __device__ __forceinline__ float wave_sum_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum over the wave, returned as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Equal shares of a work list of W positions cut into n: share w starts at w * W / n.
+__device__ __forceinline__ int64_t share_begin(int64_t w, int64_t W, int64_t n) { return w * W / n; }
+
+// Index of the share holding work position x.
+__device__ __forceinline__ int64_t share_of(int64_t x, int64_t W, int64_t n) {
+  return ((x + 1) * n - 1) / W;
+}
+
 template <int KV, int D>
 struct Frag {
   using T = KvTraits<KV>;

@@ -404,8 +404,9 @@ def _multi_query_bench(args, wl):
     qb = 4 if wl.q_dtype == "f32" else 2
     roof["q_out_bytes"] = 2 * case.num_q_tokens * Hq * D * qb
     try:
+        kname = "paged_attention_mq_split" if ws_bytes else "paged_attention_prefill"
         tpath = args.traffic_json or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                                                  f"paged_attention_prefill__{wl.name}__hbm_traffic.json")
+                                                  f"{kname}__{wl.name}__hbm_traffic.json")
         with open(tpath) as f:
             tj = json.load(f)
         if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha(

@@ -300,6 +300,18 @@ __device__ __forceinline__ void issue_append_store(const DecodeArgs& a, const Ap
   }
 }
 
+// Partial (accumulator, max, sum) of head h of piece `piece`; lane (h, row) holds dims
+// 16*n + 4*row .. +3 of each 16-dim tile n.
+template <int D>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece, int h, int row, const f32x4* acc,
+                                              float2 ml) {
+  float* wacc = a.ws_acc + (piece * a.G + h) * D;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n)
+    *reinterpret_cast<float4*>(wacc + 16 * n + 4 * row) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
+  if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = ml;
+}
+
 template <int KV, int D, int BS, int NSUB, bool APPEND>
 __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
@@ -310,7 +322,14 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   constexpr int64_t REGION = int64_t(BS) * D * T::EB;
 
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * kWavesPerWG + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = blockIdx.x * kWavesPerWG + wv;
+  // The partial of a share's first segment waits in LDS until the share's loads are done: a
+  // wave's loads and stores complete in issue order, so a store in the middle of the share
+  // would hold up every load behind it.  Each lane reads back only what it wrote.
+  __shared__ f32x4 s_hold[kWavesPerWG][F::NT][64];
+  __shared__ float2 s_hold_ml[kWavesPerWG][64];
+  bool holding = false;
   const int W = total_work(a, BS, lane);
   if (wave == 0) {
     // Work offset of every sequence, for the merge pass.
@@ -505,15 +524,13 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
       }
     } else {
       const int slot = pos == c_begin ? 0 : 1;
-      const int64_t piece = int64_t(wave) * 2 + slot;
-      if (head_ok) {
-        float* wacc = a.ws_acc + (piece * a.G + h) * D;
+      if (slot == 0) {
 #pragma unroll
-        for (int n = 0; n < F::NT; ++n)
-          *reinterpret_cast<float4*>(wacc + 16 * n + 4 * row) =
-              make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-        if (row == 0)
-          *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = make_float2(m_run, l_tot);
+        for (int n = 0; n < F::NT; ++n) s_hold[wv][n][lane] = acc[n];
+        s_hold_ml[wv][lane] = make_float2(m_run, l_tot);
+        holding = true;
+      } else if (head_ok) {
+        store_partial<D>(a, int64_t(wave) * 2 + 1, h, row, acc, make_float2(m_run, l_tot));
       }
     }
 
@@ -531,6 +548,12 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     }
   }
 
+  if (holding && head_ok) {
+    f32x4 acc[F::NT];
+#pragma unroll
+    for (int n = 0; n < F::NT; ++n) acc[n] = s_hold[wv][n][lane];
+    store_partial<D>(a, int64_t(wave) * 2, h, row, acc, s_hold_ml[wv][lane]);
+  }
   if constexpr (APPEND) {
     if (held.sub >= 0) issue_append_store<KV, D>(a, held, lane);
   }

@@ -462,6 +462,18 @@ __device__ void mq_locate(const MqArgs& a, int bs, int lane, int x, int& s_out, 
   off_out = base;
 }
 
+// Partial (accumulator, max, sum) of column c in piece `piece`; lane (column c % 16, row)
+// holds dims 16*nn + 4*row .. +3 of each 16-dim tile nn.
+template <int D>
+__device__ __forceinline__ void store_mq_partial(const MqArgs& a, int64_t piece, int c, int row,
+                                                 const f32x4* acc, float2 ml) {
+  float* wacc = a.ws_acc + (piece * kMqCols + c) * D;
+#pragma unroll
+  for (int nn = 0; nn < D / 16; ++nn)
+    *reinterpret_cast<float4*>(wacc + 16 * nn + 4 * row) = make_float4(acc[nn][0], acc[nn][1], acc[nn][2], acc[nn][3]);
+  if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = ml;
+}
+
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs a) {
   using F = Frag<KV, D>;
@@ -473,7 +485,27 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
   constexpr int CT = kMqCols / 16;
 
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * kMqWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = blockIdx.x * kMqWaves + wv;
+  // The partial of a share's first segment waits in LDS until the share's loads are done: a
+  // wave's loads and stores complete in issue order, so a store in the middle of the share
+  // would hold up every load behind it.  Each lane reads back only what it wrote.
+  __shared__ f32x4 s_hold[kMqWaves][CT * F::NT][64];
+  __shared__ float2 s_hold_ml[kMqWaves][CT][64];
+  int hold_cols = 0;   // valid columns of the partial held in LDS (0: none)
+  auto flush_hold = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + (lane & 15);
+      if (c >= hold_cols) continue;
+      f32x4 h[F::NT];
+#pragma unroll
+      for (int nn = 0; nn < F::NT; ++nn) h[nn] = s_hold[wv][ct * F::NT + nn][lane];
+      store_mq_partial<D>(a, int64_t(wave) * 2, c, lane >> 4, h, s_hold_ml[wv][ct][lane]);
+    }
+    hold_cols = 0;
+  };
+
   const int W = mq_total(a, BS, lane);
   if (wave == 0) {
     int base = 0;
@@ -626,15 +658,15 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
                            pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
           }
         }
-      } else {
-        float* wacc = a.ws_acc + (piece * kMqCols + c) * D;
+      } else if (slot == 0) {
 #pragma unroll
-        for (int nn = 0; nn < F::NT; ++nn)
-          *reinterpret_cast<float4*>(wacc + 16 * nn + 4 * row) =
-              make_float4(acc[ct][nn][0], acc[ct][nn][1], acc[ct][nn][2], acc[ct][nn][3]);
-        if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = make_float2(m_run[ct], l_tot);
+        for (int nn = 0; nn < F::NT; ++nn) s_hold[wv][ct * F::NT + nn][lane] = acc[ct][nn];
+        s_hold_ml[wv][ct][lane] = make_float2(m_run[ct], l_tot);
+      } else {
+        store_mq_partial<D>(a, piece, c, row, acc[ct], make_float2(m_run[ct], l_tot));
       }
     }
+    if (slot == 0 && !full) hold_cols = n * a.G;
 
     pos = seg_end;
     if (pos >= c_end) break;
@@ -650,6 +682,8 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       nb = (L + BS - 1) / BS;
     }
   }
+
+  if (hold_cols > 0) flush_hold();
 }
 
 // One wave per (four columns, kv head, sequence), four waves per workgroup: merges the

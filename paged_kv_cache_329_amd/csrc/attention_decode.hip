@@ -559,31 +559,54 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
   }
 }
 
-// One wave per (query head, sequence): merges the partials of a (sequence, kv head) unit
-// that spans several shares, or writes zeros for an empty sequence.  The unit's place in the
-// work list comes from the offsets the split pass left in the workspace.  Partials are
-// folded eight at a time with the running-softmax rule (load a batch's (max, sum) and
-// accumulators together, raise the running max, rescale, add), and the next batch's loads
-// are issued before the current batch is folded, so a unit with many partials (long
-// contexts) keeps two batches in flight.
+// One wave per (four query heads, sequence): merges the partials of a (sequence, kv head)
+// unit that spans several shares, or writes zeros for an empty sequence.  Lanes 16*i ..
+// 16*i+15 take head 4*hq + i of the group, each with D/16 consecutive dims, so a partial
+// costs a lane two 16-byte loads and its head's (max, sum).  The unit's place in the work
+// list comes from the offsets the split pass left in the workspace.  Partials are folded
+// eight at a time with the running-softmax rule (load a batch's (max, sum) and accumulators
+// together, raise the running max, rescale, add), and the next batch's loads are issued
+// before the current batch is folded, so a unit with many partials (long contexts) keeps
+// two batches in flight.
+constexpr int kMergeHeads = 4;   // query heads per merge wave
+
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;   // output dims per lane
+  constexpr int EPL = D / 16;   // output dims per lane
   constexpr int BATCH = 8;      // partials per batch
   const int lane = threadIdx.x;
-  const int g = blockIdx.x / a.G, h = blockIdx.x % a.G, s = blockIdx.y;
+  const int hq_per_g = (a.G + kMergeHeads - 1) / kMergeHeads;
+  const int g = blockIdx.x / hq_per_g, s = blockIdx.y;
+  const int h_raw = (blockIdx.x % hq_per_g) * kMergeHeads + (lane >> 4);
+  const bool head_ok = h_raw < a.G;
+  const int h = head_ok ? h_raw : a.G - 1;   // idle lanes read a valid row and write nothing
+  const int d0 = (lane & 15) * EPL;
   const int before = a.ws_seq[s];
   const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
   const int W = a.ws_seq[a.B];
-  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D;
-  if (nb == 0) {
+  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D + d0;
+  auto write = [&](const float* v, float inv) {
+    if (!head_ok) return;
+    if constexpr (KV == PKV_F32) {
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      if constexpr (KV == PKV_F32)
-        static_cast<float*>(a.out)[orow + lane + 64 * r] = 0.f;
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + e) =
+            make_float4(v[e] * inv, v[e + 1] * inv, v[e + 2] * inv, v[e + 3] * inv);
+    } else {
+      uint32_t w[EPL / 2];
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) w[e] = pack_bf16x2(v[2 * e] * inv, v[2 * e + 1] * inv);
+      if constexpr (EPL == 8)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = make_uint4(w[0], w[1], w[2], w[3]);
       else
-        static_cast<uint16_t*>(a.out)[orow + lane + 64 * r] = 0;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow) = make_uint2(w[0], w[1]);
     }
+  };
+  float num[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+  if (nb == 0) {
+    write(num, 0.f);
     return;
   }
   const int nshare = std::min(a.splits, W);
@@ -595,21 +618,20 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
   // begins exactly where the share does; in every later share it is the first segment.
   const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
 
-  auto load = [&](int j0, float2* ml, float (*x)[PER]) {
+  auto load = [&](int j0, float2* ml, float4 (*x)[EPL / 4]) {
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
       const int j = std::min(j0 + t, np - 1);
       const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
-      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + (pc * a.G + h) * 2);
-      const float* pacc = a.ws_acc + (pc * a.G + h) * D + lane;
+      const int64_t r = pc * a.G + h;
+      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
+      const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
 #pragma unroll
-      for (int r = 0; r < PER; ++r) x[t][r] = pacc[64 * r];
+      for (int i = 0; i < EPL / 4; ++i) x[t][i] = px[i];
     }
   };
-  float M = -INFINITY, den = 0.f, num[PER];
-#pragma unroll
-  for (int r = 0; r < PER; ++r) num[r] = 0.f;
-  auto fold = [&](int j0, const float2* ml, const float (*x)[PER]) {
+  float M = -INFINITY, den = 0.f;
+  auto fold = [&](int j0, const float2* ml, const float4 (*x)[EPL / 4]) {
     float mb = M;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t)
@@ -617,18 +639,23 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
     const float alpha = __builtin_amdgcn_exp2f(M - mb);
     den *= alpha;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) num[r] *= alpha;
+    for (int e = 0; e < EPL; ++e) num[e] *= alpha;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
       const float c = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
       den += ml[t].y * c;
 #pragma unroll
-      for (int r = 0; r < PER; ++r) num[r] += x[t][r] * c;
+      for (int i = 0; i < EPL / 4; ++i) {
+        num[4 * i + 0] += x[t][i].x * c;
+        num[4 * i + 1] += x[t][i].y * c;
+        num[4 * i + 2] += x[t][i].z * c;
+        num[4 * i + 3] += x[t][i].w * c;
+      }
     }
     M = mb;
   };
   float2 mlA[BATCH], mlB[BATCH];
-  float xA[BATCH][PER], xB[BATCH][PER];
+  float4 xA[BATCH][EPL / 4], xB[BATCH][EPL / 4];
   load(0, mlA, xA);
   for (int j0 = 0; j0 < np; j0 += 2 * BATCH) {
     if (j0 + BATCH < np) load(j0 + BATCH, mlB, xB);
@@ -637,15 +664,7 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
     if (j0 + 2 * BATCH < np) load(j0 + 2 * BATCH, mlA, xA);
     fold(j0 + BATCH, mlB, xB);
   }
-  const float inv = a.v_scale / den;
-#pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int64_t o = orow + lane + 64 * r;
-    if constexpr (KV == PKV_F32)
-      static_cast<float*>(a.out)[o] = num[r] * inv;
-    else
-      static_cast<uint16_t*>(a.out)[o] = uint16_t(bf16_rne(num[r] * inv));
-  }
+  write(num, a.v_scale / den);
 }
 
 // ---- host side --------------------------------------------------------------------------
@@ -853,7 +872,8 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));
   }
   if (phase != kSplitOnly) {
-    hipLaunchKernelGGL(kp.merge, dim3(unsigned(Hkv * G), unsigned(B)), dim3(64), 0, hs, a);
+    const unsigned merge_x = unsigned(Hkv * ((G + kMergeHeads - 1) / kMergeHeads));
+    hipLaunchKernelGGL(kp.merge, dim3(merge_x, unsigned(B)), dim3(64), 0, hs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
   }

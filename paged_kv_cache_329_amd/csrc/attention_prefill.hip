@@ -688,43 +688,53 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
 
 // One wave per (four columns, kv head, sequence), four waves per workgroup: merges the
 // partials of a split unit's columns, or writes zeros for the queries of a sequence without
-// keys.  The four columns' partials of a batch of pieces are all requested before any is
-// folded.
+// keys.  Lanes 16*i .. 16*i+15 take column c0 + i, each with D/16 consecutive dims, so every
+// piece costs a lane two 16-byte loads and its column's (max, sum); a batch of pieces is
+// requested before any is folded.
 constexpr int kMqMergeCols = 4;
 constexpr int kMqMergeWaves = 4;
 
 template <int KV, int D, int BS>
 __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_kernel(MqArgs a) {
-  constexpr int PER = D / 64;
+  constexpr int EPL = D / 16;  // dims per lane
   constexpr int BATCH = 8;     // pieces per round of loads: a unit rarely spans more shares
-  constexpr int C4 = kMqMergeCols;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c0 = (blockIdx.x * kMqMergeWaves + wave) * C4, g = blockIdx.y, s = blockIdx.z;
+  const int c0 = (blockIdx.x * kMqMergeWaves + wave) * kMqMergeCols, g = blockIdx.y, s = blockIdx.z;
   int q0, n;
   mq_queries(a, s, q0, n);
-  const int ncols = std::min(C4, n * a.G - c0);     // valid columns of this wave
+  const int ncols = std::min(kMqMergeCols, n * a.G - c0);   // valid columns of this wave
   if (ncols <= 0) return;
+  const bool col_ok = (lane >> 4) < ncols;
+  const int c = c0 + std::min(lane >> 4, ncols - 1);         // this lane's column
+  const int d0 = (lane & 15) * EPL;
   const int before = a.ws_seq[s];
   const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
   const int W = a.ws_seq[a.B];
-  auto write = [&](int c, const float* v, float inv) {
+  auto write = [&](const float* v, float inv) {
+    if (!col_ok) return;
     const int qi = c / a.G, hh = c % a.G;
-    const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+    const int64_t o = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D + d0;
+    if constexpr (KV == PKV_F32) {
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int64_t o = orow + lane + 64 * r;
-      if constexpr (KV == PKV_F32) static_cast<float*>(a.out)[o] = v[r] * inv;
-      else static_cast<uint16_t*>(a.out)[o] = uint16_t(pack_bf16x2(v[r] * inv, 0.f) & 0xFFFFu);
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + o + e) =
+            make_float4(v[e] * inv, v[e + 1] * inv, v[e + 2] * inv, v[e + 3] * inv);
+    } else {
+      uint32_t w[EPL / 2];
+#pragma unroll
+      for (int e = 0; e < EPL / 2; ++e) w[e] = pack_bf16x2(v[2 * e] * inv, v[2 * e + 1] * inv);
+      if constexpr (EPL == 8)
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + o) = make_uint4(w[0], w[1], w[2], w[3]);
+      else
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = make_uint2(w[0], w[1]);
     }
   };
-  float num[C4][PER];
+  float num[EPL];
 #pragma unroll
-  for (int cc = 0; cc < C4; ++cc)
-#pragma unroll
-    for (int r = 0; r < PER; ++r) num[cc][r] = 0.f;
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
   if (nb == 0) {
-    for (int cc = 0; cc < ncols; ++cc) write(c0 + cc, num[cc], 0.f);
+    write(num, 0.f);
     return;
   }
   const int nshare = std::min(a.splits, W);
@@ -733,50 +743,44 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
   if (wf == wl) return;
   const int np = int(wl - wf + 1);
   const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
-  float M[C4], den[C4];
-#pragma unroll
-  for (int cc = 0; cc < C4; ++cc) {
-    M[cc] = -INFINITY;
-    den[cc] = 0.f;
-  }
+  float M = -INFINITY, den = 0.f;
   for (int j0 = 0; j0 < np; j0 += BATCH) {
-    float2 ml[BATCH][C4];
-    float x[BATCH][C4][PER];
+    float2 ml[BATCH];
+    float4 x[BATCH][EPL / 4];
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
       const int j = std::min(j0 + t, np - 1);
       const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
+      const int64_t r = pc * kMqCols + c;
+      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
+      const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
 #pragma unroll
-      for (int cc = 0; cc < C4; ++cc) {
-        const int c = c0 + std::min(cc, ncols - 1);
-        ml[t][cc] = *reinterpret_cast<const float2*>(a.ws_ml + (pc * kMqCols + c) * 2);
-        const float* pacc = a.ws_acc + (pc * kMqCols + c) * D + lane;
+      for (int i = 0; i < EPL / 4; ++i) x[t][i] = px[i];
+    }
+    float mb = M;
 #pragma unroll
-        for (int r = 0; r < PER; ++r) x[t][cc][r] = pacc[64 * r];
+    for (int t = 0; t < BATCH; ++t)
+      if (j0 + t < np) mb = fmaxf(mb, ml[t].x);
+    if (mb == -INFINITY) continue;                   // nothing attended yet
+    const float alpha = __builtin_amdgcn_exp2f(M - mb);
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      const float w = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
+      den += ml[t].y * w;
+#pragma unroll
+      for (int i = 0; i < EPL / 4; ++i) {
+        num[4 * i + 0] += x[t][i].x * w;
+        num[4 * i + 1] += x[t][i].y * w;
+        num[4 * i + 2] += x[t][i].z * w;
+        num[4 * i + 3] += x[t][i].w * w;
       }
     }
-#pragma unroll
-    for (int cc = 0; cc < C4; ++cc) {
-      float mb = M[cc];
-#pragma unroll
-      for (int t = 0; t < BATCH; ++t)
-        if (j0 + t < np) mb = fmaxf(mb, ml[t][cc].x);
-      if (mb == -INFINITY) continue;                   // nothing attended yet
-      const float alpha = __builtin_amdgcn_exp2f(M[cc] - mb);
-      den[cc] *= alpha;
-#pragma unroll
-      for (int r = 0; r < PER; ++r) num[cc][r] *= alpha;
-#pragma unroll
-      for (int t = 0; t < BATCH; ++t) {
-        const float w = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t][cc].x - mb) : 0.f;
-        den[cc] += ml[t][cc].y * w;
-#pragma unroll
-        for (int r = 0; r < PER; ++r) num[cc][r] += x[t][cc][r] * w;
-      }
-      M[cc] = mb;
-    }
+    M = mb;
   }
-  for (int cc = 0; cc < ncols; ++cc) write(c0 + cc, num[cc], den[cc] > 0.f ? a.v_scale / den[cc] : 0.f);
+  write(num, den > 0.f ? a.v_scale / den : 0.f);
 }
 
 using MqFn = void (*)(MqArgs);

@@ -19,11 +19,15 @@ SMALL = {
     "llama3_8b_bf16": WORKLOADS["llama3_8b_bf16"].scaled(batch=6, length_dist=("uniform", 1, 700)),
     "long_ctx_splitk_bf16": WORKLOADS["long_ctx_splitk_bf16"].scaled(batch=2, length_dist=("uniform", 2000, 5000)),
     "fp8_kv": WORKLOADS["fp8_kv"].scaled(batch=4, length_dist=("uniform", 1, 1500)),
-    # Other supported shapes: D 64 / bs 32 / G 2, G 16, f32 with D 128 and bs 32, fp8 with D 64.
+    # Other supported shapes: D 64 / bs 32 / G 2, G 16, f32 with D 128 and bs 32, fp8 with D 64,
+    # G 6 and G 3.
     "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 5, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 300)),
     "bf16_g16": Workload("bf16_g16", 3, 32, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 400)),
     "f32_d128_bs32_g4": Workload("f32_d128_bs32_g4", 3, 16, 4, 128, 32, "f32", "f32", ("uniform", 1, 300)),
     "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 500)),
+    # Groups that are not a multiple of the merge's four heads per wave: idle lanes.
+    "bf16_g6": Workload("bf16_g6", 4, 12, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 900)),
+    "f32_d64_g3": Workload("f32_d64_g3", 3, 9, 3, 64, 16, "f32", "f32", ("uniform", 1, 400)),
 }
 
 

@@ -30,6 +30,7 @@ CASES = {
     "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 5, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 300)),
     "f32_d128_bs32_g4": Workload("f32_d128_bs32_g4", 3, 16, 4, 128, 32, "f32", "f32", ("uniform", 1, 300)),
     "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 500)),
+    "bf16_g6": Workload("bf16_g6", 4, 12, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 900)),
 }
 
 

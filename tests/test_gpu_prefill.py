@@ -155,6 +155,9 @@ FEW = {
                             query_dist=("fixed", 2)),
     "bf16_g1_n32": Workload("bf16_g1_n32", 3, 4, 4, 128, 16, "bf16", "bf16", ("uniform", 1, 400),
                             query_dist=("fixed", 32)),
+    # 15 columns: the merge wave of columns 12..15 has one idle column of lanes.
+    "bf16_g3_n5": Workload("bf16_g3_n5", 4, 6, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 600),
+                           query_dist=("fixed", 5)),
 }
 
 

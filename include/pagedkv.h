@@ -110,10 +110,12 @@ const char* pkv_last_error(void);
  *   context_lens    int32 [num_seqs], 0 <= context_lens[s] <= max_blocks_per_seq * bs
  *                   (larger values are clamped to that bound).
  *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
- *   num_splits      number of equal shares the total (sequence, kv head, block) work is
- *                   cut into, one per wavefront; 0 = pkv_paged_attention_default_splits.
- *                   Results depend only on the split count, not on the physical block
- *                   numbering.
+ *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits.
+ *                   The kv heads are grouped c = 4, 2 or 1 at a time (the largest that
+ *                   divides Hkv and is at most num_splits), and the (sequence, head group,
+ *                   block) list is cut into num_splits / c equal shares, each walked by c
+ *                   waves side by side, one kv head each.  Results depend only on the
+ *                   split count and Hkv, not on the physical block numbering.
  *   workspace       device scratch of at least pkv_paged_attention_workspace_size()
  *                   bytes, owned by the caller, no initial contents required; holds the
  *                   partial (max, sum, accumulator) of every sequence head whose work

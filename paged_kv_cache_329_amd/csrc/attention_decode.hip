@@ -6,13 +6,16 @@
 // running softmax, which yields exactly attention over a contiguous K/V layout.
 //
 // How it maps onto CDNA4
-//  * Work: the total work is the list of (sequence, kv head, block) triples in
-//    sequence-major order; it is cut into `splits` equal shares, one per wavefront, so
-//    a wave's cost does not depend on how skewed the context lengths are.  A share may
-//    end inside a (sequence, kv head) unit; such a unit leaves one partial
-//    (max, sum, accumulator) per share it touches, and the merge pass combines them with
-//    the same rescaling the running softmax uses.  Units that fit in one share are
-//    finished in the split pass.
+//  * Work: the total work is the list of (sequence, kv-head group, block) triples in
+//    sequence-major order, where a group is `coop` adjacent kv heads (4 when Hkv allows,
+//    else 2 or 1); it is cut into splits / coop equal shares, one per group of `coop`
+//    consecutive waves of a workgroup, so a wave's cost does not depend on how skewed the
+//    context lengths are.  The waves of a group walk the same blocks side by side, each on
+//    its own kv head, so together they stream the adjacent head regions of every block
+//    (16 KiB of K, then of V, for bf16 D 128).  A share may end inside a (sequence, group)
+//    unit; such a unit leaves one partial (max, sum, accumulator) per share and kv head,
+//    and the merge pass combines them with the same rescaling the running softmax uses.
+//    Units that fit in one share are finished in the split pass.
 //  * Operands: a 16-token sub-tile of a (block, kv head) is one contiguous region; wave
 //    load i, lane l reads the 16-byte chunk 64*i + l.  The pool layout makes that chunk
 //    exactly lane l's operand of the gfx950 matrix instructions:
@@ -64,6 +67,10 @@ struct DecodeArgs {
   float* ws_ml;   // [splits*2][G][2]  (max in log2 units, sum)
   int* ws_seq;    // [B+1]: Hkv * blocks of the sequences before s; [B] = total work W
   int B, Hkv, G, num_blocks, max_blocks, splits;
+  // Waves that walk one share together, each on its own kv head of the same blocks: the
+  // work list is (sequence, group of `coop` kv heads, block).  A power of two that divides
+  // both Hkv and kWavesPerWG, so a group's waves are consecutive waves of one workgroup.
+  int coop;
   float qk_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
   // Decode step with append: each sequence's token at position L-1 is taken from
@@ -92,22 +99,27 @@ __device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int bs) {
   return L > cap ? int(cap) : L;
 }
 
-// Total work W = Hkv * sum_s blocks(s) (wave-uniform; the host checks it fits in int).
+// Units (groups of `coop` kv heads) per sequence.
+__device__ __forceinline__ int head_groups(const DecodeArgs& a) { return a.Hkv / a.coop; }
+
+// Total work W = head_groups * sum_s blocks(s) (wave-uniform; the host checks it fits in int).
 __device__ int total_work(const DecodeArgs& a, int bs, int lane) {
   int acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
     acc += s < a.B ? seq_blocks(a, s, bs) : 0;
   }
-  return wave_sum(acc) * a.Hkv;
+  return wave_sum(acc) * head_groups(a);
 }
 
-// Sequence whose units contain work position x (0 <= x < W), and Hkv * blocks before it.
+// Sequence whose units contain work position x (0 <= x < W), and head_groups * blocks
+// before it.
 __device__ void locate(const DecodeArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
   int base = 0;
+  const int hg = head_groups(a);
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int s = b0 + lane;
-    const int w = s < a.B ? seq_blocks(a, s, bs) * a.Hkv : 0;
+    const int w = s < a.B ? seq_blocks(a, s, bs) * hg : 0;
     const int incl = wave_incl_scan(w, lane);
     const int lo = base + (incl - w), hi = base + incl;
     const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
@@ -313,7 +325,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
 }
 
 template <int KV, int D, int BS, int NSUB, bool APPEND>
-__global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;                  // cached elements per 16-byte chunk
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int sq = b0 + lane;
-      const int w = sq < a.B ? seq_blocks(a, sq, BS) * a.Hkv : 0;
+      const int w = sq < a.B ? seq_blocks(a, sq, BS) * head_groups(a) : 0;
       const int incl = wave_incl_scan(w, lane);
       if (sq < a.B) a.ws_seq[sq] = base + incl - w;
       base += __builtin_amdgcn_readlane(incl, 63);
@@ -344,18 +356,24 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     if (lane == 0) a.ws_seq[a.B] = base;
   }
   if (W == 0) return;
-  const int nshare = std::min(a.splits, W);
-  if (wave >= nshare) return;
-  const int c_begin = int(share_begin(wave, W, nshare));
-  const int c_end = int(share_begin(wave + 1, W, nshare));
+  // Share of this wave's group of `coop` consecutive waves, walked side by side on kv heads
+  // coop*hg + sub, so that together they read the adjacent head regions of each block.
+  // Pieces stay numbered per wave (2 * wave + slot).
+  const int share = wave / a.coop;
+  const int sub = wave % a.coop;
+  const int nshare = std::min(a.splits / a.coop, W);
+  if (share >= nshare) return;
+  const int c_begin = int(share_begin(share, W, nshare));
+  const int c_end = int(share_begin(share + 1, W, nshare));
 
   int s, seq_off;
   locate(a, BS, lane, c_begin, s, seq_off);
   if (s >= a.B) return;
   int L = seq_len(a, s, BS);
   int nb = (L + BS - 1) / BS;
-  int g = (c_begin - seq_off) / nb;
-  int unit_off = seq_off + g * nb;
+  int hg = (c_begin - seq_off) / nb;
+  int g = hg * a.coop + sub;
+  int unit_off = seq_off + hg * nb;
   int pos = c_begin;
 
   const int h = lane & 15;       // head (within the group) of this lane's QK/PV column
@@ -538,14 +556,15 @@ __global__ __launch_bounds__(256, 2) void paged_attention_split_kernel(DecodeArg
     if (pos >= c_end) break;
     // Next unit: next kv head of this sequence, else the next non-empty sequence.
     unit_off = unit_end;
-    if (++g == a.Hkv) {
-      g = 0;
+    if (++hg == head_groups(a)) {
+      hg = 0;
       do {
         done = ++s >= a.B;
       } while (!done && (L = seq_len(a, s, BS)) == 0);
       if (done) break;
       nb = (L + BS - 1) / BS;
     }
+    g = hg * a.coop + sub;
   }
 
   if (holding && head_ok) {
@@ -582,7 +601,7 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
   const int h = head_ok ? h_raw : a.G - 1;   // idle lanes read a valid row and write nothing
   const int d0 = (lane & 15) * EPL;
   const int before = a.ws_seq[s];
-  const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
+  const int nb = (a.ws_seq[s + 1] - before) / (a.Hkv / a.coop);
   const int W = a.ws_seq[a.B];
   const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D + d0;
   auto write = [&](const float* v, float inv) {
@@ -609,20 +628,22 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
     write(num, 0.f);
     return;
   }
-  const int nshare = std::min(a.splits, W);
-  const int off = before + g * nb;
+  const int nshare = std::min(a.splits / a.coop, W);
+  const int C = a.coop, sub = g % C;
+  const int off = before + (g / C) * nb;
   const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
   if (wf == wl) return;
   const int np = int(wl - wf + 1);
-  // The unit's piece in share wf is that share's first segment (slot 0) only if the unit
-  // begins exactly where the share does; in every later share it is the first segment.
-  const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  // Share w's pieces of kv head g are those of its wave C*w + g%C.  The unit's piece in
+  // share wf is that share's first segment (slot 0) only if the unit begins exactly where
+  // the share does; in every later share it is the first segment.
+  const int64_t piece0 = (wf * C + sub) * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
 
   auto load = [&](int j0, float2* ml, float4 (*x)[EPL / 4]) {
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
       const int j = std::min(j0 + t, np - 1);
-      const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
+      const int64_t pc = j == 0 ? piece0 : ((wf + j) * C + sub) * 2;
       const int64_t r = pc * a.G + h;
       ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
       const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
@@ -753,18 +774,18 @@ pkv_status check_shape(const char* fn, int B, int Hq, int Hkv, int D, int bs, pk
   return PKV_OK;
 }
 
-// Default split count of a kernel variant: one share per wave of `target` workgroups per CU,
+// Default split count of a kernel variant: one share per wave of `target` waves per CU,
 // capped by what the plain and the appending split kernels can keep resident (the lower of
 // the two, so both entry points, and the merge that recomputes the shares, agree).  Measured
-// on MI355X: f32 / bf16 caches stream best with 2 workgroups (2 waves per SIMD) per CU,
-// fp8 caches, with more arithmetic per byte, with 4.
+// on MI355X: f32 / bf16 caches stream best with 8 waves (2 per SIMD) per CU, fp8 caches,
+// with more arithmetic per byte, with 16 where registers allow it.
 pkv_status default_splits(const KernelPair& kp, pkv_dtype kv, int* splits) {
   int a = 0, b = 0, cus = 0;
   pkv_status st = resident_wgs(kp.split, &a, &cus);
   if (st != PKV_OK) return st;
   if ((st = resident_wgs(kp.split_append, &b, &cus)) != PKV_OK) return st;
-  const int target = kv == PKV_FP8_E4M3FN ? 4 : 2;
-  *splits = cus * std::min(target, std::min(a, b)) * kWavesPerWG;
+  const int target_wgs = (kv == PKV_FP8_E4M3FN ? 16 : 8) / kWavesPerWG;
+  *splits = cus * std::max(1, std::min(target_wgs, std::min(a, b))) * kWavesPerWG;
   return PKV_OK;
 }
 
@@ -845,6 +866,8 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   // More shares than (sequence, kv head, block) triples would only launch idle waves; the
   // table width bounds the triples without reading the device-side lengths.
   a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * max_blocks)));
+  a.coop = 1;
+  while (a.coop < kWavesPerWG && Hkv % (2 * a.coop) == 0 && a.splits >= 2 * a.coop) a.coop *= 2;
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
   a.k_new = k_new;

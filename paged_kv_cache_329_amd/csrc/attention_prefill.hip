@@ -226,18 +226,26 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   };
 
   // One step's work for this wave; MASK: apply the causal mask and zero V of slots at or
-  // past L (the steps on the diagonal and the last ones).
+  // past L (the steps on the diagonal and the last ones).  The running softmax is updated
+  // once per UPD sub-tiles (64 tokens): every QK product of the update is issued first, then
+  // one branch decides on the (rare) rescale for all column tiles, and the exponentials and
+  // PV products of the update's sub-tile pairs follow in one straight run, so the compiler
+  // can overlap one pair's exponentials with the previous pair's matrix instructions.
   const float sl2 = a.qk_scale_log2;
+  constexpr int UPD = SUBS < 4 ? SUBS : 4;
+  static_assert(SUBS % UPD == 0 && UPD % 2 == 0, "softmax update tiling");
   auto compute = [&](const uint4* buf, int tok_step, auto mask_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr bool TAIL = MASK;
 #pragma unroll
-    for (int u0 = 0; u0 < SUBS; u0 += 2) {
-      // Two sub-tiles (32 tokens) per running-softmax update and per PV product.
-      float sc[CT][2][4];   // raw logits; -inf where masked
+    for (int ub = 0; ub < SUBS; ub += UPD) {
+      float sc[CT][UPD][4];   // raw logits; -inf where masked
+      // The two waves of a SIMD run in step (one barrier per step); a raised priority while a
+      // wave issues its matrix instructions lets the other wave's vector work fill the gaps.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const int u = u0 + uu;
+      for (int uu = 0; uu < UPD; ++uu) {
+        const int u = ub + uu;
         uint4 kf[F::NLOAD];
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i) kf[i] = buf[u * SUB_CHUNKS + 64 * i + lane];
@@ -249,96 +257,113 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
           for (int j = 0; j < 4; ++j) sc[ct][uu][j] = !MASK || t0 + j <= pos[ct] ? c[j] : -INFINITY;
         }
       }
-      float p[CT][2][4];
+      __builtin_amdgcn_s_setprio(0);
+      float cmax[CT];
+      bool grow = false;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        float cmax = -INFINITY;
+        float v = -INFINITY;
 #pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
+        for (int uu = 0; uu < UPD; ++uu)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) cmax = fmaxf(cmax, sc[ct][uu][j]);
-        cmax = wave_max_rows(cmax);
-        // The accumulators are rescaled only when some column's max grew by more than 2^8 in
-        // probability: until then p = 2^(s - m) stays below 256, which float32 sums and bf16
-        // operands hold without loss of relative precision.
-        if (__any((cmax - m_run[ct]) * sl2 > 8.f)) {
-          const float m_new = fmaxf(m_run[ct], cmax);
+          for (int j = 0; j < 4; ++j) v = fmaxf(v, sc[ct][uu][j]);
+        cmax[ct] = wave_max_rows(v);
+        grow |= (cmax[ct] - m_run[ct]) * sl2 > 8.f;
+      }
+      // The accumulators are rescaled only when some column's max grew by more than 2^8 in
+      // probability: until then p = 2^(s - m) stays below 256, which float32 sums and bf16
+      // operands hold without loss of relative precision.
+      if (__any(grow)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float m_new = fmaxf(m_run[ct], cmax[ct]);
           const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
           m_run[ct] = m_new;
           l_run[ct] *= alpha;
 #pragma unroll
           for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
         }
-        const float m_off = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][uu][j], sl2, m_off));   // 0 where masked
-            l_run[ct] += p[ct][uu][j];
-          }
       }
-      const uint4* vsrc = buf + SUBS * SUB_CHUNKS;
-      if constexpr (VPAIR) {
-        // vp[e][i]: the paired operand of output tile 2i+e.
-        uint4 vp[2][F::NLOAD];
+      float m_off[CT];
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+      for (int ct = 0; ct < CT; ++ct) m_off[ct] = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
 #pragma unroll
-          for (int i = 0; i < F::NLOAD; ++i) vp[e][i] = vsrc[(u0 + e) * SUB_CHUNKS + 64 * i + lane];
-        if constexpr (TAIL) {
-          // Element order within a paired operand: tokens 4r..4r+3 of the first sub-tile,
-          // then of the second.
-          const int t0 = tok_step + 16 * u0 + 4 * row;
-          uint32_t lo = 0, hi = 0;
+      for (int u0 = ub; u0 < ub + UPD; u0 += 2) {
+        const int pu = u0 - ub;
+        float p[CT][2][4];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            lo |= (t0 + j < L ? 0xFFFFu : 0u) << (16 * j);
-            hi |= (t0 + 2 + j < L ? 0xFFFFu : 0u) << (16 * j);
-          }
-          uint32_t lo1 = 0, hi1 = 0;
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            lo1 |= (t0 + 16 + j < L ? 0xFFFFu : 0u) << (16 * j);
-            hi1 |= (t0 + 18 + j < L ? 0xFFFFu : 0u) << (16 * j);
-          }
+          for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][pu + uu][j], sl2, m_off[ct]));   // 0 where masked
+              l_run[ct] += p[ct][uu][j];
+            }
+        const uint4* vsrc = buf + SUBS * SUB_CHUNKS;
+        if constexpr (VPAIR) {
+          // vp[e][i]: the paired operand of output tile 2i+e.
+          uint4 vp[2][F::NLOAD];
 #pragma unroll
           for (int e = 0; e < 2; ++e)
 #pragma unroll
-            for (int i = 0; i < F::NLOAD; ++i) {
-              vp[e][i].x &= lo; vp[e][i].y &= hi; vp[e][i].z &= lo1; vp[e][i].w &= hi1;
-            }
-        }
+            for (int i = 0; i < F::NLOAD; ++i) vp[e][i] = vsrc[(u0 + e) * SUB_CHUNKS + 64 * i + lane];
+          if constexpr (TAIL) {
+            // Element order within a paired operand: tokens 4r..4r+3 of the first sub-tile,
+            // then of the second.
+            const int t0 = tok_step + 16 * u0 + 4 * row;
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const uint4 bop = make_uint4(pack_bf16x2(p[ct][0][0], p[ct][0][1]), pack_bf16x2(p[ct][0][2], p[ct][0][3]),
-                                       pack_bf16x2(p[ct][1][0], p[ct][1][1]), pack_bf16x2(p[ct][1][2], p[ct][1][3]));
+            for (int j = 0; j < 2; ++j) {
+              lo |= (t0 + j < L ? 0xFFFFu : 0u) << (16 * j);
+              hi |= (t0 + 2 + j < L ? 0xFFFFu : 0u) << (16 * j);
+            }
+            uint32_t lo1 = 0, hi1 = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              lo1 |= (t0 + 16 + j < L ? 0xFFFFu : 0u) << (16 * j);
+              hi1 |= (t0 + 18 + j < L ? 0xFFFFu : 0u) << (16 * j);
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+              for (int i = 0; i < F::NLOAD; ++i) {
+                vp[e][i].x &= lo; vp[e][i].y &= hi; vp[e][i].z &= lo1; vp[e][i].w &= hi1;
+              }
+          }
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const uint4 bop = make_uint4(pack_bf16x2(p[ct][0][0], p[ct][0][1]), pack_bf16x2(p[ct][0][2], p[ct][0][3]),
+                                         pack_bf16x2(p[ct][1][0], p[ct][1][1]), pack_bf16x2(p[ct][1][2], p[ct][1][3]));
+#pragma unroll
+            for (int i = 0; i < F::NLOAD; ++i) {
+              acc[ct][2 * i + 0] = mfma_bf16_k32(vp[0][i], bop, acc[ct][2 * i + 0]);
+              acc[ct][2 * i + 1] = mfma_bf16_k32(vp[1][i], bop, acc[ct][2 * i + 1]);
+            }
+          }
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          uint4 vf0[F::NLOAD], vf1[F::NLOAD];
 #pragma unroll
           for (int i = 0; i < F::NLOAD; ++i) {
-            acc[ct][2 * i + 0] = mfma_bf16_k32(vp[0][i], bop, acc[ct][2 * i + 0]);
-            acc[ct][2 * i + 1] = mfma_bf16_k32(vp[1][i], bop, acc[ct][2 * i + 1]);
+            vf0[i] = vsrc[u0 * SUB_CHUNKS + 64 * i + lane];
+            vf1[i] = vsrc[(u0 + 1) * SUB_CHUNKS + 64 * i + lane];
           }
-        }
-      } else {
-        uint4 vf0[F::NLOAD], vf1[F::NLOAD];
+          if constexpr (TAIL) {
+            const int t0 = tok_step + 16 * u0 + 4 * row;
+            uint32_t vm0 = 0, vm1 = 0;
 #pragma unroll
-        for (int i = 0; i < F::NLOAD; ++i) {
-          vf0[i] = vsrc[u0 * SUB_CHUNKS + 64 * i + lane];
-          vf1[i] = vsrc[(u0 + 1) * SUB_CHUNKS + 64 * i + lane];
-        }
-        if constexpr (TAIL) {
-          const int t0 = tok_step + 16 * u0 + 4 * row;
-          uint32_t vm0 = 0, vm1 = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            vm0 |= (t0 + j < L ? 1u : 0u) << j;
-            vm1 |= (t0 + 16 + j < L ? 1u : 0u) << j;
+            for (int j = 0; j < 4; ++j) {
+              vm0 |= (t0 + j < L ? 1u : 0u) << j;
+              vm1 |= (t0 + 16 + j < L ? 1u : 0u) << j;
+            }
+            mask_v<KV, D>(vf0, vm0);
+            mask_v<KV, D>(vf1, vm1);
           }
-          mask_v<KV, D>(vf0, vm0);
-          mask_v<KV, D>(vf1, vm1);
-        }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) pv_pair<KV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
+          for (int ct = 0; ct < CT; ++ct) pv_pair<KV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
+        }
       }
     }
   };

@@ -437,6 +437,9 @@ struct MqArgs {
   float* ws_ml;   // [splits*2][kMqCols][2]  (max in log2 units, sum)
   int* ws_seq;    // [B+1]: Hkv * blocks of the sequences before s; [B] = total work W
   int B, Hkv, G, num_blocks, max_blocks, num_q_tokens, splits;
+  // Waves that walk one share together, each on its own kv head of the same blocks (a power
+  // of two dividing Hkv and kMqWaves): the work list is (sequence, head group, block).
+  int coop;
   float qk_scale_log2;
   float v_scale;
 };
@@ -463,7 +466,7 @@ __device__ int mq_total(const MqArgs& a, int bs, int lane) {
     const int s = base + lane;
     acc += s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs : 0;
   }
-  return wave_sum(acc) * a.Hkv;
+  return wave_sum(acc) * (a.Hkv / a.coop);
 }
 
 // Sequence whose units contain work position x, and Hkv * blocks before it.
@@ -471,7 +474,7 @@ __device__ void mq_locate(const MqArgs& a, int bs, int lane, int x, int& s_out, 
   int base = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int s = b0 + lane;
-    const int w = s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs * a.Hkv : 0;
+    const int w = s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs * (a.Hkv / a.coop) : 0;
     const int incl = wave_incl_scan(w, lane);
     const int lo = base + (incl - w), hi = base + incl;
     const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int sq = b0 + lane;
-      const int w = sq < a.B ? (mq_len(a, sq, BS) + BS - 1) / BS * a.Hkv : 0;
+      const int w = sq < a.B ? (mq_len(a, sq, BS) + BS - 1) / BS * (a.Hkv / a.coop) : 0;
       const int incl = wave_incl_scan(w, lane);
       if (sq < a.B) a.ws_seq[sq] = base + incl - w;
       base += __builtin_amdgcn_readlane(incl, 63);
@@ -544,18 +547,23 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     if (lane == 0) a.ws_seq[a.B] = base;
   }
   if (W == 0) return;
-  const int nshare = std::min(a.splits, W);
-  if (wave >= nshare) return;
-  const int c_begin = int(share_begin(wave, W, nshare));
-  const int c_end = int(share_begin(wave + 1, W, nshare));
+  // Share of this wave's group of `coop` consecutive waves, walked side by side on kv heads
+  // coop*hg + sub, so that together they read the adjacent head regions of each block.
+  // Pieces stay numbered per wave (2 * wave + slot).
+  const int share = wave / a.coop, sub = wave % a.coop;
+  const int nshare = std::min(a.splits / a.coop, W);
+  if (share >= nshare) return;
+  const int c_begin = int(share_begin(share, W, nshare));
+  const int c_end = int(share_begin(share + 1, W, nshare));
 
   int s, seq_off;
   mq_locate(a, BS, lane, c_begin, s, seq_off);
   if (s >= a.B) return;
   int L = mq_len(a, s, BS);
   int nb = (L + BS - 1) / BS;
-  int g = (c_begin - seq_off) / nb;
-  int unit_off = seq_off + g * nb;
+  int hg = (c_begin - seq_off) / nb;
+  int g = hg * a.coop + sub;
+  int unit_off = seq_off + hg * nb;
   int pos = c_begin;
   const int row = lane >> 4;
   const float sl2 = a.qk_scale_log2;
@@ -697,8 +705,8 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     if (pos >= c_end) break;
     // Next unit: next kv head of this sequence, else the next non-empty sequence.
     unit_off = unit_end;
-    if (++g == a.Hkv) {
-      g = 0;
+    if (++hg == a.Hkv / a.coop) {
+      hg = 0;
       bool done;
       do {
         done = ++s >= a.B;
@@ -706,6 +714,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       if (done) break;
       nb = (L + BS - 1) / BS;
     }
+    g = hg * a.coop + sub;
   }
 
   if (hold_cols > 0) flush_hold();
@@ -734,7 +743,7 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
   const int c = c0 + std::min(lane >> 4, ncols - 1);         // this lane's column
   const int d0 = (lane & 15) * EPL;
   const int before = a.ws_seq[s];
-  const int nb = (a.ws_seq[s + 1] - before) / a.Hkv;
+  const int nb = (a.ws_seq[s + 1] - before) / (a.Hkv / a.coop);
   const int W = a.ws_seq[a.B];
   auto write = [&](const float* v, float inv) {
     if (!col_ok) return;
@@ -762,12 +771,14 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
     write(num, 0.f);
     return;
   }
-  const int nshare = std::min(a.splits, W);
-  const int off = before + g * nb;
+  const int C = a.coop, sub = g % C;
+  const int nshare = std::min(a.splits / C, W);
+  const int off = before + (g / C) * nb;
   const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
   if (wf == wl) return;
   const int np = int(wl - wf + 1);
-  const int64_t piece0 = wf * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  // Share w's pieces of kv head g are those of its wave C*w + g%C.
+  const int64_t piece0 = (wf * C + sub) * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
   float M = -INFINITY, den = 0.f;
   for (int j0 = 0; j0 < np; j0 += BATCH) {
     float2 ml[BATCH];
@@ -775,7 +786,7 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
       const int j = std::min(j0 + t, np - 1);
-      const int64_t pc = j == 0 ? piece0 : (wf + j) * 2;
+      const int64_t pc = j == 0 ? piece0 : ((wf + j) * C + sub) * 2;
       const int64_t r = pc * kMqCols + c;
       ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
       const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
@@ -1005,6 +1016,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     a.max_blocks = max_blocks_per_seq;
     a.num_q_tokens = num_q_tokens;
     a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * std::max(1, max_blocks_per_seq))));
+    a.coop = 1;
+    while (a.coop < kMqWaves && Hkv % (2 * a.coop) == 0 && a.splits >= 2 * a.coop) a.coop *= 2;
     a.qk_scale_log2 = scale * k_scale * kLog2e;
     a.v_scale = v_scale;
     const unsigned wgs = unsigned((int64_t(a.splits) + kMqWaves - 1) / kMqWaves);

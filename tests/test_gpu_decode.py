@@ -28,6 +28,9 @@ SMALL = {
     # Groups that are not a multiple of the merge's four heads per wave: idle lanes.
     "bf16_g6": Workload("bf16_g6", 4, 12, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 900)),
     "f32_d64_g3": Workload("f32_d64_g3", 3, 9, 3, 64, 16, "f32", "f32", ("uniform", 1, 400)),
+    # Kv heads walked in groups: 6 heads go in pairs, 16 heads in four groups of four.
+    "bf16_hkv6_g2": Workload("bf16_hkv6_g2", 3, 12, 6, 128, 16, "bf16", "bf16", ("uniform", 1, 500)),
+    "f32_d64_hkv16_g1": Workload("f32_d64_hkv16_g1", 2, 16, 16, 64, 16, "f32", "f32", ("uniform", 1, 300)),
 }
 
 
@@ -43,7 +46,7 @@ def test_parity_small(name, seed):
     assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_bf16", "long_ctx_splitk_bf16", "tiny_fp32", "fp8_kv"])
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "long_ctx_splitk_bf16", "tiny_fp32", "fp8_kv", "bf16_hkv6_g2"])
 def test_split_count_does_not_change_the_result(name):
     require_gpu()
     wl = SMALL[name]
@@ -51,7 +54,7 @@ def test_split_count_does_not_change_the_result(name):
     k, v = pack(case)
     ref = oatt.decode_case(case)
     outs = []
-    for n in (1, 2, 7, 64, 1000, 0):
+    for n in (1, 2, 3, 4, 7, 64, 1000, 0):
         log(f"splits {name} num_splits={n}")
         got = as_f64(decode(case, k, v, num_splits=n))
         assert_close(got, ref, wl.kv_dtype, f"{name} splits={n}")

@@ -162,7 +162,7 @@ FEW = {
 
 
 @pytest.mark.parametrize("name", list(FEW))
-@pytest.mark.parametrize("splits", [0, 5, 997])
+@pytest.mark.parametrize("splits", [0, 3, 5, 997])
 def test_few_query_path_parity(name, splits):
     require_gpu()
     import torch

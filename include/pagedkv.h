@@ -241,7 +241,8 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *   max_query_len  host bound on every n_s: query rows past it in a sequence are neither
  *                  computed nor written.  It also picks the kernel: with max_query_len * G
  *                  <= 32 (a few drafted tokens, short chunks) the work is cut like decode's
- *                  into num_splits equal shares of the (sequence, kv head, block) list with a
+ *                  (kv heads in groups of 4, 2 or 1, num_splits / group equal shares of the
+ *                  (sequence, head group, block) list, one wave per head of a group) with a
  *                  merge pass, which needs the workspace; otherwise query tiles of 256
  *                  (query, head) columns each stream their sequence's K/V through LDS, with no
  *                  workspace.

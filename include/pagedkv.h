@@ -252,8 +252,8 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *                  the tile path, where it may be NULL); no initial contents needed.
  *   Every other argument as for pkv_paged_attention_decode.  out is written once per
  *   query row and head.
- * Limits: on the tile path max_blocks_per_seq <= 16376 (the sequence's table entries are
- * staged on chip); num_q_tokens * Hq < 2^31.
+ * Limits: on the tile path max_blocks_per_seq <= 16376 and num_blocks * Hkv < 2^31 (the
+ * sequence's table entries are staged on chip, as phys * Hkv); num_q_tokens * Hq < 2^31.
  * ------------------------------------------------------------------------------------ */
 pkv_status pkv_paged_attention_prefill_workspace_size(int num_seqs, int num_q_heads,
                                                       int num_kv_heads, int head_dim,

@@ -128,7 +128,12 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   // The table entries the workgroup reads, then kTblPad entries of -1: a step's lookups
   // past the last block land there instead of outside the array.
   const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-  for (int e = tid; e < nblk + kTblPad; e += kThreads) s_tbl[e] = e < nblk ? trow[e] : -1;
+  // Entries are kept as phys * Hkv (the block's first kv-head region), or -1 for an entry
+  // outside [0, num_blocks): a staged chunk's address is then one shift and add.
+  for (int e = tid; e < nblk + kTblPad; e += kThreads) {
+    const int phys = e < nblk ? trow[e] : -1;
+    s_tbl[e] = unsigned(phys) < unsigned(a.num_blocks) ? phys * a.Hkv : -1;
+  }
 
   // This lane's columns: (query qi, head hh) for column col0 + 16*(wave*CT + ct) + lane%16.
   const int row = lane >> 4;
@@ -161,17 +166,23 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   // Running max in raw logit units (before the scale), sum and accumulators per column.
   f32x4 acc[CT][F::NT];
   float m_run[CT], l_run[CT];
+  // bf16 caches: the running sum of each column comes from the matrix unit, as the product
+  // of an all-ones A operand with the same bf16 probabilities PV uses; every row of lsum[ct]
+  // then holds the sum of column lane % 16.  (For fp8 caches the vector sum measured faster.)
+  f32x4 lsum[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
     for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[ct] = -INFINITY;
     l_run[ct] = 0.f;
+    lsum[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  constexpr bool MSUM = KV == PKV_BF16;
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
   const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
-  const int64_t block_stride = int64_t(a.Hkv) * REGION;
   __syncthreads();   // s_tbl
 
   // Chunk tid + 256*r of a step: K or V, sub-tile u, chunk w.  Sub-tiles past the keys the
@@ -196,12 +207,12 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
       const int w = ci % SUB_CHUNKS;
       const int k = step * SUBS + u;
       // k / NSB < nblk + 7 (a step starts below nsub), inside the padded table.
-      const int phys = s_tbl[k / NSB];
-      const bool ok = k < nsub && unsigned(phys) < unsigned(a.num_blocks);
+      const int region = s_tbl[k / NSB];
+      const bool ok = k < nsub && region >= 0;
       zmask |= ok ? 0u : 1u << r;
-      pre[r] = *reinterpret_cast<const uint4*>((which ? vbase : kbase) +
-                                               (ok ? int64_t(phys) * block_stride + (k % NSB) * SUB_BYTES : 0) +
-                                               w * 16);
+      pre[r] = *reinterpret_cast<const uint4*>(
+          (which ? vbase : kbase) + (ok ? int64_t(uint32_t(region)) * REGION + (k % NSB) * SUB_BYTES : 0) +
+          w * 16);
     }
   };
   auto stage_write = [&](uint4* buf) {
@@ -279,7 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
           const float m_new = fmaxf(m_run[ct], cmax[ct]);
           const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
           m_run[ct] = m_new;
-          l_run[ct] *= alpha;
+          if constexpr (MSUM) lsum[ct] *= alpha;
+          else l_run[ct] *= alpha;
 #pragma unroll
           for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
         }
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               p[ct][uu][j] = __builtin_amdgcn_exp2f(fmaf(sc[ct][pu + uu][j], sl2, m_off[ct]));   // 0 where masked
-              l_run[ct] += p[ct][uu][j];
+              if constexpr (!MSUM) l_run[ct] += p[ct][uu][j];
             }
         const uint4* vsrc = buf + SUBS * SUB_CHUNKS;
         if constexpr (VPAIR) {
@@ -336,6 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
           for (int ct = 0; ct < CT; ++ct) {
             const uint4 bop = make_uint4(pack_bf16x2(p[ct][0][0], p[ct][0][1]), pack_bf16x2(p[ct][0][2], p[ct][0][3]),
                                          pack_bf16x2(p[ct][1][0], p[ct][1][1]), pack_bf16x2(p[ct][1][2], p[ct][1][3]));
+            lsum[ct] = mfma_bf16_k32(ones, bop, lsum[ct]);
 #pragma unroll
             for (int i = 0; i < F::NLOAD; ++i) {
               acc[ct][2 * i + 0] = mfma_bf16_k32(vp[0][i], bop, acc[ct][2 * i + 0]);
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
 
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    const float l_tot = wave_sum_rows(l_run[ct]);
+    const float l_tot = MSUM ? lsum[ct][0] : wave_sum_rows(l_run[ct]);
     const int c = col0 + 16 * (wave * CT + ct) + (lane & 15);
     const int qi = c / a.G, hh = c % a.G;
     if (qi >= n) continue;
@@ -1040,6 +1053,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     return PKV_OK;
   }
   const int64_t tbl_bytes = (int64_t(max_blocks_per_seq) + kTblPad) * 4;
+  if (int64_t(num_blocks) * Hkv > int64_t(INT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_blocks * num_kv_heads exceeds 2^31", fn);
   if (tbl_bytes > kMaxTableBytes)
     return pkv::fail(PKV_UNSUPPORTED, "%s: max_blocks_per_seq=%d exceeds %d", fn, max_blocks_per_seq,
                      kMaxTableBytes / 4 - kTblPad);

@@ -83,19 +83,28 @@ constexpr int step_subtiles() {
 
 template <int KV, int D, int BS, int CT>
 __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(PrefillArgs a) {
-  using F = Frag<KV, D>;
-  using T = KvTraits<KV>;
+  // KV is the pool's element type; CKV the type staged in LDS and used by the matrix
+  // products.  An fp8 cache is widened to bf16 (exactly) once, while the workgroup stages a
+  // step, instead of by each of its waves in every product.
+  constexpr int CKV = KV == PKV_FP8_E4M3FN ? PKV_BF16 : KV;
+  using F = Frag<CKV, D>;
+  using T = KvTraits<CKV>;
   constexpr int X = 16 / T::EB;
-  constexpr int SUB_BYTES = 16 * D * T::EB;
+  constexpr int SUB_BYTES = 16 * D * T::EB;                 // an LDS sub-tile
   constexpr int SUB_CHUNKS = SUB_BYTES / 16;
+  constexpr int SUB_BYTES_P = 16 * D * KvTraits<KV>::EB;    // a pool sub-tile
+  constexpr int SUB_CHUNKS_P = SUB_BYTES_P / 16;
+  constexpr int WIDEN = SUB_CHUNKS / SUB_CHUNKS_P;          // LDS chunks per pool chunk
+  static_assert(WIDEN == 1 || (WIDEN == 2 && KV == PKV_FP8_E4M3FN), "staging widening");
   constexpr int NSB = BS / 16;
-  constexpr int64_t REGION = int64_t(BS) * D * T::EB;
-  constexpr int SUBS = step_subtiles<KV, D>();
+  constexpr int64_t REGION = int64_t(BS) * D * KvTraits<KV>::EB;   // in the pool
+  constexpr int SUBS = step_subtiles<CKV, D>();
   constexpr int STEP_TOK = 16 * SUBS;
   constexpr int COLS = kWaves * 16 * CT;
-  constexpr int STAGE_CHUNKS = 2 * SUBS * SUB_CHUNKS;      // K then V
-  constexpr int PER_THREAD = STAGE_CHUNKS / kThreads;
-  static_assert(STAGE_CHUNKS % kThreads == 0, "staging tiling");
+  constexpr int STAGE_CHUNKS = 2 * SUBS * SUB_CHUNKS;       // K then V, in LDS
+  constexpr int FETCH_CHUNKS = 2 * SUBS * SUB_CHUNKS_P;     // K then V, from the pool
+  constexpr int PER_THREAD = FETCH_CHUNKS / kThreads;
+  static_assert(FETCH_CHUNKS % kThreads == 0, "staging tiling");
   __shared__ __attribute__((aligned(16))) uint4 stage[2][STAGE_CHUNKS];
   extern __shared__ int32_t s_tbl[];
 
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   float m_run[CT], l_run[CT];
   // bf16 caches: the running sum of each column comes from the matrix unit, as the product
   // of an all-ones A operand with the same bf16 probabilities PV uses; every row of lsum[ct]
-  // then holds the sum of column lane % 16.  (For fp8 caches the vector sum measured faster.)
+  // then holds the sum of column lane % 16 (fp8 caches are staged as bf16, so they too).
   f32x4 lsum[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
     l_run[ct] = 0.f;
     lsum[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  constexpr bool MSUM = KV == PKV_BF16;
+  constexpr bool MSUM = CKV == PKV_BF16;
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
   const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   // pair of sub-tiles (2p, 2p+1) are interleaved by 8-byte halves, [pair][half e][chunk w]
   // [sub-tile parity]: one 16-byte read of (p, e, w) is then exactly the k = 32 PV operand
   // {sub-tile 2p half e, sub-tile 2p+1 half e} of output tile 2i+e, with no register moves.
-  constexpr bool VPAIR = KV == PKV_BF16;
+  constexpr bool VPAIR = CKV == PKV_BF16;
   __builtin_assume(tid < kThreads);
   uint4 pre[PER_THREAD];
   uint32_t zmask = 0;
@@ -202,16 +211,16 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
       const int ci = tid + kThreads * r;
-      const int which = ci / (SUBS * SUB_CHUNKS);
-      const int u = (ci / SUB_CHUNKS) % SUBS;
-      const int w = ci % SUB_CHUNKS;
+      const int which = ci / (SUBS * SUB_CHUNKS_P);
+      const int u = (ci / SUB_CHUNKS_P) % SUBS;
+      const int w = ci % SUB_CHUNKS_P;
       const int k = step * SUBS + u;
       // k / NSB < nblk + 7 (a step starts below nsub), inside the padded table.
       const int region = s_tbl[k / NSB];
       const bool ok = k < nsub && region >= 0;
       zmask |= ok ? 0u : 1u << r;
       pre[r] = *reinterpret_cast<const uint4*>(
-          (which ? vbase : kbase) + (ok ? int64_t(uint32_t(region)) * REGION + (k % NSB) * SUB_BYTES : 0) +
+          (which ? vbase : kbase) + (ok ? int64_t(uint32_t(region)) * REGION + (k % NSB) * SUB_BYTES_P : 0) +
           w * 16);
     }
   };
@@ -221,17 +230,43 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
       for (int r = 0; r < PER_THREAD; ++r)
         if ((zmask >> r) & 1u) pre[r] = make_uint4(0u, 0u, 0u, 0u);
     }
+    // LDS chunk w of sub-tile u of K (which 0) or V (which 1).
+    auto put = [&](int which, int u, int w, uint4 val) {
+      if (!VPAIR || which == 0) {
+        buf[(which * SUBS + u) * SUB_CHUNKS + w] = val;
+      } else {
+        uint2* vb = reinterpret_cast<uint2*>(buf + SUBS * SUB_CHUNKS);
+        const int base = (u >> 1) * 2 * SUB_CHUNKS;
+        vb[2 * (base + w) + (u & 1)] = make_uint2(val.x, val.y);
+        vb[2 * (base + SUB_CHUNKS + w) + (u & 1)] = make_uint2(val.z, val.w);
+      }
+    };
 #pragma unroll
     for (int r = 0; r < PER_THREAD; ++r) {
       const int ci = tid + kThreads * r;
-      if (!VPAIR || ci < SUBS * SUB_CHUNKS) {
-        buf[ci] = pre[r];
+      const int which = ci / (SUBS * SUB_CHUNKS_P);
+      const int u = (ci / SUB_CHUNKS_P) % SUBS, w = ci % SUB_CHUNKS_P;
+      if constexpr (WIDEN == 1) {
+        put(which, u, w, pre[r]);
       } else {
-        const int u = (ci / SUB_CHUNKS) % SUBS, w = ci % SUB_CHUNKS;
-        uint2* vb = reinterpret_cast<uint2*>(buf + SUBS * SUB_CHUNKS);
-        const int base = (u >> 1) * 2 * SUB_CHUNKS;
-        vb[2 * (base + w) + (u & 1)] = make_uint2(pre[r].x, pre[r].y);
-        vb[2 * (base + SUB_CHUNKS + w) + (u & 1)] = make_uint2(pre[r].z, pre[r].w);
+        // An fp8 chunk (64i + l) widens to two bf16 chunks; lo holds its bytes 0..7, hi 8..15.
+        const uint4 lo = make_uint4(fp8x2_to_bf16x2<false>(pre[r].x), fp8x2_to_bf16x2<true>(pre[r].x),
+                                    fp8x2_to_bf16x2<false>(pre[r].y), fp8x2_to_bf16x2<true>(pre[r].y));
+        const uint4 hi = make_uint4(fp8x2_to_bf16x2<false>(pre[r].z), fp8x2_to_bf16x2<true>(pre[r].z),
+                                    fp8x2_to_bf16x2<false>(pre[r].w), fp8x2_to_bf16x2<true>(pre[r].w));
+        const int i = w >> 6, l = w & 63;
+        if (which == 0) {
+          // K: token l % 16, dims 16 (4i + l/16) .. +16, i.e. bf16 dim groups q and q + 1 of
+          // 8, which are LDS chunks 64 (q/4) + 16 (q%4) + l % 16.
+          const int q = 2 * (4 * i + (l >> 4)), t = l & 15;
+          put(0, u, 64 * (q >> 2) + 16 * (q & 3) + t, lo);
+          put(0, u, 64 * ((q + 1) >> 2) + 16 * ((q + 1) & 3) + t, hi);
+        } else {
+          // V: dims 64i + 16e + l % 16 for e = 0..3 (tokens 4 (l/16) .. +3): e = 0, 1 are
+          // bf16 chunk 64 (2i) + l, e = 2, 3 chunk 64 (2i + 1) + l.
+          put(1, u, 64 * (2 * i) + l, lo);
+          put(1, u, 64 * (2 * i + 1) + l, hi);
+        }
       }
     }
   };
@@ -263,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
         const int t0 = tok_step + 16 * u + 4 * row;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
+          const f32x4 c = qk_subtile<CKV, D>(kf, qf[ct]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) sc[ct][uu][j] = !MASK || t0 + j <= pos[ct] ? c[j] : -INFINITY;
         }
@@ -371,11 +406,11 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
               vm0 |= (t0 + j < L ? 1u : 0u) << j;
               vm1 |= (t0 + 16 + j < L ? 1u : 0u) << j;
             }
-            mask_v<KV, D>(vf0, vm0);
-            mask_v<KV, D>(vf1, vm1);
+            mask_v<CKV, D>(vf0, vm0);
+            mask_v<CKV, D>(vf1, vm1);
           }
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) pv_pair<KV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
+          for (int ct = 0; ct < CT; ++ct) pv_pair<CKV, D>(acc[ct], vf0, vf1, p[ct][0], p[ct][1]);
         }
       }
     }

@@ -141,3 +141,14 @@ def test_vmm_create_rejects_bad_sizes_without_a_device_call():
     assert b"max_seqs" in lib.pkv_last_error()
     assert not lib.pkv_vmm_create(0, 4, 16, 100, 0)        # block bytes not a multiple of 16
     assert lib.pkv_vmm_num_blocks(None) == -1 and lib.pkv_vmm_mapped_bytes(None) == 0
+
+
+def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
+    """The tile path stages block-table entries as phys * Hkv in 32 bits; a pool whose
+    num_blocks * Hkv reaches 2^31 is rejected on the host, before any HIP call."""
+    lib = pkv.lib()
+    a = ctypes.c_void_p(256)
+    # 64 queries x G 1 > 32 columns: the tile path.  2^28 blocks x 8 kv heads = 2^31.
+    st = lib.pkv_paged_attention_prefill(a, a, a, a, a, a, a, 1, 64, 8, 8, 128, 16, 1 << 28, 8, 64,
+                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, None)
+    assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()

@@ -339,7 +339,10 @@ pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int dst_num_blocks, const v
  *   block_tables   int32 [num_seqs, max_blocks_per_seq] (device, updated in place); row s
  *                  belongs to the s-th sequence passed to pkv_seq_append.
  *   context_lens   int32 [num_seqs] (device, updated in place).
- *   slot_mapping   int64 [num_seqs] (device); a negative slot leaves row s unchanged.
+ *   slot_mapping   int64 [num_seqs], in device memory or in pinned host memory (read by the
+ *                  kernel over the host link, so a step needs no upload; the caller must not
+ *                  rewrite it before the kernel has run); a negative slot leaves row s
+ *                  unchanged.  Any other pointer: PKV_INVALID_ARG.
  * Rows whose slot does not match their length (slot % bs != p % bs) or whose new position
  * lies past max_blocks_per_seq blocks are left unchanged (a caller error, never a fault).
  * ------------------------------------------------------------------------------------ */

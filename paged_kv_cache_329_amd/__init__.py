@@ -437,14 +437,19 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, block_mapping, head_dim: int, stream
 
 
 def apply_append(block_tables, context_lens, slot_mapping, block_size: int, num_blocks: int, stream=None):
-    """Mirror a decode step's append on device tables / lengths (pkv_apply_append)."""
+    """Mirror a decode step's append on device tables / lengths (pkv_apply_append).
+    slot_mapping may be a device tensor or a pinned host tensor (read by the kernel)."""
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or slot_mapping.dtype != torch.int64:
         raise TypeError("block_tables / context_lens must be int32 and slot_mapping int64")
     n = context_lens.shape[0]
     if block_tables.dim() != 2 or block_tables.shape[0] != n or slot_mapping.shape != (n,):
         raise ValueError("block_tables [n, max_blocks], context_lens [n], slot_mapping [n]")
+    if not slot_mapping.is_cuda and not slot_mapping.is_pinned():
+        raise ValueError("slot_mapping must be a device tensor or a pinned host tensor")
+    if not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous")
     _check(lib().pkv_apply_append(_dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
-                                  _dev(slot_mapping, "slot_mapping"), n, block_tables.shape[1], block_size,
+                                  slot_mapping.data_ptr(), n, block_tables.shape[1], block_size,
                                   num_blocks, _stream(stream)))
 
 

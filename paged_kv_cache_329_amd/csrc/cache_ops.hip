@@ -430,8 +430,14 @@ extern "C" pkv_status pkv_apply_append(int32_t* block_tables, int32_t* context_l
   if (num_seqs == 0) return PKV_OK;
   if (!block_tables || !context_lens || !slot_mapping)
     return pkv::fail(PKV_INVALID_ARG, "pkv_apply_append: null pointer");
+  // The slots may sit in pinned host memory: the kernel then reads them over the host link
+  // (a few KiB), which saves the step a separate upload.
+  void* slots = nullptr;
+  pkv_status st = device_view("pkv_apply_append", "slot_mapping", slot_mapping, &slots);
+  if (st != PKV_OK) return st;
   hipLaunchKernelGGL(apply_append_kernel, dim3(unsigned((num_seqs + 255) / 256)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), block_tables, context_lens, slot_mapping,
-                     num_seqs, max_blocks_per_seq, block_size, int64_t(num_blocks) * block_size);
+                     reinterpret_cast<hipStream_t>(stream), block_tables, context_lens,
+                     static_cast<const int64_t*>(slots), num_seqs, max_blocks_per_seq, block_size,
+                     int64_t(num_blocks) * block_size);
   return launch_status("pkv_apply_append");
 }

@@ -136,6 +136,32 @@ def test_apply_append_mirrors_the_allocator_tables():
     assert n_cow == _expected_cow(case)
 
 
+def test_apply_append_reads_slots_from_pinned_host_memory():
+    """The same forty steps with each step's slots left in one of two pinned host buffers,
+    as a serving loop does, read by the kernel directly (no upload)."""
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 9)
+    wl = case.wl
+    a, k, v, members = build_prefix_batch(case)
+    steps = 40
+    max_blocks = int((case.lengths.max() + steps + wl.block_size) // wl.block_size) + 1
+    tables, lens = a.block_tables(members, max_blocks)
+    t_dev = torch.from_numpy(tables).cuda()
+    l_dev = torch.from_numpy(lens).cuda()
+    host = [torch.empty(len(members), dtype=torch.int64, pin_memory=True) for _ in range(2)]
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    for i in range(steps):
+        hb = host[i % 2]
+        done[i % 2].synchronize()           # the kernel that read this buffer has run
+        a.append(members, hb.numpy())
+        pkv.apply_append(t_dev, l_dev, hb, wl.block_size, case.num_blocks)
+        done[i % 2].record()
+    torch.cuda.synchronize()
+    want_t, want_l = a.block_tables(members, max_blocks)
+    assert np.array_equal(t_dev.cpu().numpy(), want_t)
+    assert np.array_equal(l_dev.cpu().numpy(), want_l)
+
+
 def test_apply_append_skips_negative_and_inconsistent_slots():
     require_gpu()
     tables = torch.full((3, 4), -1, dtype=torch.int32, device="cuda")

@@ -589,11 +589,19 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 // two batches in flight.
 constexpr int kMergeHeads = 4;   // query heads per merge wave
 
-template <int KV, int D, int BS>
-__global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a) {
+// MW waves per workgroup (1, or 4 when units span many shares, as long contexts do): each
+// wave folds a contiguous MW-th of the unit's pieces, and the waves' states meet in LDS.
+constexpr int kMergeWavesLong = 4;
+constexpr int kLongMergePieces = 16;   // shares per (sequence, kv head), at least, for MW = 4
+
+template <int KV, int D, int BS, int MW>
+__global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeArgs a) {
   constexpr int EPL = D / 16;   // output dims per lane
   constexpr int BATCH = 8;      // partials per batch
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = MW == 1 ? 0 : __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  __shared__ float s_num[MW > 1 ? MW : 1][MW > 1 ? EPL : 1][64];
+  __shared__ float2 s_md[MW > 1 ? MW : 1][64];
   const int hq_per_g = (a.G + kMergeHeads - 1) / kMergeHeads;
   const int g = blockIdx.x / hq_per_g, s = blockIdx.y;
   const int h_raw = (blockIdx.x % hq_per_g) * kMergeHeads + (lane >> 4);
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) num[e] = 0.f;
   if (nb == 0) {
-    write(num, 0.f);
+    if (wv == 0) write(num, 0.f);
     return;
   }
   const int nshare = std::min(a.splits / a.coop, W);
@@ -638,11 +646,13 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
   // share wf is that share's first segment (slot 0) only if the unit begins exactly where
   // the share does; in every later share it is the first segment.
   const int64_t piece0 = (wf * C + sub) * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  // This wave's pieces: [jb, je).
+  const int jb = wv * np / MW, je = (wv + 1) * np / MW;
 
   auto load = [&](int j0, float2* ml, float4 (*x)[EPL / 4]) {
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
-      const int j = std::min(j0 + t, np - 1);
+      const int j = std::min(j0 + t, je - 1);
       const int64_t pc = j == 0 ? piece0 : ((wf + j) * C + sub) * 2;
       const int64_t r = pc * a.G + h;
       ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
@@ -656,14 +666,14 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
     float mb = M;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t)
-      if (j0 + t < np) mb = fmaxf(mb, ml[t].x);
+      if (j0 + t < je) mb = fmaxf(mb, ml[t].x);
     const float alpha = __builtin_amdgcn_exp2f(M - mb);
     den *= alpha;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) num[e] *= alpha;
 #pragma unroll
     for (int t = 0; t < BATCH; ++t) {
-      const float c = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
+      const float c = j0 + t < je ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;
       den += ml[t].y * c;
 #pragma unroll
       for (int i = 0; i < EPL / 4; ++i) {
@@ -677,15 +687,42 @@ __global__ __launch_bounds__(64) void paged_attention_merge_kernel(DecodeArgs a)
   };
   float2 mlA[BATCH], mlB[BATCH];
   float4 xA[BATCH][EPL / 4], xB[BATCH][EPL / 4];
-  load(0, mlA, xA);
-  for (int j0 = 0; j0 < np; j0 += 2 * BATCH) {
-    if (j0 + BATCH < np) load(j0 + BATCH, mlB, xB);
-    fold(j0, mlA, xA);
-    if (j0 + BATCH >= np) break;
-    if (j0 + 2 * BATCH < np) load(j0 + 2 * BATCH, mlA, xA);
-    fold(j0 + BATCH, mlB, xB);
+  if (jb < je) {
+    load(jb, mlA, xA);
+    for (int j0 = jb; j0 < je; j0 += 2 * BATCH) {
+      if (j0 + BATCH < je) load(j0 + BATCH, mlB, xB);
+      fold(j0, mlA, xA);
+      if (j0 + BATCH >= je) break;
+      if (j0 + 2 * BATCH < je) load(j0 + 2 * BATCH, mlA, xA);
+      fold(j0 + BATCH, mlB, xB);
+    }
   }
-  write(num, a.v_scale / den);
+  if constexpr (MW == 1) {
+    write(num, a.v_scale / den);
+    return;
+  }
+  // The waves' running states (max, sum, accumulator) meet in LDS; wave 0 folds them with
+  // the same rule and writes the head.  A wave with no pieces holds (-inf, 0, 0).
+  s_md[wv][lane] = make_float2(M, den);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_num[wv][e][lane] = num[e];
+  __syncthreads();
+  if (wv != 0) return;
+  float Mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) Mx = fmaxf(Mx, s_md[w][lane].x);
+  float dsum = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < MW; ++w) {
+    const float2 md = s_md[w][lane];
+    const float c = md.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(md.x - Mx);
+    dsum += md.y * c;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += s_num[w][e][lane] * c;
+  }
+  write(acc, a.v_scale / dsum);
 }
 
 // ---- host side --------------------------------------------------------------------------
@@ -702,14 +739,16 @@ using KernelFn = void (*)(DecodeArgs);
 struct KernelPair {
   KernelFn split;         // plain decode
   KernelFn split_append;  // decode step that stores each sequence's appended token first
-  KernelFn merge;
+  KernelFn merge;         // one wave per (sequence, kv head, four query heads)
+  KernelFn merge_long;    // kMergeWavesLong waves each, for units that span many shares
 };
 
 template <int KV, int D, int BS>
 KernelPair kernels_for() {
   return {paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), false>,
           paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), true>,
-          paged_attention_merge_kernel<KV, D, BS>};
+          paged_attention_merge_kernel<KV, D, BS, 1>,
+          paged_attention_merge_kernel<KV, D, BS, kMergeWavesLong>};
 }
 
 bool pick_kernels(pkv_dtype kv, int D, int bs, KernelPair* kp) {
@@ -896,7 +935,13 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   }
   if (phase != kSplitOnly) {
     const unsigned merge_x = unsigned(Hkv * ((G + kMergeHeads - 1) / kMergeHeads));
-    hipLaunchKernelGGL(kp.merge, dim3(merge_x, unsigned(B)), dim3(64), 0, hs, a);
+    // Units span about splits / (B * Hkv) shares each: many (long contexts) take the merge
+    // whose waves split a unit's pieces; a few take one wave per unit.
+    const bool long_units = int64_t(a.splits) >= int64_t(kLongMergePieces) * B * Hkv;
+    if (long_units)
+      hipLaunchKernelGGL(kp.merge_long, dim3(merge_x, unsigned(B)), dim3(64 * kMergeWavesLong), 0, hs, a);
+    else
+      hipLaunchKernelGGL(kp.merge, dim3(merge_x, unsigned(B)), dim3(64), 0, hs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: merge launch: %s", fn, hipGetErrorString(e));
   }

@@ -24,7 +24,7 @@ SMALL = {
     "verify_bf16": WORKLOADS["spec_verify_llama3_8b_bf16"].scaled(batch=6, length_dist=("uniform", 1, 500)),
     "prefill_fp8": WORKLOADS["prefill_fp8_kv"].scaled(batch=3, length_dist=("uniform", 1, 300)),
     # Other shapes: D 64 / bs 32 / G 2, G 16, G 1, G 3 (column tiles cross query tokens),
-    # f32 with D 128 and bs 32, fp8 with D 64.
+    # f32 with D 128 and bs 32, fp8 with D 64 and with D 128 / bs 16.
     "bf16_d64_bs32_g2": Workload("bf16_d64_bs32_g2", 3, 8, 4, 64, 32, "bf16", "bf16", ("uniform", 1, 200),
                                  query_dist=("fixed", 50)),
     "bf16_g16": Workload("bf16_g16", 2, 32, 2, 128, 16, "bf16", "bf16", ("uniform", 1, 150),
@@ -37,6 +37,9 @@ SMALL = {
                                  query_dist=("all",)),
     "fp8_d64_bs16_g8": Workload("fp8_d64_bs16_g8", 3, 16, 2, 64, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 200),
                                 query_dist=("fixed", 40)),
+    # fp8 widened to bf16 at staging: D 128 with 16-token blocks as well.
+    "fp8_d128_bs16_g2": Workload("fp8_d128_bs16_g2", 3, 8, 4, 128, 16, "bf16", "fp8_e4m3fn", ("uniform", 1, 250),
+                                 query_dist=("fixed", 40)),
 }
 
 

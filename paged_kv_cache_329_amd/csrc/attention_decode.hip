@@ -592,7 +592,7 @@ constexpr int kMergeHeads = 4;   // query heads per merge wave
 // MW waves per workgroup (1, or 4 when units span many shares, as long contexts do): each
 // wave folds a contiguous MW-th of the unit's pieces, and the waves' states meet in LDS.
 constexpr int kMergeWavesLong = 4;
-constexpr int kLongMergePieces = 16;   // shares per (sequence, kv head), at least, for MW = 4
+constexpr int kLongMergePieces = 16;   // shares per (sequence, kv-head group), at least, for MW = 4
 
 template <int KV, int D, int BS, int MW>
 __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeArgs a) {
@@ -935,9 +935,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   }
   if (phase != kSplitOnly) {
     const unsigned merge_x = unsigned(Hkv * ((G + kMergeHeads - 1) / kMergeHeads));
-    // Units span about splits / (B * Hkv) shares each: many (long contexts) take the merge
-    // whose waves split a unit's pieces; a few take one wave per unit.
-    const bool long_units = int64_t(a.splits) >= int64_t(kLongMergePieces) * B * Hkv;
+    // Units span about (shares) / (units) shares each, where the table width bounds the
+    // work list: many (long contexts) take the merge whose waves split a unit's pieces; a
+    // few take one wave per unit.
+    const int64_t units = int64_t(B) * (Hkv / a.coop);
+    const int64_t shares = std::min<int64_t>(a.splits / a.coop, units * max_blocks);
+    const bool long_units = shares >= int64_t(kLongMergePieces) * units;
     if (long_units)
       hipLaunchKernelGGL(kp.merge_long, dim3(merge_x, unsigned(B)), dim3(64 * kMergeWavesLong), 0, hs, a);
     else

@@ -111,7 +111,7 @@ def _cpu_baseline(case, bytes_per_token, budget_s=10.0, max_passes=3):
 def main():
     args = _args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+        print("bench.py: the benchmark runs on one GPU only; multi-GPU runs are not supported "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 

@@ -539,14 +539,24 @@ __device__ void mq_locate(const MqArgs& a, int bs, int lane, int x, int& s_out, 
 }
 
 // Partial (accumulator, max, sum) of column c in piece `piece`; lane (column c % 16, row)
-// holds dims 16*nn + 4*row .. +3 of each 16-dim tile nn.
-template <int D>
+// holds dims 16*nn + 4*row .. +3 of each 16-dim tile nn.  With bf16 or fp8 caches the
+// accumulator is stored as bf16 (the output's precision; the sums and maxima stay float32),
+// which halves the partial traffic.
+template <int KV, int D>
 __device__ __forceinline__ void store_mq_partial(const MqArgs& a, int64_t piece, int c, int row,
                                                  const f32x4* acc, float2 ml) {
-  float* wacc = a.ws_acc + (piece * kMqCols + c) * D;
+  if constexpr (KV == PKV_F32) {
+    float* wacc = a.ws_acc + (piece * kMqCols + c) * D;
 #pragma unroll
-  for (int nn = 0; nn < D / 16; ++nn)
-    *reinterpret_cast<float4*>(wacc + 16 * nn + 4 * row) = make_float4(acc[nn][0], acc[nn][1], acc[nn][2], acc[nn][3]);
+    for (int nn = 0; nn < D / 16; ++nn)
+      *reinterpret_cast<float4*>(wacc + 16 * nn + 4 * row) = make_float4(acc[nn][0], acc[nn][1], acc[nn][2], acc[nn][3]);
+  } else {
+    uint16_t* wacc = reinterpret_cast<uint16_t*>(a.ws_acc) + (piece * kMqCols + c) * D;
+#pragma unroll
+    for (int nn = 0; nn < D / 16; ++nn)
+      *reinterpret_cast<uint2*>(wacc + 16 * nn + 4 * row) =
+          make_uint2(pack_bf16x2(acc[nn][0], acc[nn][1]), pack_bf16x2(acc[nn][2], acc[nn][3]));
+  }
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = ml;
 }
 
@@ -577,7 +587,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       f32x4 h[F::NT];
 #pragma unroll
       for (int nn = 0; nn < F::NT; ++nn) h[nn] = s_hold[wv][ct * F::NT + nn][lane];
-      store_mq_partial<D>(a, int64_t(wave) * 2, c, lane >> 4, h, s_hold_ml[wv][ct][lane]);
+      store_mq_partial<KV, D>(a, int64_t(wave) * 2, c, lane >> 4, h, s_hold_ml[wv][ct][lane]);
     }
     hold_cols = 0;
   };
@@ -744,7 +754,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
         for (int nn = 0; nn < F::NT; ++nn) s_hold[wv][ct * F::NT + nn][lane] = acc[ct][nn];
         s_hold_ml[wv][ct][lane] = make_float2(m_run[ct], l_tot);
       } else {
-        store_mq_partial<D>(a, piece, c, row, acc[ct], make_float2(m_run[ct], l_tot));
+        store_mq_partial<KV, D>(a, piece, c, row, acc[ct], make_float2(m_run[ct], l_tot));
       }
     }
     if (slot == 0 && !full) hold_cols = n * a.G;
@@ -837,9 +847,26 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
       const int64_t pc = j == 0 ? piece0 : ((wf + j) * C + sub) * 2;
       const int64_t r = pc * kMqCols + c;
       ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
-      const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
+      if constexpr (KV == PKV_F32) {
+        const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
 #pragma unroll
-      for (int i = 0; i < EPL / 4; ++i) x[t][i] = px[i];
+        for (int i = 0; i < EPL / 4; ++i) x[t][i] = px[i];
+      } else {
+        // EPL bf16 values, 2 per dword.
+        const uint32_t* pb = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(a.ws_acc) + r * D + d0);
+        uint32_t w[EPL / 2];
+        if constexpr (EPL == 8) {
+          const uint4 v = *reinterpret_cast<const uint4*>(pb);
+          w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(pb);
+          w[0] = v.x; w[1] = v.y;
+        }
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i)
+          x[t][i] = make_float4(__uint_as_float(w[2 * i] << 16), __uint_as_float(w[2 * i] & 0xFFFF0000u),
+                                __uint_as_float(w[2 * i + 1] << 16), __uint_as_float(w[2 * i + 1] & 0xFFFF0000u));
+      }
     }
     float mb = M;
 #pragma unroll

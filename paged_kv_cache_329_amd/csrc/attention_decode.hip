@@ -54,6 +54,7 @@ namespace {
 using namespace pkv::tile;
 
 constexpr int kWavesPerWG = 4;
+constexpr int kXcds = 8;   // MI355X: workgroups are dealt to the 8 XCDs round-robin
 constexpr int kMaxGroup = 16;
 
 struct DecodeArgs {
@@ -335,7 +336,14 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave = blockIdx.x * kWavesPerWG + wv;
+  // Workgroup b runs on XCD b % 8.  Each XCD takes a contiguous eighth of the work list
+  // (logical workgroup (b % 8) * (n / 8) + b / 8), so sequences next to each other, such as
+  // the members of a group that share prefix blocks, read those blocks through one XCD's L2
+  // at about the same time.  Shares and pieces are numbered by the logical wave.
+  const int nwg = int(gridDim.x), full = nwg - nwg % kXcds;
+  const int b = int(blockIdx.x);
+  const int lwg = b < full ? (b % kXcds) * (full / kXcds) + b / kXcds : b;
+  const int wave = lwg * kWavesPerWG + wv;
   // The partial of a share's first segment waits in LDS until the share's loads are done: a
   // wave's loads and stores complete in issue order, so a store in the middle of the share
   // would hold up every load behind it.  Each lane reads back only what it wrote.

@@ -572,7 +572,12 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wave = blockIdx.x * kMqWaves + wv;
+  // Each XCD (workgroup b runs on XCD b % kXcds) takes a contiguous eighth of the work list;
+  // shares and pieces are numbered by the logical wave.
+  const int nwg = int(gridDim.x), full = nwg - nwg % kXcds;
+  const int b = int(blockIdx.x);
+  const int lwg = b < full ? (b % kXcds) * (full / kXcds) + b / kXcds : b;
+  const int wave = lwg * kMqWaves + wv;
   // The partial of a share's first segment waits in LDS until the share's loads are done: a
   // wave's loads and stores complete in issue order, so a store in the middle of the share
   // would hold up every load behind it.  Each lane reads back only what it wrote.

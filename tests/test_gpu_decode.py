@@ -81,6 +81,23 @@ def test_physical_block_permutation_is_bit_identical(name):
     assert raw_bytes(base) == raw_bytes(other)
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "tiny_fp32"])
+@pytest.mark.parametrize("num_splits", [0, 3000])
+def test_long_and_short_sequences_together(name, num_splits):
+    """One long sequence beside short and empty ones: the table is wide enough that the
+    merge splits each head's pieces over four waves, while the short sequences' heads have
+    fewer pieces than waves (some waves fold nothing)."""
+    require_gpu()
+    wl = SMALL[name].scaled(batch=5)
+    lengths = np.array([1800 if wl.kv_dtype != "f32" else 400, 20, 0, 40, 3], dtype=np.int64)
+    case = make_decode_case(wl, 6, lengths=lengths)
+    log(f"long and short {name} splits={num_splits} lengths={lengths.tolist()}")
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v, num_splits=num_splits))
+    assert np.all(got[2] == 0)
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "tiny_fp32", "fp8_kv"])
 def test_empty_and_single_token_sequences(name):
     require_gpu()

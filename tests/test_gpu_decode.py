@@ -118,6 +118,21 @@ def test_empty_and_single_token_sequences(name):
                 assert np.array_equal(got[s, h], vals[h // G])
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
+@pytest.mark.parametrize("num_splits", [0, 7, 64])
+def test_many_short_sequences(name, num_splits):
+    """A batch of 300 short sequences (some empty): the per-sequence work offsets are
+    scanned over five 64-sequence chunks, and one share walks many whole units."""
+    require_gpu()
+    wl = SMALL[name].scaled(batch=300, length_dist=("uniform", 0, 40), pool_blocks=None)
+    case = make_decode_case(wl, 12)
+    log(f"many short {name} splits={num_splits} sum L={int(case.lengths.sum())}")
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v, num_splits=num_splits))
+    assert np.all(got[case.lengths == 0] == 0)
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, f"{name} splits={num_splits}")
+
+
 def test_all_sequences_empty():
     require_gpu()
     wl = SMALL["llama3_8b_bf16"].scaled(batch=3)

@@ -185,6 +185,38 @@ def test_few_query_path_parity(name, splits):
     assert_close(as_f64(out), oatt.prefill_case(case), wl.kv_dtype, name)
 
 
+@pytest.mark.parametrize("splits", [0, 7])
+def test_few_query_path_many_short_sequences(splits):
+    """200 short sequences with 0..5 queries each (lengths 0..60, so some queries sit before
+    position 0): many units per share, and sequence offsets over several 64-entry chunks."""
+    require_gpu()
+    wl = FEW["bf16_g4_n8"].scaled(batch=200, length_dist=("uniform", 0, 60))
+    rng = np.random.default_rng(31)
+    lengths = rng.integers(0, 61, size=200)
+    q_lens = rng.integers(0, 6, size=200)
+    case = make_prefill_case(wl, 9, lengths=lengths, q_lens=q_lens)
+    log(f"few-query many short splits={splits} queries={int(q_lens.sum())}")
+    k, v = pack(case)
+    assert int(case.q_lens.max()) * wl.group_size <= 32
+    got = as_f64(prefill(case, k, v) if splits == 0 else _prefill_splits(case, k, v, splits))
+    assert_close(got, oatt.prefill_case(case), wl.kv_dtype, f"few-query many short splits={splits}")
+
+
+def _prefill_splits(case, k, v, splits):
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from gpu_helpers import to_dev
+    wl = case.wl
+    q = to_dev(case.q, wl.q_dtype)
+    out = torch.empty_like(q)
+    pkv.paged_attention_prefill(out, q, k, v, torch.from_numpy(case.block_tables).cuda(),
+                                torch.from_numpy(case.lengths.astype(np.int32)).cuda(),
+                                torch.from_numpy(case.query_start).cuda(), int(case.q_lens.max()), case.scale,
+                                float(case.k_scale), float(case.v_scale), num_splits=splits)
+    torch.cuda.synchronize()
+    return out
+
+
 def test_few_query_path_edges_and_placement():
     """n > L (the first queries see nothing), L = 0, n = 0, single tokens; and the same
     bytes when the blocks sit elsewhere in the pool."""

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -121,6 +121,15 @@ const char* pkv_last_error(void);
  *                   partial (max, sum, accumulator) of every sequence head whose work
  *                   spans more than one share and every sequence's offset in the work
  *                   list (written by the split pass, read by the reduce pass).
+ *   shared_blocks   0 or 1, a load-policy hint; the output is bit-identical either way.
+ *                   Sequences may share physical blocks (forks and common prefixes, shared
+ *                   through reference counts: "What is PagedAttention?", glossary, "Share
+ *                   Without Mutating State").  0: each block is read by one sequence of the
+ *                   call, and K/V are streamed with the non-temporal hint, the faster way
+ *                   on MI355X to read bytes used once.  1: the tables of this call reference
+ *                   some blocks from several sequences; K/V then go through ordinary cached
+ *                   loads, so that sequences reading a shared block at about the same time
+ *                   can find it in L2 or the MALL.  Anything else is INVALID_ARG.
  * Preconditions (not checked on the device): block table entries of used blocks lie in
  * [0, num_blocks) — an entry outside that range is read as a block of zeros, never out
  * of bounds; out does not alias any input.
@@ -145,7 +154,8 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                       int block_size, int num_blocks, int max_blocks_per_seq,
                                       float scale, float k_scale, float v_scale,
                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes,
+                                      int shared_blocks, void* stream);
 
 /* Phase 1 alone: every wavefront streams its share of blocks with a running softmax;
  * sequence heads that fit in one share are written to `out` finished, the others leave
@@ -157,11 +167,13 @@ pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cac
                                      int block_size, int num_blocks, int max_blocks_per_seq,
                                      float scale, float k_scale, float v_scale,
                                      pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     void* workspace, size_t workspace_bytes,
+                                     int shared_blocks, void* stream);
 
 /* Phase 2 alone: merges the partials of split sequence heads (rescaling each by
  * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow
- * phase 1 on the same stream with identical arguments. */
+ * phase 1 on the same stream with identical arguments (shared_blocks is checked, and has
+ * no effect here). */
 pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int num_seqs,
@@ -169,7 +181,8 @@ pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_ca
                                       int block_size, int num_blocks, int max_blocks_per_seq,
                                       float scale, float k_scale, float v_scale,
                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes,
+                                      int shared_blocks, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode step with append: the KV-cache write of each sequence's new token fused into the
@@ -198,7 +211,8 @@ pkv_status pkv_paged_decode_step(void* out, const void* q, const void* k_new, co
                                  int num_kv_heads, int head_dim, int block_size, int num_blocks,
                                  int max_blocks_per_seq, float scale, float k_scale, float v_scale,
                                  pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
-                                 void* workspace, size_t workspace_bytes, void* stream);
+                                 void* workspace, size_t workspace_bytes,
+                                 int shared_blocks, void* stream);
 
 /* Phase 1 of the decode step alone (append + split pass); phase 2 is
  * pkv_paged_attention_reduce with the same arguments and workspace. */
@@ -210,7 +224,7 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
                                        int max_blocks_per_seq, float scale, float k_scale,
                                        float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,
                                        int num_splits, void* workspace, size_t workspace_bytes,
-                                       void* stream);
+                                       int shared_blocks, void* stream);
 
 /* Measurement aid: the next split pass launched on the calling thread (by any decode or
  * decode-step entry point), or the next multi-query attention kernel
@@ -248,6 +262,8 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *                  workspace.
  *   num_splits     shares for the few-query path (0 = a default like decode's); ignored
  *                  otherwise.
+ *   shared_blocks  as for pkv_paged_attention_decode, on the few-query path; the tile path
+ *                  always reads through the caches (its query tiles re-read K/V).
  *   workspace      device scratch of pkv_paged_attention_prefill_workspace_size bytes (0 on
  *                  the tile path, where it may be NULL); no initial contents needed.
  *   Every other argument as for pkv_paged_attention_decode.  out is written once per
@@ -268,7 +284,8 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        int num_blocks, int max_blocks_per_seq, int max_query_len,
                                        float scale, float k_scale, float v_scale,
                                        pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
-                                       void* workspace, size_t workspace_bytes, void* stream);
+                                       void* workspace, size_t workspace_bytes,
+                                       int shared_blocks, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",

@@ -49,8 +49,8 @@ _lib = None
 _lock = threading.Lock()
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _DECODE_ARGS = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_p]
-_STEP_ARGS = [_c_p] * 8 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p]
+                _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_int, _c_p]
+_STEP_ARGS = [_c_p] * 8 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_int, _c_p]
 _SIGNATURES = {
     "pkv_abi_version": ([], _c_int),
     "pkv_last_error": ([], ctypes.c_char_p),
@@ -63,7 +63,7 @@ _SIGNATURES = {
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
-    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
+    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_int, _c_p],
                                     _c_int),
     "pkv_paged_attention_prefill_workspace_size": ([_c_int] * 9 + [ctypes.POINTER(_c_sz)], _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -217,7 +217,7 @@ def _workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
 
 
 def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
-                 v_scale, num_splits, workspace, stream):
+                 v_scale, num_splits, workspace, stream, shared_blocks):
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
     B, Hq, D = q.shape
@@ -238,29 +238,35 @@ def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, 
     _check(getattr(lib(), fn_name)(*ptrs, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                                    float(scale), float(k_scale), float(v_scale), qd, kd,
                                    int(num_splits), _dev(workspace, "workspace"),
-                                   workspace.numel() * workspace.element_size(), st))
+                                   workspace.numel() * workspace.element_size(),
+                                   int(bool(shared_blocks)), st))
     return out
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                           k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
-    """Decode attention through block tables (both phases); see pkv_paged_attention_decode."""
+                           k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
+                           shared_blocks=False):
+    """Decode attention through block tables (both phases); see pkv_paged_attention_decode.
+    shared_blocks=True when the tables reference some blocks from several sequences (forks,
+    common prefixes): K/V then go through cached loads; the output is the same bits."""
     return _decode_call("pkv_paged_attention_decode", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
 
 
 def paged_attention_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                          k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+                          k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
+                          shared_blocks=False):
     """Phase 1 only (streams K/V, writes finished heads and partials)."""
     return _decode_call("pkv_paged_attention_split", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
 
 
 def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                           k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+                           k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
+                           shared_blocks=False):
     """Phase 2 only (merges partials); same arguments and workspace as phase 1."""
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
 
 
 def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -274,7 +280,7 @@ def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
                             max_query_len, scale, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None,
-                            stream=None):
+                            stream=None, shared_blocks=False):
     """Causal multi-query attention (pkv_paged_attention_prefill): sequence s's queries are
     q rows query_start[s] .. query_start[s+1]-1, its last tokens, each attending to every
     token up to its own position.  q / out are [num_q_tokens, Hq, D].  A workspace is made
@@ -303,7 +309,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
                                              float(v_scale), qd, kd, int(num_splits),
                                              _dev(workspace, "workspace") if workspace is not None else None,
                                              workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                             st))
+                                             int(bool(shared_blocks)), st))
     return out
 
 
@@ -320,7 +326,7 @@ def _mq_workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
 
 
 def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-               k_scale, v_scale, num_splits, workspace, stream):
+               k_scale, v_scale, num_splits, workspace, stream, shared_blocks):
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
     B, Hq, D = q.shape
@@ -344,24 +350,27 @@ def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, co
     _check(getattr(lib(), fn_name)(*ptrs, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                                    float(scale), float(k_scale), float(v_scale), qd, kd,
                                    int(num_splits), _dev(workspace, "workspace"),
-                                   workspace.numel() * workspace.element_size(), st))
+                                   workspace.numel() * workspace.element_size(),
+                                   int(bool(shared_blocks)), st))
     return out
 
 
 def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-                      k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+                      k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
+                      shared_blocks=False):
     """Decode step with append (pkv_paged_decode_step): stores every sequence's new token
     (k_new / v_new [num_seqs, Hkv, D], q's dtype) at position context_lens[s] - 1, then
     attends over all context_lens[s] tokens; the store is fused into the split pass."""
     return _step_call("pkv_paged_decode_step", out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
 
 
 def paged_decode_step_split(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-                            k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+                            k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
+                            shared_blocks=False):
     """Phase 1 of the decode step (append + split pass); phase 2 is paged_attention_reduce."""
     return _step_call("pkv_paged_decode_step_split", out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream)
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
 
 
 def set_launch_events(start, stop):

@@ -27,6 +27,9 @@
 //    So the softmax needs no data movement between the two products, and the per-head
 //    statistics live in the lanes of head l%16.  No LDS is used: every K/V byte is
 //    read by exactly one wave, straight into registers.
+//  * Loads: K/V chunks carry the non-temporal hint, unless the caller says that the block
+//    tables share blocks between sequences; then ordinary cached loads let the sequences
+//    that read a shared block at about the same time find it in L2 or the MALL.
 //  * Running softmax (base 2): m = max(m, chunk max); rescale acc and sum by 2^(m_old-m);
 //    p = 2^(s - m).  The chunk max needs two cross-row shuffles (xor 16, xor 32).
 //  * Masking: tokens at or past the context length get s = -inf (select, so garbage or
@@ -325,7 +328,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = ml;
 }
 
-template <int KV, int D, int BS, int NSUB, bool APPEND>
+template <int KV, int D, int BS, int NSUB, bool APPEND, bool NT>
 __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
@@ -464,12 +467,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i)
-          kf[u][i] = load_stream(kbase + off[u] + i * 1024);
+          kf[u][i] = load_kv<NT>(kbase + off[u] + i * 1024);
 #pragma unroll
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i)
-          vf[u][i] = load_stream(vbase + off[u] + i * 1024);
+          vf[u][i] = load_kv<NT>(vbase + off[u] + i * 1024);
       // Everything below is branch-free on the loaded data: a branch around QK or PV
       // would let the compiler sink the chunk loads into it and wait on them one by one.
       // Sub-tiles past the chunk's end and out-of-range blocks are masked instead: their
@@ -745,16 +748,21 @@ constexpr int subtiles_per_step() {
 using KernelFn = void (*)(DecodeArgs);
 
 struct KernelPair {
-  KernelFn split;         // plain decode
-  KernelFn split_append;  // decode step that stores each sequence's appended token first
-  KernelFn merge;         // one wave per (sequence, kv head, four query heads)
-  KernelFn merge_long;    // kMergeWavesLong waves each, for units that span many shares
+  // Index [shared]: 0 streams K/V with the non-temporal hint, 1 uses cached loads (block
+  // tables that reference shared blocks).
+  KernelFn split[2];         // plain decode
+  KernelFn split_append[2];  // decode step that stores each sequence's appended token first
+  KernelFn merge;            // one wave per (sequence, kv head, four query heads)
+  KernelFn merge_long;       // kMergeWavesLong waves each, for units that span many shares
 };
 
 template <int KV, int D, int BS>
 KernelPair kernels_for() {
-  return {paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), false>,
-          paged_attention_split_kernel<KV, D, BS, subtiles_per_step<KV, D>(), true>,
+  constexpr int N = subtiles_per_step<KV, D>();
+  return {{paged_attention_split_kernel<KV, D, BS, N, false, true>,
+           paged_attention_split_kernel<KV, D, BS, N, false, false>},
+          {paged_attention_split_kernel<KV, D, BS, N, true, true>,
+           paged_attention_split_kernel<KV, D, BS, N, true, false>},
           paged_attention_merge_kernel<KV, D, BS, 1>,
           paged_attention_merge_kernel<KV, D, BS, kMergeWavesLong>};
 }
@@ -828,9 +836,11 @@ pkv_status check_shape(const char* fn, int B, int Hq, int Hkv, int D, int bs, pk
 // with more arithmetic per byte, with 16 where registers allow it.
 pkv_status default_splits(const KernelPair& kp, pkv_dtype kv, int* splits) {
   int a = 0, b = 0, cus = 0;
-  pkv_status st = resident_wgs(kp.split, &a, &cus);
+  // The streaming variants: the split count must not depend on the load policy, since the
+  // reduce pass recomputes the shares.
+  pkv_status st = resident_wgs(kp.split[0], &a, &cus);
   if (st != PKV_OK) return st;
-  if ((st = resident_wgs(kp.split_append, &b, &cus)) != PKV_OK) return st;
+  if ((st = resident_wgs(kp.split_append[0], &b, &cus)) != PKV_OK) return st;
   const int target_wgs = (kv == PKV_FP8_E4M3FN ? 16 : 8) / kWavesPerWG;
   *splits = cus * std::max(1, std::min(target_wgs, std::min(a, b))) * kWavesPerWG;
   return PKV_OK;
@@ -864,7 +874,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int bs,
                       int num_blocks, int max_blocks, float scale, float k_scale, float v_scale,
                       pkv_dtype qd, pkv_dtype kd, int num_splits, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, int shared_blocks, void* stream) {
   const bool append = k_new != nullptr || v_new != nullptr;
   pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
   if (st != PKV_OK) return st;
@@ -873,6 +883,8 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
       k_scale == INFINITY || v_scale == INFINITY)
     return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (shared_blocks != 0 && shared_blocks != 1)
+    return pkv::fail(PKV_INVALID_ARG, "%s: shared_blocks=%d must be 0 or 1", fn, shared_blocks);
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks > 0 && !block_tables))
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
@@ -926,7 +938,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {
     const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
-    KernelFn kfn = append ? kp.split_append : kp.split;
+    KernelFn kfn = append ? kp.split_append[shared_blocks] : kp.split[shared_blocks];
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       // The dispatch itself records the events, so they time the kernel alone.
@@ -994,11 +1006,12 @@ pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_
       const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
       float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
-      int num_splits, void *workspace, size_t workspace_bytes, void *stream
+      int num_splits, void *workspace, size_t workspace_bytes, int shared_blocks, void *stream
 #define PKV_DECODE_ARGS                                                                          \
   out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,     \
       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
-      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes, stream
+      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes,        \
+      shared_blocks, stream
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_decode", kBoth, PKV_DECODE_ARGS);
@@ -1015,11 +1028,12 @@ pkv_status pkv_paged_attention_reduce(PKV_DECODE_PARAMS) {
       const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
       float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
-      int num_splits, void *workspace, size_t workspace_bytes, void *stream
+      int num_splits, void *workspace, size_t workspace_bytes, int shared_blocks, void *stream
 #define PKV_STEP_ARGS                                                                            \
   out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables, context_lens,         \
       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
-      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes, stream
+      scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes,        \
+      shared_blocks, stream
 
 pkv_status pkv_paged_decode_step(PKV_STEP_PARAMS) {
   if (!k_new || !v_new) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step: null k_new / v_new");

@@ -560,7 +560,7 @@ __device__ __forceinline__ void store_mq_partial(const MqArgs& a, int64_t piece,
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = ml;
 }
 
-template <int KV, int D, int BS>
+template <int KV, int D, int BS, bool NT>
 __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
@@ -689,9 +689,9 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
       uint4 kf[F::NLOAD], vf[F::NLOAD];
 #pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_stream(kbase + off + i * 1024);
+      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_kv<NT>(kbase + off + i * 1024);
 #pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_stream(vbase + off + i * 1024);
+      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_kv<NT>(vbase + off + i * 1024);
       const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
 #pragma unroll
       for (int i = 0; i < F::NLOAD; ++i) {
@@ -901,12 +901,14 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
 
 using MqFn = void (*)(MqArgs);
 struct MqPair {
-  MqFn split, merge;
+  MqFn split[2];   // [shared]: 0 streams K/V with the non-temporal hint, 1 uses cached loads
+  MqFn merge;
 };
 
 template <int KV, int D, int BS>
 MqPair mq_kernels() {
-  return {paged_attention_mq_split_kernel<KV, D, BS>, paged_attention_mq_merge_kernel<KV, D, BS>};
+  return {{paged_attention_mq_split_kernel<KV, D, BS, true>, paged_attention_mq_split_kernel<KV, D, BS, false>},
+          paged_attention_mq_merge_kernel<KV, D, BS>};
 }
 
 bool pick_mq(pkv_dtype kv, int D, int bs, MqPair* kp) {
@@ -937,7 +939,8 @@ pkv_status mq_default_splits(const MqPair& kp, pkv_dtype kv, int* splits) {
     (void)hipGetLastError();
     return pkv::fail(PKV_HIP_ERROR, "pkv_paged_attention_prefill: no current device");
   }
-  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(kp.split));
+  // The streaming variant: the share count must not depend on the load policy.
+  const auto key = std::make_pair(dev, reinterpret_cast<const void*>(kp.split[0]));
   std::pair<int, int> cu_res;
   {
     std::lock_guard<std::mutex> lock(mu);
@@ -1040,7 +1043,7 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
     int max_blocks_per_seq, int max_query_len, float scale, float k_scale, float v_scale,
     pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits, void* workspace, size_t workspace_bytes,
-    void* stream) {
+    int shared_blocks, void* stream) {
   const char* fn = "pkv_paged_attention_prefill";
   const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads;
   pkv_status cst = check_mq_shape(fn, B, num_q_tokens, max_query_len, Hq, Hkv, head_dim, block_size, q_dtype,
@@ -1052,6 +1055,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
       k_scale == INFINITY || v_scale == INFINITY)
     return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
+  if (shared_blocks != 0 && shared_blocks != 1)
+    return pkv::fail(PKV_INVALID_ARG, "%s: shared_blocks=%d must be 0 or 1", fn, shared_blocks);
   if (B == 0 || num_q_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !query_start ||
       (max_blocks_per_seq > 0 && !block_tables))
@@ -1104,11 +1109,12 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       void* kargs[] = {&a};
-      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kp.split), dim3(wgs), dim3(kMqWaves * 64),
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kp.split[shared_blocks]), dim3(wgs),
+                                        dim3(kMqWaves * 64),
                                         kargs, 0, hs, static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
       if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
     } else {
-      hipLaunchKernelGGL(kp.split, dim3(wgs), dim3(kMqWaves * 64), 0, hs, a);
+      hipLaunchKernelGGL(kp.split[shared_blocks], dim3(wgs), dim3(kMqWaves * 64), 0, hs, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));

@@ -48,12 +48,19 @@ struct KvTraits<PKV_FP8_E4M3FN> {
   static constexpr int QB = 2;
 };
 
-// Cached K/V bytes are read exactly once per call, so they are loaded with the
-// non-temporal hint: on MI355X this lifts a random 4 KiB-chunk gather from about
-// 5.9 to 6.5 TB/s, because streaming data no longer displaces cache lines.
-__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// A 16-byte K/V chunk.  NT: the block is read once per call, so the load carries the
+// non-temporal hint; on MI355X this lifts a random 4 KiB-chunk gather from about 5.9 to
+// 6.5 TB/s, because streaming data no longer displaces cache lines.  Without NT (blocks
+// shared by several sequences of the call) it is an ordinary cached load, so that the
+// sequences reading a shared block at about the same time can find it in L2 or the MALL.
+template <bool NT>
+__device__ __forceinline__ uint4 load_kv(const uint8_t* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {

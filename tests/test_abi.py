@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_single_hip_runtime_and_abi_version():
-    assert pkv.abi_version() == 1
+    assert pkv.abi_version() == 2
     with open("/proc/self/maps") as f:
         runtimes = {os.path.realpath(l.split()[-1]) for l in f if "libamdhip64" in l}
     assert len(runtimes) <= 1, runtimes
@@ -64,23 +64,34 @@ def test_decode_rejects_on_host_without_touching_a_device():
     f = lib.pkv_paged_attention_decode
     # Unsupported dtype pair: rejected before any HIP call.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.BF16, 1, None, 0, None)
+           pkv.F32, pkv.BF16, 1, None, 0, 0, None)
     assert st == 2
     # Non-positive scale.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.0, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, 0, None)
     assert st == 1
     # Null pointers with a non-empty batch.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, 0, None)
     assert st == 1
     # Too small a workspace (splits given, so no device query).
     p = ctypes.c_void_p(16)
-    st = f(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 16, None)
+    st = f(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 16, 0, None)
     assert st == 1 and b"workspace" in lib.pkv_last_error()
+    # The load-policy hint is 0 or 1.
+    for fn in (lib.pkv_paged_attention_decode, lib.pkv_paged_attention_split, lib.pkv_paged_attention_reduce):
+        st = fn(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 1 << 30, 2, None)
+        assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
+    for fn in (lib.pkv_paged_decode_step, lib.pkv_paged_decode_step_split):
+        st = fn(p, p, p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 1 << 30,
+                -1, None)
+        assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
+    st = lib.pkv_paged_attention_prefill(p, p, p, p, p, p, p, 1, 4, 8, 8, 64, 16, 64, 7, 4, 0.125, 1.0, 1.0,
+                                         pkv.F32, pkv.F32, 8, p, 1 << 30, 3, None)
+    assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
     # Empty batch is a no-op.
     st = f(None, None, None, None, None, None, 0, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, 0, None)
     assert st == 0
 
 
@@ -110,7 +121,7 @@ def test_misaligned_tensors_are_rejected_on_host():
     assert lib.pkv_copy_blocks(a, m, a, 2, 8, 128, 16, 10, pkv.BF16, None) == 1
     assert b"aligned" in lib.pkv_last_error()
     st = lib.pkv_paged_attention_decode(a, m, a, a, a, a, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-                                        pkv.F32, pkv.F32, 8, a, 1 << 30, None)
+                                        pkv.F32, pkv.F32, 8, a, 1 << 30, 0, None)
     assert st == 1 and b"aligned" in lib.pkv_last_error()
 
 
@@ -150,5 +161,5 @@ def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
     a = ctypes.c_void_p(256)
     # 64 queries x G 1 > 32 columns: the tile path.  2^28 blocks x 8 kv heads = 2^31.
     st = lib.pkv_paged_attention_prefill(a, a, a, a, a, a, a, 1, 64, 8, 8, 128, 16, 1 << 28, 8, 64,
-                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, None)
+                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, 0, None)
     assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()

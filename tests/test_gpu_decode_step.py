@@ -54,7 +54,7 @@ def _withheld(case):
     return k, v, to_dev(kn, wl.q_dtype), to_dev(vn, wl.q_dtype)
 
 
-def _step(case, k, v, kn, vn, num_splits=0, split_only=False):
+def _step(case, k, v, kn, vn, num_splits=0, split_only=False, shared_blocks=False):
     wl = case.wl
     q = to_dev(case.q, wl.q_dtype)
     out = torch.empty_like(q)
@@ -62,12 +62,12 @@ def _step(case, k, v, kn, vn, num_splits=0, split_only=False):
     lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
     if split_only:
         pkv.paged_decode_step_split(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
-                                    float(case.v_scale), num_splits=num_splits)
+                                    float(case.v_scale), num_splits=num_splits, shared_blocks=shared_blocks)
         pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, float(case.k_scale),
                                    float(case.v_scale), num_splits=num_splits)
     else:
         pkv.paged_decode_step(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
-                              float(case.v_scale), num_splits=num_splits)
+                              float(case.v_scale), num_splits=num_splits, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     return out
 
@@ -145,3 +145,19 @@ def test_decode_step_full_size(name):
     got = as_f64(out)
     assert np.all(np.isfinite(got))
     assert_close(got[seqs], oatt.decode_case(case, seqs), case.wl.kv_dtype, name)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
+@pytest.mark.parametrize("split_only", [False, True])
+def test_shared_block_loads_give_the_same_bits(name, split_only):
+    """The decode step with the shared-block load policy writes the same pool and the same
+    output bits as with non-temporal loads."""
+    require_gpu()
+    case = make_decode_case(CASES[name], 7)
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn, split_only=split_only)
+    k2, v2, kn2, vn2 = _withheld(case)
+    out2 = _step(case, k2, v2, kn2, vn2, split_only=split_only, shared_blocks=True)
+    assert raw_bytes(out) == raw_bytes(out2)
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k2))
+    assert np.array_equal(_pool_bytes(v), _pool_bytes(v2))

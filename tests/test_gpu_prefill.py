@@ -217,6 +217,17 @@ def _prefill_splits(case, k, v, splits):
     return out
 
 
+@pytest.mark.parametrize("name", ["bf16_g4_n8", "fp8_g4_n8", "f32_d64_g2_n16"])
+def test_few_query_path_shared_block_loads_give_the_same_bits(name):
+    require_gpu()
+    wl = FEW[name]
+    case = make_prefill_case(wl, 4)
+    k, v = pack(case)
+    a = prefill(case, k, v)
+    b = prefill(case, k, v, shared_blocks=True)
+    assert raw_bytes(a) == raw_bytes(b)
+
+
 def test_few_query_path_edges_and_placement():
     """n > L (the first queries see nothing), L = 0, n = 0, single tokens; and the same
     bytes when the blocks sit elsewhere in the pool."""

@@ -88,6 +88,23 @@ def test_shared_prefix_equals_unshared_copies_bitwise():
     assert raw_bytes(shared_out) == raw_bytes(out2)
 
 
+@pytest.mark.parametrize("num_splits", [0, 7])
+def test_shared_block_loads_give_the_same_bits(num_splits):
+    """The shared-block load policy (ordinary cached loads instead of non-temporal ones)
+    changes no bit of the output, on tables whose prefixes really are shared."""
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 5)
+    a, k, v, members = build_prefix_batch(case)
+    out, _, tables, lens = prefix_step(case, a, k, v, members, num_splits=num_splits, shared_blocks=True)
+    assert_close(as_f64(out), oatt.prefix_step_case(case), "bf16", "prefix step, shared-block loads")
+    qd = to_dev(case.q, case.wl.q_dtype)
+    again = torch.empty_like(qd)
+    pkv.paged_attention_decode(again, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               case.scale, num_splits=num_splits, shared_blocks=False)
+    torch.cuda.synchronize()
+    assert raw_bytes(again) == raw_bytes(out)
+
+
 @pytest.mark.timeout(600)
 def test_prefix_step_parity_full_size():
     """256 sequences in groups of 8 sharing a 1024-token prefix, lognormal lengths (median

@@ -834,8 +834,11 @@ def _prefix_step_bench(args, wl):
 
     bufs = [HostBuf(), HostBuf()]
     # Forked groups share their prefix blocks, which the allocator's reference counts show:
-    # the decode kernels then read K/V through the caches instead of streaming it.
-    shared = a.stats()["shared_blocks"] > 0
+    # the decode kernels read each sequence's shared leading blocks through the caches and
+    # stream the rest.  Taken once: later copy-on-write only shortens a shared prefix by its
+    # tail, and a stale count changes which loads are cached, never the result.
+    prefix_counts = a.shared_prefix_blocks(members)
+    shared = torch.from_numpy(prefix_counts).to(dev) if prefix_counts.any() else None
     tables0, lens0 = a.block_tables(members, max_blocks)
     tables_d = torch.from_numpy(tables0).to(dev)      # uploaded once; each step updates it
     lens_d = torch.from_numpy(lens0).to(dev)          # on the device (pkv_apply_append)
@@ -866,9 +869,10 @@ def _prefix_step_bench(args, wl):
         if ev is not None:
             pkv.set_launch_events(ev[0], ev[1])
         pkv.paged_decode_step_split(out, q, k_new, v_new, k, v, tables_d, lens_d, case.scale,
-                                    num_splits=args.num_splits, workspace=ws, shared_blocks=shared)
+                                    num_splits=args.num_splits, workspace=ws,
+                                    shared_prefix_blocks=shared)
         pkv.paged_attention_reduce(out, q, k, v, tables_d, lens_d, case.scale, num_splits=args.num_splits,
-                                   workspace=ws, shared_blocks=shared)
+                                   workspace=ws, shared_prefix_blocks=shared)
 
     # Load every kernel of the step once on a scratch pool, so that the first step's
     # timing (the one that copies every shared partial tail) holds no first-launch cost.
@@ -881,8 +885,8 @@ def _prefix_step_bench(args, wl):
     pkv.apply_append(torch.zeros((1, 1), dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
                      torch.full((1,), -1, dtype=torch.int64, device=dev), bs, 4)
     pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, workspace=ws,
-                                shared_blocks=shared)
-    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, workspace=ws, shared_blocks=shared)
+                                shared_prefix_blocks=shared)
+    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, workspace=ws, shared_prefix_blocks=shared)
     del sk, sv, one, st
     # The first step copies every shared partial tail; time it on its own.
     e_first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -964,7 +968,9 @@ def _prefix_step_bench(args, wl):
                           "merge_incl_gap": round(merge_us, 2),
                           "gpu_step": round(gpu_step_us, 2)}},
         "host_allocator_us_per_step": round(host_s[0] / args.steps * 1e6, 1),
-        "kv_loads": "cached (the tables share blocks)" if shared else "non-temporal",
+        "kv_loads": ("cached for each sequence's shared leading blocks, non-temporal for the rest"
+                     if shared is not None else "non-temporal"),
+        "shared_leading_blocks": int(prefix_counts.sum()),
         "first_step": {"copy_on_write_pairs": int(first_cow),
                        "gpu_us_copy_blocks_to_merge_end": round(first_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

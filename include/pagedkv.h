@@ -121,15 +121,19 @@ const char* pkv_last_error(void);
  *                   partial (max, sum, accumulator) of every sequence head whose work
  *                   spans more than one share and every sequence's offset in the work
  *                   list (written by the split pass, read by the reduce pass).
- *   shared_blocks   0 or 1, a load-policy hint; the output is bit-identical either way.
- *                   Sequences may share physical blocks (forks and common prefixes, shared
- *                   through reference counts: "What is PagedAttention?", glossary, "Share
- *                   Without Mutating State").  0: each block is read by one sequence of the
- *                   call, and K/V are streamed with the non-temporal hint, the faster way
- *                   on MI355X to read bytes used once.  1: the tables of this call reference
- *                   some blocks from several sequences; K/V then go through ordinary cached
- *                   loads, so that sequences reading a shared block at about the same time
- *                   can find it in L2 or the MALL.  Anything else is INVALID_ARG.
+ *   shared_prefix_blocks  device int32 [num_seqs] or NULL, a load-policy hint; the output
+ *                   bits do not depend on it.  Sequences may share physical blocks (forks
+ *                   and common prefixes, counted by reference: "What is PagedAttention?",
+ *                   glossary, "Share Without Mutating State"), and those are always leading
+ *                   blocks.  Entry s is how many leading logical blocks of sequence s other
+ *                   sequences of the call also read (pkv_alloc_shared_prefix_blocks).  K/V
+ *                   of those blocks go through ordinary cached loads, so that the sequences
+ *                   reading a shared block at about the same time can find it in L2 or the
+ *                   MALL.  Every other block, and every block when the pointer is NULL, is
+ *                   streamed with the non-temporal hint, the faster way on MI355X to read
+ *                   bytes used once.  Any value is safe: <= 0 means none, and a value past
+ *                   the sequence's blocks means all.  Must be 4-byte aligned.  (The decode
+ *                   step over an f32 cache with head_dim 128 always streams.)
  * Preconditions (not checked on the device): block table entries of used blocks lie in
  * [0, num_blocks) — an entry outside that range is read as a block of zeros, never out
  * of bounds; out does not alias any input.
@@ -155,7 +159,7 @@ pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_ca
                                       float scale, float k_scale, float v_scale,
                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                       void* workspace, size_t workspace_bytes,
-                                      int shared_blocks, void* stream);
+                                      const int32_t* shared_prefix_blocks, void* stream);
 
 /* Phase 1 alone: every wavefront streams its share of blocks with a running softmax;
  * sequence heads that fit in one share are written to `out` finished, the others leave
@@ -168,12 +172,12 @@ pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cac
                                      float scale, float k_scale, float v_scale,
                                      pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                      void* workspace, size_t workspace_bytes,
-                                     int shared_blocks, void* stream);
+                                     const int32_t* shared_prefix_blocks, void* stream);
 
 /* Phase 2 alone: merges the partials of split sequence heads (rescaling each by
  * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow
- * phase 1 on the same stream with identical arguments (shared_blocks is checked, and has
- * no effect here). */
+ * phase 1 on the same stream with identical arguments (shared_prefix_blocks has no effect
+ * here). */
 pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int num_seqs,
@@ -182,7 +186,7 @@ pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_ca
                                       float scale, float k_scale, float v_scale,
                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                       void* workspace, size_t workspace_bytes,
-                                      int shared_blocks, void* stream);
+                                      const int32_t* shared_prefix_blocks, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode step with append: the KV-cache write of each sequence's new token fused into the
@@ -212,7 +216,7 @@ pkv_status pkv_paged_decode_step(void* out, const void* q, const void* k_new, co
                                  int max_blocks_per_seq, float scale, float k_scale, float v_scale,
                                  pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                  void* workspace, size_t workspace_bytes,
-                                 int shared_blocks, void* stream);
+                                 const int32_t* shared_prefix_blocks, void* stream);
 
 /* Phase 1 of the decode step alone (append + split pass); phase 2 is
  * pkv_paged_attention_reduce with the same arguments and workspace. */
@@ -224,7 +228,7 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
                                        int max_blocks_per_seq, float scale, float k_scale,
                                        float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,
                                        int num_splits, void* workspace, size_t workspace_bytes,
-                                       int shared_blocks, void* stream);
+                                       const int32_t* shared_prefix_blocks, void* stream);
 
 /* Measurement aid: the next split pass launched on the calling thread (by any decode or
  * decode-step entry point), or the next multi-query attention kernel
@@ -262,8 +266,8 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *                  workspace.
  *   num_splits     shares for the few-query path (0 = a default like decode's); ignored
  *                  otherwise.
- *   shared_blocks  as for pkv_paged_attention_decode, on the few-query path; the tile path
- *                  always reads through the caches (its query tiles re-read K/V).
+ *   shared_prefix_blocks  as for pkv_paged_attention_decode, on the few-query path; the
+ *                  tile path always reads through the caches (its query tiles re-read K/V).
  *   workspace      device scratch of pkv_paged_attention_prefill_workspace_size bytes (0 on
  *                  the tile path, where it may be NULL); no initial contents needed.
  *   Every other argument as for pkv_paged_attention_decode.  out is written once per
@@ -285,7 +289,7 @@ pkv_status pkv_paged_attention_prefill(void* out, const void* q, const void* k_c
                                        float scale, float k_scale, float v_scale,
                                        pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                        void* workspace, size_t workspace_bytes,
-                                       int shared_blocks, void* stream);
+                                       const int32_t* shared_prefix_blocks, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * KV-cache write: stores T new tokens into their slots ("What is PagedAttention?",
@@ -425,6 +429,14 @@ pkv_status pkv_seq_free(pkv_alloc* a, int64_t seq_id);
  * allocators need the same block size; seq_id must not exist in `to`. */
 pkv_status pkv_seq_swap(pkv_alloc* from, pkv_alloc* to, int64_t seq_id, int32_t* pairs_out,
                         int* n_pairs_out);
+
+/* For each listed sequence, how many of its leading blocks have a reference count above 1,
+ * i.e. are also read by another sequence (a prefix shared by forking: "What is
+ * PagedAttention?", glossary, "Share Without Mutating State"), into host int32 out[n].  The
+ * attention calls take these counts as their shared_prefix_blocks hint.  UNKNOWN_SEQ if a
+ * sequence does not exist (nothing written). */
+pkv_status pkv_alloc_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int n,
+                                          int32_t* out);
 
 /* Writes block tables (host int32 [n][max_blocks], padded with -1) and lengths (host
  * int32 [n], nullable) for the listed sequences. */

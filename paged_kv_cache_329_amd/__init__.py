@@ -49,8 +49,8 @@ _lib = None
 _lock = threading.Lock()
 _c_int, _c_i64, _c_f, _c_p, _c_sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 _DECODE_ARGS = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_int, _c_p]
-_STEP_ARGS = [_c_p] * 8 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_int, _c_p]
+                _c_int, _c_f, _c_f, _c_f, _c_int, _c_int, _c_int, _c_p, _c_sz, _c_p, _c_p]
+_STEP_ARGS = [_c_p] * 8 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p, _c_p]
 _SIGNATURES = {
     "pkv_abi_version": ([], _c_int),
     "pkv_last_error": ([], ctypes.c_char_p),
@@ -63,7 +63,7 @@ _SIGNATURES = {
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
     "pkv_paged_decode_step_split": (_STEP_ARGS, _c_int),
-    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_int, _c_p],
+    "pkv_paged_attention_prefill": ([_c_p] * 7 + [_c_int] * 9 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p, _c_p],
                                     _c_int),
     "pkv_paged_attention_prefill_workspace_size": ([_c_int] * 9 + [ctypes.POINTER(_c_sz)], _c_int),
     "pkv_kv_cache_write": ([_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -91,6 +91,7 @@ _SIGNATURES = {
     "pkv_seq_append": ([_c_p, _c_p, _c_int, _c_p, _c_p, _c_p], _c_int),
     "pkv_seq_free": ([_c_p, _c_i64], _c_int),
     "pkv_alloc_block_tables": ([_c_p, _c_p, _c_int, _c_int, _c_p, _c_p], _c_int),
+    "pkv_alloc_shared_prefix_blocks": ([_c_p, _c_p, _c_int, _c_p], _c_int),
     "pkv_alloc_num_free": ([_c_p], _c_int),
     "pkv_alloc_num_blocks": ([_c_p], _c_int),
     "pkv_alloc_block_size": ([_c_p], _c_int),
@@ -216,8 +217,17 @@ def _workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
     return ws
 
 
+def _prefix_arg(t, n: int):
+    """Device address of a shared_prefix_blocks hint (contiguous int32 [n] on the device), or None."""
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.shape != (n,) or not t.is_contiguous():
+        raise ValueError("shared_prefix_blocks must be a contiguous int32 [num_seqs] tensor")
+    return _dev(t, "shared_prefix_blocks")
+
+
 def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
-                 v_scale, num_splits, workspace, stream, shared_blocks):
+                 v_scale, num_splits, workspace, stream, shared_prefix_blocks):
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
     B, Hq, D = q.shape
@@ -239,34 +249,38 @@ def _decode_call(fn_name, out, q, k_cache, v_cache, block_tables, context_lens, 
                                    float(scale), float(k_scale), float(v_scale), qd, kd,
                                    int(num_splits), _dev(workspace, "workspace"),
                                    workspace.numel() * workspace.element_size(),
-                                   int(bool(shared_blocks)), st))
+                                   _prefix_arg(shared_prefix_blocks, B), st))
     return out
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                            k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
-                           shared_blocks=False):
+                           shared_prefix_blocks=None):
     """Decode attention through block tables (both phases); see pkv_paged_attention_decode.
-    shared_blocks=True when the tables reference some blocks from several sequences (forks,
-    common prefixes): K/V then go through cached loads; the output is the same bits."""
+    shared_prefix_blocks: optional device int32 [num_seqs], the leading blocks of each sequence
+    that other sequences also read (BlockAllocator.shared_prefix_blocks); those are read
+    through the caches, the rest streamed.  The output bits do not depend on it."""
     return _decode_call("pkv_paged_attention_decode", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
+                      shared_prefix_blocks)
 
 
 def paged_attention_split(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                           k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
-                          shared_blocks=False):
+                          shared_prefix_blocks=None):
     """Phase 1 only (streams K/V, writes finished heads and partials)."""
     return _decode_call("pkv_paged_attention_split", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
+                      shared_prefix_blocks)
 
 
 def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                            k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
-                           shared_blocks=False):
+                           shared_prefix_blocks=None):
     """Phase 2 only (merges partials); same arguments and workspace as phase 1."""
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
-                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
+                        context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
+                      shared_prefix_blocks)
 
 
 def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -280,7 +294,7 @@ def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, 
 
 def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
                             max_query_len, scale, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None,
-                            stream=None, shared_blocks=False):
+                            stream=None, shared_prefix_blocks=None):
     """Causal multi-query attention (pkv_paged_attention_prefill): sequence s's queries are
     q rows query_start[s] .. query_start[s+1]-1, its last tokens, each attending to every
     token up to its own position.  q / out are [num_q_tokens, Hq, D].  A workspace is made
@@ -309,7 +323,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
                                              float(v_scale), qd, kd, int(num_splits),
                                              _dev(workspace, "workspace") if workspace is not None else None,
                                              workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                             int(bool(shared_blocks)), st))
+                                             _prefix_arg(shared_prefix_blocks, B), st))
     return out
 
 
@@ -326,7 +340,7 @@ def _mq_workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
 
 
 def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-               k_scale, v_scale, num_splits, workspace, stream, shared_blocks):
+               k_scale, v_scale, num_splits, workspace, stream, shared_prefix_blocks):
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
     B, Hq, D = q.shape
@@ -351,26 +365,28 @@ def _step_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, co
                                    float(scale), float(k_scale), float(v_scale), qd, kd,
                                    int(num_splits), _dev(workspace, "workspace"),
                                    workspace.numel() * workspace.element_size(),
-                                   int(bool(shared_blocks)), st))
+                                   _prefix_arg(shared_prefix_blocks, B), st))
     return out
 
 
 def paged_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
                       k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
-                      shared_blocks=False):
+                      shared_prefix_blocks=None):
     """Decode step with append (pkv_paged_decode_step): stores every sequence's new token
     (k_new / v_new [num_seqs, Hkv, D], q's dtype) at position context_lens[s] - 1, then
     attends over all context_lens[s] tokens; the store is fused into the split pass."""
     return _step_call("pkv_paged_decode_step", out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
+                      shared_prefix_blocks)
 
 
 def paged_decode_step_split(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
                             k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None,
-                            shared_blocks=False):
+                            shared_prefix_blocks=None):
     """Phase 1 of the decode step (append + split pass); phase 2 is paged_attention_reduce."""
     return _step_call("pkv_paged_decode_step_split", out, q, k_new, v_new, k_cache, v_cache, block_tables,
-                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream, shared_blocks)
+                      context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
+                      shared_prefix_blocks)
 
 
 def set_launch_events(start, stop):
@@ -646,6 +662,14 @@ class BlockAllocator:
     @property
     def num_seqs(self) -> int:
         return lib().pkv_alloc_num_seqs(self._h)
+
+    def shared_prefix_blocks(self, seq_ids) -> np.ndarray:
+        """Leading blocks of each sequence with a reference count above 1, int32 [n]
+        (pkv_alloc_shared_prefix_blocks): the attention calls' shared_prefix_blocks hint."""
+        ids = _np(seq_ids, np.int64)
+        out = np.empty(len(ids), dtype=np.int32)
+        _check(lib().pkv_alloc_shared_prefix_blocks(self._h, ids.ctypes.data, len(ids), out.ctypes.data))
+        return out
 
     def refcount(self, block: int) -> int:
         return lib().pkv_alloc_refcount(self._h, block)

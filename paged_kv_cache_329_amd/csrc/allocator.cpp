@@ -297,6 +297,24 @@ pkv_status pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, in
   return PKV_OK;
 }
 
+pkv_status pkv_alloc_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int n,
+                                          int32_t* out) {
+  if (!a) return fail(PKV_INVALID_ARG, "pkv_alloc_shared_prefix_blocks: null allocator");
+  if (n < 0 || (n > 0 && (!seq_ids || !out)))
+    return fail(PKV_INVALID_ARG, "pkv_alloc_shared_prefix_blocks: bad arguments");
+  for (int i = 0; i < n; ++i)
+    if (a->seqs.find(seq_ids[i]) == a->seqs.end())
+      return fail(PKV_UNKNOWN_SEQ, "pkv_alloc_shared_prefix_blocks: unknown sequence %lld",
+                  (long long)seq_ids[i]);
+  for (int i = 0; i < n; ++i) {
+    const auto& blocks = a->seqs.find(seq_ids[i])->second.blocks;
+    int32_t c = 0;
+    while (size_t(c) < blocks.size() && a->refcount[blocks[c]] > 1) ++c;
+    out[i] = c;
+  }
+  return PKV_OK;
+}
+
 int pkv_alloc_num_free(const pkv_alloc* a) { return a ? int(a->free_stack.size()) : -1; }
 int pkv_alloc_num_blocks(const pkv_alloc* a) { return a ? a->num_blocks : -1; }
 int pkv_alloc_block_size(const pkv_alloc* a) { return a ? a->block_size : -1; }

@@ -27,9 +27,10 @@
 //    So the softmax needs no data movement between the two products, and the per-head
 //    statistics live in the lanes of head l%16.  No LDS is used: every K/V byte is
 //    read by exactly one wave, straight into registers.
-//  * Loads: K/V chunks carry the non-temporal hint, unless the caller says that the block
-//    tables share blocks between sequences; then ordinary cached loads let the sequences
-//    that read a shared block at about the same time find it in L2 or the MALL.
+//  * Loads: K/V chunks carry the non-temporal hint, except in the leading blocks of a
+//    sequence that the caller marks as shared with other sequences of the call (forked
+//    prefixes); those go through ordinary cached loads, so that the sequences reading a
+//    shared block at about the same time find it in L2 or the MALL.
 //  * Running softmax (base 2): m = max(m, chunk max); rescale acc and sum by 2^(m_old-m);
 //    p = 2^(s - m).  The chunk max needs two cross-row shuffles (xor 16, xor 32).
 //  * Masking: tokens at or past the context length get s = -inf (select, so garbage or
@@ -84,6 +85,8 @@ struct DecodeArgs {
   uint8_t* k_cache_w;
   uint8_t* v_cache_w;
   float k_inv, v_inv;  // float32 1/k_scale, 1/v_scale (fp8 caches)
+  // [B] or null: leading logical blocks of sequence s that other sequences also read.
+  const int32_t* shared_prefix;
 };
 
 
@@ -328,7 +331,7 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = ml;
 }
 
-template <int KV, int D, int BS, int NSUB, bool APPEND, bool NT>
+template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX>
 __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
@@ -406,6 +409,8 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
     const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
     const int k0 = j0 * NSB;
     const int k1 = (std::min(j1 * BS, Lc) + 15) / 16;                   // sub-tiles [k0, k1)
+    // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
+    const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
 
     // q fragments of (s, g): lane (h, row) holds q[s, g*G+h, X*(4i+row) .. +X].
     uint4 qf[F::NLOAD * F::QCH];
@@ -467,12 +472,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i)
-          kf[u][i] = load_kv<NT>(kbase + off[u] + i * 1024);
+          kf[u][i] = load_kv(kbase + off[u] + i * 1024, MIX && k + u < ks);
 #pragma unroll
       for (int u = 0; u < NSUB; ++u)
 #pragma unroll
         for (int i = 0; i < F::NLOAD; ++i)
-          vf[u][i] = load_kv<NT>(vbase + off[u] + i * 1024);
+          vf[u][i] = load_kv(vbase + off[u] + i * 1024, MIX && k + u < ks);
       // Everything below is branch-free on the loaded data: a branch around QK or PV
       // would let the compiler sink the chunk loads into it and wait on them one by one.
       // Sub-tiles past the chunk's end and out-of-range blocks are masked instead: their
@@ -748,8 +753,8 @@ constexpr int subtiles_per_step() {
 using KernelFn = void (*)(DecodeArgs);
 
 struct KernelPair {
-  // Index [shared]: 0 streams K/V with the non-temporal hint, 1 uses cached loads (block
-  // tables that reference shared blocks).
+  // Index [mixed]: 0 streams all K/V with the non-temporal hint, 1 reads the leading
+  // blocks that a sequence shares through the caches.
   KernelFn split[2];         // plain decode
   KernelFn split_append[2];  // decode step that stores each sequence's appended token first
   KernelFn merge;            // one wave per (sequence, kv head, four query heads)
@@ -759,10 +764,13 @@ struct KernelPair {
 template <int KV, int D, int BS>
 KernelPair kernels_for() {
   constexpr int N = subtiles_per_step<KV, D>();
-  return {{paged_attention_split_kernel<KV, D, BS, N, false, true>,
-           paged_attention_split_kernel<KV, D, BS, N, false, false>},
-          {paged_attention_split_kernel<KV, D, BS, N, true, true>,
-           paged_attention_split_kernel<KV, D, BS, N, true, false>},
+  // The f32, D 128 decode step has no registers to spare for the per-sequence policy (it
+  // would spill), so it always streams.
+  constexpr bool kMix = !(KV == PKV_F32 && D == 128);
+  return {{paged_attention_split_kernel<KV, D, BS, N, false, false>,
+           paged_attention_split_kernel<KV, D, BS, N, false, true>},
+          {paged_attention_split_kernel<KV, D, BS, N, true, false>,
+           paged_attention_split_kernel<KV, D, BS, N, true, kMix>},
           paged_attention_merge_kernel<KV, D, BS, 1>,
           paged_attention_merge_kernel<KV, D, BS, kMergeWavesLong>};
 }
@@ -874,7 +882,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int bs,
                       int num_blocks, int max_blocks, float scale, float k_scale, float v_scale,
                       pkv_dtype qd, pkv_dtype kd, int num_splits, void* workspace,
-                      size_t workspace_bytes, int shared_blocks, void* stream) {
+                      size_t workspace_bytes, const int32_t* shared_prefix, void* stream) {
   const bool append = k_new != nullptr || v_new != nullptr;
   pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
   if (st != PKV_OK) return st;
@@ -883,8 +891,6 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
       k_scale == INFINITY || v_scale == INFINITY)
     return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
-  if (shared_blocks != 0 && shared_blocks != 1)
-    return pkv::fail(PKV_INVALID_ARG, "%s: shared_blocks=%d must be 0 or 1", fn, shared_blocks);
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks > 0 && !block_tables))
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
@@ -892,6 +898,8 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     return pkv::fail(PKV_INVALID_ARG, "%s: k_new and v_new must both be given", fn);
   if (!pkv::aligned16({out, q, k_cache, v_cache, k_new, v_new, workspace}))
     return pkv::fail(PKV_INVALID_ARG, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(shared_prefix) % 4 != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: shared_prefix_blocks must be 4-byte aligned", fn);
   KernelPair kp;
   pick_kernels(kd, D, bs, &kp);
   int splits = 0;
@@ -935,10 +943,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.v_cache_w = static_cast<uint8_t*>(v_cache_w);
   a.k_inv = 1.0f / k_scale;
   a.v_inv = 1.0f / v_scale;
+  a.shared_prefix = shared_prefix;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {
     const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
-    KernelFn kfn = append ? kp.split_append[shared_blocks] : kp.split[shared_blocks];
+    const int mixed = shared_prefix != nullptr ? 1 : 0;
+    KernelFn kfn = append ? kp.split_append[mixed] : kp.split[mixed];
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       // The dispatch itself records the events, so they time the kernel alone.
@@ -1006,12 +1016,13 @@ pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_
       const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
       float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
-      int num_splits, void *workspace, size_t workspace_bytes, int shared_blocks, void *stream
+      int num_splits, void *workspace, size_t workspace_bytes, const int32_t *shared_prefix_blocks, \
+      void *stream
 #define PKV_DECODE_ARGS                                                                          \
   out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables, context_lens,     \
       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
       scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes,        \
-      shared_blocks, stream
+      shared_prefix_blocks, stream
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_decode", kBoth, PKV_DECODE_ARGS);
@@ -1028,12 +1039,13 @@ pkv_status pkv_paged_attention_reduce(PKV_DECODE_PARAMS) {
       const int32_t *block_tables, const int32_t *context_lens, int num_seqs, int num_q_heads,  \
       int num_kv_heads, int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,   \
       float scale, float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,          \
-      int num_splits, void *workspace, size_t workspace_bytes, int shared_blocks, void *stream
+      int num_splits, void *workspace, size_t workspace_bytes, const int32_t *shared_prefix_blocks, \
+      void *stream
 #define PKV_STEP_ARGS                                                                            \
   out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables, context_lens,         \
       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, \
       scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace, workspace_bytes,        \
-      shared_blocks, stream
+      shared_prefix_blocks, stream
 
 pkv_status pkv_paged_decode_step(PKV_STEP_PARAMS) {
   if (!k_new || !v_new) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step: null k_new / v_new");

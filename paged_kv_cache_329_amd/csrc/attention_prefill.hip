@@ -490,6 +490,7 @@ struct MqArgs {
   int coop;
   float qk_scale_log2;
   float v_scale;
+  const int32_t* shared_prefix;   // [B] or null: leading blocks other sequences also read
 };
 
 __device__ __forceinline__ int mq_len(const MqArgs& a, int s, int bs) {
@@ -560,7 +561,7 @@ __device__ __forceinline__ void store_mq_partial(const MqArgs& a, int64_t piece,
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * kMqCols + c) * 2) = ml;
 }
 
-template <int KV, int D, int BS, bool NT>
+template <int KV, int D, int BS, bool MIX>
 __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs a) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
@@ -639,6 +640,8 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     const int k0 = j0 * NSB;
     const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
 
+    // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
+    const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
     int q0, n;
     mq_queries(a, s, q0, n);
     // Column c = 16*ct + lane%16 is (query c / G, head c % G); query i sits at L - n + i.
@@ -689,9 +692,9 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
       uint4 kf[F::NLOAD], vf[F::NLOAD];
 #pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_kv<NT>(kbase + off + i * 1024);
+      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_kv(kbase + off + i * 1024, MIX && k < ks);
 #pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_kv<NT>(vbase + off + i * 1024);
+      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_kv(vbase + off + i * 1024, MIX && k < ks);
       const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
 #pragma unroll
       for (int i = 0; i < F::NLOAD; ++i) {
@@ -901,13 +904,13 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
 
 using MqFn = void (*)(MqArgs);
 struct MqPair {
-  MqFn split[2];   // [shared]: 0 streams K/V with the non-temporal hint, 1 uses cached loads
+  MqFn split[2];   // [mixed]: 0 streams all K/V non-temporally, 1 caches shared leading blocks
   MqFn merge;
 };
 
 template <int KV, int D, int BS>
 MqPair mq_kernels() {
-  return {{paged_attention_mq_split_kernel<KV, D, BS, true>, paged_attention_mq_split_kernel<KV, D, BS, false>},
+  return {{paged_attention_mq_split_kernel<KV, D, BS, false>, paged_attention_mq_split_kernel<KV, D, BS, true>},
           paged_attention_mq_merge_kernel<KV, D, BS>};
 }
 
@@ -1043,7 +1046,7 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     int num_q_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
     int max_blocks_per_seq, int max_query_len, float scale, float k_scale, float v_scale,
     pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits, void* workspace, size_t workspace_bytes,
-    int shared_blocks, void* stream) {
+    const int32_t* shared_prefix_blocks, void* stream) {
   const char* fn = "pkv_paged_attention_prefill";
   const int B = num_seqs, Hq = num_q_heads, Hkv = num_kv_heads;
   pkv_status cst = check_mq_shape(fn, B, num_q_tokens, max_query_len, Hq, Hkv, head_dim, block_size, q_dtype,
@@ -1055,8 +1058,8 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   if (!(scale > 0.f) || !(k_scale > 0.f) || !(v_scale > 0.f) || scale == INFINITY ||
       k_scale == INFINITY || v_scale == INFINITY)
     return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
-  if (shared_blocks != 0 && shared_blocks != 1)
-    return pkv::fail(PKV_INVALID_ARG, "%s: shared_blocks=%d must be 0 or 1", fn, shared_blocks);
+  if (reinterpret_cast<uintptr_t>(shared_prefix_blocks) % 4 != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: shared_prefix_blocks must be 4-byte aligned", fn);
   if (B == 0 || num_q_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !query_start ||
       (max_blocks_per_seq > 0 && !block_tables))
@@ -1105,16 +1108,18 @@ extern "C" pkv_status pkv_paged_attention_prefill(
     while (a.coop < kMqWaves && Hkv % (2 * a.coop) == 0 && a.splits >= 2 * a.coop) a.coop *= 2;
     a.qk_scale_log2 = scale * k_scale * kLog2e;
     a.v_scale = v_scale;
+    a.shared_prefix = shared_prefix_blocks;
+    const int mixed = shared_prefix_blocks != nullptr ? 1 : 0;
     const unsigned wgs = unsigned((int64_t(a.splits) + kMqWaves - 1) / kMqWaves);
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       void* kargs[] = {&a};
-      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kp.split[shared_blocks]), dim3(wgs),
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kp.split[mixed]), dim3(wgs),
                                         dim3(kMqWaves * 64),
                                         kargs, 0, hs, static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1), 0);
       if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: %s", fn, hipGetErrorString(e));
     } else {
-      hipLaunchKernelGGL(kp.split[shared_blocks], dim3(wgs), dim3(kMqWaves * 64), 0, hs, a);
+      hipLaunchKernelGGL(kp.split[mixed], dim3(wgs), dim3(kMqWaves * 64), 0, hs, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: split launch: %s", fn, hipGetErrorString(e));

@@ -48,19 +48,19 @@ struct KvTraits<PKV_FP8_E4M3FN> {
   static constexpr int QB = 2;
 };
 
-// A 16-byte K/V chunk.  NT: the block is read once per call, so the load carries the
-// non-temporal hint; on MI355X this lifts a random 4 KiB-chunk gather from about 5.9 to
-// 6.5 TB/s, because streaming data no longer displaces cache lines.  Without NT (blocks
-// shared by several sequences of the call) it is an ordinary cached load, so that the
-// sequences reading a shared block at about the same time can find it in L2 or the MALL.
-template <bool NT>
-__device__ __forceinline__ uint4 load_kv(const uint8_t* p) {
-  if constexpr (NT) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-  } else {
-    return *reinterpret_cast<const uint4*>(p);
-  }
+// A 16-byte K/V chunk of a block read once per call: the load carries the non-temporal
+// hint, which on MI355X lifts a random 4 KiB-chunk gather from about 5.9 to 6.5 TB/s,
+// because streaming data no longer displaces cache lines.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// A chunk of a block that several sequences of the call read (a shared prefix): an ordinary
+// cached load, so that the sequences reading it at about the same time can find it in L2 or
+// the MALL.  `shared` is wave-uniform.
+__device__ __forceinline__ uint4 load_kv(const uint8_t* p, bool shared) {
+  return shared ? *reinterpret_cast<const uint4*>(p) : load_stream(p);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {

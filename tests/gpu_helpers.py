@@ -62,7 +62,7 @@ def pack(case, tables=None, poison=True):
     return k, v
 
 
-def decode(case, k, v, tables=None, num_splits=0, q=None, lengths=None, shared_blocks=False):
+def decode(case, k, v, tables=None, num_splits=0, q=None, lengths=None, shared_prefix_blocks=None):
     wl = case.wl
     tables = case.block_tables if tables is None else tables
     lengths = case.lengths if lengths is None else lengths
@@ -71,9 +71,16 @@ def decode(case, k, v, tables=None, num_splits=0, q=None, lengths=None, shared_b
     pkv.paged_attention_decode(out, qd, k, v, torch.from_numpy(np.ascontiguousarray(tables, np.int32)).cuda(),
                                torch.from_numpy(np.asarray(lengths, np.int32)).cuda(), case.scale,
                                float(case.k_scale), float(case.v_scale), num_splits=num_splits,
-                               shared_blocks=shared_blocks)
+                               shared_prefix_blocks=_hint(shared_prefix_blocks))
     torch.cuda.synchronize()
     return out
+
+
+def _hint(counts):
+    """A host array of shared leading-block counts as the device int32 tensor the calls take."""
+    if counts is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(counts, dtype=np.int32)).cuda()
 
 
 def raw_bytes(t: torch.Tensor) -> bytes:
@@ -139,7 +146,7 @@ def build_prefix_batch(case, poison=True):
     return a, k, v, list(range(wl.batch))
 
 
-def prefix_step(case, a, k, v, members, num_splits=0, shared_blocks=False):
+def prefix_step(case, a, k, v, members, num_splits=0, shared_prefix=False):
     """One continuous-batching step: append a token to every member (allocator), copy the
     shared partial tails it reports (copy_blocks), write the new tokens (kv_cache_write),
     then decode.  Returns (out, cow pairs, block tables, lengths)."""
@@ -153,13 +160,14 @@ def prefix_step(case, a, k, v, members, num_splits=0, shared_blocks=False):
     qd = to_dev(case.q, wl.q_dtype)
     out = torch.empty_like(qd)
     pkv.paged_attention_decode(out, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                               case.scale, num_splits=num_splits, shared_blocks=shared_blocks)
+                               case.scale, num_splits=num_splits,
+                               shared_prefix_blocks=_hint(a.shared_prefix_blocks(members)) if shared_prefix else None)
     torch.cuda.synchronize()
     return out, cows, tables, lens
 
 
 def prefill(case, k, v, tables=None, lengths=None, query_start=None, q=None, max_query_len=None,
-            shared_blocks=False):
+            shared_prefix_blocks=None):
     """Multi-query attention of a PrefillCase through pkv.paged_attention_prefill."""
     wl = case.wl
     tables = case.block_tables if tables is None else tables
@@ -172,6 +180,7 @@ def prefill(case, k, v, tables=None, lengths=None, query_start=None, q=None, max
     pkv.paged_attention_prefill(out, qd, k, v, torch.from_numpy(np.ascontiguousarray(tables, np.int32)).cuda(),
                                 torch.from_numpy(np.asarray(lengths, np.int32)).cuda(),
                                 torch.from_numpy(np.asarray(qs, np.int32)).cuda(), max_query_len,
-                                case.scale, float(case.k_scale), float(case.v_scale), shared_blocks=shared_blocks)
+                                case.scale, float(case.k_scale), float(case.v_scale),
+                                shared_prefix_blocks=_hint(shared_prefix_blocks))
     torch.cuda.synchronize()
     return out

@@ -64,34 +64,35 @@ def test_decode_rejects_on_host_without_touching_a_device():
     f = lib.pkv_paged_attention_decode
     # Unsupported dtype pair: rejected before any HIP call.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.BF16, 1, None, 0, 0, None)
+           pkv.F32, pkv.BF16, 1, None, 0, None, None)
     assert st == 2
     # Non-positive scale.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.0, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, None, None)
     assert st == 1
     # Null pointers with a non-empty batch.
     st = f(None, None, None, None, None, None, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, None, None)
     assert st == 1
     # Too small a workspace (splits given, so no device query).
     p = ctypes.c_void_p(16)
-    st = f(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 16, 0, None)
+    st = f(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 16, None, None)
     assert st == 1 and b"workspace" in lib.pkv_last_error()
-    # The load-policy hint is 0 or 1.
+    # The shared-prefix hint is an int32 array: a misaligned pointer is rejected.
+    odd = ctypes.c_void_p(18)
     for fn in (lib.pkv_paged_attention_decode, lib.pkv_paged_attention_split, lib.pkv_paged_attention_reduce):
-        st = fn(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 1 << 30, 2, None)
-        assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
+        st = fn(p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 1 << 30, odd, None)
+        assert st == 1 and b"shared_prefix_blocks" in lib.pkv_last_error()
     for fn in (lib.pkv_paged_decode_step, lib.pkv_paged_decode_step_split):
         st = fn(p, p, p, p, p, p, p, p, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0, pkv.F32, pkv.F32, 8, p, 1 << 30,
-                -1, None)
-        assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
+                odd, None)
+        assert st == 1 and b"shared_prefix_blocks" in lib.pkv_last_error()
     st = lib.pkv_paged_attention_prefill(p, p, p, p, p, p, p, 1, 4, 8, 8, 64, 16, 64, 7, 4, 0.125, 1.0, 1.0,
-                                         pkv.F32, pkv.F32, 8, p, 1 << 30, 3, None)
-    assert st == 1 and b"shared_blocks" in lib.pkv_last_error()
+                                         pkv.F32, pkv.F32, 8, p, 1 << 30, odd, None)
+    assert st == 1 and b"shared_prefix_blocks" in lib.pkv_last_error()
     # Empty batch is a no-op.
     st = f(None, None, None, None, None, None, 0, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-           pkv.F32, pkv.F32, 1, None, 0, 0, None)
+           pkv.F32, pkv.F32, 1, None, 0, None, None)
     assert st == 0
 
 
@@ -121,7 +122,7 @@ def test_misaligned_tensors_are_rejected_on_host():
     assert lib.pkv_copy_blocks(a, m, a, 2, 8, 128, 16, 10, pkv.BF16, None) == 1
     assert b"aligned" in lib.pkv_last_error()
     st = lib.pkv_paged_attention_decode(a, m, a, a, a, a, 4, 8, 8, 64, 16, 64, 7, 0.125, 1.0, 1.0,
-                                        pkv.F32, pkv.F32, 8, a, 1 << 30, 0, None)
+                                        pkv.F32, pkv.F32, 8, a, 1 << 30, None, None)
     assert st == 1 and b"aligned" in lib.pkv_last_error()
 
 
@@ -161,5 +162,5 @@ def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
     a = ctypes.c_void_p(256)
     # 64 queries x G 1 > 32 columns: the tile path.  2^28 blocks x 8 kv heads = 2^31.
     st = lib.pkv_paged_attention_prefill(a, a, a, a, a, a, a, 1, 64, 8, 8, 128, 16, 1 << 28, 8, 64,
-                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, 0, None)
+                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, None, None)
     assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()

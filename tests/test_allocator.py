@@ -213,6 +213,27 @@ def test_copy_on_write_at_shared_partial_tail_matches_the_pages_rule():
     assert (t1[0, :2] == t0[0, :2]).all()
 
 
+def test_shared_prefix_blocks_counts_leading_blocks_held_by_several_sequences():
+    """Worked by hand: a 40-token root (blocks r0 r1 r2, 16-token blocks) forked at 40 and at
+    20 tokens; copy-on-write of the shared partial tail leaves the first fork with two shared
+    blocks; a sequence of its own shares none."""
+    a = pkv.BlockAllocator(12, 16)
+    a.seq_create(0, 40)
+    a.fork(0, 1, 40)          # shares r0 r1 r2
+    a.fork(0, 2, 20)          # shares r0 r1 (r1 partly: 20 tokens)
+    a.seq_create(3, 5)
+    assert a.shared_prefix_blocks([0, 1, 2, 3]).tolist() == [3, 3, 2, 0]
+    a.append([1])             # r2 is shared and partly filled: copied, so 1 keeps r0 r1
+    assert a.shared_prefix_blocks([0, 1, 2, 3]).tolist() == [2, 2, 2, 0]
+    a.free(2)                 # r1 is now held by 0 and 1 only; r0 by 0 and 1 as well
+    assert a.shared_prefix_blocks([1, 0]).tolist() == [2, 2]
+    a.free(1)
+    assert a.shared_prefix_blocks([0]).tolist() == [0]
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.shared_prefix_blocks([0, 99])
+    assert e.value.status_name == "UNKNOWN_SEQ"
+
+
 def test_invalid_create_arguments():
     with pytest.raises(pkv.PagedKVError):
         pkv.BlockAllocator(0, 16)

@@ -54,7 +54,7 @@ def _withheld(case):
     return k, v, to_dev(kn, wl.q_dtype), to_dev(vn, wl.q_dtype)
 
 
-def _step(case, k, v, kn, vn, num_splits=0, split_only=False, shared_blocks=False):
+def _step(case, k, v, kn, vn, num_splits=0, split_only=False, shared_prefix_blocks=None):
     wl = case.wl
     q = to_dev(case.q, wl.q_dtype)
     out = torch.empty_like(q)
@@ -62,12 +62,14 @@ def _step(case, k, v, kn, vn, num_splits=0, split_only=False, shared_blocks=Fals
     lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
     if split_only:
         pkv.paged_decode_step_split(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
-                                    float(case.v_scale), num_splits=num_splits, shared_blocks=shared_blocks)
+                                    float(case.v_scale), num_splits=num_splits,
+                                    shared_prefix_blocks=shared_prefix_blocks)
         pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, float(case.k_scale),
                                    float(case.v_scale), num_splits=num_splits)
     else:
         pkv.paged_decode_step(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
-                              float(case.v_scale), num_splits=num_splits, shared_blocks=shared_blocks)
+                              float(case.v_scale), num_splits=num_splits,
+                                    shared_prefix_blocks=shared_prefix_blocks)
     torch.cuda.synchronize()
     return out
 
@@ -150,14 +152,16 @@ def test_decode_step_full_size(name):
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
 @pytest.mark.parametrize("split_only", [False, True])
 def test_shared_block_loads_give_the_same_bits(name, split_only):
-    """The decode step with the shared-block load policy writes the same pool and the same
-    output bits as with non-temporal loads."""
+    """The decode step with cached loads for leading blocks (counts from -1 to past the
+    table) writes the same pool and the same output bits as with streamed loads."""
     require_gpu()
     case = make_decode_case(CASES[name], 7)
     k, v, kn, vn = _withheld(case)
     out = _step(case, k, v, kn, vn, split_only=split_only)
+    counts = np.random.default_rng(3).integers(-1, case.block_tables.shape[1] + 2, size=case.wl.batch)
     k2, v2, kn2, vn2 = _withheld(case)
-    out2 = _step(case, k2, v2, kn2, vn2, split_only=split_only, shared_blocks=True)
+    out2 = _step(case, k2, v2, kn2, vn2, split_only=split_only,
+                 shared_prefix_blocks=torch.from_numpy(counts.astype(np.int32)).cuda())
     assert raw_bytes(out) == raw_bytes(out2)
     assert np.array_equal(_pool_bytes(k), _pool_bytes(k2))
     assert np.array_equal(_pool_bytes(v), _pool_bytes(v2))

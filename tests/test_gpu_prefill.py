@@ -224,7 +224,8 @@ def test_few_query_path_shared_block_loads_give_the_same_bits(name):
     case = make_prefill_case(wl, 4)
     k, v = pack(case)
     a = prefill(case, k, v)
-    b = prefill(case, k, v, shared_blocks=True)
+    counts = np.random.default_rng(5).integers(-1, case.block_tables.shape[1] + 2, size=wl.batch)
+    b = prefill(case, k, v, shared_prefix_blocks=counts)
     assert raw_bytes(a) == raw_bytes(b)
 
 

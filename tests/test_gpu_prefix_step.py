@@ -90,19 +90,24 @@ def test_shared_prefix_equals_unshared_copies_bitwise():
 
 @pytest.mark.parametrize("num_splits", [0, 7])
 def test_shared_block_loads_give_the_same_bits(num_splits):
-    """The shared-block load policy (ordinary cached loads instead of non-temporal ones)
-    changes no bit of the output, on tables whose prefixes really are shared."""
+    """Cached loads for the shared leading blocks (the allocator's counts), for every block,
+    or for none change no bit of the output, on tables whose prefixes really are shared."""
     require_gpu()
     case = make_prefix_step_case(SMALL, 5)
     a, k, v, members = build_prefix_batch(case)
-    out, _, tables, lens = prefix_step(case, a, k, v, members, num_splits=num_splits, shared_blocks=True)
+    out, _, tables, lens = prefix_step(case, a, k, v, members, num_splits=num_splits, shared_prefix=True)
     assert_close(as_f64(out), oatt.prefix_step_case(case), "bf16", "prefix step, shared-block loads")
+    counts = a.shared_prefix_blocks(members)
+    assert counts.max() > 0 and counts.min() >= 0
     qd = to_dev(case.q, case.wl.q_dtype)
-    again = torch.empty_like(qd)
-    pkv.paged_attention_decode(again, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                               case.scale, num_splits=num_splits, shared_blocks=False)
-    torch.cuda.synchronize()
-    assert raw_bytes(again) == raw_bytes(out)
+    for hint in (None, counts, np.full(len(members), 1 << 20), np.full(len(members), -3)):
+        again = torch.empty_like(qd)
+        pkv.paged_attention_decode(again, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                   case.scale, num_splits=num_splits,
+                                   shared_prefix_blocks=None if hint is None else
+                                   torch.from_numpy(np.asarray(hint, np.int32)).cuda())
+        torch.cuda.synchronize()
+        assert raw_bytes(again) == raw_bytes(out)
 
 
 @pytest.mark.timeout(600)

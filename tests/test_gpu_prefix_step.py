@@ -119,8 +119,18 @@ def test_prefix_step_parity_full_size():
     case = make_prefix_step_case(FULL, 0)
     log(f"prefix step full size: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks")
     a, k, v, members = build_prefix_batch(case)
-    out, cows, _, lens = prefix_step(case, a, k, v, members)
+    out, cows, tables, lens = prefix_step(case, a, k, v, members)
     assert len(cows) == _expected_cow(case)
+    # The benchmark reads each sequence's shared leading blocks through the caches: the
+    # same bits.
+    counts = a.shared_prefix_blocks(members)
+    assert counts.min() >= 1
+    qd = to_dev(case.q, case.wl.q_dtype)
+    hinted = torch.empty_like(qd)
+    pkv.paged_attention_decode(hinted, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                               case.scale, shared_prefix_blocks=torch.from_numpy(counts).cuda())
+    torch.cuda.synchronize()
+    assert raw_bytes(hinted) == raw_bytes(out)
     L = case.lengths
     cow_seq = np.flatnonzero((L <= 1024) & (L % 16 != 0))
     long_seq = np.argsort(L)[-3:]

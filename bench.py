@@ -884,9 +884,10 @@ def _prefix_step_bench(args, wl):
     pkv.copy_blocks(sk, sv, torch.tensor([[0, 1]], dtype=torch.int32, device=dev), D)
     pkv.apply_append(torch.zeros((1, 1), dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
                      torch.full((1,), -1, dtype=torch.int64, device=dev), bs, 4)
-    pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, workspace=ws,
-                                shared_prefix_blocks=shared)
-    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, workspace=ws, shared_prefix_blocks=shared)
+    pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, num_splits=args.num_splits,
+                                workspace=ws, shared_prefix_blocks=shared)
+    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, num_splits=args.num_splits, workspace=ws,
+                               shared_prefix_blocks=shared)
     del sk, sv, one, st
     # The first step copies every shared partial tail; time it on its own.
     e_first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

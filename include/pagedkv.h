@@ -110,14 +110,16 @@ const char* pkv_last_error(void);
  *   context_lens    int32 [num_seqs], 0 <= context_lens[s] <= max_blocks_per_seq * bs
  *                   (larger values are clamped to that bound).
  *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
- *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits.
+ *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits,
+ *                   or twice that when shared_prefix_blocks is given (measured faster then).
  *                   The kv heads are grouped c = 4, 2 or 1 at a time (the largest that
  *                   divides Hkv and is at most num_splits), and the (sequence, head group,
  *                   block) list is cut into num_splits / c equal shares, each walked by c
  *                   waves side by side, one kv head each.  Results depend only on the
  *                   split count and Hkv, not on the physical block numbering.
  *   workspace       device scratch of at least pkv_paged_attention_workspace_size()
- *                   bytes, owned by the caller, no initial contents required; holds the
+ *                   bytes (with num_splits = 0 that size covers both defaults), owned by
+ *                   the caller, no initial contents required; holds the
  *                   partial (max, sum, accumulator) of every sequence head whose work
  *                   spans more than one share and every sequence's offset in the work
  *                   list (written by the split pass, read by the reduce pass).
@@ -143,10 +145,11 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
                                               pkv_dtype kv_dtype, int num_splits,
                                               size_t* bytes /* host, out */);
 
-/* The split count used when num_splits = 0: one share per wave of 2 workgroups (of 4 waves)
- * per CU for f32 / bf16 caches and 4 for fp8 caches (the fastest counts measured on
- * MI355X), capped by what the current device keeps resident of the plain and the appending
- * split kernels (queried once per device and cached). */
+/* The split count used when num_splits = 0 and shared_prefix_blocks is NULL: one share per
+ * wave of 2 workgroups (of 4 waves) per CU for f32 / bf16 caches and 4 for fp8 caches (the
+ * fastest counts measured on MI355X), capped by what the current device keeps resident of
+ * the plain and the appending split kernels (queried once per device and cached).  Calls
+ * given shared_prefix_blocks use twice this count. */
 pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_dtype q_dtype,
                                               pkv_dtype kv_dtype, int* splits /* host, out */);
 

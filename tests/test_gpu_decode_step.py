@@ -65,11 +65,12 @@ def _step(case, k, v, kn, vn, num_splits=0, split_only=False, shared_prefix_bloc
                                     float(case.v_scale), num_splits=num_splits,
                                     shared_prefix_blocks=shared_prefix_blocks)
         pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, float(case.k_scale),
-                                   float(case.v_scale), num_splits=num_splits)
+                                   float(case.v_scale), num_splits=num_splits,
+                                   shared_prefix_blocks=shared_prefix_blocks)
     else:
         pkv.paged_decode_step(out, q, kn, vn, k, v, tables, lens, case.scale, float(case.k_scale),
                               float(case.v_scale), num_splits=num_splits,
-                                    shared_prefix_blocks=shared_prefix_blocks)
+                              shared_prefix_blocks=shared_prefix_blocks)
     torch.cuda.synchronize()
     return out
 
@@ -157,11 +158,16 @@ def test_shared_block_loads_give_the_same_bits(name, split_only):
     require_gpu()
     case = make_decode_case(CASES[name], 7)
     k, v, kn, vn = _withheld(case)
-    out = _step(case, k, v, kn, vn, split_only=split_only)
+    out = _step(case, k, v, kn, vn, num_splits=1000, split_only=split_only)
     counts = np.random.default_rng(3).integers(-1, case.block_tables.shape[1] + 2, size=case.wl.batch)
+    hint = torch.from_numpy(counts.astype(np.int32)).cuda()
     k2, v2, kn2, vn2 = _withheld(case)
-    out2 = _step(case, k2, v2, kn2, vn2, split_only=split_only,
-                 shared_prefix_blocks=torch.from_numpy(counts.astype(np.int32)).cuda())
+    out2 = _step(case, k2, v2, kn2, vn2, num_splits=1000, split_only=split_only, shared_prefix_blocks=hint)
     assert raw_bytes(out) == raw_bytes(out2)
     assert np.array_equal(_pool_bytes(k), _pool_bytes(k2))
     assert np.array_equal(_pool_bytes(v), _pool_bytes(v2))
+    # At the default split count the hinted call takes twice as many shares: the oracle's result.
+    k3, v3, kn3, vn3 = _withheld(case)
+    out3 = _step(case, k3, v3, kn3, vn3, split_only=split_only, shared_prefix_blocks=hint)
+    assert_close(as_f64(out3), oatt.decode_case(case), case.wl.kv_dtype, f"{name} hinted default")
+    assert np.array_equal(_pool_bytes(k3), _pool_bytes(k))

@@ -179,8 +179,9 @@ pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cac
 
 /* Phase 2 alone: merges the partials of split sequence heads (rescaling each by
  * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow
- * phase 1 on the same stream with identical arguments (shared_prefix_blocks has no effect
- * here). */
+ * phase 1 on the same stream with identical arguments, shared_prefix_blocks included (with
+ * num_splits = 0 it sets the split count).  Offsets in the workspace that no such phase 1
+ * writes are ignored, so a mismatch gives a wrong result but no read outside the workspace. */
 pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int num_seqs,

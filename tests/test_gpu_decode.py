@@ -164,3 +164,15 @@ def test_unpoisoned_pool_gives_the_same_bits():
     a = raw_bytes(decode(case, k, v))
     b = raw_bytes(decode(case, k0, v0))
     assert a == b
+
+
+def test_default_workspace_covers_the_shared_prefix_default():
+    """num_splits = 0: calls given shared-prefix counts use twice the default split count,
+    and the default workspace size is enough for them."""
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    for kd, bs in ((pkv.BF16, 16), (pkv.FP8_E4M3FN, 32)):
+        d = pkv.paged_attention_default_splits(128, bs, pkv.BF16, kd)
+        ws0 = pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, 0)
+        assert ws0 == pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, 2 * d)
+        assert ws0 > pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, d)

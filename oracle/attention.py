@@ -60,7 +60,7 @@ def kv_to_f64(x: np.ndarray, kv_dtype: str, scale=1.0) -> np.ndarray:
     if kv_dtype == "bf16":
         return codecs.bf16_to_f64(x)
     if kv_dtype == "fp8_e4m3fn":
-        codes = codecs.quantize_bf16_to_e4m3fn(x, codecs.inverse_scale(scale))
+        codes = codecs.bf16_to_e4m3fn_table(codecs.inverse_scale(scale))[np.asarray(x, dtype=np.uint16)]
         return codecs.e4m3fn_to_f64(codes) * np.float64(np.float32(scale))
     raise ValueError(kv_dtype)
 

@@ -80,3 +80,18 @@ def quantize_e4m3fn(x_f32: np.ndarray, inv_scale) -> np.ndarray:
 def quantize_bf16_to_e4m3fn(bits: np.ndarray, inv_scale) -> np.ndarray:
     """bf16-stored values -> e4m3fn codes (the bf16 -> float32 step is exact)."""
     return quantize_e4m3fn(bf16_to_f32(bits), inv_scale)
+
+
+_BF16_TO_E4M3FN = {}
+
+
+def bf16_to_e4m3fn_table(inv_scale) -> np.ndarray:
+    """``quantize_bf16_to_e4m3fn`` evaluated once for each of the 2^16 bf16 bit patterns (a
+    uint8 table indexed by the bits): a bf16 input has only that many values, so looking its
+    code up gives the quantiser's own result without searching the grid per element."""
+    key = np.float32(inv_scale).tobytes()
+    if key not in _BF16_TO_E4M3FN:
+        with np.errstate(over="ignore", invalid="ignore"):   # the table spans inf and NaN inputs too
+            _BF16_TO_E4M3FN[key] = quantize_bf16_to_e4m3fn(
+                np.arange(1 << 16, dtype=np.uint32).astype(np.uint16), inv_scale)
+    return _BF16_TO_E4M3FN[key]

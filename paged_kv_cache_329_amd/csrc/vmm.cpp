@@ -87,7 +87,21 @@ char* slice(const pkv_vmm* v, int pool, int seq) {
   return static_cast<char*>(v->va[pool]) + v->base_bytes + size_t(seq) * v->slice_bytes;
 }
 
+// Waits for all work on the pool's device, so that no kernel still in flight reads pages
+// about to be unmapped (an unmapped address faults the GPU).  The caller's current device is
+// kept.
+hipError_t drain(const pkv_vmm* v) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != v->device && (e = hipSetDevice(v->device)) != hipSuccess) return e;
+  e = hipDeviceSynchronize();
+  if (cur != v->device) (void)hipSetDevice(cur);
+  return e;
+}
+
 void destroy(pkv_vmm* v) {
+  (void)drain(v);
   for (int s = 0; s < int(v->mapped.size()); ++s) {
     auto& hs = v->mapped[s];
     const size_t n = hs.size() / 2;
@@ -222,6 +236,10 @@ pkv_status pkv_vmm_release(pkv_vmm* v, int seq) {
   if (seq < 0 || seq >= v->max_seqs) return fail(PKV_INVALID_ARG, "pkv_vmm_release: seq=%d", seq);
   auto& hs = v->mapped[seq];
   const size_t n = hs.size() / 2;
+  if (n == 0) return PKV_OK;
+  const hipError_t e = drain(v);
+  if (e != hipSuccess)
+    return fail(PKV_HIP_ERROR, "pkv_vmm_release: synchronising the device: %s", hipGetErrorString(e));
   for (size_t g = 0; g < n; ++g) {
     unmap_granule(v, slice(v, 0, seq) + g * v->gran, hs[g]);
     unmap_granule(v, slice(v, 1, seq) + g * v->gran, hs[n + g]);

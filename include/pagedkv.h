@@ -110,19 +110,20 @@ const char* pkv_last_error(void);
  *   context_lens    int32 [num_seqs], 0 <= context_lens[s] <= max_blocks_per_seq * bs
  *                   (larger values are clamped to that bound).
  *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
- *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits,
- *                   or twice that when shared_prefix_blocks is given (measured faster then).
+ *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits
+ *                   (the same with or without shared_prefix_blocks).
  *                   The kv heads are grouped c = 4, 2 or 1 at a time (the largest that
  *                   divides Hkv and is at most num_splits), and the (sequence, head group,
  *                   block) list is cut into num_splits / c equal shares, each walked by c
  *                   waves side by side, one kv head each.  Results depend only on the
  *                   split count and Hkv, not on the physical block numbering.
  *   workspace       device scratch of at least pkv_paged_attention_workspace_size()
- *                   bytes (with num_splits = 0 that size covers both defaults), owned by
- *                   the caller, no initial contents required; holds the
- *                   partial (max, sum, accumulator) of every sequence head whose work
- *                   spans more than one share and every sequence's offset in the work
- *                   list (written by the split pass, read by the reduce pass).
+ *                   bytes, owned by the caller, no initial contents required.  It starts
+ *                   with a header of round_up(4 * (num_seqs + 4), 256) bytes: every sequence's
+ *                   offset in the work list and the split pass's own record of its share
+ *                   count and head grouping.  The partial (max, sum, accumulator) of every
+ *                   sequence head whose work spans more than one share follows.  The split
+ *                   pass writes all of it; the reduce pass reads it.
  *   shared_prefix_blocks  device int32 [num_seqs] or NULL, a load-policy hint; the output
  *                   bits do not depend on it.  Sequences may share physical blocks (forks
  *                   and common prefixes, counted by reference: "What is PagedAttention?",
@@ -145,11 +146,10 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
                                               pkv_dtype kv_dtype, int num_splits,
                                               size_t* bytes /* host, out */);
 
-/* The split count used when num_splits = 0 and shared_prefix_blocks is NULL: one share per
- * wave of 2 workgroups (of 4 waves) per CU for f32 / bf16 caches and 4 for fp8 caches (the
- * fastest counts measured on MI355X), capped by what the current device keeps resident of
- * the plain and the appending split kernels (queried once per device and cached).  Calls
- * given shared_prefix_blocks use twice this count. */
+/* The split count used when num_splits = 0: one share per wave of 2 workgroups (of 4 waves)
+ * per CU for f32 / bf16 caches and 4 for fp8 caches (the fastest counts measured on MI355X),
+ * capped by what the current device keeps resident of the plain and the appending split
+ * kernels (queried once per device and cached). */
 pkv_status pkv_paged_attention_default_splits(int head_dim, int block_size, pkv_dtype q_dtype,
                                               pkv_dtype kv_dtype, int* splits /* host, out */);
 
@@ -178,10 +178,16 @@ pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cac
                                      const int32_t* shared_prefix_blocks, void* stream);
 
 /* Phase 2 alone: merges the partials of split sequence heads (rescaling each by
- * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow
- * phase 1 on the same stream with identical arguments, shared_prefix_blocks included (with
- * num_splits = 0 it sets the split count).  Offsets in the workspace that no such phase 1
- * writes are ignored, so a mismatch gives a wrong result but no read outside the workspace. */
+ * exp(m_p - max m)) into `out` and writes zeros for empty sequences.  Must follow phase 1
+ * over the same sequences (out, q, tables, lengths, shapes) on the same stream and
+ * workspace.  It takes the share count and head grouping from the record phase 1 left in
+ * the workspace header, so whatever its own num_splits and shared_prefix_blocks, it merges
+ * exactly the partials phase 1 wrote, and it needs only the header to lie inside
+ * workspace_bytes.  Its num_splits only picks between two merge kernels that fold the
+ * partials in different orders: with phase 1's num_splits the bits equal those of
+ * pkv_paged_attention_decode, otherwise they may differ by rounding.  A header that no phase 1 over num_seqs sequences wrote, or
+ * one whose partials would lie outside workspace_bytes, is not followed: the heads this pass
+ * would merge are set to NaN, and nothing outside the workspace is read. */
 pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int num_seqs,
@@ -191,6 +197,31 @@ pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_ca
                                       pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits,
                                       void* workspace, size_t workspace_bytes,
                                       const int32_t* shared_prefix_blocks, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Decode attention over a contiguous per-sequence placement: the alternative to paging that
+ * keeps each sequence's K/V at consecutive addresses of a virtual range and maps physical
+ * pages as it grows ("What is PagedAttention?", glossary, "Frequently Asked Questions" and
+ * "Common Use Cases"; the pkv_vmm_* pool below provides such ranges).  The result is the
+ * attention of pkv_paged_attention_decode; only the addressing differs: logical block j of
+ * sequence s is pool block seq_first_block[s] + j of the pools at k_base / v_base (the pool
+ * layout above), so no block table is read.
+ *
+ *   seq_first_block  int32 [num_seqs] (device): each sequence's first pool block.  Blocks
+ *                    seq_first_block[s] .. + ceil(context_lens[s] / bs) - 1 must be mapped
+ *                    and inside [0, num_blocks); a block outside that range reads as zeros.
+ *   max_blocks_per_seq  blocks each sequence may span (its slice); lengths are clamped to
+ *                    max_blocks_per_seq * bs.
+ *   Every other argument as for pkv_paged_attention_decode (no shared-prefix counts); both
+ *   passes are enqueued, on the same workspace layout.
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_contiguous_attention_decode(void* out, const void* q, const void* k_base, const void* v_base,
+                                           const int32_t* seq_first_block, const int32_t* context_lens,
+                                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                           int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                                           float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                           int num_splits, void* workspace, size_t workspace_bytes,
+                                           void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Decode step with append: the KV-cache write of each sequence's new token fused into the
@@ -499,8 +530,10 @@ pkv_status pkv_build_slot_mapping(const int32_t* tables, const int32_t* lens, in
  *
  * pkv_vmm_reserve maps physical memory (page by page, K and V) so that blocks
  * [0, num_blocks) of seq's slice are backed; all-or-nothing.  pkv_vmm_release unmaps and
- * frees all of seq's pages.  Both synchronise with the device as the HIP virtual-memory
- * calls do; no kernel may read a slice beyond its mapped blocks.
+ * frees all of seq's pages, and pkv_vmm_destroy everything; both first wait for all work on
+ * the pool's device (hipDeviceSynchronize), so that no kernel still in flight reads an
+ * unmapped page (pkv_vmm_release returns PKV_HIP_ERROR, with nothing unmapped, if that wait
+ * fails).  No kernel may read a slice beyond its mapped blocks.
  *
  * Sequence seq's logical block j is pool block pkv_vmm_seq_first_block(seq) + j of the
  * pools at pkv_vmm_k_base / pkv_vmm_v_base, which hold pkv_vmm_num_blocks blocks (most of

@@ -26,6 +26,7 @@ __all__ = [
     "allocate_kv_pool", "paged_attention_workspace_size", "paged_attention_default_splits",
     "paged_attention_decode",
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
+    "contiguous_attention_decode",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
     "paged_attention_prefill", "paged_attention_prefill_workspace_size", "allocate_host_pool", "swap_blocks", "VmmPool",
@@ -59,6 +60,8 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_split": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
+    "pkv_contiguous_attention_decode": ([_c_p] * 6 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
+                                        _c_int),
     "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
     "pkv_set_launch_events": ([_c_p, _c_p], _c_int),
     "pkv_apply_append": ([_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p], _c_int),
@@ -281,6 +284,32 @@ def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens,
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
                         context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
                       shared_prefix_blocks)
+
+
+def contiguous_attention_decode(out, q, k_base, v_base, seq_first_block, context_lens, max_blocks_per_seq,
+                                scale, k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """Decode attention over contiguous per-sequence placement (pkv_contiguous_attention_decode):
+    logical block j of sequence s is pool block seq_first_block[s] + j; no block table."""
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    B, Hq, D = q.shape
+    NB, Hkv, bs = _pool_dims(k_base, D)
+    if v_base.shape != k_base.shape or v_base.dtype != k_base.dtype:
+        raise ValueError("v_base must match k_base")
+    if seq_first_block.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("seq_first_block and context_lens must be int32")
+    if seq_first_block.shape != (B,) or context_lens.shape != (B,):
+        raise ValueError("seq_first_block and context_lens must be [num_seqs]")
+    qd, kd = _dtype_code(q.dtype), _dtype_code(k_base.dtype)
+    st = _stream(stream)
+    if workspace is None:
+        workspace = _workspace(paged_attention_workspace_size(B, Hq, Hkv, D, bs, qd, kd, num_splits), q.device, st)
+    _check(lib().pkv_contiguous_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_base, "k_base"), _dev(v_base, "v_base"),
+        _dev(seq_first_block, "seq_first_block"), _dev(context_lens, "context_lens"), B, Hq, Hkv, D, bs, NB,
+        int(max_blocks_per_seq), float(scale), float(k_scale), float(v_scale), qd, kd, int(num_splits),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), st))
+    return out
 
 
 def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

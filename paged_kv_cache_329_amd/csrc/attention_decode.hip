@@ -61,6 +61,15 @@ constexpr int kWavesPerWG = 4;
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt to the 8 XCDs round-robin
 constexpr int kMaxGroup = 16;
 
+// Workspace layout: header (per-sequence work offsets and the split pass's record), partial
+// accumulators, partial (max, sum) pairs; each part rounded up to 256 bytes.
+__host__ __device__ constexpr int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
+__host__ __device__ constexpr int64_t header_bytes(int B) { return round256((int64_t(B) + 4) * 4); }
+__host__ __device__ constexpr int64_t acc_bytes(int splits, int G, int D) {
+  return round256(int64_t(splits) * 2 * G * D * 4);
+}
+__host__ __device__ constexpr int64_t ml_bytes(int splits, int G) { return round256(int64_t(splits) * 2 * G * 2 * 4); }
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -68,9 +77,16 @@ struct DecodeArgs {
   const uint8_t* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  // Workspace: a header at its start, then the partials.  The header is
+  //   ws_seq[0..B-1]  work offset of sequence s (head groups * blocks of the sequences before it)
+  //   ws_seq[B]       total work W
+  //   ws_seq[B+1..3]  the split pass's share count, head-group width and num_seqs,
+  // written by the split pass; the merge takes the layout of the partials from it, so it
+  // always reads them where the split pass that preceded it wrote them.
+  int* ws_seq;
   float* ws_acc;  // [splits*2][G][D]
   float* ws_ml;   // [splits*2][G][2]  (max in log2 units, sum)
-  int* ws_seq;    // [B+1]: Hkv * blocks of the sequences before s; [B] = total work W
+  int64_t ws_bytes;
   int B, Hkv, G, num_blocks, max_blocks, splits;
   // Waves that walk one share together, each on its own kv head of the same blocks: the
   // work list is (sequence, group of `coop` kv heads, block).  A power of two that divides
@@ -87,6 +103,9 @@ struct DecodeArgs {
   float k_inv, v_inv;  // float32 1/k_scale, 1/v_scale (fp8 caches)
   // [B] or null: leading logical blocks of sequence s that other sequences also read.
   const int32_t* shared_prefix;
+  // Contiguous placement (no block table): logical block j of sequence s is pool block
+  // seq_first_block[s] + j.
+  const int32_t* seq_first_block;
 };
 
 
@@ -331,8 +350,11 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
   if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = ml;
 }
 
-template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX>
+// CONTIG: the sequence's blocks are consecutive pool blocks from seq_first_block[s] on, so
+// a block's address is computed instead of looked up (no table loads).
+template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG = false>
 __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
+  static_assert(!(CONTIG && APPEND), "the contiguous placement has no decode step with append");
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;                  // cached elements per 16-byte chunk
@@ -367,7 +389,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       if (sq < a.B) a.ws_seq[sq] = base + incl - w;
       base += __builtin_amdgcn_readlane(incl, 63);
     }
-    if (lane == 0) a.ws_seq[a.B] = base;
+    if (lane == 0) {
+      a.ws_seq[a.B] = base;
+      a.ws_seq[a.B + 1] = a.splits;
+      a.ws_seq[a.B + 2] = a.coop;
+      a.ws_seq[a.B + 3] = a.B;
+    }
   }
   if (W == 0) return;
   // Share of this wave's group of `coop` consecutive waves, walked side by side on kv heads
@@ -428,9 +455,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 
     // The first window of block-table entries is requested together with q, so that both
     // arrive in one round trip.
-    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+    const int32_t* trow = CONTIG ? nullptr : a.block_tables + int64_t(s) * a.max_blocks;
     int tbase = k0 / NSB;
-    int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+    int tbl = -1;
+    int first = 0;
+    if constexpr (CONTIG) first = __builtin_amdgcn_readfirstlane(a.seq_first_block[s]);
+    else tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
     const bool ends_unit = APPEND && seg_end == unit_end;
     AppendRegs<KV, D> app;
     if constexpr (APPEND) {
@@ -448,7 +478,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
     for (int k = k0; k < k1; k += NSUB) {
       const int cnt = std::min(NSUB, k1 - k);
       const int jlast = (k + cnt - 1) / NSB;
-      if (k / NSB < tbase || jlast >= tbase + 64) {
+      if (!CONTIG && (k / NSB < tbase || jlast >= tbase + 64)) {
         tbase = k / NSB;
         const int jj = tbase + lane;
         tbl = jj < nb ? trow[jj] : -1;
@@ -464,9 +494,10 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 #pragma unroll
       for (int u = 0; u < NSUB; ++u) {
         const int ku = u < cnt ? k + u : k;
-        const int phys = __builtin_amdgcn_readlane(tbl, (ku / NSB - tbase) & 63);
-        bad[u] = unsigned(phys) >= unsigned(a.num_blocks);
-        off[u] = (bad[u] ? 0 : int64_t(phys) * block_stride) + (ku % NSB) * SUB_BYTES + lane * 16;
+        const int64_t phys = CONTIG ? int64_t(first) + ku / NSB
+                                    : int64_t(__builtin_amdgcn_readlane(tbl, (ku / NSB - tbase) & 63));
+        bad[u] = uint64_t(phys) >= uint64_t(a.num_blocks);
+        off[u] = (bad[u] ? 0 : phys * block_stride) + (ku % NSB) * SUB_BYTES + lane * 16;
       }
 #pragma unroll
       for (int u = 0; u < NSUB; ++u)
@@ -624,17 +655,34 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
   const bool head_ok = h_raw < a.G;
   const int h = head_ok ? h_raw : a.G - 1;   // idle lanes read a valid row and write nothing
   const int d0 = (lane & 15) * EPL;
+  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D + d0;
+  // The split pass's record: share count, head-group width, and where the partials lie.
   const int before = a.ws_seq[s];
   const int after = a.ws_seq[s + 1];
   const int W = a.ws_seq[a.B];
-  // The offsets come from a split pass with the same arguments.  Values that no such pass
-  // writes (a reduce called with another split count or hint) are not followed: every
-  // piece index below then stays inside this call's workspace.
-  if (before < 0 || after < before || W < after ||
-      int64_t(W) > int64_t(a.B) * (a.Hkv / a.coop) * a.max_blocks)
+  const int splits = a.ws_seq[a.B + 1];
+  const int C = a.ws_seq[a.B + 2];
+  const bool layout_ok = a.ws_seq[a.B + 3] == a.B && splits >= 1 && (C == 1 || C == 2 || C == 4) &&
+                         a.Hkv % C == 0 && splits >= C &&
+                         header_bytes(a.B) + acc_bytes(splits, a.G, D) + ml_bytes(splits, a.G) <= a.ws_bytes;
+  // A workspace no split pass over these sequences wrote is not followed (every piece index
+  // below then stays inside it): the heads of this wave read NaN instead, so the mistake
+  // shows in the output rather than passing as a plausible result.
+  if (!layout_ok || before < 0 || after < before || W < after ||
+      int64_t(W) > int64_t(a.B) * (a.Hkv / C) * a.max_blocks) {
+    if (wv == 0 && head_ok) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if constexpr (KV == PKV_F32) static_cast<float*>(a.out)[orow + e] = __builtin_nanf("");
+        else static_cast<uint16_t*>(a.out)[orow + e] = 0x7FC0u;
+      }
+    }
     return;
-  const int nb = (after - before) / (a.Hkv / a.coop);
-  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D + d0;
+  }
+  const float* ws_acc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.ws_seq) + header_bytes(a.B));
+  const float* ws_ml = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ws_acc) +
+                                                      acc_bytes(splits, a.G, D));
+  const int nb = (after - before) / (a.Hkv / C);
   auto write = [&](const float* v, float inv) {
     if (!head_ok) return;
     if constexpr (KV == PKV_F32) {
@@ -659,8 +707,8 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
     if (wv == 0) write(num, 0.f);
     return;
   }
-  const int nshare = std::min(a.splits / a.coop, W);
-  const int C = a.coop, sub = g % C;
+  const int nshare = std::min(splits / C, W);
+  const int sub = g % C;
   const int off = before + (g / C) * nb;
   const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
   if (wf == wl) return;
@@ -678,8 +726,8 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
       const int j = std::min(j0 + t, je - 1);
       const int64_t pc = j == 0 ? piece0 : ((wf + j) * C + sub) * 2;
       const int64_t r = pc * a.G + h;
-      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + r * 2);
-      const float4* px = reinterpret_cast<const float4*>(a.ws_acc + r * D + d0);
+      ml[t] = *reinterpret_cast<const float2*>(ws_ml + r * 2);
+      const float4* px = reinterpret_cast<const float4*>(ws_acc + r * D + d0);
 #pragma unroll
       for (int i = 0; i < EPL / 4; ++i) x[t][i] = px[i];
     }
@@ -764,6 +812,7 @@ struct KernelPair {
   // blocks that a sequence shares through the caches.
   KernelFn split[2];         // plain decode
   KernelFn split_append[2];  // decode step that stores each sequence's appended token first
+  KernelFn split_contig;     // plain decode over contiguous per-sequence placement
   KernelFn merge;            // one wave per (sequence, kv head, four query heads)
   KernelFn merge_long;       // kMergeWavesLong waves each, for units that span many shares
 };
@@ -778,6 +827,7 @@ KernelPair kernels_for() {
            paged_attention_split_kernel<KV, D, BS, N, false, true>},
           {paged_attention_split_kernel<KV, D, BS, N, true, false>,
            paged_attention_split_kernel<KV, D, BS, N, true, kMix>},
+          paged_attention_split_kernel<KV, D, BS, N, false, false, true>,
           paged_attention_merge_kernel<KV, D, BS, 1>,
           paged_attention_merge_kernel<KV, D, BS, kMergeWavesLong>};
 }
@@ -846,13 +896,12 @@ pkv_status check_shape(const char* fn, int B, int Hq, int Hkv, int D, int bs, pk
 
 // Default split count of a kernel variant: one share per wave of `target` waves per CU,
 // capped by what the plain and the appending split kernels can keep resident (the lower of
-// the two, so both entry points, and the merge that recomputes the shares, agree).  Measured
-// on MI355X: f32 / bf16 caches stream best with 8 waves (2 per SIMD) per CU, fp8 caches,
-// with more arithmetic per byte, with 16 where registers allow it.
+// the two, so that both entry points launch the same shares).  Measured on MI355X: f32 /
+// bf16 caches stream best with 8 waves (2 per SIMD) per CU, fp8 caches, with more
+// arithmetic per byte, with 16 where registers allow it.  The count depends on neither the
+// load policy nor shared_prefix_blocks, so the output bits do not either.
 pkv_status default_splits(const KernelPair& kp, pkv_dtype kv, int* splits) {
   int a = 0, b = 0, cus = 0;
-  // The streaming variants: the split count must not depend on the load policy, since the
-  // reduce pass recomputes the shares.
   pkv_status st = resident_wgs(kp.split[0], &a, &cus);
   if (st != PKV_OK) return st;
   if ((st = resident_wgs(kp.split_append[0], &b, &cus)) != PKV_OK) return st;
@@ -861,28 +910,17 @@ pkv_status default_splits(const KernelPair& kp, pkv_dtype kv, int* splits) {
   return PKV_OK;
 }
 
-// With shared leading blocks read through the caches, twice the default count measured
-// faster on MI355X (continuous batching over shared prefixes: 235.6 against 246.7 us per
-// step): shorter shares bring the members of a group to a shared block closer together in
-// time, so more of their repeated reads hit in L2 or the MALL.  Without sharing it is slower.
-pkv_status effective_splits(const KernelPair& kp, pkv_dtype kv, int requested, bool shared, int* splits) {
+pkv_status effective_splits(const KernelPair& kp, pkv_dtype kv, int requested, int* splits) {
   if (requested < 0) return pkv::fail(PKV_INVALID_ARG, "num_splits=%d must be >= 0", requested);
   if (requested > 0) {
     *splits = requested;
     return PKV_OK;
   }
-  pkv_status st = default_splits(kp, kv, splits);
-  if (st == PKV_OK && shared) *splits *= 2;
-  return st;
+  return default_splits(kp, kv, splits);
 }
 
-// Workspace: partial accumulators, partial (max, sum) pairs, per-sequence work offsets.
-size_t ws_acc_bytes(int splits, int G, int D) {
-  return ((size_t(splits) * 2 * G * D * sizeof(float) + 255) / 256) * 256;
-}
-size_t ws_ml_bytes(int splits, int G) { return ((size_t(splits) * 2 * G * 2 * sizeof(float) + 255) / 256) * 256; }
 size_t workspace_bytes_for(int splits, int B, int G, int D) {
-  return ws_acc_bytes(splits, G, D) + ws_ml_bytes(splits, G) + (size_t(B) + 1) * sizeof(int);
+  return size_t(header_bytes(B) + acc_bytes(splits, G, D) + ml_bytes(splits, G));
 }
 
 enum Phase { kBoth, kSplitOnly, kMergeOnly };
@@ -895,8 +933,10 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
                       const int32_t* context_lens, int B, int Hq, int Hkv, int D, int bs,
                       int num_blocks, int max_blocks, float scale, float k_scale, float v_scale,
                       pkv_dtype qd, pkv_dtype kd, int num_splits, void* workspace,
-                      size_t workspace_bytes, const int32_t* shared_prefix, void* stream) {
+                      size_t workspace_bytes, const int32_t* shared_prefix, void* stream,
+                      const int32_t* seq_first_block = nullptr) {
   const bool append = k_new != nullptr || v_new != nullptr;
+  const bool contig = seq_first_block != nullptr;
   pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
   if (st != PKV_OK) return st;
   if (num_blocks <= 0 || max_blocks < 0)
@@ -905,8 +945,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
       k_scale == INFINITY || v_scale == INFINITY)
     return pkv::fail(PKV_INVALID_ARG, "%s: scales must be positive and finite", fn);
   if (B == 0) return PKV_OK;
-  if (!out || !q || !k_cache || !v_cache || !context_lens || (max_blocks > 0 && !block_tables))
+  if (!out || !q || !k_cache || !v_cache || !context_lens || (!contig && max_blocks > 0 && !block_tables))
     return pkv::fail(PKV_INVALID_ARG, "%s: null pointer", fn);
+  if (contig && (append || shared_prefix))
+    return pkv::fail(PKV_INVALID_ARG, "%s: the contiguous placement takes no append or shared-prefix counts", fn);
+  if (reinterpret_cast<uintptr_t>(seq_first_block) % 4 != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: seq_first_block must be 4-byte aligned", fn);
   if (append && (!k_new || !v_new || !k_cache_w || !v_cache_w))
     return pkv::fail(PKV_INVALID_ARG, "%s: k_new and v_new must both be given", fn);
   if (!pkv::aligned16({out, q, k_cache, v_cache, k_new, v_new, workspace}))
@@ -916,9 +960,11 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   KernelPair kp;
   pick_kernels(kd, D, bs, &kp);
   int splits = 0;
-  if ((st = effective_splits(kp, kd, num_splits, shared_prefix != nullptr, &splits)) != PKV_OK) return st;
+  if ((st = effective_splits(kp, kd, num_splits, &splits)) != PKV_OK) return st;
   const int G = Hq / Hkv;
-  const size_t need = workspace_bytes_for(splits, B, G, D);
+  // The reduce pass takes the partials' layout from the header the split pass wrote, so it
+  // needs only the header to be addressable; the merge kernel checks the rest on the device.
+  const size_t need = phase == kMergeOnly ? size_t(header_bytes(B)) : workspace_bytes_for(splits, B, G, D);
   if (!workspace || workspace_bytes < need)
     return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn,
                      workspace_bytes, need);
@@ -934,10 +980,6 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.v_cache = static_cast<const uint8_t*>(v_cache);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws_acc = static_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ws_acc_bytes(splits, G, D));
-  a.ws_seq = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + ws_acc_bytes(splits, G, D) +
-                                    ws_ml_bytes(splits, G));
   a.B = B;
   a.Hkv = Hkv;
   a.G = G;
@@ -946,6 +988,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   // More shares than (sequence, kv head, block) triples would only launch idle waves; the
   // table width bounds the triples without reading the device-side lengths.
   a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * max_blocks)));
+  // The partials are laid out for the share count the kernels use, which the split pass
+  // records in the header and the merge reads back.
+  a.ws_seq = static_cast<int*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + header_bytes(B));
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.ws_acc) + acc_bytes(a.splits, G, D));
+  a.ws_bytes = int64_t(workspace_bytes);
   a.coop = 1;
   while (a.coop < kWavesPerWG && Hkv % (2 * a.coop) == 0 && a.splits >= 2 * a.coop) a.coop *= 2;
   a.qk_scale_log2 = scale * k_scale * kLog2e;
@@ -957,11 +1005,12 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.k_inv = 1.0f / k_scale;
   a.v_inv = 1.0f / v_scale;
   a.shared_prefix = shared_prefix;
+  a.seq_first_block = seq_first_block;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {
     const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
     const int mixed = shared_prefix != nullptr ? 1 : 0;
-    KernelFn kfn = append ? kp.split_append[mixed] : kp.split[mixed];
+    KernelFn kfn = contig ? kp.split_contig : append ? kp.split_append[mixed] : kp.split[mixed];
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       // The dispatch itself records the events, so they time the kernel alone.
@@ -1007,9 +1056,8 @@ pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int
   if (!bytes) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_attention_workspace_size: null output");
   KernelPair kp;
   pick_kernels(kv_dtype, head_dim, block_size, &kp);
-  // num_splits = 0: enough for the default with shared_prefix_blocks too (the larger one).
   int splits = 0;
-  if ((st = effective_splits(kp, kv_dtype, num_splits, true, &splits)) != PKV_OK) return st;
+  if ((st = effective_splits(kp, kv_dtype, num_splits, &splits)) != PKV_OK) return st;
   *bytes = workspace_bytes_for(splits, num_seqs, num_q_heads / num_kv_heads, head_dim);
   return PKV_OK;
 }
@@ -1046,6 +1094,21 @@ pkv_status pkv_paged_attention_split(PKV_DECODE_PARAMS) {
 }
 pkv_status pkv_paged_attention_reduce(PKV_DECODE_PARAMS) {
   return run_decode("pkv_paged_attention_reduce", kMergeOnly, PKV_DECODE_ARGS);
+}
+
+pkv_status pkv_contiguous_attention_decode(void* out, const void* q, const void* k_base, const void* v_base,
+                                           const int32_t* seq_first_block, const int32_t* context_lens,
+                                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                           int block_size, int num_blocks, int max_blocks_per_seq, float scale,
+                                           float k_scale, float v_scale, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                           int num_splits, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (num_seqs > 0 && !seq_first_block)
+    return pkv::fail(PKV_INVALID_ARG, "pkv_contiguous_attention_decode: null seq_first_block");
+  return run_decode("pkv_contiguous_attention_decode", kBoth, out, q, nullptr, nullptr, k_base, v_base, nullptr,
+                    nullptr, nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                    num_blocks, max_blocks_per_seq, scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits,
+                    workspace, workspace_bytes, nullptr, stream, seq_first_block);
 }
 
 #define PKV_STEP_PARAMS                                                                          \

@@ -164,3 +164,4 @@ def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
     st = lib.pkv_paged_attention_prefill(a, a, a, a, a, a, a, 1, 64, 8, 8, 128, 16, 1 << 28, 8, 64,
                                          0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, None, None)
     assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()
+

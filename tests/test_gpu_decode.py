@@ -6,11 +6,12 @@ fp32 max |d| <= 1e-5; bf16 and fp8 |d| <= 2e-2 + 1e-2 |ref| per element.
 """
 import numpy as np
 import pytest
+import torch
 
 from oracle import attention as oatt
 from synth import WORKLOADS, Workload, bf16_bits_from_f32, make_decode_case
 
-from gpu_helpers import as_f64, assert_close, decode, log, pack, raw_bytes, require_gpu
+from gpu_helpers import as_f64, assert_close, decode, log, pack, raw_bytes, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -166,13 +167,83 @@ def test_unpoisoned_pool_gives_the_same_bits():
     assert a == b
 
 
-def test_default_workspace_covers_the_shared_prefix_default():
-    """num_splits = 0: calls given shared-prefix counts use twice the default split count,
-    and the default workspace size is enough for them."""
+def test_default_split_count_does_not_depend_on_the_hint():
+    """num_splits = 0 picks the same split count with or without shared-prefix counts: the
+    default workspace is that of the default count, and a hinted call at the default gives
+    the same output bits as a plain one."""
     require_gpu()
     import paged_kv_cache_329_amd as pkv
     for kd, bs in ((pkv.BF16, 16), (pkv.FP8_E4M3FN, 32)):
         d = pkv.paged_attention_default_splits(128, bs, pkv.BF16, kd)
         ws0 = pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, 0)
-        assert ws0 == pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, 2 * d)
-        assert ws0 > pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, d)
+        assert ws0 == pkv.paged_attention_workspace_size(64, 32, 8, 128, bs, pkv.BF16, kd, d)
+    case = make_decode_case(SMALL["llama3_8b_bf16"], 4)
+    k, v = pack(case)
+    counts = np.random.default_rng(4).integers(-1, case.block_tables.shape[1] + 2, size=case.wl.batch)
+    assert raw_bytes(decode(case, k, v)) == raw_bytes(decode(case, k, v, shared_prefix_blocks=counts))
+
+
+def _split_then_reduce(case, k, v, split_kw, reduce_kw, ws):
+    import paged_kv_cache_329_amd as pkv
+    wl = case.wl
+    q = to_dev(case.q, wl.q_dtype)
+    out = torch.full_like(q, 7.0)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).cuda()
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
+    pkv.paged_attention_split(out, q, k, v, tables, lens, case.scale, workspace=ws, **split_kw)
+    pkv.paged_attention_reduce(out, q, k, v, tables, lens, case.scale, workspace=ws, **reduce_kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_reduce_follows_the_split_pass_record():
+    """The reduce pass takes the split count and head grouping from the header the split
+    pass wrote at the start of the workspace: a reduce given another num_splits or other
+    shared-prefix counts still merges what the split pass left (the oracle's result), and
+    with the split pass's num_splits gives the one-call decode's bits."""
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    case = make_decode_case(SMALL["llama3_8b_bf16"], 5)
+    k, v = pack(case)
+    wl = case.wl
+    ws = torch.zeros(pkv.paged_attention_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                        wl.block_size, pkv.BF16, pkv.BF16, 640),
+                     dtype=torch.uint8, device="cuda")
+    counts = torch.from_numpy(np.full(wl.batch, 2, np.int32)).cuda()
+    want = decode(case, k, v, num_splits=640)
+    ref = oatt.decode_case(case)
+    for split_kw, reduce_kw in (({"num_splits": 640}, {"num_splits": 640}),
+                                ({"num_splits": 640, "shared_prefix_blocks": counts}, {"num_splits": 640}),
+                                ({"num_splits": 640, "shared_prefix_blocks": counts}, {"num_splits": 0}),
+                                ({"num_splits": 640}, {"num_splits": 3, "shared_prefix_blocks": counts})):
+        got = _split_then_reduce(case, k, v, split_kw, reduce_kw, ws)
+        assert_close(as_f64(got), ref, wl.kv_dtype, f"split {split_kw} then reduce {reduce_kw}")
+        if reduce_kw["num_splits"] == 640:
+            # Same merge kernel as the one-call decode: the same bits.
+            assert raw_bytes(got) == raw_bytes(want), (split_kw, reduce_kw)
+        else:
+            # Another split count may pick the other merge variant (a different fold order):
+            # the same partials, merged within a bf16 rounding of the one-call result.
+            d = np.abs(as_f64(got) - as_f64(want))
+            assert np.all(d <= 2.0 ** -7 * np.abs(as_f64(want)) + 1e-6), (split_kw, reduce_kw, d.max())
+
+
+def test_reduce_without_a_split_pass_writes_nan():
+    """A reduce pass over a workspace that no split pass over these sequences wrote (here
+    zeroed) follows nothing in it and writes NaN into the heads it merges, so the mistake
+    shows; the sequences' other heads are untouched."""
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    case = make_decode_case(SMALL["llama3_8b_bf16"], 5)
+    k, v = pack(case)
+    wl = case.wl
+    q = to_dev(case.q, wl.q_dtype)
+    out = torch.zeros_like(q)
+    ws = torch.zeros(pkv.paged_attention_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                        wl.block_size, pkv.BF16, pkv.BF16, 640),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_attention_reduce(out, q, k, v, torch.from_numpy(np.ascontiguousarray(case.block_tables)).cuda(),
+                               torch.from_numpy(case.lengths.astype(np.int32)).cuda(), case.scale,
+                               num_splits=640, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()

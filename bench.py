@@ -83,17 +83,55 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_UNIT = ("HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, scaled by a plain copy "
+                "of known size)")
+
+
+def _set_blas_threads() -> int:
+    """Gives the oracle's BLAS every core this process may run on; returns that count."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(n)
+    except Exception:  # pragma: no cover
+        pass
+    return n
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _traffic_from_profile(args, kernel: str, workload: str, files):
+    """HBM bytes per launch from profiles/<kernel>__<workload>__hbm_traffic.json, reported only
+    while the kernel sources it was taken on are the current ones."""
+    path = args.traffic_json or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                              f"{kernel}__{workload}__hbm_traffic.json")
+    try:
+        with open(path) as f:
+            tj = json.load(f)
+        if tj.get("workload") == workload and tj.get("kernel_source_sha") == _kernel_sha(files):
+            return tj.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
 def _cpu_baseline(case, bytes_per_token, budget_s=10.0, max_passes=3):
     """The oracle, as it stands, on the batch's sequences in a seeded random order, one at a
     time, until about `budget_s` of host time or `max_passes` passes over the batch.
 
-    Returns (seconds, K/V bytes the oracle went through, sequences done, BLAS threads)."""
+    Returns (seconds, K/V bytes the oracle went through, sequences done, BLAS threads = the
+    cores this process may run on)."""
     from oracle import attention as oatt
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
+    blas_threads = _set_blas_threads()
     B = case.wl.batch
     order = np.random.default_rng(0).permutation(B)
     done_bytes, done_seqs = 0, 0
@@ -242,24 +280,14 @@ def main():
     value = kv_bytes / (us_per_step * 1e-6) / 1e9
     achieved = kv_bytes / (split_us * 1e-6) / 1e9
 
-    traffic = None
-    traffic_json = args.traffic_json or os.path.join(
-        os.path.dirname(os.path.abspath(__file__)), "profiles",
-        f"paged_attention_split__{wl.name}__hbm_traffic.json")
-    try:
-        with open(traffic_json) as f:
-            tj = json.load(f)
-        # Counters taken on another version of the kernel source say nothing about this one.
-        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha():
-            traffic = tj.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        traffic = None
+    traffic = _traffic_from_profile(args, "paged_attention_split", wl.name, ("attention_decode.hip", "attention_tile.h"))
 
     cpu = None
     if not args.no_cpu_baseline:
         _log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
         t_cpu, cpu_bytes, cpu_seqs, threads = _cpu_baseline(case, Hkv * D * 2 * eb)
         cpu = {"value": round(cpu_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "cpu_model": _cpu_model(),
                "sample": f"{cpu_seqs} sequences of the batch ({B} sequences, sum L = {sum_l}) in a seeded random "
                          f"order, up to 3 passes or about 10 s: {cpu_bytes / 1e9:.3f} GB of K/V in {t_cpu:.2f} s, "
                          f"fp64 numpy oracle incl. decoding K/V to fp64"}
@@ -290,8 +318,7 @@ def main():
         "host_metadata_us": round(host_meta_us, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "traffic_unit": "HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, "
-                                     "scaled by a plain copy of known size)",
+                     "traffic_unit": TRAFFIC_UNIT,
                      "algorithmic_bytes": kv_bytes, "kernel": "paged_attention_split_kernel (decode step with append)"},
         "cpu_baseline": cpu,
     }
@@ -409,26 +436,17 @@ def _multi_query_bench(args, wl):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes": kv_bytes}
     roof["kernel"] = "paged_attention_mq_split_kernel" if ws_bytes else "paged_attention_prefill_kernel"
     roof["path"] = path
-    roof["traffic_unit"] = ("HBM bytes read + written per launch (rocprofv3 FETCH_SIZE, WRITE_SIZE, scaled by a plain "
-                            "copy of known size)")
+    roof["traffic_unit"] = TRAFFIC_UNIT
     qb = 4 if wl.q_dtype == "f32" else 2
     roof["q_out_bytes"] = 2 * case.num_q_tokens * Hq * D * qb
-    try:
-        kname = "paged_attention_mq_split" if ws_bytes else "paged_attention_prefill"
-        tpath = args.traffic_json or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                                                  f"{kname}__{wl.name}__hbm_traffic.json")
-        with open(tpath) as f:
-            tj = json.load(f)
-        if tj.get("workload") == wl.name and tj.get("kernel_source_sha") == _kernel_sha(
-                ("attention_prefill.hip", "attention_tile.h")):
-            roof["traffic"] = tj.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
-        pass
+    roof["traffic"] = _traffic_from_profile(args, "paged_attention_mq_split" if ws_bytes else "paged_attention_prefill",
+                                            wl.name, ("attention_prefill.hip", "attention_tile.h"))
 
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import attention as oatt
         _log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
+        threads = _set_blas_threads()
         # Query rows spread evenly over the batch, in chunks, until about 10 s of oracle work.
         order = np.linspace(0, case.num_q_tokens - 1, min(case.num_q_tokens, 16384)).astype(np.int64)
         order = order[np.random.default_rng(0).permutation(len(order))]   # every chunk spans the batch
@@ -450,17 +468,13 @@ def _multi_query_bench(args, wl):
             P = int(case.lengths[s_]) - int(case.q_lens[s_]) + (r - int(qs[s_]))
             sample_keys += max(P + 1, 0)
         sflops = sample_keys * Hq * 4 * D
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = 1
         if mfma_bound:
             cval, cunit = sflops / t_cpu / 1e12, "TFLOP/s"
         else:
             # The sample's share of the batch's work, in the metric's bytes.
             cval, cunit = kv_bytes * (sample_keys / max(keys, 1)) / t_cpu / 1e9, "GB/s"
         cpu = {"value": round(cval, 6), "unit": cunit, "cores": threads, "kind": "oracle",
+               "cpu_model": _cpu_model(),
                "sample": f"{nrows} query rows drawn evenly over the batch ({sample_keys} keys in all, about 10 s), "
                          f"fp64 numpy oracle incl. decoding each touched sequence's K/V to fp64, {t_cpu:.1f} s"}
 
@@ -783,6 +797,7 @@ def _prefix_step_bench(args, wl):
 
     import torch
     import paged_kv_cache_329_amd as pkv
+    from paged_kv_cache_329_amd.step import DecodeStep
     from synth import make_prefix_step_case
 
     t0 = time.perf_counter()
@@ -822,57 +837,29 @@ def _prefix_step_bench(args, wl):
     max_blocks = int(math.ceil((int(case.lengths.max()) + n_steps + 21) / bs))
     k_new, v_new, q = bf16(case.new_k), bf16(case.new_v), bf16(case.q)
     out = torch.empty_like(q)
-    ws = torch.zeros(pkv.paged_attention_workspace_size(B, Hq, Hkv, D, bs, pkv.BF16, pkv.BF16, args.num_splits),
-                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    class HostBuf:
-        def __init__(self):
-            self.slots = torch.empty(B, dtype=torch.int64, pin_memory=True)
-            self.cow = torch.empty((B, 2), dtype=torch.int32, pin_memory=True)
-            self.done = torch.cuda.Event()
-
-    bufs = [HostBuf(), HostBuf()]
-    # Forked groups share their prefix blocks, which the allocator's reference counts show:
-    # the decode kernels read each sequence's shared leading blocks through the caches and
-    # stream the rest.  Taken once: later copy-on-write only shortens a shared prefix by its
-    # tail, and a stale count changes which loads are cached, never the result.
-    prefix_counts = a.shared_prefix_blocks(members)
-    shared = torch.from_numpy(prefix_counts).to(dev) if prefix_counts.any() else None
-    tables0, lens0 = a.block_tables(members, max_blocks)
-    tables_d = torch.from_numpy(tables0).to(dev)      # uploaded once; each step updates it
-    lens_d = torch.from_numpy(lens0).to(dev)          # on the device (pkv_apply_append)
-    lens_host = lens0.astype(np.int64)
-    cow_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    # With each sequence's shared leading blocks read through the caches, twice the default
+    # split count measured faster on MI355X: shorter shares bring the members of a group to a
+    # shared block closer together in time, so more of their repeated reads hit in L2 or the
+    # MALL.
+    default = pkv.paged_attention_default_splits(D, bs, pkv.BF16, pkv.BF16)
+    nsplits = args.num_splits or 2 * default
+    stepper = DecodeStep(a, members, k, v, D, Hq, max_blocks, num_splits=nsplits, shared_prefix=True)
+    prefix_counts = stepper.shared_counts
+    shared = stepper.shared
+    ws = stepper.ws
+    lens_host = stepper.lens.cpu().numpy().astype(np.int64)
     host_s = [0.0]
     logical_bytes = []
     cows_seen = []
 
     def step(i, ev=None, after_copy=None):
-        hb = bufs[i % 2]
-        hb.done.synchronize()                  # its previous copies have been consumed
-        th = time.perf_counter()
-        _, cows = a.append(members, hb.slots.numpy(), hb.cow.numpy())
-        host_s[0] += time.perf_counter() - th
-        n_cow = len(cows)
+        h0 = stepper.host_alloc_s
+        n_cow = stepper.run(out, q, k_new, v_new, case.scale, kernel_events=ev, after_upload=after_copy)
+        host_s[0] += stepper.host_alloc_s - h0
         cows_seen.append(n_cow)
         lens_host[:] += 1
         logical_bytes.append(int(lens_host.sum()) * Hkv * D * 2 * 2)
-        if n_cow:
-            cow_d[:n_cow].copy_(hb.cow[:n_cow], non_blocking=True)
-        if after_copy is not None:
-            after_copy.record(stream)
-        if n_cow:
-            pkv.copy_blocks(k, v, cow_d[:n_cow], D)
-        pkv.apply_append(tables_d, lens_d, hb.slots, bs, nb)   # reads the pinned slots
-        hb.done.record(stream)
-        if ev is not None:
-            pkv.set_launch_events(ev[0], ev[1])
-        pkv.paged_decode_step_split(out, q, k_new, v_new, k, v, tables_d, lens_d, case.scale,
-                                    num_splits=args.num_splits, workspace=ws,
-                                    shared_prefix_blocks=shared)
-        pkv.paged_attention_reduce(out, q, k, v, tables_d, lens_d, case.scale, num_splits=args.num_splits,
-                                   workspace=ws, shared_prefix_blocks=shared)
 
     # Load every kernel of the step once on a scratch pool, so that the first step's
     # timing (the one that copies every shared partial tail) holds no first-launch cost.
@@ -884,9 +871,9 @@ def _prefix_step_bench(args, wl):
     pkv.copy_blocks(sk, sv, torch.tensor([[0, 1]], dtype=torch.int32, device=dev), D)
     pkv.apply_append(torch.zeros((1, 1), dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
                      torch.full((1,), -1, dtype=torch.int64, device=dev), bs, 4)
-    pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, num_splits=args.num_splits,
+    pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, num_splits=nsplits,
                                 workspace=ws, shared_prefix_blocks=shared)
-    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, num_splits=args.num_splits, workspace=ws,
+    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, num_splits=nsplits, workspace=ws,
                                shared_prefix_blocks=shared)
     del sk, sv, one, st
     # The first step copies every shared partial tail; time it on its own.
@@ -940,7 +927,8 @@ def _prefix_step_bench(args, wl):
     # largest number of valid tokens any referencing sequence reads in it.
     tables, lens = a.block_tables(members, max_blocks)
     lens = lens.astype(np.int64)
-    assert np.array_equal(tables, tables_d.cpu().numpy()) and np.array_equal(lens, lens_d.cpu().numpy().astype(np.int64))
+    assert np.array_equal(tables, stepper.tables.cpu().numpy())
+    assert np.array_equal(lens, stepper.lens.cpu().numpy().astype(np.int64))
     used = {}
     for si in range(B):
         for j in range(int(math.ceil(lens[si] / bs))):
@@ -948,7 +936,31 @@ def _prefix_step_bench(args, wl):
             used[b] = max(used.get(b, 0), min(bs, int(lens[si]) - j * bs))
     unique_bytes = sum(used.values()) * Hkv * D * 2 * 2
     value = kv_bytes / (us_per_step * 1e-6) / 1e9
-    achieved = kv_bytes / (split_us * 1e-6) / 1e9
+    # The split kernel reads every distinct block once from HBM at best (shared prefix blocks
+    # re-read by other members can come from L2 or the MALL): its roofline is on distinct bytes.
+    achieved = unique_bytes / (split_us * 1e-6) / 1e9
+    traffic = _traffic_from_profile(args, "paged_decode_step", wl.name, ("attention_decode.hip", "attention_tile.h"))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attention as oatt
+        _log("[bench] timing the fp64 oracle on the host (cpu_baseline)")
+        threads = _set_blas_threads()
+        order = np.random.default_rng(0).permutation(B)
+        done_bytes, done = 0, 0
+        t_cpu0 = time.perf_counter()
+        for sq in order.tolist():
+            oatt.prefix_step_case(case, [sq])
+            done_bytes += (int(case.lengths[sq]) + 1) * Hkv * D * 2 * 2
+            done += 1
+            if time.perf_counter() - t_cpu0 > 10.0:
+                break
+        t_cpu = time.perf_counter() - t_cpu0
+        cpu = {"value": round(done_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "cpu_model": _cpu_model(),
+               "sample": f"{done} of the {B} sequences in a seeded random order (about 10 s): their logical K/V "
+                         f"after the step's append, {done_bytes / 1e9:.3f} GB in {t_cpu:.2f} s, fp64 numpy oracle "
+                         f"incl. decoding K/V to fp64"}
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(us_per_step / 1e3, 5), "higher_is_better": True,
@@ -956,7 +968,9 @@ def _prefix_step_bench(args, wl):
         "data": "synthetic (seeded N(0,1) q/K/V; groups of 8 share a live 1024-token root prefix)",
         "config": {"workload": wl.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                    "block_size": bs, "context": list(wl.length_dist), "prefix_group": wl.prefix_group,
-                   "prefix_len": P, "seed": args.seed, "num_blocks": nb},
+                   "prefix_len": P, "seed": args.seed, "num_blocks": nb, "num_splits": int(nsplits)},
+        "value_note": "value = logical KV bytes (every sequence's tokens, shared prefix blocks once per reader) "
+                      "per wall-clock step",
         "us_per_step": round(us_per_step, 2),
         "kv_bytes_logical": int(kv_bytes),
         "kv_bytes_unique_last_step": int(unique_bytes),
@@ -975,10 +989,14 @@ def _prefix_step_bench(args, wl):
         "first_step": {"copy_on_write_pairs": int(first_cow),
                        "gpu_us_copy_blocks_to_merge_end": round(first_us, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "note": "logical KV bytes (shared prefix blocks counted once per reader)",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_unit": TRAFFIC_UNIT,
+                     "algorithmic_bytes": int(unique_bytes),
+                     "algorithmic_bytes_note": "distinct K/V bytes of the step (each physical block once, with the "
+                                               "most tokens any reader uses in it)",
+                     "logical_GBps": round(kv_bytes / (split_us * 1e-6) / 1e9, 1),
                      "kernel": "paged_attention_split_kernel (decode step with append)"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
 

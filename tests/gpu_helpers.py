@@ -118,12 +118,13 @@ def write_tokens(k_pool, v_pool, k_vals, v_vals, slots, storage, k_scale=1.0, v_
 ROOT_ID_BASE = 1 << 40
 
 
-def build_prefix_batch(case, poison=True):
+def build_prefix_batch(case, poison=True, record=None):
     """Prefill a PrefixStepCase through the library's allocator and kv_cache_write.
 
     Every group's root prefix is a live sequence; member i is forked from its root over
     min(L_i, prefix_len) tokens and extended by its private tokens.  Returns
-    (allocator, k_pool, v_pool, member ids).
+    (allocator, k_pool, v_pool, member ids).  record: an optional list that receives every
+    write as (k values, v values, slots), in order.
     """
     wl = case.wl
     a = pkv.BlockAllocator(case.num_blocks, wl.block_size, free_order=case.free_order)
@@ -132,6 +133,8 @@ def build_prefix_batch(case, poison=True):
     for g in range(case.groups):
         slots = a.seq_create(ROOT_ID_BASE + g, P)
         write_tokens(k, v, case.root_k[g], case.root_v[g], slots, "bf16")
+        if record is not None:
+            record.append((case.root_k[g], case.root_v[g], slots))
     priv_slots = []
     for i in range(wl.batch):
         g = i // wl.prefix_group
@@ -143,6 +146,8 @@ def build_prefix_batch(case, poison=True):
             priv_slots.append(slots)
     if priv_slots:
         write_tokens(k, v, case.priv_k, case.priv_v, np.concatenate(priv_slots), "bf16")
+        if record is not None:
+            record.append((case.priv_k, case.priv_v, np.concatenate(priv_slots)))
     return a, k, v, list(range(wl.batch))
 
 
@@ -184,3 +189,15 @@ def prefill(case, k, v, tables=None, lengths=None, query_start=None, q=None, max
                                 shared_prefix_blocks=_hint(shared_prefix_blocks))
     torch.cuda.synchronize()
     return out
+
+
+def check_all_sequences(got, case, name, chunk=8):
+    """Every sequence of a decode batch against the oracle, `chunk` sequences at a time (to
+    bound the host memory of the fp64 K/V)."""
+    from oracle import attention as oatt
+
+    B = case.wl.batch
+    for c in range(0, B, chunk):
+        seqs = list(range(c, min(B, c + chunk)))
+        assert_close(got[seqs], oatt.decode_case(case, seqs), case.wl.kv_dtype, f"{name}, sequences {seqs}")
+    log(f"{name}: all {B} sequences match the oracle")

@@ -11,6 +11,7 @@ import torch
 
 import paged_kv_cache_329_amd as pkv
 from oracle import attention as oatt
+from oracle import pool as opool
 from synth import WORKLOADS, make_prefix_step_case
 
 from gpu_helpers import (ROOT_ID_BASE, as_f64, assert_close, build_prefix_batch, log, pool_pair, prefix_step,
@@ -88,16 +89,16 @@ def test_shared_prefix_equals_unshared_copies_bitwise():
     assert raw_bytes(shared_out) == raw_bytes(out2)
 
 
-def _shared_default_splits(wl):
-    """The split count a call given shared_prefix_blocks uses by default: twice the plain one."""
-    return 2 * pkv.paged_attention_default_splits(wl.head_dim, wl.block_size, pkv.BF16, pkv.BF16)
+def _default_splits(wl):
+    """The split count of num_splits = 0, with or without shared-prefix counts."""
+    return pkv.paged_attention_default_splits(wl.head_dim, wl.block_size, pkv.BF16, pkv.BF16)
 
 
 @pytest.mark.parametrize("num_splits", [0, 7])
 def test_shared_block_loads_give_the_same_bits(num_splits):
     """Cached loads for the shared leading blocks (the allocator's counts), for every block,
     or for none change no bit of the output at one split count, on tables whose prefixes
-    really are shared; with num_splits = 0 the hinted call uses twice the default count."""
+    really are shared; num_splits = 0 takes the same count with or without the counts."""
     require_gpu()
     case = make_prefix_step_case(SMALL, 5)
     a, k, v, members = build_prefix_batch(case)
@@ -105,7 +106,7 @@ def test_shared_block_loads_give_the_same_bits(num_splits):
     assert_close(as_f64(out), oatt.prefix_step_case(case), "bf16", "prefix step, shared-block loads")
     counts = a.shared_prefix_blocks(members)
     assert counts.max() > 0 and counts.min() >= 0
-    n = num_splits or _shared_default_splits(case.wl)
+    n = num_splits or _default_splits(case.wl)
     qd = to_dev(case.q, case.wl.q_dtype)
     for hint in (None, counts, np.full(len(members), 1 << 20), np.full(len(members), -3)):
         again = torch.empty_like(qd)
@@ -117,37 +118,65 @@ def test_shared_block_loads_give_the_same_bits(num_splits):
         assert raw_bytes(again) == raw_bytes(out)
 
 
-@pytest.mark.timeout(600)
+def _oracle_pools(case, writes, cows, step_slots, chunk=4096):
+    """The pools as oracle/pool.py builds them from the same writes, copies and appends:
+    NaN-filled, then every prefill write, the copy-on-write copies, and the step's tokens."""
+    wl = case.wl
+    pk = opool.empty_pool(case.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, "bf16", fill=0x7FC0)
+    pv = opool.empty_pool(case.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, "bf16", fill=0x7FC0)
+    for kk, vv, slots in writes:
+        for c in range(0, len(slots), chunk):
+            opool.write(pk, pv, kk[c:c + chunk], vv[c:c + chunk], slots[c:c + chunk], "bf16", "bf16", wl.block_size)
+    opool.copy_blocks(pk, pv, cows)
+    opool.write(pk, pv, case.new_k, case.new_v, step_slots, "bf16", "bf16", wl.block_size)
+    return pk, pv
+
+
+@pytest.mark.timeout(900)
 def test_prefix_step_parity_full_size():
-    """256 sequences in groups of 8 sharing a 1024-token prefix, lognormal lengths (median
-    1000, capped at 8192), at the launch configuration the benchmark uses; the oracle checks
-    a sample of sequences covering copy-on-write tails, prefix-only and long private parts."""
+    """The continuous-batching step exactly as the benchmark times it, at full size: 256
+    sequences in groups of 8 sharing a live 1024-token prefix, lognormal lengths (median 1000,
+    capped at 8192).  paged_kv_cache_329_amd.step.DecodeStep runs the allocator's append into
+    pinned slots, copy_blocks on the copy-on-write pairs, apply_append, the fused decode step
+    with the allocator's shared-prefix counts at the benchmark's split count (twice the
+    default), and the reduce.  Every sequence is checked against the oracle, and both pools bit
+    for bit against oracle/pool.py replaying the same writes, copies and appended tokens."""
     require_gpu()
-    case = make_prefix_step_case(FULL, 0)
+    _check_bench_step(make_prefix_step_case(FULL, 0), 2 * _default_splits(FULL))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("num_splits", [0, 3, 96])
+def test_bench_step_small(seed, num_splits):
+    """The benchmark's step driver on the small prefix-sharing batch, at several split
+    counts: every sequence against the oracle, the pools bit for bit."""
+    require_gpu()
+    _check_bench_step(make_prefix_step_case(SMALL, seed), num_splits)
+
+
+def _check_bench_step(case, nsplits):
+    from paged_kv_cache_329_amd.step import DecodeStep
+
+    wl = case.wl
     log(f"prefix step full size: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks")
-    a, k, v, members = build_prefix_batch(case)
-    out, cows, tables, lens = prefix_step(case, a, k, v, members)
-    assert len(cows) == _expected_cow(case)
-    # The benchmark reads each sequence's shared leading blocks through the caches, at the
-    # hinted default split count: checked below against the oracle as well.
-    counts = a.shared_prefix_blocks(members)
-    assert counts.min() >= 1
-    qd = to_dev(case.q, case.wl.q_dtype)
-    hinted = torch.empty_like(qd)
-    pkv.paged_attention_decode(hinted, qd, k, v, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
-                               case.scale, shared_prefix_blocks=torch.from_numpy(counts).cuda())
+    writes = []
+    a, k, v, members = build_prefix_batch(case, record=writes)
+    max_blocks = int((case.lengths.max() + 1 + wl.block_size - 1) // wl.block_size) + 1
+    step = DecodeStep(a, members, k, v, wl.head_dim, wl.num_q_heads, max_blocks, num_splits=nsplits)
+    assert step.shared is not None and step.shared_counts.min() >= 1
+    q, kn, vn = to_dev(case.q, "bf16"), to_dev(case.new_k, "bf16"), to_dev(case.new_v, "bf16")
+    out = torch.empty_like(q)
+    n_cow = step.run(out, q, kn, vn, case.scale)
     torch.cuda.synchronize()
-    L = case.lengths
-    cow_seq = np.flatnonzero((L <= 1024) & (L % 16 != 0))
-    long_seq = np.argsort(L)[-3:]
-    short_seq = np.argsort(L)[:2]
-    aligned = np.flatnonzero(L % 16 == 0)
-    sample = sorted(set(cow_seq[:3].tolist() + long_seq.tolist() + short_seq.tolist() + aligned[:2].tolist()))
-    log(f"sampled sequences {sample}")
-    ref = oatt.prefix_step_case(case, sample)
-    assert_close(as_f64(out)[sample], ref, "bf16", "prefix step full size")
-    assert_close(as_f64(hinted)[sample], ref, "bf16", "prefix step full size, shared-prefix loads")
-    assert np.all(np.isfinite(as_f64(out))) and np.all(np.isfinite(as_f64(hinted)))
+    assert n_cow == _expected_cow(case)
+    got = as_f64(out)
+    for c in range(0, wl.batch, 32):
+        seqs = list(range(c, min(wl.batch, c + 32)))
+        assert_close(got[seqs], oatt.prefix_step_case(case, seqs), "bf16", f"prefix step full size, seqs {c}..")
+    log(f"all {wl.batch} sequences match the oracle; checking the pools")
+    pk, pv = _oracle_pools(case, writes, step.last_cows, step.last_slots)
+    assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), pk)
+    assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), pv)
 
 
 def test_apply_append_mirrors_the_allocator_tables():

@@ -199,6 +199,29 @@ pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_ca
                                       const int32_t* shared_prefix_blocks, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Decode attention that allocates nothing, for callers that cannot allocate device memory or
+ * pass a workspace: code under HIP graph capture, tight serving loops, and harnesses that
+ * forbid allocation.  Same arguments and result as pkv_paged_attention_decode (both passes)
+ * minus the workspace: the library's own scratch stands in for it, a 48 MiB device array
+ * (PKV_NOALLOC_SCRATCH_BYTES) that every device the library runs on holds until the process
+ * ends.  A call whose workspace (pkv_paged_attention_workspace_size at its split count)
+ * exceeds that is rejected with PKV_INVALID_ARG before anything is enqueued; pass a smaller
+ * num_splits then.  No call allocates or frees memory; the first call on a device looks the
+ * array up once (hipGetSymbolAddress).  The scratch needs no initial contents and keeps the
+ * last call's; all calls on one device share it, so calls that can overlap on one device (on
+ * different streams without ordering between them) race and must be serialised by the
+ * caller.  Uses the current device; `stream` must belong to it.
+ * ------------------------------------------------------------------------------------ */
+#define PKV_NOALLOC_SCRATCH_BYTES (48u << 20)
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                              int block_size, int num_blocks, int max_blocks_per_seq,
+                                              float scale, float k_scale, float v_scale, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int num_splits,
+                                              const int32_t* shared_prefix_blocks, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * Decode attention over a contiguous per-sequence placement: the alternative to paging that
  * keeps each sequence's K/V at consecutive addresses of a virtual range and maps physical
  * pages as it grows ("What is PagedAttention?", glossary, "Frequently Asked Questions" and

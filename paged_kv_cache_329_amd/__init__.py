@@ -26,7 +26,7 @@ __all__ = [
     "allocate_kv_pool", "paged_attention_workspace_size", "paged_attention_default_splits",
     "paged_attention_decode",
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
-    "contiguous_attention_decode",
+    "contiguous_attention_decode", "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
     "paged_attention_prefill", "paged_attention_prefill_workspace_size", "allocate_host_pool", "swap_blocks", "VmmPool",
@@ -60,6 +60,8 @@ _SIGNATURES = {
     "pkv_paged_attention_decode": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_split": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
+    "pkv_paged_attention_decode_noalloc": ([_c_p] * 6 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_p],
+                                           _c_int),
     "pkv_contiguous_attention_decode": ([_c_p] * 6 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
                                         _c_int),
     "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
@@ -284,6 +286,31 @@ def paged_attention_reduce(out, q, k_cache, v_cache, block_tables, context_lens,
     return _decode_call("pkv_paged_attention_reduce", out, q, k_cache, v_cache, block_tables,
                         context_lens, scale, k_scale, v_scale, num_splits, workspace, stream,
                       shared_prefix_blocks)
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=1.0,
+                                   v_scale=1.0, num_splits=0, stream=None, shared_prefix_blocks=None):
+    """pkv_paged_attention_decode_noalloc: decode attention with the library's own scratch in
+    place of a workspace; allocates nothing (here or in the library)."""
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    B, Hq, D = q.shape
+    NB, Hkv, bs = _pool_dims(k_cache, D)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    _check(lib().pkv_paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), B, Hq, Hkv, D, bs, NB,
+        block_tables.shape[1], float(scale), float(k_scale), float(v_scale), _dtype_code(q.dtype),
+        _dtype_code(k_cache.dtype), int(num_splits), _prefix_arg(shared_prefix_blocks, B), _stream(stream)))
+    return out
 
 
 def contiguous_attention_decode(out, q, k_base, v_base, seq_first_block, context_lens, max_blocks_per_seq,

@@ -1043,9 +1043,66 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   return PKV_OK;
 }
 
+// Scratch of the entry point that allocates nothing: the workspace of
+// pkv_paged_attention_decode_noalloc lives in this file-scope array, one copy per device,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not the
+// device copy, so kernels are handed the address hipGetSymbolAddress reports for the
+// current device (resolved on the first call on each device and kept).
+constexpr size_t kScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+pkv_status scratch_address(void** ptr_out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return pkv::fail(PKV_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return pkv::fail(PKV_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    ptr[dev] = p;
+  }
+  *ptr_out = ptr[dev];
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                              int block_size, int num_blocks, int max_blocks_per_seq,
+                                              float scale, float k_scale, float v_scale, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, int num_splits,
+                                              const int32_t* shared_prefix_blocks, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_noalloc";
+  pkv_status st = check_shape(fn, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, q_dtype, kv_dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  KernelPair kp;
+  pick_kernels(kv_dtype, head_dim, block_size, &kp);
+  int splits = 0;
+  if ((st = effective_splits(kp, kv_dtype, num_splits, &splits)) != PKV_OK) return st;
+  const size_t need = workspace_bytes_for(splits, num_seqs, num_q_heads / num_kv_heads, head_dim);
+  if (need > kScratchBytes)
+    return pkv::fail(PKV_INVALID_ARG,
+                     "%s: the call needs %zu bytes of scratch, more than the %zu-byte maximum; pass a smaller "
+                     "num_splits or use pkv_paged_attention_decode with a workspace",
+                     fn, need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != PKV_OK) return st;
+  return run_decode(fn, kBoth, out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                    max_blocks_per_seq, scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, ws, kScratchBytes,
+                    shared_prefix_blocks, stream);
+}
 
 pkv_status pkv_paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                               int head_dim, int block_size, pkv_dtype q_dtype,

@@ -165,3 +165,15 @@ def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
                                          0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, None, 0, None, None)
     assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()
 
+
+def test_noalloc_decode_rejects_a_workspace_beyond_its_scratch():
+    """The entry point that allocates nothing refuses, on the host and before touching a
+    device, a call whose workspace would exceed its fixed scratch."""
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.NOALLOC_SCRATCH_BYTES
+    # 100000 shares x 2 x G 4 x D 128 x 4 bytes of partials is far past 48 MiB.
+    st = pkv.lib().pkv_paged_attention_decode_noalloc(16, 16, 16, 16, 16, 16, 64, 32, 8, 128, 16, 1000, 256,
+                                                      0.088, 1.0, 1.0, pkv.BF16, pkv.BF16, 100000, None, None)
+    assert st == 1
+    assert b"scratch" in pkv.lib().pkv_last_error()

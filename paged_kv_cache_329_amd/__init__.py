@@ -36,7 +36,11 @@ F32, BF16, FP8_E4M3FN = 0, 1, 2
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_BLOCKS", 4: "UNKNOWN_SEQ",
            5: "HIP_ERROR"}
 _PKG = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_PKG, "libpagedkv.so")
+# PKV_LIBRARY names another build of the library to load instead (the host sanitizer build of
+# the allocator, which has only the host entry points; calls to any other entry point then
+# raise AttributeError).
+_LIB_OVERRIDE = os.environ.get("PKV_LIBRARY")
+library_path = _LIB_OVERRIDE or os.path.join(_PKG, "libpagedkv.so")
 
 
 class PagedKVError(RuntimeError):
@@ -131,6 +135,8 @@ def lib():
                 raise RuntimeError(f"{library_path} is not built; run `python -m paged_kv_cache_329_amd.build`")
             handle = ctypes.CDLL(library_path)
             for name, (args, res) in _SIGNATURES.items():
+                if _LIB_OVERRIDE and not hasattr(handle, name):
+                    continue
                 fn = getattr(handle, name)
                 fn.argtypes = args
                 fn.restype = res

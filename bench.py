@@ -42,6 +42,9 @@ def _args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--num-splits", type=int, default=0)
+    p.add_argument("--prefix-groups", choices=["on", "off"], default="on",
+                   help="continuous batching over shared prefixes: read each group's shared blocks once for "
+                        "all its sequences (on), or per sequence through the caches (off)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--traffic-json", default=None,
                    help="HBM traffic summary (default: profiles/paged_attention_split__<workload>__hbm_traffic.json)")
@@ -838,13 +841,16 @@ def _prefix_step_bench(args, wl):
     k_new, v_new, q = bf16(case.new_k), bf16(case.new_v), bf16(case.q)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
-    # With each sequence's shared leading blocks read through the caches, twice the default
-    # split count measured faster on MI355X: shorter shares bring the members of a group to a
-    # shared block closer together in time, so more of their repeated reads hit in L2 or the
-    # MALL.
+    # With prefix groups each group's shared blocks are read once, for all its sequences, in
+    # the same launch as every sequence's own blocks.  Without them, each sequence's shared
+    # leading blocks go through the caches, and then twice the default split count measured
+    # faster on MI355X: shorter shares bring the members of a group to a shared block closer
+    # together in time, so more of their repeated reads hit in L2 or the MALL.
+    groups_on = args.prefix_groups == "on"
     default = pkv.paged_attention_default_splits(D, bs, pkv.BF16, pkv.BF16)
-    nsplits = args.num_splits or 2 * default
-    stepper = DecodeStep(a, members, k, v, D, Hq, max_blocks, num_splits=nsplits, shared_prefix=True)
+    nsplits = args.num_splits or (default if groups_on else 2 * default)
+    stepper = DecodeStep(a, members, k, v, D, Hq, max_blocks, num_splits=nsplits, shared_prefix=True,
+                         prefix_groups=groups_on)
     prefix_counts = stepper.shared_counts
     shared = stepper.shared
     ws = stepper.ws
@@ -871,10 +877,15 @@ def _prefix_step_bench(args, wl):
     pkv.copy_blocks(sk, sv, torch.tensor([[0, 1]], dtype=torch.int32, device=dev), D)
     pkv.apply_append(torch.zeros((1, 1), dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
                      torch.full((1,), -1, dtype=torch.int64, device=dev), bs, 4)
-    pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, num_splits=nsplits,
-                                workspace=ws, shared_prefix_blocks=shared)
-    pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, num_splits=nsplits, workspace=ws,
-                               shared_prefix_blocks=shared)
+    if groups_on:
+        zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+        pkv.paged_decode_step_grouped(out, q, k_new, v_new, sk, sv, st, one, (zeros, zeros, zeros), case.scale,
+                                      num_splits=nsplits)
+    else:
+        pkv.paged_decode_step_split(out, q, k_new, v_new, sk, sv, st, one, case.scale, num_splits=nsplits,
+                                    workspace=ws, shared_prefix_blocks=shared)
+        pkv.paged_attention_reduce(out, q, sk, sv, st, one, case.scale, num_splits=nsplits, workspace=ws,
+                                   shared_prefix_blocks=shared)
     del sk, sv, one, st
     # The first step copies every shared partial tail; time it on its own.
     e_first = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -983,7 +994,9 @@ def _prefix_step_bench(args, wl):
                           "merge_incl_gap": round(merge_us, 2),
                           "gpu_step": round(gpu_step_us, 2)}},
         "host_allocator_us_per_step": round(host_s[0] / args.steps * 1e6, 1),
-        "kv_loads": ("cached for each sequence's shared leading blocks, non-temporal for the rest"
+        "kv_loads": ("each group's shared blocks read once for all its sequences (prefix groups), non-temporal"
+                     if groups_on else
+                     "cached for each sequence's shared leading blocks, non-temporal for the rest"
                      if shared is not None else "non-temporal"),
         "shared_leading_blocks": int(prefix_counts.sum()),
         "first_step": {"copy_on_write_pairs": int(first_cow),
@@ -995,7 +1008,8 @@ def _prefix_step_bench(args, wl):
                      "algorithmic_bytes_note": "distinct K/V bytes of the step (each physical block once, with the "
                                                "most tokens any reader uses in it)",
                      "logical_GBps": round(kv_bytes / (split_us * 1e-6) / 1e9, 1),
-                     "kernel": "paged_attention_split_kernel (decode step with append)"},
+                     "kernel": ("paged_attention_grouped_kernel (decode step with append, prefix groups)"
+                                if groups_on else "paged_attention_split_kernel (decode step with append)")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

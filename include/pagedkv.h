@@ -288,6 +288,58 @@ pkv_status pkv_paged_decode_step_split(void* out, const void* q, const void* k_n
                                        int num_splits, void* workspace, size_t workspace_bytes,
                                        const int32_t* shared_prefix_blocks, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Decode with prefix groups: blocks that several sequences share are read once for all of
+ * them.  Sharers' block tables point at the same physical blocks ("PagedAttention: Optimizing
+ * KV Cache in vLLM", §4 "Copy-on-Write"; "What is PagedAttention?", glossary, "Share Without
+ * Mutating State"); the pages keep attention per sequence, and reading a shared block once
+ * per group is this library's own use of that layout.  The result is that of
+ * pkv_paged_attention_decode / pkv_paged_decode_step over the same tables.
+ *
+ * The sequences come in column chunks of consecutive sequences (pkv_alloc_prefix_groups):
+ *   chunk_first   int32 [num_seqs] (device): index of the first sequence of s's chunk; a chunk
+ *                 holds at most 32 / G sequences (G = Hq / Hkv), so that its (sequence, query
+ *                 head) pairs are at most 32 columns.
+ *   chunk_src     int32 [num_seqs] (device), read at each chunk's first sequence: the chunk
+ *                 sequence whose table row holds the shared blocks.
+ *   group_blocks  int32 [num_seqs] (device): leading blocks of s read for it in the group
+ *                 pass; at the source, the most of any chunk sequence.
+ * Precondition (not checked on the device): for every s, its first group_blocks[s] table
+ * entries equal its chunk source's.  The kernel takes group_blocks[s] only up to the full
+ * blocks of s's cached tokens (with append, the block receiving the new token is never among
+ * them) and up to the source's own count; a chunk that is not well formed (first or source
+ * outside the chunk's 32 / G sequences) reads no group blocks, so its sequences are walked on
+ * their own.  One split pass walks every chunk's shared blocks once, for all its sequences'
+ * query heads at once, and every sequence's remaining blocks; the merge pass combines the two
+ * parts.  Both passes are enqueued.
+ *
+ *   workspace      pkv_paged_attention_grouped_workspace_size bytes (it depends on num_splits
+ *                  and max_blocks_per_seq), no initial contents needed.
+ *   Every other argument as for pkv_paged_attention_decode / pkv_paged_decode_step (no
+ *   shared_prefix_blocks: shared blocks are read once anyway).  num_splits >= 2 is used (at
+ *   least one share of each kind).
+ * ------------------------------------------------------------------------------------ */
+pkv_status pkv_paged_attention_grouped_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                                      int block_size, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                                      int num_splits, int max_blocks_per_seq,
+                                                      size_t* bytes /* host, out */);
+pkv_status pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              const int32_t* chunk_first, const int32_t* chunk_src,
+                                              const int32_t* group_blocks, int num_seqs, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                              int max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                                              pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+pkv_status pkv_paged_decode_step_grouped(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                         const int32_t* chunk_first, const int32_t* chunk_src,
+                                         const int32_t* group_blocks, int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                         float scale, float k_scale, float v_scale, pkv_dtype q_dtype,
+                                         pkv_dtype kv_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Measurement aid: the next split pass launched on the calling thread (by any decode or
  * decode-step entry point), or the next multi-query attention kernel
  * (pkv_paged_attention_prefill), records start_event when its kernel begins and stop_event
@@ -495,6 +547,18 @@ pkv_status pkv_seq_swap(pkv_alloc* from, pkv_alloc* to, int64_t seq_id, int32_t*
  * sequence does not exist (nothing written). */
 pkv_status pkv_alloc_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq_ids, int n,
                                           int32_t* out);
+
+/* Column chunks for the decode with prefix groups (host arrays [n], for the listed sequences
+ * in order).  A group is a run of listed sequences whose first block is the same shared
+ * physical block (reference count > 1; a sequence whose first block is not shared is a group
+ * of its own); each group is cut into chunks of at most max_chunk consecutive sequences
+ * (max_chunk = 32 / G for the attention calls).  chunk_first[i] = index of the first sequence
+ * of i's chunk; chunk_src[i] = the chunk sequence with the most shared leading blocks (its
+ * table row is read); group_blocks[i] = leading blocks i shares with the source (equal table
+ * entries), and at the source the most of any other chunk sequence (0 for a chunk of one).
+ * UNKNOWN_SEQ if a sequence does not exist (nothing written). */
+pkv_status pkv_alloc_prefix_groups(const pkv_alloc* a, const int64_t* seq_ids, int n, int max_chunk,
+                                   int32_t* chunk_first, int32_t* chunk_src, int32_t* group_blocks);
 
 /* Writes block tables (host int32 [n][max_blocks], padded with -1) and lengths (host
  * int32 [n], nullable) for the listed sequences. */

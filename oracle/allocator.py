@@ -200,6 +200,57 @@ class AllocatorModel:
                 "tokens": sum(n for _, n in self.seqs.values()),
                 "stored_tokens": sum(max(h) for h in holders.values()), "num_seqs": len(self.seqs)}
 
+    def prefix_groups(self, sids, max_chunk: int):
+        """Column chunks for reading shared leading blocks once per group: a group is a run of
+        listed sequences whose first block is the same block with a count above one (any other
+        sequence is a group of its own), cut into chunks of at most ``max_chunk`` sequences.
+        Per listed sequence: the index of its chunk's first sequence, the chunk's source (the
+        member with the most leading blocks held by several sequences, the first such on a
+        tie), and how many leading table entries it has equal to the source's -- at the
+        source, the most of any other member (0 alone).  Sharing blocks is the pages' own
+        structure ("PagedAttention: Optimizing KV Cache in vLLM", §4: sharers' tables point at
+        the same physical blocks); the chunking is this library's."""
+        if max_chunk < 1:
+            raise AllocError(INVALID_ARG)
+        rows = []
+        for sid in sids:
+            if sid not in self.seqs:
+                raise AllocError(UNKNOWN_SEQ)
+            rows.append(self.seqs[sid][0])
+        n = len(rows)
+
+        def head(i):
+            b = rows[i]
+            return b[0] if b and self.ref[b[0]] > 1 else None
+
+        def lead(i):
+            c = 0
+            while c < len(rows[i]) and self.ref[rows[i][c]] > 1:
+                c += 1
+            return c
+
+        first, src, blocks = [0] * n, [0] * n, [0] * n
+        i = 0
+        while i < n:
+            end = i + 1
+            if head(i) is not None:
+                while end < n and head(end) == head(i):
+                    end += 1
+            for c0 in range(i, end, max_chunk):
+                members = list(range(c0, min(end, c0 + max_chunk)))
+                best = max(lead(k) for k in members)
+                source = next(k for k in members if lead(k) == best)
+                for k in members:
+                    first[k], src[k] = c0, source
+                    same = 0
+                    while (same < len(rows[k]) and same < len(rows[source])
+                           and rows[k][same] == rows[source][same]):
+                        same += 1
+                    blocks[k] = same
+                blocks[source] = max([blocks[k] for k in members if k != source], default=0)
+            i = end
+        return first, src, blocks
+
     # ---- invariants ----------------------------------------------------------------
     def check_invariants(self):
         check_allocator_state(self.num_blocks, self.bs, set(self.free), self.ref,

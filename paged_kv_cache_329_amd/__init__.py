@@ -26,7 +26,8 @@ __all__ = [
     "allocate_kv_pool", "paged_attention_workspace_size", "paged_attention_default_splits",
     "paged_attention_decode",
     "paged_attention_split", "paged_attention_reduce", "paged_decode_step", "paged_decode_step_split",
-    "contiguous_attention_decode", "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "contiguous_attention_decode", "paged_attention_grouped_workspace_size", "paged_attention_decode_grouped",
+    "paged_decode_step_grouped", "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
     "paged_attention_prefill", "paged_attention_prefill_workspace_size", "allocate_host_pool", "swap_blocks", "VmmPool",
@@ -66,6 +67,12 @@ _SIGNATURES = {
     "pkv_paged_attention_reduce": (_DECODE_ARGS, _c_int),
     "pkv_paged_attention_decode_noalloc": ([_c_p] * 6 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_p],
                                            _c_int),
+    "pkv_paged_attention_grouped_workspace_size": ([_c_int] * 9 + [ctypes.POINTER(_c_sz)], _c_int),
+    "pkv_paged_attention_decode_grouped": ([_c_p] * 9 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
+                                           _c_int),
+    "pkv_paged_decode_step_grouped": ([_c_p] * 11 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
+                                      _c_int),
+    "pkv_alloc_prefix_groups": ([_c_p, _c_p, _c_int, _c_int, _c_p, _c_p, _c_p], _c_int),
     "pkv_contiguous_attention_decode": ([_c_p] * 6 + [_c_int] * 7 + [_c_f] * 3 + [_c_int] * 3 + [_c_p, _c_sz, _c_p],
                                         _c_int),
     "pkv_paged_decode_step": (_STEP_ARGS, _c_int),
@@ -316,6 +323,69 @@ def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, conte
         _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), B, Hq, Hkv, D, bs, NB,
         block_tables.shape[1], float(scale), float(k_scale), float(v_scale), _dtype_code(q.dtype),
         _dtype_code(k_cache.dtype), int(num_splits), _prefix_arg(shared_prefix_blocks, B), _stream(stream)))
+    return out
+
+
+def paged_attention_grouped_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, q_dtype,
+                                           kv_dtype, num_splits=0, max_blocks_per_seq=0) -> int:
+    n = _c_sz(0)
+    _check(lib().pkv_paged_attention_grouped_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                            q_dtype, kv_dtype, int(num_splits),
+                                                            int(max_blocks_per_seq), ctypes.byref(n)))
+    return n.value
+
+
+def _group_args(groups, B):
+    if len(groups) != 3:
+        raise ValueError("groups must be (chunk_first, chunk_src, group_blocks)")
+    for t in groups:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or t.shape != (B,):
+            raise ValueError("chunk_first, chunk_src and group_blocks must be int32 [num_seqs] device tensors")
+    return [_dev(t, "group array") for t in groups]
+
+
+def paged_attention_decode_grouped(out, q, k_cache, v_cache, block_tables, context_lens, groups, scale,
+                                   k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """Decode with prefix groups (pkv_paged_attention_decode_grouped): groups is the device
+    triple (chunk_first, chunk_src, group_blocks) of BlockAllocator.prefix_groups."""
+    return _grouped_call("pkv_paged_attention_decode_grouped", out, q, None, None, k_cache, v_cache, block_tables,
+                         context_lens, groups, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def paged_decode_step_grouped(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, groups, scale,
+                              k_scale=1.0, v_scale=1.0, num_splits=0, workspace=None, stream=None):
+    """The decode step with append, with prefix groups (pkv_paged_decode_step_grouped)."""
+    return _grouped_call("pkv_paged_decode_step_grouped", out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                         context_lens, groups, scale, k_scale, v_scale, num_splits, workspace, stream)
+
+
+def _grouped_call(fn_name, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, groups, scale,
+                  k_scale, v_scale, num_splits, workspace, stream):
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must both be [num_seqs, num_q_heads, head_dim] of one dtype")
+    B, Hq, D = q.shape
+    NB, Hkv, bs = _pool_dims(k_cache, D)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    qd, kd = _dtype_code(q.dtype), _dtype_code(k_cache.dtype)
+    st = _stream(stream)
+    if workspace is None:
+        workspace = _workspace(paged_attention_grouped_workspace_size(B, Hq, Hkv, D, bs, qd, kd, num_splits,
+                                                                      block_tables.shape[1]), q.device, st)
+    ptrs = [_dev(out, "out"), _dev(q, "q")]
+    if k_new is not None:
+        if k_new.shape != (B, Hkv, D) or v_new.shape != k_new.shape or k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+            raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim] of q's dtype")
+        ptrs += [_dev(k_new, "k_new"), _dev(v_new, "v_new")]
+    ptrs += [_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+             _dev(context_lens, "context_lens")] + _group_args(groups, B)
+    _check(getattr(lib(), fn_name)(*ptrs, B, Hq, Hkv, D, bs, NB, block_tables.shape[1], float(scale), float(k_scale),
+                                   float(v_scale), qd, kd, int(num_splits), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), st))
     return out
 
 
@@ -724,6 +794,15 @@ class BlockAllocator:
     @property
     def num_seqs(self) -> int:
         return lib().pkv_alloc_num_seqs(self._h)
+
+    def prefix_groups(self, seq_ids, max_chunk: int):
+        """pkv_alloc_prefix_groups: (chunk_first, chunk_src, group_blocks) int32 [n] host arrays."""
+        ids = _np(seq_ids, np.int64)
+        n = len(ids)
+        first, src, blocks = (np.zeros(n, np.int32) for _ in range(3))
+        _check(lib().pkv_alloc_prefix_groups(self._h, ids.ctypes.data, n, int(max_chunk), first.ctypes.data,
+                                             src.ctypes.data, blocks.ctypes.data))
+        return first, src, blocks
 
     def shared_prefix_blocks(self, seq_ids) -> np.ndarray:
         """Leading blocks of each sequence with a reference count above 1, int32 [n]

@@ -315,6 +315,60 @@ pkv_status pkv_alloc_shared_prefix_blocks(const pkv_alloc* a, const int64_t* seq
   return PKV_OK;
 }
 
+pkv_status pkv_alloc_prefix_groups(const pkv_alloc* a, const int64_t* seq_ids, int n, int max_chunk,
+                                   int32_t* chunk_first, int32_t* chunk_src, int32_t* group_blocks) {
+  if (!a) return fail(PKV_INVALID_ARG, "pkv_alloc_prefix_groups: null allocator");
+  if (n < 0 || max_chunk < 1 || (n > 0 && (!seq_ids || !chunk_first || !chunk_src || !group_blocks)))
+    return fail(PKV_INVALID_ARG, "pkv_alloc_prefix_groups: bad arguments (n=%d max_chunk=%d)", n, max_chunk);
+  std::vector<const pkv_alloc::Seq*> seq(n);
+  for (int i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PKV_UNKNOWN_SEQ, "pkv_alloc_prefix_groups: unknown sequence %lld", (long long)seq_ids[i]);
+    seq[i] = &it->second;
+  }
+  auto first_shared = [&](int i) -> int32_t {
+    const auto& b = seq[i]->blocks;
+    return !b.empty() && a->refcount[b[0]] > 1 ? b[0] : -1;
+  };
+  auto shared_lead = [&](int i) {
+    const auto& b = seq[i]->blocks;
+    size_t c = 0;
+    while (c < b.size() && a->refcount[b[c]] > 1) ++c;
+    return c;
+  };
+  int i = 0;
+  while (i < n) {
+    // A group: the run of listed sequences starting with the same shared physical block.
+    const int32_t head = first_shared(i);
+    int end = i + 1;
+    if (head >= 0)
+      while (end < n && first_shared(end) == head) ++end;
+    for (int c0 = i; c0 < end; c0 += max_chunk) {
+      const int c1 = std::min(end, c0 + max_chunk);
+      // The chunk reads its shared blocks from the member with the longest shared lead.
+      int src = c0;
+      for (int k = c0 + 1; k < c1; ++k)
+        if (shared_lead(k) > shared_lead(src)) src = k;
+      const auto& sb = seq[src]->blocks;
+      int32_t most = 0;
+      for (int k = c0; k < c1; ++k) {
+        chunk_first[k] = c0;
+        chunk_src[k] = src;
+        if (k == src) continue;
+        const auto& kb = seq[k]->blocks;
+        int32_t same = 0;
+        while (size_t(same) < kb.size() && size_t(same) < sb.size() && kb[same] == sb[same]) ++same;
+        group_blocks[k] = same;
+        most = std::max(most, same);
+      }
+      group_blocks[src] = most;
+    }
+    i = end;
+  }
+  return PKV_OK;
+}
+
 int pkv_alloc_num_free(const pkv_alloc* a) { return a ? int(a->free_stack.size()) : -1; }
 int pkv_alloc_num_blocks(const pkv_alloc* a) { return a ? a->num_blocks : -1; }
 int pkv_alloc_block_size(const pkv_alloc* a) { return a ? a->block_size : -1; }

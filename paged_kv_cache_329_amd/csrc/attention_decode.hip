@@ -60,6 +60,7 @@ using namespace pkv::tile;
 constexpr int kWavesPerWG = 4;
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt to the 8 XCDs round-robin
 constexpr int kMaxGroup = 16;
+constexpr int kGroupCols = 32;   // (member, query head) columns of a group share: two 16-column tiles
 
 // Workspace layout: header (per-sequence work offsets and the split pass's record), partial
 // accumulators, partial (max, sum) pairs; each part rounded up to 256 bytes.
@@ -106,6 +107,21 @@ struct DecodeArgs {
   // Contiguous placement (no block table): logical block j of sequence s is pool block
   // seq_first_block[s] + j.
   const int32_t* seq_first_block;
+  // Prefix groups ([B] each, or null): the first sequence of s's column chunk, the chunk's
+  // table source (read at the chunk's first sequence) and s's leading blocks that the group
+  // pass reads for it (the same physical blocks as the source's first ones).
+  const int32_t* chunk_first;
+  const int32_t* chunk_src;
+  const int32_t* group_blocks;
+  // Grouped workspace parts (see grouped_layout): member pieces of units finished inside one
+  // share, group pieces of shares, group pieces of units finished inside one share.
+  float* ws_macc;  // [B * Hkv][G][D]
+  float* ws_mml;   // [B * Hkv][G][2]
+  float* ws_gacc;  // [splits * 2][kGroupCols][D]
+  float* ws_gml;   // [splits * 2][kGroupCols][2]
+  float* ws_fgacc; // [B * Hkv][kGroupCols][D]
+  float* ws_fgml;  // [B * Hkv][kGroupCols][2]
+  int appending;   // 1 for the decode step with append (token L-1 is the appended one)
 };
 
 
@@ -128,24 +144,72 @@ __device__ __forceinline__ int seq_len(const DecodeArgs& a, int s, int bs) {
 // Units (groups of `coop` kv heads) per sequence.
 __device__ __forceinline__ int head_groups(const DecodeArgs& a) { return a.Hkv / a.coop; }
 
+// Full blocks of sequence s's cached tokens (with append, token L-1 is not cached yet).
+__device__ __forceinline__ int cached_full_blocks(const DecodeArgs& a, int s, int bs) {
+  const int L = seq_len(a, s, bs);
+  return (L - (a.appending && L > 0 ? 1 : 0)) / bs;
+}
+
+// Blocks the group pass reads for the chunk whose first sequence is f (0 unless f starts a
+// well-formed chunk): the source's count, limited to the source's full cached blocks.
+__device__ __forceinline__ int chunk_blocks(const DecodeArgs& a, int f, int bs) {
+  const int M = kGroupCols / a.G;
+  if (a.chunk_first[f] != f) return 0;
+  const int src = a.chunk_src[f];
+  if (src < f || src - f >= M || src >= a.B || a.chunk_first[src] != f) return 0;
+  return min(max(a.group_blocks[src], 0), cached_full_blocks(a, src, bs));
+}
+
+// Leading blocks of sequence s that the group pass reads for it (its own count, limited to
+// its full cached blocks and to its chunk's blocks; 0 when its chunk is not well formed).  The
+// block receiving an appended token is never among them, so the appended token always falls
+// in the sequence's own part.
+__device__ __forceinline__ int group_skip(const DecodeArgs& a, int s, int bs) {
+  const int M = kGroupCols / a.G;
+  const int f = a.chunk_first[s];
+  if (f < 0 || f > s || s - f >= M) return 0;
+  return min(min(max(a.group_blocks[s], 0), chunk_blocks(a, f, bs)), cached_full_blocks(a, s, bs));
+}
+
+// Blocks of sequence s walked by the per-sequence (member) part: all of them, or with prefix
+// groups those after the leading blocks the group pass reads.
+template <bool GROUPED>
+__device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int s, int bs) {
+  const int nb = seq_blocks(a, s, bs);
+  if constexpr (GROUPED) return nb - group_skip(a, s, bs);
+  return nb;
+}
+
 // Total work W = head_groups * sum_s blocks(s) (wave-uniform; the host checks it fits in int).
+template <bool GROUPED = false>
 __device__ int total_work(const DecodeArgs& a, int bs, int lane) {
   int acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
-    acc += s < a.B ? seq_blocks(a, s, bs) : 0;
+    acc += s < a.B ? unit_blocks<GROUPED>(a, s, bs) : 0;
+  }
+  return wave_sum(acc) * head_groups(a);
+}
+
+// Group work: head_groups * sum over chunk first sequences f of chunk_blocks(f).
+__device__ int group_work(const DecodeArgs& a, int bs, int lane) {
+  int acc = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int s = base + lane;
+    acc += s < a.B ? chunk_blocks(a, s, bs) : 0;
   }
   return wave_sum(acc) * head_groups(a);
 }
 
 // Sequence whose units contain work position x (0 <= x < W), and head_groups * blocks
-// before it.
+// before it.  GROUP: over the group work list (chunk first sequences and their blocks).
+template <bool GROUPED = false, bool GROUP = false>
 __device__ void locate(const DecodeArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
   int base = 0;
   const int hg = head_groups(a);
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int s = b0 + lane;
-    const int w = s < a.B ? seq_blocks(a, s, bs) * hg : 0;
+    const int w = s < a.B ? (GROUP ? chunk_blocks(a, s, bs) : unit_blocks<GROUPED>(a, s, bs)) * hg : 0;
     const int incl = wave_incl_scan(w, lane);
     const int lo = base + (incl - w), hi = base + incl;
     const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
@@ -338,23 +402,41 @@ __device__ __forceinline__ void issue_append_store(const DecodeArgs& a, const Ap
   }
 }
 
-// Partial (accumulator, max, sum) of head h of piece `piece`; lane (h, row) holds dims
-// 16*n + 4*row .. +3 of each 16-dim tile n.
+// Partial (accumulator, max, sum) of one column into row r of a piece array (D floats per row
+// of acc_base, two per row of ml_base); lane (column, row) holds dims 16*n + 4*row .. +3 of
+// each 16-dim tile n.
 template <int D>
-__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece, int h, int row, const f32x4* acc,
-                                              float2 ml) {
-  float* wacc = a.ws_acc + (piece * a.G + h) * D;
+__device__ __forceinline__ void store_row(float* acc_base, float* ml_base, int64_t r, int row, const f32x4* acc,
+                                          float2 ml) {
+  float* wacc = acc_base + r * D;
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
     *reinterpret_cast<float4*>(wacc + 16 * n + 4 * row) = make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
-  if (row == 0) *reinterpret_cast<float2*>(a.ws_ml + (piece * a.G + h) * 2) = ml;
+  if (row == 0) *reinterpret_cast<float2*>(ml_base + r * 2) = ml;
 }
 
-// CONTIG: the sequence's blocks are consecutive pool blocks from seq_first_block[s] on, so
-// a block's address is computed instead of looked up (no table loads).
-template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG = false>
-__global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
+// Partial of head h of piece `piece`.
+template <int D>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece, int h, int row, const f32x4* acc,
+                                              float2 ml) {
+  store_row<D>(a.ws_acc, a.ws_ml, piece * a.G + h, row, acc, ml);
+}
+
+// One share of the (sequence, head group, block) work list: positions [c_begin, c_end),
+// walked by wave `sub` of the share's group of `coop` waves on kv heads coop * hg + sub, so
+// that together they read the adjacent head regions of each block.  The share's pieces are
+// numbered (share * coop + sub) * 2 + slot.
+//  CONTIG: the sequence's blocks are consecutive pool blocks from seq_first_block[s] on, so a
+//    block's address is computed instead of looked up (no table loads).
+//  GROUPED: the list holds each sequence's blocks after the leading ones the group pass reads
+//    for it; a unit finished inside the share goes to its (sequence, kv head) slot instead of
+//    `out` when the group pass also holds part of it.
+// hold / hold_ml: this wave's LDS rows for the partial of the share's first segment.
+template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG, bool GROUPED>
+__device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin,
+                                           int c_end, f32x4 (*hold)[64], float2* hold_ml) {
   static_assert(!(CONTIG && APPEND), "the contiguous placement has no decode step with append");
+  static_assert(!(GROUPED && (MIX || CONTIG)), "prefix groups read shared blocks once, through tables");
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;                  // cached elements per 16-byte chunk
@@ -362,56 +444,14 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
   constexpr int NSB = BS / 16;                    // sub-tiles per block
   constexpr int64_t REGION = int64_t(BS) * D * T::EB;
 
-  const int lane = threadIdx.x & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Workgroup b runs on XCD b % 8.  Each XCD takes a contiguous eighth of the work list
-  // (logical workgroup (b % 8) * (n / 8) + b / 8), so sequences next to each other, such as
-  // the members of a group that share prefix blocks, read those blocks through one XCD's L2
-  // at about the same time.  Shares and pieces are numbered by the logical wave.
-  const int nwg = int(gridDim.x), full = nwg - nwg % kXcds;
-  const int b = int(blockIdx.x);
-  const int lwg = b < full ? (b % kXcds) * (full / kXcds) + b / kXcds : b;
-  const int wave = lwg * kWavesPerWG + wv;
-  // The partial of a share's first segment waits in LDS until the share's loads are done: a
-  // wave's loads and stores complete in issue order, so a store in the middle of the share
-  // would hold up every load behind it.  Each lane reads back only what it wrote.
-  __shared__ f32x4 s_hold[kWavesPerWG][F::NT][64];
-  __shared__ float2 s_hold_ml[kWavesPerWG][64];
   bool holding = false;
-  const int W = total_work(a, BS, lane);
-  if (wave == 0) {
-    // Work offset of every sequence, for the merge pass.
-    int base = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-      const int sq = b0 + lane;
-      const int w = sq < a.B ? seq_blocks(a, sq, BS) * head_groups(a) : 0;
-      const int incl = wave_incl_scan(w, lane);
-      if (sq < a.B) a.ws_seq[sq] = base + incl - w;
-      base += __builtin_amdgcn_readlane(incl, 63);
-    }
-    if (lane == 0) {
-      a.ws_seq[a.B] = base;
-      a.ws_seq[a.B + 1] = a.splits;
-      a.ws_seq[a.B + 2] = a.coop;
-      a.ws_seq[a.B + 3] = a.B;
-    }
-  }
-  if (W == 0) return;
-  // Share of this wave's group of `coop` consecutive waves, walked side by side on kv heads
-  // coop*hg + sub, so that together they read the adjacent head regions of each block.
-  // Pieces stay numbered per wave (2 * wave + slot).
-  const int share = wave / a.coop;
-  const int sub = wave % a.coop;
-  const int nshare = std::min(a.splits / a.coop, W);
-  if (share >= nshare) return;
-  const int c_begin = int(share_begin(share, W, nshare));
-  const int c_end = int(share_begin(share + 1, W, nshare));
-
   int s, seq_off;
-  locate(a, BS, lane, c_begin, s, seq_off);
+  locate<GROUPED>(a, BS, lane, c_begin, s, seq_off);
   if (s >= a.B) return;
   int L = seq_len(a, s, BS);
-  int nb = (L + BS - 1) / BS;
+  int skip = GROUPED ? group_skip(a, s, BS) : 0;   // leading blocks the group pass reads
+  int nbt = (L + BS - 1) / BS;                     // blocks of the sequence
+  int nb = nbt - skip;                             // blocks of each of its units in this list
   int hg = (c_begin - seq_off) / nb;
   int g = hg * a.coop + sub;
   int unit_off = seq_off + hg * nb;
@@ -433,11 +473,11 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
     const int unit_end = unit_off + nb;
     const int seg_end = std::min(c_end, unit_end);
     const bool full = pos == unit_off && seg_end == unit_end;
-    const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
+    const int j0 = skip + pos - unit_off, j1 = skip + seg_end - unit_off;   // blocks [j0, j1)
     const int k0 = j0 * NSB;
     const int k1 = (std::min(j1 * BS, Lc) + 15) / 16;                   // sub-tiles [k0, k1)
     // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
-    const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
+    const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nbt) * NSB : 0;
 
     // q fragments of (s, g): lane (h, row) holds q[s, g*G+h, X*(4i+row) .. +X].
     uint4 qf[F::NLOAD * F::QCH];
@@ -460,7 +500,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
     int tbl = -1;
     int first = 0;
     if constexpr (CONTIG) first = __builtin_amdgcn_readfirstlane(a.seq_first_block[s]);
-    else tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+    else tbl = tbase + lane < nbt ? trow[tbase + lane] : -1;
     const bool ends_unit = APPEND && seg_end == unit_end;
     AppendRegs<KV, D> app;
     if constexpr (APPEND) {
@@ -481,7 +521,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       if (!CONTIG && (k / NSB < tbase || jlast >= tbase + 64)) {
         tbase = k / NSB;
         const int jj = tbase + lane;
-        tbl = jj < nb ? trow[jj] : -1;
+        tbl = jj < nbt ? trow[jj] : -1;
       }
       // Issue every K load of the chunk, then every V load, with no branches between
       // them, so QK can start while V is still in flight.  Sub-tiles past the chunk's
@@ -570,7 +610,11 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       }
     }
     const float l_tot = wave_sum_rows(l_run);
-    if (full) {
+    if (GROUPED && full && skip > 0) {
+      // The group pass holds the rest of this (sequence, kv head): the merge combines them.
+      if (head_ok) store_row<D>(a.ws_macc, a.ws_mml, (int64_t(s) * a.Hkv + g) * a.G + h, row, acc,
+                                make_float2(m_run, l_tot));
+    } else if (full) {
       if (head_ok) {
         const float inv = a.v_scale / l_tot;
         const int64_t orow = (int64_t(s) * a.Hkv * a.G + int64_t(g) * a.G + h) * D;
@@ -591,11 +635,11 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       const int slot = pos == c_begin ? 0 : 1;
       if (slot == 0) {
 #pragma unroll
-        for (int n = 0; n < F::NT; ++n) s_hold[wv][n][lane] = acc[n];
-        s_hold_ml[wv][lane] = make_float2(m_run, l_tot);
+        for (int n = 0; n < F::NT; ++n) hold[n][lane] = acc[n];
+        hold_ml[lane] = make_float2(m_run, l_tot);
         holding = true;
       } else if (head_ok) {
-        store_partial<D>(a, int64_t(wave) * 2 + 1, h, row, acc, make_float2(m_run, l_tot));
+        store_partial<D>(a, (int64_t(share) * a.coop + sub) * 2 + 1, h, row, acc, make_float2(m_run, l_tot));
       }
     }
 
@@ -607,9 +651,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
       hg = 0;
       do {
         done = ++s >= a.B;
-      } while (!done && (L = seq_len(a, s, BS)) == 0);
+      } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
       if (done) break;
-      nb = (L + BS - 1) / BS;
+      L = seq_len(a, s, BS);
+      skip = GROUPED ? group_skip(a, s, BS) : 0;
+      nbt = (L + BS - 1) / BS;
+      nb = nbt - skip;
     }
     g = hg * a.coop + sub;
   }
@@ -617,11 +664,290 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
   if (holding && head_ok) {
     f32x4 acc[F::NT];
 #pragma unroll
-    for (int n = 0; n < F::NT; ++n) acc[n] = s_hold[wv][n][lane];
-    store_partial<D>(a, int64_t(wave) * 2, h, row, acc, s_hold_ml[wv][lane]);
+    for (int n = 0; n < F::NT; ++n) acc[n] = hold[n][lane];
+    store_partial<D>(a, (int64_t(share) * a.coop + sub) * 2, h, row, acc, hold_ml[lane]);
   }
   if constexpr (APPEND) {
     if (held.sub >= 0) issue_append_store<KV, D>(a, held, lane);
+  }
+}
+
+// Logical wave of this lane's wave.  Workgroup b runs on XCD b % 8; each XCD takes a contiguous
+// eighth of the work list (logical workgroup (b % 8) * (n / 8) + b / 8), so sequences next to
+// each other, such as the members of a group that share prefix blocks, read those blocks
+// through one XCD's L2 at about the same time.  Shares and pieces are numbered by the logical
+// wave.
+__device__ __forceinline__ int logical_wave(int wv) {
+  const int nwg = int(gridDim.x), full = nwg - nwg % kXcds;
+  const int b = int(blockIdx.x);
+  const int lwg = b < full ? (b % kXcds) * (full / kXcds) + b / kXcds : b;
+  return lwg * kWavesPerWG + wv;
+}
+
+// Writes every sequence's offset in a work list ([B], then the total at [B]) for the merge.
+// GROUP: the group work list (chunk first sequences).
+template <bool GROUPED, bool GROUP>
+__device__ __forceinline__ void write_offsets(const DecodeArgs& a, int bs, int lane, int* dst) {
+  int base = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int sq = b0 + lane;
+    const int w = sq < a.B ? (GROUP ? chunk_blocks(a, sq, bs) : unit_blocks<GROUPED>(a, sq, bs)) * head_groups(a) : 0;
+    const int incl = wave_incl_scan(w, lane);
+    if (sq < a.B) dst[sq] = base + incl - w;
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (lane == 0) dst[a.B] = base;
+}
+
+template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG = false>
+__global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_kernel(DecodeArgs a) {
+  using F = Frag<KV, D>;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = logical_wave(wv);
+  // The partial of a share's first segment waits in LDS until the share's loads are done: a
+  // wave's loads and stores complete in issue order, so a store in the middle of the share
+  // would hold up every load behind it.  Each lane reads back only what it wrote.
+  __shared__ f32x4 s_hold[kWavesPerWG][F::NT][64];
+  __shared__ float2 s_hold_ml[kWavesPerWG][64];
+  const int W = total_work(a, BS, lane);
+  if (wave == 0) {
+    write_offsets<false, false>(a, BS, lane, a.ws_seq);
+    if (lane == 0) {
+      a.ws_seq[a.B + 1] = a.splits;
+      a.ws_seq[a.B + 2] = a.coop;
+      a.ws_seq[a.B + 3] = a.B;
+    }
+  }
+  if (W == 0) return;
+  const int share = wave / a.coop;
+  const int sub = wave % a.coop;
+  const int nshare = std::min(a.splits / a.coop, W);
+  if (share >= nshare) return;
+  split_walk<KV, D, BS, NSUB, APPEND, MIX, CONTIG, false>(a, lane, share, sub, int(share_begin(share, W, nshare)),
+                                                          int(share_begin(share + 1, W, nshare)), s_hold[wv],
+                                                          s_hold_ml[wv]);
+}
+
+// One share of the group work list (chunk first sequence f, head group, block j < P_f):
+// positions [c_begin, c_end) of W.  A chunk's shared blocks come from its source sequence's
+// table and are read once for all its members: the 32 columns are (member m, query head h) =
+// (c / G, c % G) for the members f + m of the chunk, in two 16-column tiles, each column
+// masked to the tokens of its member's own shared blocks.  Every segment leaves a partial per
+// column: a unit finished inside the share in its (f, kv head) slot, the share's first and
+// last segments as pieces (share * coop + sub) * 2 + slot.
+template <int KV, int D, int BS>
+__device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin, int c_end,
+                                           f32x4 (*hold)[64], float2 (*hold_ml)[64]) {
+  using F = Frag<KV, D>;
+  using T = KvTraits<KV>;
+  constexpr int X = 16 / T::EB;
+  constexpr int SUB_BYTES = 16 * D * T::EB;
+  constexpr int NSB = BS / 16;
+  constexpr int64_t REGION = int64_t(BS) * D * T::EB;
+  constexpr int CT = kGroupCols / 16;
+  const int M = kGroupCols / a.G;
+  const int row = lane >> 4;
+  bool holding = false;
+
+  int f, chunk_off;
+  locate<false, true>(a, BS, lane, c_begin, f, chunk_off);
+  if (f >= a.B) return;
+  int P = chunk_blocks(a, f, BS);
+  int hg = (c_begin - chunk_off) / P;
+  int g = hg * a.coop + sub;
+  int unit_off = chunk_off + hg * P;
+  int pos = c_begin;
+  const int64_t block_stride = int64_t(a.Hkv) * REGION;
+
+  while (pos < c_end) {
+    const int unit_end = unit_off + P;
+    const int seg_end = std::min(c_end, unit_end);
+    const bool full = pos == unit_off && seg_end == unit_end;
+    const int k0 = (pos - unit_off) * NSB, k1 = (seg_end - unit_off) * NSB;   // whole blocks
+    // Columns: this lane's member and head in each tile, its token limit and q fragments.
+    int lim[CT];
+    uint4 qf[CT][F::NLOAD * F::QCH];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + (lane & 15);
+      const int m = c / a.G, hh = c % a.G, sq = f + m;
+      const bool member = m < M && sq < a.B && a.chunk_first[sq] == f;
+      lim[ct] = member ? group_skip(a, sq, BS) * BS : 0;
+      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                            ((int64_t(sq) * a.Hkv + g) * a.G + hh) * D * T::QB;
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i)
+#pragma unroll
+        for (int cc = 0; cc < F::QCH; ++cc)
+          qf[ct][i * F::QCH + cc] =
+              lim[ct] > 0 ? *reinterpret_cast<const uint4*>(qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * cc)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int32_t* trow = a.block_tables + int64_t(__builtin_amdgcn_readfirstlane(a.chunk_src[f])) * a.max_blocks;
+    int tbase = k0 / NSB;
+    int tbl = tbase + lane < P ? trow[tbase + lane] : -1;
+    f32x4 acc[CT][F::NT];
+    float m_run[CT], l_run[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+      for (int n = 0; n < F::NT; ++n) acc[ct][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[ct] = -INFINITY;
+      l_run[ct] = 0.f;
+    }
+    const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
+    const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
+
+    for (int k = k0; k < k1; ++k) {
+      if (k / NSB >= tbase + 64) {
+        tbase = k / NSB;
+        tbl = tbase + lane < P ? trow[tbase + lane] : -1;
+      }
+      // K and V of the sub-tile, loaded together with no branch before their use; a table
+      // entry outside [0, num_blocks) reads block 0, whose keys and values are zeroed.
+      const int phys = __builtin_amdgcn_readlane(tbl, k / NSB - tbase);
+      const bool bad = unsigned(phys) >= unsigned(a.num_blocks);
+      const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
+      uint4 kf[F::NLOAD], vf[F::NLOAD];
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_stream(kbase + off + i * 1024);
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_stream(vbase + off + i * 1024);
+      const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < F::NLOAD; ++i) {
+        kf[i].x &= km; kf[i].y &= km; kf[i].z &= km; kf[i].w &= km;
+      }
+      const int t0 = k * 16 + 4 * row;
+      float p[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
+        float sc[4];
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[j] = t0 + j < lim[ct] ? c[j] * a.qk_scale_log2 : -INFINITY;
+          cmax = fmaxf(cmax, sc[j]);
+        }
+        cmax = wave_max_rows(cmax);
+        const float m_new = fmaxf(m_run[ct], cmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;   // a column with no token yet
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+        m_run[ct] = m_new;
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int n = 0; n < F::NT; ++n) acc[ct][n] *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p[ct][j] = __builtin_amdgcn_exp2f(sc[j] - m_use);        // 0 where masked
+          l_run[ct] += p[ct][j];
+        }
+      }
+      mask_v<KV, D>(vf, bad ? 0u : 0xFu);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct]);
+    }
+
+    const int slot = pos == c_begin ? 0 : 1;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float l_tot = wave_sum_rows(l_run[ct]);
+      const int c = 16 * ct + (lane & 15);
+      if (full) {
+        store_row<D>(a.ws_fgacc, a.ws_fgml, (int64_t(f) * a.Hkv + g) * kGroupCols + c, row, acc[ct],
+                     make_float2(m_run[ct], l_tot));
+      } else if (slot == 0) {
+#pragma unroll
+        for (int n = 0; n < F::NT; ++n) hold[ct * F::NT + n][lane] = acc[ct][n];
+        hold_ml[ct][lane] = make_float2(m_run[ct], l_tot);
+      } else {
+        store_row<D>(a.ws_gacc, a.ws_gml, ((int64_t(share) * a.coop + sub) * 2 + 1) * kGroupCols + c, row, acc[ct],
+                     make_float2(m_run[ct], l_tot));
+      }
+    }
+    if (slot == 0 && !full) holding = true;
+
+    pos = seg_end;
+    if (pos >= c_end) break;
+    // Next unit: next kv-head group of this chunk, else the next chunk with blocks to read.
+    unit_off = unit_end;
+    if (++hg == head_groups(a)) {
+      hg = 0;
+      do {
+        ++f;
+      } while (f < a.B && chunk_blocks(a, f, BS) == 0);
+      if (f >= a.B) break;
+      P = chunk_blocks(a, f, BS);
+    }
+    g = hg * a.coop + sub;
+  }
+  if (holding) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x4 acc[F::NT];
+#pragma unroll
+      for (int n = 0; n < F::NT; ++n) acc[n] = hold[ct * F::NT + n][lane];
+      store_row<D>(a.ws_gacc, a.ws_gml, ((int64_t(share) * a.coop + sub) * 2) * kGroupCols + 16 * ct + (lane & 15), row,
+                   acc, hold_ml[ct][lane]);
+    }
+  }
+}
+
+// Share counts of a grouped launch: S shares in all, nsg of them over the group work list
+// (in proportion to its positions, at least one when it has any) and the rest over the
+// member work list; neither list gets more shares than it has positions.
+__device__ __forceinline__ void grouped_shares(const DecodeArgs& a, int Wm, int Wg, int& S, int& nsg) {
+  S = std::min(a.splits / a.coop, Wm + Wg);
+  nsg = 0;
+  if (Wg > 0) {
+    nsg = Wm == 0 ? S : int((int64_t(S) * Wg + (Wm + Wg) / 2) / (Wm + Wg));
+    nsg = std::min(std::max(nsg, 1), Wg);
+    nsg = std::min(nsg, S - (Wm > 0 ? 1 : 0));
+    nsg = std::max(nsg, S - Wm);
+  }
+}
+
+// The split pass with prefix groups: each share is a group share or a member share, spread
+// evenly over the launch (share w is a group share when floor((w+1) nsg / S) exceeds
+// floor(w nsg / S)), so that both kinds run on every XCD at once.  Header: member offsets
+// [B+1] (total at [B]), the split count, head-group width and B at [B+1..B+3], group offsets
+// [B+1] from [B+4] (total at [2B+4]), nsg at [2B+5].
+template <int KV, int D, int BS, int NSUB, bool APPEND>
+__global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_kernel(DecodeArgs a) {
+  using F = Frag<KV, D>;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = logical_wave(wv);
+  __shared__ f32x4 s_hold[kWavesPerWG][(kGroupCols / 16) * F::NT][64];
+  __shared__ float2 s_hold_ml[kWavesPerWG][kGroupCols / 16][64];
+  const int Wm = total_work<true>(a, BS, lane);
+  const int Wg = group_work(a, BS, lane);
+  int S, nsg;
+  grouped_shares(a, Wm, Wg, S, nsg);
+  if (wave == 0) {
+    write_offsets<true, false>(a, BS, lane, a.ws_seq);
+    write_offsets<false, true>(a, BS, lane, a.ws_seq + a.B + 4);
+    if (lane == 0) {
+      a.ws_seq[a.B + 1] = a.splits;
+      a.ws_seq[a.B + 2] = a.coop;
+      a.ws_seq[a.B + 3] = a.B;
+      a.ws_seq[2 * a.B + 5] = nsg;
+    }
+  }
+  const int share = wave / a.coop;
+  const int sub = wave % a.coop;
+  if (share >= S) return;
+  const int gi = int(int64_t(share) * nsg / S);
+  if (int64_t(share + 1) * nsg / S > gi) {
+    group_walk<KV, D, BS>(a, lane, gi, sub, int(share_begin(gi, Wg, nsg)), int(share_begin(gi + 1, Wg, nsg)),
+                          s_hold[wv], s_hold_ml[wv]);
+  } else {
+    const int ms = share - gi, nsm = S - nsg;
+    split_walk<KV, D, BS, NSUB, APPEND, false, false, true>(a, lane, ms, sub, int(share_begin(ms, Wm, nsm)),
+                                                            int(share_begin(ms + 1, Wm, nsm)), s_hold[wv],
+                                                            s_hold_ml[wv][0]);
   }
 }
 
@@ -796,6 +1122,143 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
   write(acc, a.v_scale / dsum);
 }
 
+// Merge of the split pass with prefix groups: one wave per (four query heads, kv head,
+// sequence).  A head's result is spread over the group pass's pieces of its column (member
+// s - f of chunk f: the (f, kv head) slot if one share finished the chunk's unit, else the
+// pieces of the shares it spans) and over its own unit's pieces (the (s, kv head) slot, or
+// the shares' pieces); all of them are folded with the running-softmax rule, eight at a time.
+// A piece whose column saw no token (max -inf) adds nothing.  Units the split pass finished
+// without a group part were written to `out` there; sequences without tokens get zeros.
+template <int KV, int D, int BS>
+__global__ __launch_bounds__(64) void paged_attention_grouped_merge_kernel(DecodeArgs a) {
+  constexpr int EPL = D / 16;
+  constexpr int BATCH = 8;
+  const int lane = threadIdx.x & 63;
+  const int hq_per_g = (a.G + kMergeHeads - 1) / kMergeHeads;
+  const int g = blockIdx.x / hq_per_g, s = blockIdx.y;
+  const int h_raw = (blockIdx.x % hq_per_g) * kMergeHeads + (lane >> 4);
+  const bool head_ok = h_raw < a.G;
+  const int h = head_ok ? h_raw : a.G - 1;
+  const int d0 = (lane & 15) * EPL;
+  const int64_t orow = ((int64_t(s) * a.Hkv + g) * a.G + h) * D + d0;
+  const int C = a.coop, sub = g % C, hg = g / C;
+  const int* goff = a.ws_seq + a.B + 4;
+  const int Wm = a.ws_seq[a.B], Wg = goff[a.B], nsg = a.ws_seq[2 * a.B + 5];
+  int S = 0, nsg_again = 0;   // the split pass's share counts, from the same arguments
+  grouped_shares(a, Wm, Wg, S, nsg_again);
+  const int nsm = S - nsg;
+
+  const int skip = group_skip(a, s, BS);
+  const int nbm = seq_blocks(a, s, BS) - skip;
+  // Group pieces [0, ng) and member pieces [ng, ng + nm): where each lies.
+  int ng = 0, nm = 0;
+  int64_t g_first = 0, g_wf = 0, m_first = 0, m_wf = 0;
+  bool g_slot = false, m_slot = false;
+  int col = 0;
+  int f = 0;
+  if (skip > 0) {
+    f = a.chunk_first[s];
+    col = (s - f) * a.G + h;
+    const int P = chunk_blocks(a, f, BS);
+    const int off = goff[f] + hg * P;
+    const int64_t wf = share_of(off, Wg, nsg), wl = share_of(off + P - 1, Wg, nsg);
+    g_slot = wf == wl;
+    ng = g_slot ? 1 : int(wl - wf + 1);
+    g_wf = wf;
+    g_first = (wf * C + sub) * 2 + (off != share_begin(wf, Wg, nsg) ? 1 : 0);
+  }
+  if (nbm > 0) {
+    const int off = a.ws_seq[s] + hg * nbm;
+    const int64_t wf = share_of(off, Wm, nsm), wl = share_of(off + nbm - 1, Wm, nsm);
+    if (wf == wl && skip == 0) return;   // finished and written by the split pass
+    m_slot = wf == wl;
+    nm = m_slot ? 1 : int(wl - wf + 1);
+    m_wf = wf;
+    m_first = (wf * C + sub) * 2 + (off != share_begin(wf, Wm, nsm) ? 1 : 0);
+  }
+  auto row_of = [&](int j, const float*& acc, const float*& ml) {
+    int64_t r;
+    if (j < ng) {
+      const int64_t pc = j == 0 ? g_first : ((g_wf + j) * C + sub) * 2;
+      if (g_slot) {
+        r = (int64_t(f) * a.Hkv + g) * kGroupCols + col;
+        acc = a.ws_fgacc; ml = a.ws_fgml;
+      } else {
+        r = pc * kGroupCols + col;
+        acc = a.ws_gacc; ml = a.ws_gml;
+      }
+    } else {
+      const int jm = j - ng;
+      const int64_t pc = jm == 0 ? m_first : ((m_wf + jm) * C + sub) * 2;
+      if (m_slot) {
+        r = (int64_t(s) * a.Hkv + g) * a.G + h;
+        acc = a.ws_macc; ml = a.ws_mml;
+      } else {
+        r = pc * a.G + h;
+        acc = a.ws_acc; ml = a.ws_ml;
+      }
+    }
+    acc += r * D + d0;
+    ml += r * 2;
+  };
+  float num[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+  float M = -INFINITY, den = 0.f;
+  const int np = ng + nm;
+  for (int j0 = 0; j0 < np; j0 += BATCH) {
+    float2 ml[BATCH];
+    float4 x[BATCH][EPL / 4];
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      const float* pa;
+      const float* pm;
+      row_of(std::min(j0 + t, np - 1), pa, pm);
+      ml[t] = *reinterpret_cast<const float2*>(pm);
+#pragma unroll
+      for (int i = 0; i < EPL / 4; ++i) x[t][i] = reinterpret_cast<const float4*>(pa)[i];
+    }
+    float mb = M;
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t)
+      if (j0 + t < np) mb = fmaxf(mb, ml[t].x);
+    if (mb == -INFINITY) continue;                  // nothing attended yet
+    const float alpha = __builtin_amdgcn_exp2f(M - mb);
+    den *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) num[e] *= alpha;
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t) {
+      const float c = j0 + t < np ? __builtin_amdgcn_exp2f(ml[t].x - mb) : 0.f;   // 0 for a -inf piece
+      den += ml[t].y * c;
+#pragma unroll
+      for (int i = 0; i < EPL / 4; ++i) {
+        num[4 * i + 0] += x[t][i].x * c;
+        num[4 * i + 1] += x[t][i].y * c;
+        num[4 * i + 2] += x[t][i].z * c;
+        num[4 * i + 3] += x[t][i].w * c;
+      }
+    }
+    M = mb;
+  }
+  if (!head_ok) return;
+  const float inv = den > 0.f ? a.v_scale / den : 0.f;
+  if constexpr (KV == PKV_F32) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + e) =
+          make_float4(num[e] * inv, num[e + 1] * inv, num[e + 2] * inv, num[e + 3] * inv);
+  } else {
+    uint32_t w[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL / 2; ++e) w[e] = pack_bf16x2(num[2 * e] * inv, num[2 * e + 1] * inv);
+    if constexpr (EPL == 8)
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + orow) = make_uint4(w[0], w[1], w[2], w[3]);
+    else
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow) = make_uint2(w[0], w[1]);
+  }
+}
+
 // ---- host side --------------------------------------------------------------------------
 
 // Sub-tiles per loop iteration: about 4 KiB of K (and as much V) per wave per step.
@@ -813,6 +1276,8 @@ struct KernelPair {
   KernelFn split[2];         // plain decode
   KernelFn split_append[2];  // decode step that stores each sequence's appended token first
   KernelFn split_contig;     // plain decode over contiguous per-sequence placement
+  KernelFn grouped[2];       // [append]: split pass with prefix groups read once per chunk
+  KernelFn grouped_merge;
   KernelFn merge;            // one wave per (sequence, kv head, four query heads)
   KernelFn merge_long;       // kMergeWavesLong waves each, for units that span many shares
 };
@@ -828,6 +1293,8 @@ KernelPair kernels_for() {
           {paged_attention_split_kernel<KV, D, BS, N, true, false>,
            paged_attention_split_kernel<KV, D, BS, N, true, kMix>},
           paged_attention_split_kernel<KV, D, BS, N, false, false, true>,
+          {paged_attention_grouped_kernel<KV, D, BS, N, false>, paged_attention_grouped_kernel<KV, D, BS, N, true>},
+          paged_attention_grouped_merge_kernel<KV, D, BS>,
           paged_attention_merge_kernel<KV, D, BS, 1>,
           paged_attention_merge_kernel<KV, D, BS, kMergeWavesLong>};
 }
@@ -923,6 +1390,34 @@ size_t workspace_bytes_for(int splits, int B, int G, int D) {
   return size_t(header_bytes(B) + acc_bytes(splits, G, D) + ml_bytes(splits, G));
 }
 
+// Workspace of the split pass with prefix groups, in order: a header (member and group work
+// offsets and the record), the member pieces of shares (as without groups), member units
+// finished inside a share [B * Hkv][G], the group pieces of shares [splits * 2][32], group
+// units finished inside a share [B * Hkv][32]; accumulators float32 [D] and (max, sum) pairs.
+struct GroupedLayout {
+  int64_t hdr, sacc, sml, macc, mml, gacc, gml, fgacc, fgml;
+  int64_t total() const { return hdr + sacc + sml + macc + mml + gacc + gml + fgacc + fgml; }
+};
+
+GroupedLayout grouped_layout(int splits, int B, int Hkv, int G, int D) {
+  GroupedLayout l;
+  l.hdr = round256((2 * int64_t(B) + 8) * 4);
+  l.sacc = acc_bytes(splits, G, D);
+  l.sml = ml_bytes(splits, G);
+  l.macc = round256(int64_t(B) * Hkv * G * D * 4);
+  l.mml = round256(int64_t(B) * Hkv * G * 2 * 4);
+  l.gacc = round256(int64_t(splits) * 2 * kGroupCols * D * 4);
+  l.gml = round256(int64_t(splits) * 2 * kGroupCols * 2 * 4);
+  l.fgacc = round256(int64_t(B) * Hkv * kGroupCols * D * 4);
+  l.fgml = round256(int64_t(B) * Hkv * kGroupCols * 2 * 4);
+  return l;
+}
+
+// Split count of the grouped pass: as requested, at least two (one share of each kind).
+int grouped_splits(int splits, int B, int Hkv, int max_blocks) {
+  return int(std::max<int64_t>(2, std::min<int64_t>(splits, 2 * int64_t(B) * Hkv * std::max(1, max_blocks))));
+}
+
 enum Phase { kBoth, kSplitOnly, kMergeOnly };
 
 // k_new / v_new non-null: the decode step with append (the split pass stores each
@@ -934,9 +1429,11 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
                       int num_blocks, int max_blocks, float scale, float k_scale, float v_scale,
                       pkv_dtype qd, pkv_dtype kd, int num_splits, void* workspace,
                       size_t workspace_bytes, const int32_t* shared_prefix, void* stream,
-                      const int32_t* seq_first_block = nullptr) {
+                      const int32_t* seq_first_block = nullptr, const int32_t* chunk_first = nullptr,
+                      const int32_t* chunk_src = nullptr, const int32_t* group_blocks = nullptr) {
   const bool append = k_new != nullptr || v_new != nullptr;
   const bool contig = seq_first_block != nullptr;
+  const bool grouped = chunk_first != nullptr || chunk_src != nullptr || group_blocks != nullptr;
   pkv_status st = check_shape(fn, B, Hq, Hkv, D, bs, qd, kd);
   if (st != PKV_OK) return st;
   if (num_blocks <= 0 || max_blocks < 0)
@@ -951,6 +1448,13 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     return pkv::fail(PKV_INVALID_ARG, "%s: the contiguous placement takes no append or shared-prefix counts", fn);
   if (reinterpret_cast<uintptr_t>(seq_first_block) % 4 != 0)
     return pkv::fail(PKV_INVALID_ARG, "%s: seq_first_block must be 4-byte aligned", fn);
+  if (grouped && (!chunk_first || !chunk_src || !group_blocks))
+    return pkv::fail(PKV_INVALID_ARG, "%s: chunk_first, chunk_src and group_blocks must all be given", fn);
+  if (grouped && (contig || shared_prefix || phase != kBoth))
+    return pkv::fail(PKV_INVALID_ARG, "%s: prefix groups take no contiguous placement or shared-prefix counts", fn);
+  if ((reinterpret_cast<uintptr_t>(chunk_first) | reinterpret_cast<uintptr_t>(chunk_src) |
+       reinterpret_cast<uintptr_t>(group_blocks)) % 4 != 0)
+    return pkv::fail(PKV_INVALID_ARG, "%s: chunk_first, chunk_src and group_blocks must be 4-byte aligned", fn);
   if (append && (!k_new || !v_new || !k_cache_w || !v_cache_w))
     return pkv::fail(PKV_INVALID_ARG, "%s: k_new and v_new must both be given", fn);
   if (!pkv::aligned16({out, q, k_cache, v_cache, k_new, v_new, workspace}))
@@ -964,13 +1468,15 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   const int G = Hq / Hkv;
   // The reduce pass takes the partials' layout from the header the split pass wrote, so it
   // needs only the header to be addressable; the merge kernel checks the rest on the device.
-  const size_t need = phase == kMergeOnly ? size_t(header_bytes(B)) : workspace_bytes_for(splits, B, G, D);
+  const size_t need = grouped ? size_t(grouped_layout(grouped_splits(splits, B, Hkv, max_blocks), B, Hkv, G, D).total())
+                      : phase == kMergeOnly ? size_t(header_bytes(B))
+                                            : workspace_bytes_for(splits, B, G, D);
   if (!workspace || workspace_bytes < need)
     return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn,
                      workspace_bytes, need);
   if (int64_t(B) > 65535 || Hkv > 65535)
     return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
-  if (int64_t(B) * max_blocks * Hkv > int64_t(INT32_MAX))
+  if (int64_t(B) * max_blocks * Hkv * (grouped ? 2 : 1) > int64_t(INT32_MAX))
     return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31", fn);
 
   DecodeArgs a;
@@ -986,8 +1492,10 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.num_blocks = num_blocks;
   a.max_blocks = max_blocks;
   // More shares than (sequence, kv head, block) triples would only launch idle waves; the
-  // table width bounds the triples without reading the device-side lengths.
-  a.splits = int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * max_blocks)));
+  // table width bounds the triples without reading the device-side lengths (with prefix
+  // groups, twice: group and member lists; and at least one share of each kind).
+  a.splits = grouped ? grouped_splits(splits, B, Hkv, max_blocks)
+                     : int(std::max<int64_t>(1, std::min<int64_t>(splits, int64_t(B) * Hkv * max_blocks)));
   // The partials are laid out for the share count the kernels use, which the split pass
   // records in the header and the merge reads back.
   a.ws_seq = static_cast<int*>(workspace);
@@ -995,7 +1503,9 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(a.ws_acc) + acc_bytes(a.splits, G, D));
   a.ws_bytes = int64_t(workspace_bytes);
   a.coop = 1;
-  while (a.coop < kWavesPerWG && Hkv % (2 * a.coop) == 0 && a.splits >= 2 * a.coop) a.coop *= 2;
+  // With prefix groups every head group must leave at least two shares (one of each kind).
+  const int coop_min_shares = grouped ? 4 : 2;
+  while (a.coop < kWavesPerWG && Hkv % (2 * a.coop) == 0 && a.splits >= coop_min_shares * a.coop) a.coop *= 2;
   a.qk_scale_log2 = scale * k_scale * kLog2e;
   a.v_scale = v_scale;
   a.k_new = k_new;
@@ -1006,11 +1516,32 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
   a.v_inv = 1.0f / v_scale;
   a.shared_prefix = shared_prefix;
   a.seq_first_block = seq_first_block;
+  a.chunk_first = chunk_first;
+  a.chunk_src = chunk_src;
+  a.group_blocks = group_blocks;
+  a.appending = append ? 1 : 0;
+  if (grouped) {
+    // Grouped layout: the member share pieces sit where the plain layout puts its pieces.
+    const GroupedLayout l = grouped_layout(a.splits, B, Hkv, G, D);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.ws_seq = reinterpret_cast<int*>(w);
+    a.ws_acc = reinterpret_cast<float*>(w + l.hdr);
+    a.ws_ml = reinterpret_cast<float*>(w + l.hdr + l.sacc);
+    a.ws_macc = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml);
+    a.ws_mml = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc);
+    a.ws_gacc = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml);
+    a.ws_gml = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc);
+    a.ws_fgacc = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc + l.gml);
+    a.ws_fgml = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc + l.gml + l.fgacc);
+  }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {
     const unsigned wgs = unsigned((int64_t(a.splits) + kWavesPerWG - 1) / kWavesPerWG);
     const int mixed = shared_prefix != nullptr ? 1 : 0;
-    KernelFn kfn = contig ? kp.split_contig : append ? kp.split_append[mixed] : kp.split[mixed];
+    KernelFn kfn = grouped  ? kp.grouped[append ? 1 : 0]
+                   : contig ? kp.split_contig
+                   : append ? kp.split_append[mixed]
+                            : kp.split[mixed];
     void *ev0 = nullptr, *ev1 = nullptr;
     if (pkv::take_launch_events(&ev0, &ev1)) {
       // The dispatch itself records the events, so they time the kernel alone.
@@ -1033,7 +1564,9 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     const int64_t units = int64_t(B) * (Hkv / a.coop);
     const int64_t shares = std::min<int64_t>(a.splits / a.coop, units * max_blocks);
     const bool long_units = shares >= int64_t(kLongMergePieces) * units;
-    if (long_units)
+    if (grouped)
+      hipLaunchKernelGGL(kp.grouped_merge, dim3(merge_x, unsigned(B)), dim3(64), 0, hs, a);
+    else if (long_units)
       hipLaunchKernelGGL(kp.merge_long, dim3(merge_x, unsigned(B)), dim3(64 * kMergeWavesLong), 0, hs, a);
     else
       hipLaunchKernelGGL(kp.merge, dim3(merge_x, unsigned(B)), dim3(64), 0, hs, a);
@@ -1185,6 +1718,59 @@ pkv_status pkv_paged_decode_step(PKV_STEP_PARAMS) {
   if (!k_new || !v_new) return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step: null k_new / v_new");
   return run_decode("pkv_paged_decode_step", kBoth, PKV_STEP_ARGS);
 }
+pkv_status pkv_paged_attention_grouped_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                                      int block_size, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                                                      int num_splits, int max_blocks_per_seq, size_t* bytes) {
+  pkv_status st = check_shape("pkv_paged_attention_grouped_workspace_size", num_seqs, num_q_heads, num_kv_heads,
+                              head_dim, block_size, q_dtype, kv_dtype);
+  if (st != PKV_OK) return st;
+  if (!bytes || max_blocks_per_seq < 0)
+    return pkv::fail(PKV_INVALID_ARG, "pkv_paged_attention_grouped_workspace_size: bad arguments");
+  KernelPair kp;
+  pick_kernels(kv_dtype, head_dim, block_size, &kp);
+  int splits = 0;
+  if ((st = effective_splits(kp, kv_dtype, num_splits, &splits)) != PKV_OK) return st;
+  *bytes = size_t(grouped_layout(grouped_splits(splits, num_seqs, num_kv_heads, max_blocks_per_seq), num_seqs,
+                                 num_kv_heads, num_q_heads / num_kv_heads, head_dim)
+                      .total());
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_attention_decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              const int32_t* chunk_first, const int32_t* chunk_src,
+                                              const int32_t* group_blocks, int num_seqs, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                              int max_blocks_per_seq, float scale, float k_scale, float v_scale,
+                                              pkv_dtype q_dtype, pkv_dtype kv_dtype, int num_splits, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_paged_attention_decode_grouped";
+  if (num_seqs > 0 && (!chunk_first || !chunk_src || !group_blocks))
+    return pkv::fail(PKV_INVALID_ARG, "%s: null chunk_first / chunk_src / group_blocks", fn);
+  return run_decode(fn, kBoth, out, q, nullptr, nullptr, k_cache, v_cache, nullptr, nullptr, block_tables,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                    max_blocks_per_seq, scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace,
+                    workspace_bytes, nullptr, stream, nullptr, chunk_first, chunk_src, group_blocks);
+}
+
+pkv_status pkv_paged_decode_step_grouped(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                         const int32_t* chunk_first, const int32_t* chunk_src,
+                                         const int32_t* group_blocks, int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                         float scale, float k_scale, float v_scale, pkv_dtype q_dtype,
+                                         pkv_dtype kv_dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  const char* fn = "pkv_paged_decode_step_grouped";
+  if (!k_new || !v_new) return pkv::fail(PKV_INVALID_ARG, "%s: null k_new / v_new", fn);
+  if (num_seqs > 0 && (!chunk_first || !chunk_src || !group_blocks))
+    return pkv::fail(PKV_INVALID_ARG, "%s: null chunk_first / chunk_src / group_blocks", fn);
+  return run_decode(fn, kBoth, out, q, k_new, v_new, k_cache, v_cache, k_cache, v_cache, block_tables,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                    max_blocks_per_seq, scale, k_scale, v_scale, q_dtype, kv_dtype, num_splits, workspace,
+                    workspace_bytes, nullptr, stream, nullptr, chunk_first, chunk_src, group_blocks);
+}
+
 pkv_status pkv_paged_decode_step_split(PKV_STEP_PARAMS) {
   if (!k_new || !v_new)
     return pkv::fail(PKV_INVALID_ARG, "pkv_paged_decode_step_split: null k_new / v_new");

@@ -14,7 +14,11 @@ Blocks" and "Share Without Mutating State"; "PagedAttention: Optimizing KV Cache
   3. pkv_apply_append updates the device copies of the tables and lengths, reading the slots
      straight from the pinned buffer (no upload);
   4. pkv_paged_decode_step_split stores each sequence's new token into its slot and runs the
-     split pass over every token, then pkv_paged_attention_reduce merges.
+     split pass over every token, then pkv_paged_attention_reduce merges.  With prefix groups
+     (``prefix_groups=True``), pkv_paged_decode_step_grouped does both passes instead, reading
+     each group's shared blocks once for all its sequences; the groups (pkv_alloc_prefix_groups)
+     are taken again after every append that copied a shared tail, and go to the device from
+     the same pinned buffer.
 The two host buffers alternate, so the host prepares step i+1 while the device runs step i.
 """
 from __future__ import annotations
@@ -24,15 +28,16 @@ import time
 import numpy as np
 import torch
 
-from . import (BF16, apply_append, copy_blocks, paged_attention_default_splits, paged_attention_reduce,
-               paged_attention_workspace_size, paged_decode_step_split, set_launch_events, _dtype_code,
-               _pool_dims)
+from . import (BF16, apply_append, copy_blocks, paged_attention_default_splits, paged_attention_grouped_workspace_size,
+               paged_attention_reduce, paged_attention_workspace_size, paged_decode_step_grouped,
+               paged_decode_step_split, set_launch_events, _dtype_code, _pool_dims)
 
 
 class _HostBuf:
     def __init__(self, n: int):
         self.slots = torch.empty(n, dtype=torch.int64, pin_memory=True)
         self.cow = torch.empty((n, 2), dtype=torch.int32, pin_memory=True)
+        self.groups = torch.empty((3, n), dtype=torch.int32, pin_memory=True)
         self.done = torch.cuda.Event()
 
 
@@ -48,7 +53,7 @@ class DecodeStep:
     """
 
     def __init__(self, alloc, members, k_cache, v_cache, head_dim: int, num_q_heads: int, max_blocks: int,
-                 num_splits: int = 0, shared_prefix: bool = True):
+                 num_splits: int = 0, shared_prefix: bool = True, prefix_groups: bool = False):
         self.alloc = alloc
         self.members = np.ascontiguousarray(members, dtype=np.int64)
         self.k, self.v = k_cache, v_cache
@@ -64,8 +69,18 @@ class DecodeStep:
         counts = alloc.shared_prefix_blocks(self.members)
         self.shared_counts = counts
         self.shared = torch.from_numpy(counts).to(dev) if shared_prefix and counts.any() else None
-        self.ws = torch.empty(paged_attention_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, BF16, kd,
-                                                             self.num_splits), dtype=torch.uint8, device=dev)
+        self.prefix_groups = prefix_groups
+        self.max_chunk = 32 // (num_q_heads // self.Hkv)
+        if prefix_groups:
+            self.shared = None                 # shared blocks are read once, streamed
+            self.groups = torch.empty((3, B), dtype=torch.int32, device=dev)
+            self._groups_host = None
+            nbytes = paged_attention_grouped_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, BF16, kd,
+                                                            self.num_splits, max_blocks)
+        else:
+            nbytes = paged_attention_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, BF16, kd,
+                                                    self.num_splits)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.cow_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
         self.bufs = [_HostBuf(B), _HostBuf(B)]
         self.steps = 0
@@ -96,9 +111,23 @@ class DecodeStep:
         if n_cow:
             copy_blocks(self.k, self.v, self.cow_d[:n_cow], self.D)
         apply_append(self.tables, self.lens, hb.slots, self.bs, self.num_blocks)
+        if self.prefix_groups and (n_cow or self._groups_host is None):
+            # A copy-on-write changed which leading blocks sequences share: take the groups again.
+            t0 = time.perf_counter()
+            self._groups_host = self.alloc.prefix_groups(self.members, self.max_chunk)
+            self.host_alloc_s += time.perf_counter() - t0
+            gh = hb.groups.numpy()
+            for i in range(3):
+                gh[i] = self._groups_host[i]
+            self.groups.copy_(hb.groups, non_blocking=True)
         hb.done.record(stream)
         if kernel_events is not None:
             set_launch_events(kernel_events[0], kernel_events[1])
+        if self.prefix_groups:
+            paged_decode_step_grouped(out, q, k_new, v_new, self.k, self.v, self.tables, self.lens,
+                                      (self.groups[0], self.groups[1], self.groups[2]), scale, k_scale, v_scale,
+                                      num_splits=self.num_splits, workspace=self.ws)
+            return n_cow
         paged_decode_step_split(out, q, k_new, v_new, self.k, self.v, self.tables, self.lens, scale, k_scale,
                                 v_scale, num_splits=self.num_splits, workspace=self.ws,
                                 shared_prefix_blocks=self.shared)

@@ -159,6 +159,10 @@ class AllocatorMachine(RuleBasedStateMachine):
         _compare(self.a, self.m)
         _compare(self.ah, self.mh)
         assert self.a.stats() == self.m.stats() and self.ah.stats() == self.mh.stats()
+        ids = self._ids()
+        for k in (1, 2, 3, 8):
+            got = [x.tolist() for x in self.a.prefix_groups(ids, k)]
+            assert got == [list(x) for x in self.m.prefix_groups(ids, k)], (ids, k)
         self.m.check_invariants()
         self.mh.check_invariants()
 
@@ -231,6 +235,40 @@ def test_shared_prefix_blocks_counts_leading_blocks_held_by_several_sequences():
     assert a.shared_prefix_blocks([0]).tolist() == [0]
     with pytest.raises(pkv.PagedKVError) as e:
         a.shared_prefix_blocks([0, 99])
+    assert e.value.status_name == "UNKNOWN_SEQ"
+
+
+def test_prefix_groups_worked_example():
+    """Worked by hand (16-token blocks): root 0 of 40 tokens (blocks r0 r1 r2) with forks 1 at
+    40 and 2 at 20 tokens, a sequence 3 of its own, then 4 forked from 0 at 33 tokens.
+    Listed as [1, 2, 0, 4, 3]: 1, 2, 0 and 4 start with r0 (shared); 3 does not.  In one chunk
+    the source is the first member with the longest shared lead (1: r0 r1 r2 all shared), and
+    each member counts its entries equal to 1's: 2 has r0 r1, 0 has r0 r1 r2, 4 has r0 r1 r2;
+    the source takes the most of the others, 3.  With chunks of 2: [1, 2] (source 1, 2 shares
+    2, so 1 gets 2) and [0, 4] (source 0, 4 shares 3).  Then after a copy-on-write, below."""
+    a = pkv.BlockAllocator(12, 16)
+    a.seq_create(0, 40)
+    a.fork(0, 1, 40)
+    a.fork(0, 2, 20)
+    a.seq_create(3, 5)
+    a.fork(0, 4, 33)
+    first, src, blocks = a.prefix_groups([1, 2, 0, 4, 3], 8)
+    assert first.tolist() == [0, 0, 0, 0, 4]
+    assert src.tolist() == [0, 0, 0, 0, 4]
+    assert blocks.tolist() == [3, 2, 3, 3, 0]
+    first, src, blocks = a.prefix_groups([1, 2, 0, 4, 3], 2)
+    assert first.tolist() == [0, 0, 2, 2, 4]
+    assert src.tolist() == [0, 0, 2, 2, 4]
+    assert blocks.tolist() == [2, 2, 3, 3, 0]
+    # 1 appends into r2 (shared, 40 tokens): it gets a copy c.  Leads: 1 has r0 r1 (2), 2 has
+    # r0 r1 (2), 0 and 4 have r0 r1 r2 (3): the source is index 2 (sequence 0).  Equal entries:
+    # 1 has r0 r1 (c differs), 2 has its two blocks, 4 all three; the source takes 3.
+    a.append([1])
+    first, src, blocks = a.prefix_groups([1, 2, 0, 4, 3], 8)
+    assert src.tolist() == [2, 2, 2, 2, 4]
+    assert blocks.tolist() == [2, 2, 3, 3, 0]
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.prefix_groups([1, 99], 8)
     assert e.value.status_name == "UNKNOWN_SEQ"
 
 

@@ -62,6 +62,34 @@ constexpr int kXcds = 8;   // MI355X: workgroups are dealt to the 8 XCDs round-r
 constexpr int kMaxGroup = 16;
 constexpr int kGroupCols = 32;   // (member, query head) columns of a group share: two 16-column tiles
 
+// Work lists are cut by estimated cost, not by block count.  A unit (one sequence's blocks for
+// one head group) weighs kUnitW plus kBlockW per block: its q and table round trip and its
+// epilogue cost about 1.5 blocks' time, measured on MI355X (with equal blocks per share, a
+// share crossing 16 units ended 54 us after one crossing a single unit, 1.5 blocks' time per
+// extra unit).  A group share's block, with 32 columns of matrix and softmax work, weighs
+// kGroupBlockW (measured 2.73 against 2.41 us per block).  A block belongs to the share
+// holding its first weighted position.
+constexpr int kBlockW = 8;
+constexpr int kGroupBlockW = 9;
+constexpr int kUnitW = 12;
+
+__host__ __device__ __forceinline__ int unit_span(int nb, int block_w) { return nb > 0 ? nb * block_w + kUnitW : 0; }
+
+// Shares of a work list of W weighted positions: at most `want`, and none shorter than a
+// block's weight, so that every share lying inside a unit holds a block of it (the merge
+// takes a piece from each share between the unit's first block and its last).
+__host__ __device__ __forceinline__ int list_shares(int want, int W, int block_w) {
+  return std::min(want, W / block_w);
+}
+
+// Blocks [j0, j1) of a unit (first weighted position unit_off, nb blocks of weight block_w)
+// whose first weighted positions lie in [lo, hi).
+__device__ __forceinline__ void unit_blocks_in(int unit_off, int nb, int block_w, int lo, int hi, int& j0, int& j1) {
+  const int base = unit_off + kUnitW;
+  j0 = lo <= base ? 0 : std::min(nb, (lo - base + block_w - 1) / block_w);
+  j1 = hi <= base ? 0 : std::min(nb, (hi - base + block_w - 1) / block_w);
+}
+
 // Workspace layout: header (per-sequence work offsets and the split pass's record), partial
 // accumulators, partial (max, sum) pairs; each part rounded up to 256 bytes.
 __host__ __device__ constexpr int64_t round256(int64_t n) { return (n + 255) / 256 * 256; }
@@ -180,36 +208,40 @@ __device__ __forceinline__ int unit_blocks(const DecodeArgs& a, int s, int bs) {
   return nb;
 }
 
-// Total work W = head_groups * sum_s blocks(s) (wave-uniform; the host checks it fits in int).
+// Total work W = head_groups * sum_s unit_span(blocks(s)) (wave-uniform; the host checks it
+// fits in int).
 template <bool GROUPED = false>
 __device__ int total_work(const DecodeArgs& a, int bs, int lane) {
   int acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
-    acc += s < a.B ? unit_blocks<GROUPED>(a, s, bs) : 0;
+    acc += s < a.B ? unit_span(unit_blocks<GROUPED>(a, s, bs), kBlockW) : 0;
   }
   return wave_sum(acc) * head_groups(a);
 }
 
-// Group work: head_groups * sum over chunk first sequences f of chunk_blocks(f).
+// Group work: head_groups * sum over chunk first sequences f of their units' spans.
 __device__ int group_work(const DecodeArgs& a, int bs, int lane) {
   int acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
-    acc += s < a.B ? chunk_blocks(a, s, bs) : 0;
+    acc += s < a.B ? unit_span(chunk_blocks(a, s, bs), kGroupBlockW) : 0;
   }
   return wave_sum(acc) * head_groups(a);
 }
 
-// Sequence whose units contain work position x (0 <= x < W), and head_groups * blocks
-// before it.  GROUP: over the group work list (chunk first sequences and their blocks).
+// Sequence whose units contain work position x (0 <= x < W), and the weighted positions of
+// the units before it.  GROUP: over the group work list (chunk first sequences and their
+// blocks).
 template <bool GROUPED = false, bool GROUP = false>
 __device__ void locate(const DecodeArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
   int base = 0;
   const int hg = head_groups(a);
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int s = b0 + lane;
-    const int w = s < a.B ? (GROUP ? chunk_blocks(a, s, bs) : unit_blocks<GROUPED>(a, s, bs)) * hg : 0;
+    const int w = s < a.B ? (GROUP ? unit_span(chunk_blocks(a, s, bs), kGroupBlockW)
+                                   : unit_span(unit_blocks<GROUPED>(a, s, bs), kBlockW)) * hg
+                          : 0;
     const int incl = wave_incl_scan(w, lane);
     const int lo = base + (incl - w), hi = base + incl;
     const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
@@ -452,10 +484,30 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
   int skip = GROUPED ? group_skip(a, s, BS) : 0;   // leading blocks the group pass reads
   int nbt = (L + BS - 1) / BS;                     // blocks of the sequence
   int nb = nbt - skip;                             // blocks of each of its units in this list
-  int hg = (c_begin - seq_off) / nb;
+  int span = unit_span(nb, kBlockW);
+  int hg = (c_begin - seq_off) / span;
   int g = hg * a.coop + sub;
-  int unit_off = seq_off + hg * nb;
+  int unit_off = seq_off + hg * span;
   int pos = c_begin;
+  bool done = false;
+  // Next unit: next kv head of this sequence, else the next sequence with blocks in the list.
+  auto next_unit = [&]() {
+    unit_off += span;
+    if (++hg == head_groups(a)) {
+      hg = 0;
+      do {
+        done = ++s >= a.B;
+      } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
+      if (done) return false;
+      L = seq_len(a, s, BS);
+      skip = GROUPED ? group_skip(a, s, BS) : 0;
+      nbt = (L + BS - 1) / BS;
+      nb = nbt - skip;
+      span = unit_span(nb, kBlockW);
+    }
+    g = hg * a.coop + sub;
+    return true;
+  };
 
   const int h = lane & 15;       // head (within the group) of this lane's QK/PV column
   const int row = lane >> 4;     // token group 4*row.. of this lane's QK/PV rows
@@ -467,13 +519,19 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
   // its pool stores in registers until the wave has issued its last load: a wave's loads and
   // stores complete in issue order, so a store ahead of the remaining loads would delay them.
   AppendStore<KV, D> held;
-  bool done = false;
   while (pos < c_end) {
     const int Lc = APPEND ? L - 1 : L;
-    const int unit_end = unit_off + nb;
+    const int unit_end = unit_off + span;
     const int seg_end = std::min(c_end, unit_end);
-    const bool full = pos == unit_off && seg_end == unit_end;
-    const int j0 = skip + pos - unit_off, j1 = skip + seg_end - unit_off;   // blocks [j0, j1)
+    int r0, r1;                                       // the unit's blocks this share holds
+    unit_blocks_in(unit_off, nb, kBlockW, c_begin, c_end, r0, r1);
+    if (r1 <= r0) {                                   // none: the share ends or starts in this
+      pos = seg_end;                                  // unit's weight without a block start
+      if (pos >= c_end || !next_unit()) break;
+      continue;
+    }
+    const bool full = r0 == 0 && r1 == nb;
+    const int j0 = skip + r0, j1 = skip + r1;         // blocks [j0, j1) of the sequence
     const int k0 = j0 * NSB;
     const int k1 = (std::min(j1 * BS, Lc) + 15) / 16;                   // sub-tiles [k0, k1)
     // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
@@ -501,7 +559,7 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
     int first = 0;
     if constexpr (CONTIG) first = __builtin_amdgcn_readfirstlane(a.seq_first_block[s]);
     else tbl = tbase + lane < nbt ? trow[tbase + lane] : -1;
-    const bool ends_unit = APPEND && seg_end == unit_end;
+    const bool ends_unit = APPEND && r1 == nb;
     AppendRegs<KV, D> app;
     if constexpr (APPEND) {
       if (ends_unit) load_append_regs<KV, D>(a, s, g, lane, app);
@@ -632,7 +690,9 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
         }
       }
     } else {
-      const int slot = pos == c_begin ? 0 : 1;
+      // The share's first segment (it begins within this unit's weight) waits in LDS; any
+      // other unfinished segment is the share's last.
+      const int slot = c_begin >= unit_off ? 0 : 1;
       if (slot == 0) {
 #pragma unroll
         for (int n = 0; n < F::NT; ++n) hold[n][lane] = acc[n];
@@ -644,21 +704,7 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
     }
 
     pos = seg_end;
-    if (pos >= c_end) break;
-    // Next unit: next kv head of this sequence, else the next non-empty sequence.
-    unit_off = unit_end;
-    if (++hg == head_groups(a)) {
-      hg = 0;
-      do {
-        done = ++s >= a.B;
-      } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
-      if (done) break;
-      L = seq_len(a, s, BS);
-      skip = GROUPED ? group_skip(a, s, BS) : 0;
-      nbt = (L + BS - 1) / BS;
-      nb = nbt - skip;
-    }
-    g = hg * a.coop + sub;
+    if (pos >= c_end || !next_unit()) break;
   }
 
   if (holding && head_ok) {
@@ -691,7 +737,9 @@ __device__ __forceinline__ void write_offsets(const DecodeArgs& a, int bs, int l
   int base = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int sq = b0 + lane;
-    const int w = sq < a.B ? (GROUP ? chunk_blocks(a, sq, bs) : unit_blocks<GROUPED>(a, sq, bs)) * head_groups(a) : 0;
+    const int w = sq < a.B ? (GROUP ? unit_span(chunk_blocks(a, sq, bs), kGroupBlockW)
+                                    : unit_span(unit_blocks<GROUPED>(a, sq, bs), kBlockW)) * head_groups(a)
+                           : 0;
     const int incl = wave_incl_scan(w, lane);
     if (sq < a.B) dst[sq] = base + incl - w;
     base += __builtin_amdgcn_readlane(incl, 63);
@@ -722,7 +770,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
   if (W == 0) return;
   const int share = wave / a.coop;
   const int sub = wave % a.coop;
-  const int nshare = std::min(a.splits / a.coop, W);
+  const int nshare = list_shares(a.splits / a.coop, W, kBlockW);
   if (share >= nshare) return;
   split_walk<KV, D, BS, NSUB, APPEND, MIX, CONTIG, false>(a, lane, share, sub, int(share_begin(share, W, nshare)),
                                                           int(share_begin(share + 1, W, nshare)), s_hold[wv],
@@ -754,17 +802,39 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
   locate<false, true>(a, BS, lane, c_begin, f, chunk_off);
   if (f >= a.B) return;
   int P = chunk_blocks(a, f, BS);
-  int hg = (c_begin - chunk_off) / P;
+  int span = unit_span(P, kGroupBlockW);
+  int hg = (c_begin - chunk_off) / span;
   int g = hg * a.coop + sub;
-  int unit_off = chunk_off + hg * P;
+  int unit_off = chunk_off + hg * span;
   int pos = c_begin;
   const int64_t block_stride = int64_t(a.Hkv) * REGION;
+  // Next unit: next kv-head group of this chunk, else the next chunk with blocks to read.
+  auto next_unit = [&]() {
+    unit_off += span;
+    if (++hg == head_groups(a)) {
+      hg = 0;
+      do {
+        ++f;
+      } while (f < a.B && chunk_blocks(a, f, BS) == 0);
+      if (f >= a.B) return false;
+      P = chunk_blocks(a, f, BS);
+      span = unit_span(P, kGroupBlockW);
+    }
+    g = hg * a.coop + sub;
+    return true;
+  };
 
   while (pos < c_end) {
-    const int unit_end = unit_off + P;
-    const int seg_end = std::min(c_end, unit_end);
-    const bool full = pos == unit_off && seg_end == unit_end;
-    const int k0 = (pos - unit_off) * NSB, k1 = (seg_end - unit_off) * NSB;   // whole blocks
+    const int seg_end = std::min(c_end, unit_off + span);
+    int r0, r1;                                       // the unit's blocks this share holds
+    unit_blocks_in(unit_off, P, kGroupBlockW, c_begin, c_end, r0, r1);
+    if (r1 <= r0) {
+      pos = seg_end;
+      if (pos >= c_end || !next_unit()) break;
+      continue;
+    }
+    const bool full = r0 == 0 && r1 == P;
+    const int k0 = r0 * NSB, k1 = r1 * NSB;           // whole blocks
     // Columns: this lane's member and head in each tile, its token limit and q fragments.
     int lim[CT];
     uint4 qf[CT][F::NLOAD * F::QCH];
@@ -850,7 +920,7 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
       for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct]);
     }
 
-    const int slot = pos == c_begin ? 0 : 1;
+    const int slot = c_begin >= unit_off ? 0 : 1;   // first segment of the share, or its last
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const float l_tot = wave_sum_rows(l_run[ct]);
@@ -870,18 +940,7 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
     if (slot == 0 && !full) holding = true;
 
     pos = seg_end;
-    if (pos >= c_end) break;
-    // Next unit: next kv-head group of this chunk, else the next chunk with blocks to read.
-    unit_off = unit_end;
-    if (++hg == head_groups(a)) {
-      hg = 0;
-      do {
-        ++f;
-      } while (f < a.B && chunk_blocks(a, f, BS) == 0);
-      if (f >= a.B) break;
-      P = chunk_blocks(a, f, BS);
-    }
-    g = hg * a.coop + sub;
+    if (pos >= c_end || !next_unit()) break;
   }
   if (holding) {
 #pragma unroll
@@ -896,16 +955,17 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
 }
 
 // Share counts of a grouped launch: S shares in all, nsg of them over the group work list
-// (in proportion to its positions, at least one when it has any) and the rest over the
-// member work list; neither list gets more shares than it has positions.
+// (in proportion to its weighted positions, at least one when it has any) and the rest over
+// the member work list; neither list gets a share shorter than one of its blocks' weight.
 __device__ __forceinline__ void grouped_shares(const DecodeArgs& a, int Wm, int Wg, int& S, int& nsg) {
-  S = std::min(a.splits / a.coop, Wm + Wg);
+  const int max_g = Wg / kGroupBlockW, max_m = Wm / kBlockW;   // shares no shorter than a block
+  S = std::min(a.splits / a.coop, max_g + max_m);
   nsg = 0;
   if (Wg > 0) {
     nsg = Wm == 0 ? S : int((int64_t(S) * Wg + (Wm + Wg) / 2) / (Wm + Wg));
-    nsg = std::min(std::max(nsg, 1), Wg);
+    nsg = std::min(std::max(nsg, 1), max_g);
     nsg = std::min(nsg, S - (Wm > 0 ? 1 : 0));
-    nsg = std::max(nsg, S - Wm);
+    nsg = std::max(nsg, S - max_m);
   }
 }
 
@@ -995,7 +1055,7 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
   // below then stays inside it): the heads of this wave read NaN instead, so the mistake
   // shows in the output rather than passing as a plausible result.
   if (!layout_ok || before < 0 || after < before || W < after ||
-      int64_t(W) > int64_t(a.B) * (a.Hkv / C) * a.max_blocks) {
+      int64_t(W) > int64_t(a.B) * (a.Hkv / C) * unit_span(a.max_blocks, kBlockW)) {
     if (wv == 0 && head_ok) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -1008,7 +1068,8 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
   const float* ws_acc = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.ws_seq) + header_bytes(a.B));
   const float* ws_ml = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ws_acc) +
                                                       acc_bytes(splits, a.G, D));
-  const int nb = (after - before) / (a.Hkv / C);
+  const int span = (after - before) / (a.Hkv / C);            // weighted positions per unit
+  const int nb = span > kUnitW ? (span - kUnitW) / kBlockW : 0;
   auto write = [&](const float* v, float inv) {
     if (!head_ok) return;
     if constexpr (KV == PKV_F32) {
@@ -1033,16 +1094,18 @@ __global__ __launch_bounds__(64 * MW) void paged_attention_merge_kernel(DecodeAr
     if (wv == 0) write(num, 0.f);
     return;
   }
-  const int nshare = std::min(splits / C, W);
+  const int nshare = list_shares(splits / C, W, kBlockW);
   const int sub = g % C;
-  const int off = before + (g / C) * nb;
-  const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
+  const int off = before + (g / C) * span;
+  // The shares holding the unit's first and last blocks (a block goes to the share of its
+  // first weighted position).
+  const int64_t wf = share_of(off + kUnitW, W, nshare), wl = share_of(off + kUnitW + (nb - 1) * kBlockW, W, nshare);
   if (wf == wl) return;
   const int np = int(wl - wf + 1);
   // Share w's pieces of kv head g are those of its wave C*w + g%C.  The unit's piece in
-  // share wf is that share's first segment (slot 0) only if the unit begins exactly where
-  // the share does; in every later share it is the first segment.
-  const int64_t piece0 = (wf * C + sub) * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  // share wf is that share's first segment (slot 0) only if the share begins within the
+  // unit's weight; in every later share it is the first segment.
+  const int64_t piece0 = (wf * C + sub) * 2 + (share_begin(wf, W, nshare) >= off ? 0 : 1);
   // This wave's pieces: [jb, je).
   const int jb = wv * np / MW, je = (wv + 1) * np / MW;
 
@@ -1160,21 +1223,21 @@ __global__ __launch_bounds__(64) void paged_attention_grouped_merge_kernel(Decod
     f = a.chunk_first[s];
     col = (s - f) * a.G + h;
     const int P = chunk_blocks(a, f, BS);
-    const int off = goff[f] + hg * P;
-    const int64_t wf = share_of(off, Wg, nsg), wl = share_of(off + P - 1, Wg, nsg);
+    const int off = goff[f] + hg * unit_span(P, kGroupBlockW);
+    const int64_t wf = share_of(off + kUnitW, Wg, nsg), wl = share_of(off + kUnitW + (P - 1) * kGroupBlockW, Wg, nsg);
     g_slot = wf == wl;
     ng = g_slot ? 1 : int(wl - wf + 1);
     g_wf = wf;
-    g_first = (wf * C + sub) * 2 + (off != share_begin(wf, Wg, nsg) ? 1 : 0);
+    g_first = (wf * C + sub) * 2 + (share_begin(wf, Wg, nsg) >= off ? 0 : 1);
   }
   if (nbm > 0) {
-    const int off = a.ws_seq[s] + hg * nbm;
-    const int64_t wf = share_of(off, Wm, nsm), wl = share_of(off + nbm - 1, Wm, nsm);
+    const int off = a.ws_seq[s] + hg * unit_span(nbm, kBlockW);
+    const int64_t wf = share_of(off + kUnitW, Wm, nsm), wl = share_of(off + kUnitW + (nbm - 1) * kBlockW, Wm, nsm);
     if (wf == wl && skip == 0) return;   // finished and written by the split pass
     m_slot = wf == wl;
     nm = m_slot ? 1 : int(wl - wf + 1);
     m_wf = wf;
-    m_first = (wf * C + sub) * 2 + (off != share_begin(wf, Wm, nsm) ? 1 : 0);
+    m_first = (wf * C + sub) * 2 + (share_begin(wf, Wm, nsm) >= off ? 0 : 1);
   }
   auto row_of = [&](int j, const float*& acc, const float*& ml) {
     int64_t r;
@@ -1476,8 +1539,9 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
                      workspace_bytes, need);
   if (int64_t(B) > 65535 || Hkv > 65535)
     return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535", fn);
-  if (int64_t(B) * max_blocks * Hkv * (grouped ? 2 : 1) > int64_t(INT32_MAX))
-    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31", fn);
+  if (int64_t(B) * Hkv * (int64_t(max_blocks) * kGroupBlockW + kUnitW) * (grouped ? 2 : 1) > int64_t(INT32_MAX))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads is too large for the work list",
+                     fn);
 
   DecodeArgs a;
   a.out = out;

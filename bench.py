@@ -578,10 +578,13 @@ def _waste_report(args):
 
 
 def _vmm_bench(args):
-    """Decode over the same K/V in three placements: the paged pool with blocks in random
-    order, and contiguous per-sequence slices of virtual memory mapped on demand (pkv_vmm_*)
-    with one-block pages and with 2 MiB pages.  Each uses --layers copies so that a step reads
-    from HBM; the split kernel is timed by its dispatch-recorded events on every step."""
+    """Decode over the same K/V in several placements: the paged pool with blocks in random
+    order, each sequence's blocks consecutive in an ordinary pool, and contiguous per-sequence
+    slices of virtual memory mapped on demand (pkv_vmm_*) with --vmm-page-kib pages (one
+    placement per process).  Contiguous placements are read both by the paged kernel through
+    a table counting up from each sequence's first block and by the contiguous kernel, which
+    computes the addresses.  Each uses --layers copies so that a step reads from HBM; the split
+    kernel is timed by its dispatch-recorded events on every step."""
     import torch
     import paged_kv_cache_329_amd as pkv
     from synth import WORKLOADS, make_decode_case
@@ -612,6 +615,19 @@ def _vmm_bench(args):
             pkv.kv_cache_write(kt, vt, k, v, pslots)
             paged.append((k, v, ptab))
         layouts["paged_random_blocks"] = (paged, case.num_blocks * Hkv * bs * D * 2 * 2 * args.layers, None)
+        # The same K/V with each sequence's blocks consecutive in an ordinary pool.
+        first = np.concatenate([[0], np.cumsum(nbs)[:-1]]).astype(np.int32)
+        ctab = np.full((B, max_blocks), -1, dtype=np.int32)
+        for s_, nb in enumerate(nbs):
+            ctab[s_, :nb] = first[s_] + np.arange(nb)
+        cslots = torch.from_numpy(pkv.build_slot_mapping(ctab, lens32, bs)).to(dev)
+        contig = []
+        for _ in range(args.layers):
+            k = pkv.allocate_kv_pool(int(sum(nbs)), Hkv, bs, D, torch.bfloat16, dev)
+            v = pkv.allocate_kv_pool(int(sum(nbs)), Hkv, bs, D, torch.bfloat16, dev)
+            pkv.kv_cache_write(kt, vt, k, v, cslots)
+            contig.append((k, v, torch.from_numpy(ctab).to(dev), None, torch.from_numpy(first).to(dev)))
+        layouts["contiguous_in_pool"] = (contig, int(sum(nbs)) * Hkv * bs * D * 2 * 2 * args.layers, None)
     else:
         page = args.vmm_page_kib << 10
         name = f"vmm_{args.vmm_page_kib}KiB_pages"
@@ -627,7 +643,8 @@ def _vmm_bench(args):
                     vmm.reserve(s_, nb)
                     tables[s_, :nb] = vmm.first_block(s_) + np.arange(nb)
                 n_pages += (vmm.mapped_bytes // vmm.page_bytes) - 2
-                pools[-1] = (vmm.k, vmm.v, torch.from_numpy(tables).to(dev), vmm)
+                firsts = torch.tensor([vmm.first_block(s_) for s_ in range(B)], dtype=torch.int32, device=dev)
+                pools[-1] = (vmm.k, vmm.v, torch.from_numpy(tables).to(dev), vmm, firsts)
                 mapped += vmm.mapped_bytes
         except pkv.PagedKVError as e:
             # Record how far the mapping got: the driver caps the number of allocations.
@@ -640,7 +657,7 @@ def _vmm_bench(args):
             pools = []
         if pools:
             map_s = time.perf_counter() - t0
-            for k, v, t, _ in pools:
+            for k, v, t, _, _ in pools:
                 slots = torch.from_numpy(pkv.build_slot_mapping(t.cpu().numpy(), lens32, bs)).to(dev)
                 pkv.kv_cache_write(kt, vt, k, v, slots)
             layouts[name] = (pools, mapped, {"page_bytes": pools[0][3].page_bytes,
@@ -651,28 +668,38 @@ def _vmm_bench(args):
     ws = torch.empty(pkv.paged_attention_workspace_size(B, Hq, Hkv, D, bs, qd, kd, 0), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     rows = {}
-    for name, (pools, mapped, extra) in layouts.items():
+    runs = [(name, entry, False) for name, entry in layouts.items()]
+    # Contiguous placements are also read by the contiguous kernel (addresses computed from each
+    # sequence's first block, no table loads).
+    runs += [(name + "+contiguous_kernel", entry, True) for name, entry in layouts.items()
+             if len(entry[0][0]) > 4]
+    for name, (pools, mapped, extra), contiguous in runs:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         for pair in evs:
             for e in pair:
                 e.record(stream)
         torch.cuda.synchronize()
         for i in range(args.warmup + args.steps):
-            k, v, t = pools[i % len(pools)][:3]
+            entry = pools[i % len(pools)]
+            k, v, t = entry[:3]
             if i >= args.warmup:
                 pkv.set_launch_events(*evs[i - args.warmup])
-            pkv.paged_attention_decode(out, q, k, v, t, lens, case.scale, num_splits=0, workspace=ws)
+            if contiguous:
+                pkv.contiguous_attention_decode(out, q, k, v, entry[4], lens, t.shape[1], case.scale, workspace=ws)
+            else:
+                pkv.paged_attention_decode(out, q, k, v, t, lens, case.scale, num_splits=0, workspace=ws)
         torch.cuda.synchronize()
         us = statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3
         rows[name] = {"split_kernel_us": round(us, 2), "GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1),
-                      "device_bytes_backing_kv": int(mapped)}
+                      "device_bytes_backing_kv": int(mapped),
+                      "kernel": "contiguous (computed addresses)" if contiguous else "paged (block table)"}
         if extra:
             rows[name].update(extra)
     print(json.dumps({"op": "vmm", "workload": wl.name, "kv_bytes": kv_bytes, "layers": args.layers,
                       "layouts": rows, "could_not_map": failed}), flush=True)
     for pools, _, _ in layouts.values():
         for entry in pools:
-            if len(entry) > 3:
+            if len(entry) > 3 and entry[3] is not None:
                 entry[3].close()
 
 

@@ -972,7 +972,11 @@ def _prefix_step_bench(args, wl):
         for j in range(int(math.ceil(lens[si] / bs))):
             b = int(tables[si, j])
             used[b] = max(used.get(b, 0), min(bs, int(lens[si]) - j * bs))
-    unique_bytes = sum(used.values()) * Hkv * D * 2 * 2
+    unique_last = sum(used.values()) * Hkv * D * 2 * 2
+    # Every step appends one private token per sequence, so the distinct bytes grow by exactly
+    # B tokens per step: their mean over the timed steps is the last state's less the growth
+    # since the middle of the timed region (the detail steps ran after it).
+    unique_bytes = unique_last - B * Hkv * D * 2 * 2 * (n_detail + (args.steps - 1) / 2)
     value = kv_bytes / (us_per_step * 1e-6) / 1e9
     # The split kernel reads every distinct block once from HBM at best (shared prefix blocks
     # re-read by other members can come from L2 or the MALL): its roofline is on distinct bytes.
@@ -1011,7 +1015,9 @@ def _prefix_step_bench(args, wl):
                       "per wall-clock step",
         "us_per_step": round(us_per_step, 2),
         "kv_bytes_logical": int(kv_bytes),
-        "kv_bytes_unique_last_step": int(unique_bytes),
+        "kv_bytes_unique": int(unique_bytes),
+        "kv_bytes_unique_note": "mean over the timed steps of the distinct K/V bytes (each physical block once, with "
+                                "the most tokens any reader uses in it); logical = mean of every sequence's tokens",
         "unique_GBps": round(unique_bytes / (us_per_step * 1e-6) / 1e9, 2),
         "hbm_frac_unique": round(unique_bytes / (us_per_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "kernel_us": {"paged_attention_split(append)": round(split_us, 2),
@@ -1032,8 +1038,8 @@ def _prefix_step_bench(args, wl):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "traffic_unit": TRAFFIC_UNIT,
                      "algorithmic_bytes": int(unique_bytes),
-                     "algorithmic_bytes_note": "distinct K/V bytes of the step (each physical block once, with the "
-                                               "most tokens any reader uses in it)",
+                     "algorithmic_bytes_note": "distinct K/V bytes of a timed step, mean (each physical block once, "
+                                               "with the most tokens any reader uses in it)",
                      "logical_GBps": round(kv_bytes / (split_us * 1e-6) / 1e9, 1),
                      "kernel": ("paged_attention_grouped_kernel (decode step with append, prefix groups)"
                                 if groups_on else "paged_attention_split_kernel (decode step with append)")},

@@ -18,6 +18,7 @@ separately, after the timed region.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -799,15 +800,47 @@ def _swap_bench(args, wl, case, pool, kvt, eb):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
+    # The same scattered swap done by the copy engines instead: one hipMemcpyAsync per block
+    # of K and per block of V, issued from the host on torch's stream (the runtime already
+    # loaded in this process, found by its mapped path).
+    hip = _loaded_hip_runtime()
+    blk = Hkv * bs * D * eb                              # one block of K (or of V), bytes
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out_np, in_np = out_pairs.cpu().numpy(), in_pairs.cpu().numpy()
+
+    def dma(dk, dv, sk, sv, pairs):
+        for src, dst in pairs.tolist():
+            for d_t, s_t in ((dk, sk), (dv, sv)):
+                rc = hip.hipMemcpyAsync(ctypes.c_void_p(d_t.data_ptr() + dst * blk),
+                                        ctypes.c_void_p(s_t.data_ptr() + src * blk), ctypes.c_size_t(blk),
+                                        4, stream)   # hipMemcpyDefault: direction from the pointers
+                if rc != 0:
+                    raise RuntimeError(f"hipMemcpyAsync failed with code {rc}")
+
     res = {"out": timed(lambda: pkv.swap_blocks(hk, hv, k, v, out_pairs, D)),
            "in": timed(lambda: pkv.swap_blocks(k, v, hk, hv, in_pairs, D)),
+           "dma_out": timed(lambda: dma(hk, hv, k, v, out_np)),
+           "dma_in": timed(lambda: dma(k, v, hk, hv, in_np)),
            "copy_d2h": timed(lambda: flat_h.copy_(flat_d, non_blocking=True)),
            "copy_h2d": timed(lambda: flat_d.copy_(flat_h, non_blocking=True))}
     gb = {key: round(nbytes / (us * 1e-6) / 1e9, 2) for key, us in res.items()}
     print(json.dumps({"op": "swap", "workload": wl.name,
                       "what": f"{n} random blocks (K and V, {nbytes} bytes) device -> pinned host and back",
+                      "dma": "dma_out / dma_in: the same pairs as 2n hipMemcpyAsync calls (one per block of K and of V)",
                       "us_per_call": {key: round(us, 2) for key, us in res.items()}, "bytes_one_way": nbytes,
                       "GBps": gb}), flush=True)
+
+
+def _loaded_hip_runtime():
+    """The HIP runtime library this process has already loaded (torch's), via its mapped path."""
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    if not paths:
+        raise RuntimeError("no HIP runtime is loaded in this process")
+    hip = ctypes.CDLL(sorted(paths)[0])
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    return hip
 
 
 def _prefix_step_bench(args, wl):

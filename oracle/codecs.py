@@ -63,7 +63,8 @@ def inverse_scale(scale) -> np.float32:
 def quantize_e4m3fn(x_f32: np.ndarray, inv_scale) -> np.ndarray:
     """float32 values -> e4m3fn codes: RNE(clamp(x * inv_scale, +-448)), ties to even."""
     x = np.asarray(x_f32, dtype=np.float32)
-    y = (x * np.float32(inv_scale)).astype(np.float32)      # one float32 multiply
+    with np.errstate(over="ignore", invalid="ignore"):   # +-inf past float32 (clamped to +-448); NaN stays NaN
+        y = (x * np.float32(inv_scale)).astype(np.float32)  # one float32 multiply
     nan = np.isnan(y)
     a = np.minimum(np.abs(np.where(nan, 0, y)).astype(np.float64), E4M3FN_MAX)
     hi = np.clip(np.searchsorted(_POS_GRID, a, side="left"), 0, 0x7E)

@@ -108,7 +108,7 @@ const char* pkv_last_error(void);
  *                   blocks of sequence s in logical order; entries past
  *                   ceil(context_lens[s] / bs) are never read (pad with -1).
  *   context_lens    int32 [num_seqs], 0 <= context_lens[s] <= max_blocks_per_seq * bs
- *                   (larger values are clamped to that bound).
+ *                   (larger values are clamped to that bound; negative ones read as 0).
  *   q_dtype/kv_dtype  supported: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN).
  *   num_splits      wavefronts the work is spread over; 0 = pkv_paged_attention_default_splits
  *                   (the same with or without shared_prefix_blocks).

@@ -134,6 +134,27 @@ def test_many_short_sequences(name, num_splits):
     assert_close(got, oatt.decode_case(case), wl.kv_dtype, f"{name} splits={num_splits}")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
+@pytest.mark.parametrize("num_splits", [0, 5])
+def test_context_lengths_outside_the_table_are_clamped(name, num_splits):
+    """context_lens past max_blocks_per_seq * bs read the full table row, and a negative
+    length reads as an empty sequence (zero output), as the boundary states."""
+    require_gpu()
+    wl = SMALL[name].scaled(batch=4)
+    bs = wl.block_size
+    lengths = np.array([20 * bs, 50, 3 * bs + 7, 9], dtype=np.int64)   # row 0 fills the table
+    case = make_decode_case(wl, 8, lengths=lengths)
+    assert case.block_tables.shape[1] * bs == lengths[0]
+    k, v = pack(case)
+    passed = lengths.copy()
+    passed[0] = lengths[0] + 37       # past the table row: clamped to its 20 blocks
+    passed[3] = -5                    # negative: no tokens
+    got = as_f64(decode(case, k, v, num_splits=num_splits, lengths=passed))
+    ref = oatt.decode_case(case)
+    assert np.all(got[3] == 0)
+    assert_close(got[:3], ref[:3], wl.kv_dtype, f"{name} splits={num_splits}")
+
+
 def test_all_sequences_empty():
     require_gpu()
     wl = SMALL["llama3_8b_bf16"].scaled(batch=3)

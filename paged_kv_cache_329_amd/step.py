@@ -64,6 +64,8 @@ class DecodeStep:
         kd = _dtype_code(k_cache.dtype)
         self.num_splits = int(num_splits) or paged_attention_default_splits(head_dim, self.bs, BF16, kd)
         tables, lens = alloc.block_tables(self.members, max_blocks)
+        self.max_blocks = int(max_blocks)
+        self.max_len = int(lens.max()) if B else 0   # every member grows by one token a step
         self.tables = torch.from_numpy(tables).to(dev)
         self.lens = torch.from_numpy(lens).to(dev)
         counts = alloc.shared_prefix_blocks(self.members)
@@ -94,12 +96,18 @@ class DecodeStep:
         kernel_events: an optional (start, stop) pair of recorded torch events that the split
         kernel's own dispatch records (set_launch_events).  after_upload: an optional event
         recorded once the pair upload is enqueued."""
+        if -(-(self.max_len + 1) // self.bs) > self.max_blocks:
+            # The device tables have no room for the new token's block: pkv_apply_append would
+            # leave those rows unchanged, and the fused write would land on the old last token.
+            raise ValueError(f"a sequence would grow past max_blocks={self.max_blocks} blocks of the device "
+                             f"block tables ({self.max_len + 1} tokens)")
         hb = self.bufs[self.steps % 2]
         hb.done.synchronize()                 # the kernels that read this buffer have run
         self.steps += 1
         t0 = time.perf_counter()
         _, cows = self.alloc.append(self.members, hb.slots.numpy(), hb.cow.numpy())
         self.host_alloc_s += time.perf_counter() - t0
+        self.max_len += 1
         n_cow = len(cows)
         self.last_slots = hb.slots.numpy().copy()
         self.last_cows = np.array(cows, dtype=np.int32).reshape(-1, 2)

@@ -12,7 +12,7 @@ import torch
 import paged_kv_cache_329_amd as pkv
 from oracle import attention as oatt
 from oracle import pool as opool
-from synth import WORKLOADS, make_prefix_step_case
+from synth import WORKLOADS, bf16_bits_from_f32, make_prefix_step_case
 
 from gpu_helpers import (ROOT_ID_BASE, as_f64, assert_close, build_prefix_batch, log, pool_pair, prefix_step,
                          raw_bytes, require_gpu, to_dev, write_tokens)
@@ -139,8 +139,9 @@ def test_prefix_step_parity_full_size():
     capped at 8192).  paged_kv_cache_329_amd.step.DecodeStep runs the allocator's append into
     pinned slots, copy_blocks on the copy-on-write pairs, apply_append, the fused decode step
     with the allocator's shared-prefix counts at the benchmark's split count (twice the
-    default), and the reduce.  Every sequence is checked against the oracle, and both pools bit
-    for bit against oracle/pool.py replaying the same writes, copies and appended tokens."""
+    default), and the reduce; the first step and two more as the timed steps run.  After each
+    step every sequence is checked against the oracle, and at the end both pools bit for bit
+    against oracle/pool.py replaying the same writes, copies and appended tokens."""
     require_gpu()
     _check_bench_step(make_prefix_step_case(FULL, 0), 2 * _default_splits(FULL))
 
@@ -148,8 +149,8 @@ def test_prefix_step_parity_full_size():
 @pytest.mark.timeout(900)
 def test_prefix_step_parity_full_size_groups():
     """The same full-size step with prefix groups (each group's 1024-token prefix read once for
-    its 8 sequences, pkv_paged_decode_step_grouped), as the benchmark runs it by default:
-    every sequence against the oracle, both pools bit for bit."""
+    its 8 sequences, pkv_paged_decode_step_grouped), as the benchmark runs it by default,
+    over three steps: every sequence against the oracle after each, both pools bit for bit."""
     require_gpu()
     _check_bench_step(make_prefix_step_case(FULL, 0), 0, prefix_groups=True)
 
@@ -239,14 +240,19 @@ def test_prefix_groups_ignore_ill_formed_chunks():
         assert_close(as_f64(got), ref, "bf16", name)
 
 
-def _check_bench_step(case, nsplits, prefix_groups=False):
+def _check_bench_step(case, nsplits, prefix_groups=False, later_steps=2):
+    """The benchmark's step driver over `case`: the first step (with its copy-on-write
+    copies), then `later_steps` more as the timed steps run (groups kept, no copies), each
+    appending fresh seeded tokens.  After every step all sequences are checked against the
+    oracle; after the last, both pools against oracle/pool.py."""
     from paged_kv_cache_329_amd.step import DecodeStep
 
     wl = case.wl
-    log(f"prefix step full size: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks")
+    log(f"prefix step: sum L = {int(case.lengths.sum())}, pool {case.num_blocks} blocks, "
+        f"splits {nsplits}, groups {prefix_groups}")
     writes = []
     a, k, v, members = build_prefix_batch(case, record=writes)
-    max_blocks = int((case.lengths.max() + 1 + wl.block_size - 1) // wl.block_size) + 1
+    max_blocks = int((case.lengths.max() + 1 + later_steps + wl.block_size - 1) // wl.block_size) + 1
     step = DecodeStep(a, members, k, v, wl.head_dim, wl.num_q_heads, max_blocks, num_splits=nsplits,
                       prefix_groups=prefix_groups)
     assert step.shared_counts.min() >= 1
@@ -260,10 +266,62 @@ def _check_bench_step(case, nsplits, prefix_groups=False):
     for c in range(0, wl.batch, 32):
         seqs = list(range(c, min(wl.batch, c + 32)))
         assert_close(got[seqs], oatt.prefix_step_case(case, seqs), "bf16", f"prefix step full size, seqs {c}..")
-    log(f"all {wl.batch} sequences match the oracle; checking the pools")
-    pk, pv = _oracle_pools(case, writes, step.last_cows, step.last_slots)
+    log(f"step 1: all {wl.batch} sequences match the oracle")
+    first_cows, first_slots = step.last_cows, step.last_slots
+    # Later steps: new tokens and queries drawn from a seeded generator, rounded to bf16.
+    rng = np.random.default_rng(1000 + case.seed)
+    B, Hkv, Hq, D = wl.batch, wl.num_kv_heads, wl.num_q_heads, wl.head_dim
+    added = []   # (k, v, slots) of each later step
+    for j in range(later_steps):
+        kj = bf16_bits_from_f32(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        vj = bf16_bits_from_f32(rng.standard_normal((B, Hkv, D), dtype=np.float32))
+        qj = bf16_bits_from_f32(rng.standard_normal((B, Hq, D), dtype=np.float32))
+        assert step.run(out, to_dev(qj, "bf16"), to_dev(kj, "bf16"), to_dev(vj, "bf16"), case.scale) == 0
+        torch.cuda.synchronize()
+        added.append((kj, vj, step.last_slots.copy()))
+        got = as_f64(out)
+        for c in range(0, B, 32):
+            seqs = list(range(c, min(B, c + 32)))
+            ks, vs = [], []
+            for i in seqs:
+                k0, v0 = case.logical_kv(i)
+                ks.append(oatt.kv_to_f64(np.concatenate([k0] + [x[0][i:i + 1] for x in added]), "bf16"))
+                vs.append(oatt.kv_to_f64(np.concatenate([v0] + [x[1][i:i + 1] for x in added]), "bf16"))
+            ref = oatt.decode_attention(oatt.q_to_f64(qj[seqs], "bf16"), ks, vs, case.scale, wl.group_size)
+            assert_close(got[seqs], ref, "bf16", f"step {j + 2}, seqs {c}..")
+        log(f"step {j + 2}: all {B} sequences match the oracle")
+    pk, pv = _oracle_pools(case, writes, first_cows, first_slots)
+    for kj, vj, sj in added:
+        opool.write(pk, pv, kj, vj, sj, "bf16", "bf16", wl.block_size)
     assert np.array_equal(k.view(torch.int16).cpu().numpy().view(np.uint16), pk)
     assert np.array_equal(v.view(torch.int16).cpu().numpy().view(np.uint16), pv)
+
+
+def test_decode_step_refuses_to_outgrow_its_tables():
+    """DecodeStep with device tables just wide enough for the longest sequence runs until
+    that sequence's last block is full, then refuses the step before the allocator appends
+    (a row the tables cannot hold would leave pkv_apply_append nothing to update)."""
+    from paged_kv_cache_329_amd.step import DecodeStep
+
+    require_gpu()
+    case = make_prefix_step_case(SMALL, 4)
+    wl = case.wl
+    bs = wl.block_size
+    a, k, v, members = build_prefix_batch(case)
+    lmax = int(case.lengths.max())
+    max_blocks = -(-lmax // bs)
+    step = DecodeStep(a, members, k, v, wl.head_dim, wl.num_q_heads, max_blocks, prefix_groups=True)
+    q, kn, vn = to_dev(case.q, "bf16"), to_dev(case.new_k, "bf16"), to_dev(case.new_v, "bf16")
+    out = torch.empty_like(q)
+    fits = max_blocks * bs - lmax
+    for _ in range(fits):
+        step.run(out, q, kn, vn, case.scale)
+    torch.cuda.synchronize()
+    before = a.block_tables(members, max_blocks + 1)[1].copy()
+    with pytest.raises(ValueError):
+        step.run(out, q, kn, vn, case.scale)
+    assert np.array_equal(a.block_tables(members, max_blocks + 1)[1], before)
+    assert np.array_equal(before, case.lengths + fits)
 
 
 def test_apply_append_mirrors_the_allocator_tables():

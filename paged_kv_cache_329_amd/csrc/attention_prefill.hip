@@ -304,7 +304,11 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      float cmax[CT];
+      // Each lane first checks only its own scores: a column's max grew by more than 2^8 in
+      // probability exactly when one of the lanes holding that column sees such a score, so
+      // the wave-wide vote below takes the same decision as the column maxima would, and the
+      // cross-row reduction is needed only in the (rare) rescale.
+      float lmax[CT];
       bool grow = false;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
@@ -313,8 +317,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
         for (int uu = 0; uu < UPD; ++uu)
 #pragma unroll
           for (int j = 0; j < 4; ++j) v = fmaxf(v, sc[ct][uu][j]);
-        cmax[ct] = wave_max_rows(v);
-        grow |= (cmax[ct] - m_run[ct]) * sl2 > 8.f;
+        lmax[ct] = v;
+        grow |= (v - m_run[ct]) * sl2 > 8.f;
       }
       // The accumulators are rescaled only when some column's max grew by more than 2^8 in
       // probability: until then p = 2^(s - m) stays below 256, which float32 sums and bf16
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
       if (__any(grow)) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const float m_new = fmaxf(m_run[ct], cmax[ct]);
+          const float m_new = fmaxf(m_run[ct], wave_max_rows(lmax[ct]));
           const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
           m_run[ct] = m_new;
           if constexpr (MSUM) lsum[ct] *= alpha;

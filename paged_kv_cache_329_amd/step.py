@@ -28,7 +28,7 @@ import time
 import numpy as np
 import torch
 
-from . import (BF16, apply_append, copy_blocks, paged_attention_default_splits, paged_attention_grouped_workspace_size,
+from . import (BF16, F32, apply_append, copy_blocks, paged_attention_default_splits, paged_attention_grouped_workspace_size,
                paged_attention_reduce, paged_attention_workspace_size, paged_decode_step_grouped,
                paged_decode_step_split, set_launch_events, _dtype_code, _pool_dims)
 
@@ -62,7 +62,8 @@ class DecodeStep:
         dev = k_cache.device
         B = len(self.members)
         kd = _dtype_code(k_cache.dtype)
-        self.num_splits = int(num_splits) or paged_attention_default_splits(head_dim, self.bs, BF16, kd)
+        qd = F32 if kd == F32 else BF16          # queries and new tokens: f32 for an f32 cache, else bf16
+        self.num_splits = int(num_splits) or paged_attention_default_splits(head_dim, self.bs, qd, kd)
         tables, lens = alloc.block_tables(self.members, max_blocks)
         self.max_blocks = int(max_blocks)
         self.max_len = int(lens.max()) if B else 0   # every member grows by one token a step
@@ -77,10 +78,10 @@ class DecodeStep:
             self.shared = None                 # shared blocks are read once, streamed
             self.groups = torch.empty((3, B), dtype=torch.int32, device=dev)
             self._groups_host = None
-            nbytes = paged_attention_grouped_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, BF16, kd,
+            nbytes = paged_attention_grouped_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, qd, kd,
                                                             self.num_splits, max_blocks)
         else:
-            nbytes = paged_attention_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, BF16, kd,
+            nbytes = paged_attention_workspace_size(B, num_q_heads, self.Hkv, head_dim, self.bs, qd, kd,
                                                     self.num_splits)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.cow_d = torch.empty((B, 2), dtype=torch.int32, device=dev)

@@ -118,6 +118,11 @@ def write_tokens(k_pool, v_pool, k_vals, v_vals, slots, storage, k_scale=1.0, v_
 ROOT_ID_BASE = 1 << 40
 
 
+def bf16_values_as_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the same values as float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def build_prefix_batch(case, poison=True, record=None):
     """Prefill a PrefixStepCase through the library's allocator and kv_cache_write.
 
@@ -130,9 +135,13 @@ def build_prefix_batch(case, poison=True, record=None):
     a = pkv.BlockAllocator(case.num_blocks, wl.block_size, free_order=case.free_order)
     k, v = pool_pair(wl, case.num_blocks, poison)
     P = wl.prefix_len
+    # The case draws bf16 values; an f32 pool is written with the same values as float32
+    # (exactly), an fp8 pool by quantising them at the scale 1.
+    st = kv_storage(wl)
+    vals = bf16_values_as_f32 if st == "f32" else (lambda x: x)
     for g in range(case.groups):
         slots = a.seq_create(ROOT_ID_BASE + g, P)
-        write_tokens(k, v, case.root_k[g], case.root_v[g], slots, "bf16")
+        write_tokens(k, v, vals(case.root_k[g]), vals(case.root_v[g]), slots, st)
         if record is not None:
             record.append((case.root_k[g], case.root_v[g], slots))
     priv_slots = []
@@ -145,7 +154,7 @@ def build_prefix_batch(case, poison=True, record=None):
             assert len(cow) == 0, "a block-aligned prefix never leaves a shared partial tail"
             priv_slots.append(slots)
     if priv_slots:
-        write_tokens(k, v, case.priv_k, case.priv_v, np.concatenate(priv_slots), "bf16")
+        write_tokens(k, v, vals(case.priv_k), vals(case.priv_v), np.concatenate(priv_slots), st)
         if record is not None:
             record.append((case.priv_k, case.priv_v, np.concatenate(priv_slots)))
     return a, k, v, list(range(wl.batch))

@@ -175,6 +175,9 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   // Running max in raw logit units (before the scale), sum and accumulators per column.
   f32x4 acc[CT][F::NT];
   float m_run[CT], l_run[CT];
+  // Kept with m_run and changed only when it is: the exponent offset -m_run * sl2 (0 while
+  // nothing was seen) and the rescale threshold m_run + 8 / sl2 (raw logit units).
+  float m_off[CT], thr[CT];
   // bf16 caches: the running sum of each column comes from the matrix unit, as the product
   // of an all-ones A operand with the same bf16 probabilities PV uses; every row of lsum[ct]
   // then holds the sum of column lane % 16 (fp8 caches are staged as bf16, so they too).
@@ -185,6 +188,8 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
     for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[ct] = -INFINITY;
     l_run[ct] = 0.f;
+    m_off[ct] = 0.f;
+    thr[ct] = -INFINITY;
     lsum[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   constexpr bool MSUM = CKV == PKV_BF16;
@@ -278,6 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   // PV products of the update's sub-tile pairs follow in one straight run, so the compiler
   // can overlap one pair's exponentials with the previous pair's matrix instructions.
   const float sl2 = a.qk_scale_log2;
+  const float grow_raw = 8.f / sl2;   // 2^8 in probability, in raw logit units
   constexpr int UPD = SUBS < 4 ? SUBS : 4;
   static_assert(SUBS % UPD == 0 && UPD % 2 == 0, "softmax update tiling");
   auto compute = [&](const uint4* buf, int tok_step, auto mask_c) {
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
 #pragma unroll
           for (int j = 0; j < 4; ++j) v = fmaxf(v, sc[ct][uu][j]);
         lmax[ct] = v;
-        grow |= (v - m_run[ct]) * sl2 > 8.f;
+        grow |= v > thr[ct];
       }
       // The accumulators are rescaled only when some column's max grew by more than 2^8 in
       // probability: until then p = 2^(s - m) stays below 256, which float32 sums and bf16
@@ -329,15 +335,14 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
           const float m_new = fmaxf(m_run[ct], wave_max_rows(lmax[ct]));
           const float alpha = m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * sl2);
           m_run[ct] = m_new;
+          m_off[ct] = m_new == -INFINITY ? 0.f : -m_new * sl2;
+          thr[ct] = m_new + grow_raw;
           if constexpr (MSUM) lsum[ct] *= alpha;
           else l_run[ct] *= alpha;
 #pragma unroll
           for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
         }
       }
-      float m_off[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) m_off[ct] = m_run[ct] == -INFINITY ? 0.f : -m_run[ct] * sl2;   // nothing seen yet
 #pragma unroll
       for (int u0 = ub; u0 < ub + UPD; u0 += 2) {
         const int pu = u0 - ub;

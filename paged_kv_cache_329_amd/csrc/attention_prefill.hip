@@ -517,22 +517,38 @@ __device__ __forceinline__ void mq_queries(const MqArgs& a, int s, int& q0, int&
   n = hi - lo;
 }
 
-// Total work W = Hkv * sum_s blocks(s) (wave-uniform).
+// The work list is cut by estimated cost, as decode's: a unit (one sequence's blocks for one
+// group of kv heads) weighs kMqUnitW for its q and table round trip and its epilogue, plus
+// kMqBlockW per block, and a block belongs to the share holding its first weighted position.
+constexpr int kMqBlockW = 8;
+constexpr int kMqUnitW = 12;
+
+__device__ __forceinline__ int mq_span(int nb) { return nb > 0 ? nb * kMqBlockW + kMqUnitW : 0; }
+
+// Blocks [j0, j1) of a unit (first weighted position unit_off, nb blocks) whose first weighted
+// positions lie in [lo, hi).
+__device__ __forceinline__ void mq_blocks_in(int unit_off, int nb, int lo, int hi, int& j0, int& j1) {
+  const int base = unit_off + kMqUnitW;
+  j0 = lo <= base ? 0 : std::min(nb, (lo - base + kMqBlockW - 1) / kMqBlockW);
+  j1 = hi <= base ? 0 : std::min(nb, (hi - base + kMqBlockW - 1) / kMqBlockW);
+}
+
+// Total work W = kv-head groups * sum_s mq_span(blocks(s)) (wave-uniform).
 __device__ int mq_total(const MqArgs& a, int bs, int lane) {
   int acc = 0;
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
-    acc += s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs : 0;
+    acc += s < a.B ? mq_span((mq_len(a, s, bs) + bs - 1) / bs) : 0;
   }
   return wave_sum(acc) * (a.Hkv / a.coop);
 }
 
-// Sequence whose units contain work position x, and Hkv * blocks before it.
+// Sequence whose units contain work position x, and the weighted positions before it.
 __device__ void mq_locate(const MqArgs& a, int bs, int lane, int x, int& s_out, int& off_out) {
   int base = 0;
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int s = b0 + lane;
-    const int w = s < a.B ? (mq_len(a, s, bs) + bs - 1) / bs * (a.Hkv / a.coop) : 0;
+    const int w = s < a.B ? mq_span((mq_len(a, s, bs) + bs - 1) / bs) * (a.Hkv / a.coop) : 0;
     const int incl = wave_incl_scan(w, lane);
     const int lo = base + (incl - w), hi = base + incl;
     const uint64_t hit = __ballot(w > 0 && lo <= x && x < hi);
@@ -612,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     int base = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int sq = b0 + lane;
-      const int w = sq < a.B ? (mq_len(a, sq, BS) + BS - 1) / BS * (a.Hkv / a.coop) : 0;
+      const int w = sq < a.B ? mq_span((mq_len(a, sq, BS) + BS - 1) / BS) * (a.Hkv / a.coop) : 0;
       const int incl = wave_incl_scan(w, lane);
       if (sq < a.B) a.ws_seq[sq] = base + incl - w;
       base += __builtin_amdgcn_readlane(incl, 63);
@@ -624,7 +640,10 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
   // coop*hg + sub, so that together they read the adjacent head regions of each block.
   // Pieces stay numbered per wave (2 * wave + slot).
   const int share = wave / a.coop, sub = wave % a.coop;
-  const int nshare = std::min(a.splits / a.coop, W);
+  // No share is shorter than one block's weight, so every share lying inside a unit holds a
+  // block of it (the merge takes a piece from each share between the unit's first block and
+  // its last).
+  const int nshare = std::min(a.splits / a.coop, W / kMqBlockW);
   if (share >= nshare) return;
   const int c_begin = int(share_begin(share, W, nshare));
   const int c_end = int(share_begin(share + 1, W, nshare));
@@ -634,147 +653,153 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
   if (s >= a.B) return;
   int L = mq_len(a, s, BS);
   int nb = (L + BS - 1) / BS;
-  int hg = (c_begin - seq_off) / nb;
+  int span = mq_span(nb);
+  int hg = (c_begin - seq_off) / span;
   int g = hg * a.coop + sub;
-  int unit_off = seq_off + hg * nb;
+  int unit_off = seq_off + hg * span;
   int pos = c_begin;
   const int row = lane >> 4;
   const float sl2 = a.qk_scale_log2;
 
   while (pos < c_end) {
-    const int unit_end = unit_off + nb;
+    const int unit_end = unit_off + span;
     const int seg_end = std::min(c_end, unit_end);
-    const bool full = pos == unit_off && seg_end == unit_end;
-    const int j0 = pos - unit_off, j1 = seg_end - unit_off;             // blocks [j0, j1)
-    const int k0 = j0 * NSB;
-    const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
+    int j0, j1;                                                          // blocks [j0, j1)
+    mq_blocks_in(unit_off, nb, c_begin, c_end, j0, j1);
+    if (j1 > j0) {
+      const bool full = j0 == 0 && j1 == nb;
+      const int k0 = j0 * NSB;
+      const int k1 = (std::min(j1 * BS, L) + 15) / 16;                    // sub-tiles [k0, k1)
 
-    // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
-    const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
-    int q0, n;
-    mq_queries(a, s, q0, n);
-    // Column c = 16*ct + lane%16 is (query c / G, head c % G); query i sits at L - n + i.
-    int posc[CT];
-    uint4 qf[CT][F::NLOAD * F::QCH];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int c = 16 * ct + (lane & 15);
-      const int qi = c / a.G, hh = c % a.G;
-      const bool ok = qi < n;
-      posc[ct] = ok ? L - n + qi : -1;
-      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
-                            ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
-#pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i)
-#pragma unroll
-        for (int cc = 0; cc < F::QCH; ++cc)
-          qf[ct][i * F::QCH + cc] =
-              ok ? *reinterpret_cast<const uint4*>(qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * cc)
-                 : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
-    int tbase = k0 / NSB;
-    int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
-    f32x4 acc[CT][F::NT];
-    float m_run[CT], l_run[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-      for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run[ct] = -INFINITY;
-      l_run[ct] = 0.f;
-    }
-    const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
-    const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
-    const int64_t block_stride = int64_t(a.Hkv) * REGION;
-
-    for (int k = k0; k < k1; ++k) {
-      if (k / NSB >= tbase + 64) {
-        tbase = k / NSB;
-        tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
-      }
-      // K and V of the sub-tile are loaded together, with no branch before their use: a
-      // table entry outside [0, num_blocks) reads block 0 and its keys and values are
-      // replaced by zeros.
-      const int phys = __builtin_amdgcn_readlane(tbl, k / NSB - tbase);
-      const bool bad = unsigned(phys) >= unsigned(a.num_blocks);
-      const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
-      uint4 kf[F::NLOAD], vf[F::NLOAD];
-#pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_kv(kbase + off + i * 1024, MIX && k < ks);
-#pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_kv(vbase + off + i * 1024, MIX && k < ks);
-      const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < F::NLOAD; ++i) {
-        kf[i].x &= km; kf[i].y &= km; kf[i].z &= km; kf[i].w &= km;
-      }
-      const int t0 = k * 16 + 4 * row;
-      float p[CT][4];
+      // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
+      const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
+      int q0, n;
+      mq_queries(a, s, q0, n);
+      // Column c = 16*ct + lane%16 is (query c / G, head c % G); query i sits at L - n + i.
+      int posc[CT];
+      uint4 qf[CT][F::NLOAD * F::QCH];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
-        float sc[4];
-        float cmax = -INFINITY;
+        const int c = 16 * ct + (lane & 15);
+        const int qi = c / a.G, hh = c % a.G;
+        const bool ok = qi < n;
+        posc[ct] = ok ? L - n + qi : -1;
+        const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
+                              ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D * T::QB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sc[j] = t0 + j <= posc[ct] ? c[j] * sl2 : -INFINITY;   // posc < L: the tail is masked too
-          cmax = fmaxf(cmax, sc[j]);
-        }
-        cmax = wave_max_rows(cmax);
-        const float m_new = fmaxf(m_run[ct], cmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;      // column with nothing yet
-        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
-        m_run[ct] = m_new;
-        l_run[ct] *= alpha;
+        for (int i = 0; i < F::NLOAD; ++i)
 #pragma unroll
-        for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[ct][j] = __builtin_amdgcn_exp2f(sc[j] - m_use);          // 0 where masked
-          l_run[ct] += p[ct][j];
-        }
+          for (int cc = 0; cc < F::QCH; ++cc)
+            qf[ct][i * F::QCH + cc] =
+                ok ? *reinterpret_cast<const uint4*>(qrow + (int64_t(X) * (4 * i + row)) * T::QB + 16 * cc)
+                   : make_uint4(0u, 0u, 0u, 0u);
       }
-      uint32_t vm = 0;
+      const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks;
+      int tbase = k0 / NSB;
+      int tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+      f32x4 acc[CT][F::NT];
+      float m_run[CT], l_run[CT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) vm |= (t0 + j < L && !bad ? 1u : 0u) << j;
-      mask_v<KV, D>(vf, vm);
+      for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct]);
-    }
+        for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[ct] = -INFINITY;
+        l_run[ct] = 0.f;
+      }
+      const uint8_t* kbase = a.k_cache + int64_t(g) * REGION;
+      const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
+      const int64_t block_stride = int64_t(a.Hkv) * REGION;
 
-    const int slot = pos == c_begin ? 0 : 1;
-    const int64_t piece = int64_t(wave) * 2 + slot;
+      for (int k = k0; k < k1; ++k) {
+        if (k / NSB >= tbase + 64) {
+          tbase = k / NSB;
+          tbl = tbase + lane < nb ? trow[tbase + lane] : -1;
+        }
+        // K and V of the sub-tile are loaded together, with no branch before their use: a
+        // table entry outside [0, num_blocks) reads block 0 and its keys and values are
+        // replaced by zeros.
+        const int phys = __builtin_amdgcn_readlane(tbl, k / NSB - tbase);
+        const bool bad = unsigned(phys) >= unsigned(a.num_blocks);
+        const int64_t off = (bad ? 0 : int64_t(phys) * block_stride) + (k % NSB) * SUB_BYTES + lane * 16;
+        uint4 kf[F::NLOAD], vf[F::NLOAD];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const float l_tot = wave_sum_rows(l_run[ct]);
-      const int c = 16 * ct + (lane & 15);
-      const int qi = c / a.G, hh = c % a.G;
-      if (qi >= n) continue;
-      if (full) {
-        const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
-        const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+        for (int i = 0; i < F::NLOAD; ++i) kf[i] = load_kv(kbase + off + i * 1024, MIX && k < ks);
 #pragma unroll
-        for (int nn = 0; nn < F::NT; ++nn) {
-          const int d = 16 * nn + 4 * row;
-          if constexpr (KV == PKV_F32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) =
-                make_float4(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv, acc[ct][nn][2] * inv, acc[ct][nn][3] * inv);
-          } else {
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) =
-                make_uint2(pack_bf16x2(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv),
-                           pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
+        for (int i = 0; i < F::NLOAD; ++i) vf[i] = load_kv(vbase + off + i * 1024, MIX && k < ks);
+        const uint32_t km = bad ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < F::NLOAD; ++i) {
+          kf[i].x &= km; kf[i].y &= km; kf[i].z &= km; kf[i].w &= km;
+        }
+        const int t0 = k * 16 + 4 * row;
+        float p[CT][4];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x4 c = qk_subtile<KV, D>(kf, qf[ct]);
+          float sc[4];
+          float cmax = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            sc[j] = t0 + j <= posc[ct] ? c[j] * sl2 : -INFINITY;   // posc < L: the tail is masked too
+            cmax = fmaxf(cmax, sc[j]);
+          }
+          cmax = wave_max_rows(cmax);
+          const float m_new = fmaxf(m_run[ct], cmax);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;      // column with nothing yet
+          const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_use);
+          m_run[ct] = m_new;
+          l_run[ct] *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < F::NT; ++nn) acc[ct][nn] *= alpha;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[ct][j] = __builtin_amdgcn_exp2f(sc[j] - m_use);          // 0 where masked
+            l_run[ct] += p[ct][j];
           }
         }
-      } else if (slot == 0) {
+        uint32_t vm = 0;
 #pragma unroll
-        for (int nn = 0; nn < F::NT; ++nn) s_hold[wv][ct * F::NT + nn][lane] = acc[ct][nn];
-        s_hold_ml[wv][ct][lane] = make_float2(m_run[ct], l_tot);
-      } else {
-        store_mq_partial<KV, D>(a, piece, c, row, acc[ct], make_float2(m_run[ct], l_tot));
+        for (int j = 0; j < 4; ++j) vm |= (t0 + j < L && !bad ? 1u : 0u) << j;
+        mask_v<KV, D>(vf, vm);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) pv_subtile<KV, D>(acc[ct], vf, p[ct]);
       }
+
+      // The share's first segment (it begins within this unit's weight) is slot 0; any other
+      // unfinished segment is the share's last, slot 1.
+      const int slot = c_begin >= unit_off ? 0 : 1;
+      const int64_t piece = int64_t(wave) * 2 + slot;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const float l_tot = wave_sum_rows(l_run[ct]);
+        const int c = 16 * ct + (lane & 15);
+        const int qi = c / a.G, hh = c % a.G;
+        if (qi >= n) continue;
+        if (full) {
+          const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
+          const int64_t orow = ((int64_t(q0) + qi) * a.Hkv * a.G + int64_t(g) * a.G + hh) * D;
+#pragma unroll
+          for (int nn = 0; nn < F::NT; ++nn) {
+            const int d = 16 * nn + 4 * row;
+            if constexpr (KV == PKV_F32) {
+              *reinterpret_cast<float4*>(static_cast<float*>(a.out) + orow + d) =
+                  make_float4(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv, acc[ct][nn][2] * inv, acc[ct][nn][3] * inv);
+            } else {
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + orow + d) =
+                  make_uint2(pack_bf16x2(acc[ct][nn][0] * inv, acc[ct][nn][1] * inv),
+                             pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
+            }
+          }
+        } else if (slot == 0) {
+#pragma unroll
+          for (int nn = 0; nn < F::NT; ++nn) s_hold[wv][ct * F::NT + nn][lane] = acc[ct][nn];
+          s_hold_ml[wv][ct][lane] = make_float2(m_run[ct], l_tot);
+        } else {
+          store_mq_partial<KV, D>(a, piece, c, row, acc[ct], make_float2(m_run[ct], l_tot));
+        }
+      }
+      if (slot == 0 && !full) hold_cols = n * a.G;
     }
-    if (slot == 0 && !full) hold_cols = n * a.G;
 
     pos = seg_end;
     if (pos >= c_end) break;
@@ -788,6 +813,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       } while (!done && (L = mq_len(a, s, BS)) == 0);
       if (done) break;
       nb = (L + BS - 1) / BS;
+      span = mq_span(nb);
     }
     g = hg * a.coop + sub;
   }
@@ -818,7 +844,8 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
   const int c = c0 + std::min(lane >> 4, ncols - 1);         // this lane's column
   const int d0 = (lane & 15) * EPL;
   const int before = a.ws_seq[s];
-  const int nb = (a.ws_seq[s + 1] - before) / (a.Hkv / a.coop);
+  const int span = (a.ws_seq[s + 1] - before) / (a.Hkv / a.coop);   // weighted positions per unit
+  const int nb = span > kMqUnitW ? (span - kMqUnitW) / kMqBlockW : 0;
   const int W = a.ws_seq[a.B];
   auto write = [&](const float* v, float inv) {
     if (!col_ok) return;
@@ -847,13 +874,18 @@ __global__ __launch_bounds__(64 * kMqMergeWaves) void paged_attention_mq_merge_k
     return;
   }
   const int C = a.coop, sub = g % C;
-  const int nshare = std::min(a.splits / C, W);
-  const int off = before + (g / C) * nb;
-  const int64_t wf = share_of(off, W, nshare), wl = share_of(off + nb - 1, W, nshare);
+  const int nshare = std::min(a.splits / C, W / kMqBlockW);
+  const int off = before + (g / C) * span;
+  // The shares holding the unit's first and last blocks (a block goes to the share of its
+  // first weighted position).
+  const int64_t wf = share_of(off + kMqUnitW, W, nshare),
+                wl = share_of(off + kMqUnitW + (nb - 1) * kMqBlockW, W, nshare);
   if (wf == wl) return;
   const int np = int(wl - wf + 1);
-  // Share w's pieces of kv head g are those of its wave C*w + g%C.
-  const int64_t piece0 = (wf * C + sub) * 2 + (off != share_begin(wf, W, nshare) ? 1 : 0);
+  // Share w's pieces of kv head g are those of its wave C*w + g%C.  The unit's piece in share
+  // wf is that share's first segment (slot 0) only if the share begins within the unit's
+  // weight; in every later share it is the first segment.
+  const int64_t piece0 = (wf * C + sub) * 2 + (share_begin(wf, W, nshare) >= off ? 0 : 1);
   float M = -INFINITY, den = 0.f;
   for (int j0 = 0; j0 < np; j0 += BATCH) {
     float2 ml[BATCH];
@@ -1091,8 +1123,9 @@ extern "C" pkv_status pkv_paged_attention_prefill(
       return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
     if (B > 65535 || Hkv > 65535)
       return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs and num_kv_heads must be <= 65535 here", fn);
-    if (int64_t(B) * max_blocks_per_seq * Hkv > int64_t(INT32_MAX))
-      return pkv::fail(PKV_UNSUPPORTED, "%s: num_seqs * max_blocks_per_seq * num_kv_heads exceeds 2^31", fn);
+    if (int64_t(B) * Hkv * (int64_t(max_blocks_per_seq) * kMqBlockW + kMqUnitW) > int64_t(INT32_MAX))
+      return pkv::fail(PKV_UNSUPPORTED,
+                       "%s: num_seqs * max_blocks_per_seq * num_kv_heads is too large for the work list", fn);
     MqArgs a;
     a.out = out;
     a.q = q;

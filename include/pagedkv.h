@@ -185,9 +185,10 @@ pkv_status pkv_paged_attention_split(void* out, const void* q, const void* k_cac
  * exactly the partials phase 1 wrote, and it needs only the header to lie inside
  * workspace_bytes.  Its num_splits only picks between two merge kernels that fold the
  * partials in different orders: with phase 1's num_splits the bits equal those of
- * pkv_paged_attention_decode, otherwise they may differ by rounding.  A header that no phase 1 over num_seqs sequences wrote, or
- * one whose partials would lie outside workspace_bytes, is not followed: the heads this pass
- * would merge are set to NaN, and nothing outside the workspace is read. */
+ * pkv_paged_attention_decode, otherwise they may differ by rounding.  A header that no
+ * phase 1 over num_seqs sequences wrote, or one whose partials would lie outside
+ * workspace_bytes, is not followed: the heads this pass would merge are set to NaN, and
+ * nothing outside the workspace is read. */
 pkv_status pkv_paged_attention_reduce(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int num_seqs,

@@ -168,12 +168,15 @@ def test_bench_step_small(seed, num_splits, prefix_groups):
 
 # Other shapes for the prefix groups: G 16 (chunks of two sequences), G 1 (the whole group of
 # eight in one chunk, 8 columns), head dim 64 with 32-token blocks, a group of 12 cut into
-# chunks of 8 and 4.
+# chunks of 8 and 4, and kv-head counts that are not a multiple of four.
 GROUP_SHAPES = {
     "g16": SMALL.scaled(num_q_heads=32, num_kv_heads=2),
     "g1": SMALL.scaled(num_q_heads=8, num_kv_heads=8),
     "d64_bs32": SMALL.scaled(head_dim=64, block_size=32, num_q_heads=8, num_kv_heads=4),
     "group12": SMALL.scaled(batch=24, prefix_group=12),
+    # kv heads walked in pairs (6 heads) and one at a time (3 heads).
+    "hkv6": SMALL.scaled(num_q_heads=24, num_kv_heads=6),
+    "hkv3": SMALL.scaled(num_q_heads=6, num_kv_heads=3),
 }
 
 

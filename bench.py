@@ -379,8 +379,10 @@ def _multi_query_bench(args, wl):
     qd = pkv.F32 if wl.q_dtype == "f32" else pkv.BF16
     kd = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
     ws_bytes = pkv.paged_attention_prefill_workspace_size(B, Hq, Hkv, D, bs, qd, kd, max_q, args.num_splits)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    path = "split over keys + merge (few queries)" if ws_bytes else "query tiles through LDS"
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    few = max_q * (Hq // Hkv) <= pkv.FEW_QUERY_COLUMNS
+    path = ("split over keys + merge (few queries)" if few
+            else "query tiles through LDS, launched longest first by a plan pass")
 
     def step(i, ev=None):
         k, v = pools[i % len(pools)]
@@ -438,12 +440,12 @@ def _multi_query_bench(args, wl):
         achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "algorithmic_bytes": kv_bytes}
-    roof["kernel"] = "paged_attention_mq_split_kernel" if ws_bytes else "paged_attention_prefill_kernel"
+    roof["kernel"] = "paged_attention_mq_split_kernel" if few else "paged_attention_prefill_kernel"
     roof["path"] = path
     roof["traffic_unit"] = TRAFFIC_UNIT
     qb = 4 if wl.q_dtype == "f32" else 2
     roof["q_out_bytes"] = 2 * case.num_q_tokens * Hq * D * qb
-    roof["traffic"] = _traffic_from_profile(args, "paged_attention_mq_split" if ws_bytes else "paged_attention_prefill",
+    roof["traffic"] = _traffic_from_profile(args, "paged_attention_mq_split" if few else "paged_attention_prefill",
                                             wl.name, ("attention_prefill.hip", "attention_tile.h"))
 
     cpu = None

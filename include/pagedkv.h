@@ -373,14 +373,19 @@ pkv_status pkv_set_launch_events(void* start_event, void* stop_event);
  *                  (kv heads in groups of 4, 2 or 1, num_splits / group equal shares of the
  *                  (sequence, head group, block) list, one wave per head of a group) with a
  *                  merge pass, which needs the workspace; otherwise query tiles of 256
- *                  (query, head) columns each stream their sequence's K/V through LDS, with no
- *                  workspace.
+ *                  (query, head) columns (128 with f32) each stream their sequence's K/V
+ *                  through LDS.
  *   num_splits     shares for the few-query path (0 = a default like decode's); ignored
  *                  otherwise.
  *   shared_prefix_blocks  as for pkv_paged_attention_decode, on the few-query path; the
  *                  tile path always reads through the caches (its query tiles re-read K/V).
- *   workspace      device scratch of pkv_paged_attention_prefill_workspace_size bytes (0 on
- *                  the tile path, where it may be NULL); no initial contents needed.
+ *   workspace      device scratch of pkv_paged_attention_prefill_workspace_size bytes; no
+ *                  initial contents needed.  The few-query path needs it.  On the tile path it
+ *                  is optional: with it, a plan pass first writes the launch order of the
+ *                  query tiles (each XCD's (sequence, kv head) units longest first, a unit's
+ *                  tiles together), one 32-byte record per workgroup slot; with NULL the
+ *                  tiles run in a fixed default order.  The output bytes are the same either
+ *                  way.  There is no plan (size 0) when num_seqs * num_kv_heads > 16384.
  *   Every other argument as for pkv_paged_attention_decode.  out is written once per
  *   query row and head.
  * Limits: on the tile path max_blocks_per_seq <= 16376 and num_blocks * Hkv < 2^31 (the

@@ -30,7 +30,8 @@ __all__ = [
     "paged_decode_step_grouped", "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "kv_cache_write", "copy_blocks",
     "build_slot_mapping", "BlockAllocator", "abi_version", "set_launch_events", "apply_append",
-    "paged_attention_prefill", "paged_attention_prefill_workspace_size", "allocate_host_pool", "swap_blocks", "VmmPool",
+    "paged_attention_prefill", "paged_attention_prefill_workspace_size", "FEW_QUERY_COLUMNS",
+    "allocate_host_pool", "swap_blocks", "VmmPool",
 ]
 
 F32, BF16, FP8_E4M3FN = 0, 1, 2
@@ -415,6 +416,11 @@ def contiguous_attention_decode(out, q, k_base, v_base, seq_first_block, context
     return out
 
 
+# pkv_paged_attention_prefill takes the few-query path (split over the keys, then a merge)
+# when max_query_len * (num_q_heads / num_kv_heads) is at most this, query tiles otherwise.
+FEW_QUERY_COLUMNS = 32
+
+
 def paged_attention_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                            q_dtype, kv_dtype, max_query_len, num_splits=0) -> int:
     n = _c_sz(0)
@@ -429,8 +435,9 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
                             stream=None, shared_prefix_blocks=None):
     """Causal multi-query attention (pkv_paged_attention_prefill): sequence s's queries are
     q rows query_start[s] .. query_start[s+1]-1, its last tokens, each attending to every
-    token up to its own position.  q / out are [num_q_tokens, Hq, D].  A workspace is made
-    (and cached per stream) when the few-query path needs one and none is given."""
+    token up to its own position.  q / out are [num_q_tokens, Hq, D].  When none is given, a
+    workspace is made (and cached per stream): the few-query path needs one, and with one the
+    tile path launches its tiles longest first."""
     if q.dim() != 3 or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must both be [num_q_tokens, num_q_heads, head_dim] of one dtype")
     T, Hq, D = q.shape
@@ -446,7 +453,7 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     st = _stream(stream)
     if workspace is None:
         nbytes = paged_attention_prefill_workspace_size(B, Hq, Hkv, D, bs, qd, kd, max_query_len, num_splits)
-        workspace = _mq_workspace(nbytes, q.device, st) if nbytes else None
+        workspace = _prefill_workspace(nbytes, q.device, st) if nbytes else None
     ptrs = [_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
             _dev(query_start, "query_start")]
@@ -459,15 +466,15 @@ def paged_attention_prefill(out, q, k_cache, v_cache, block_tables, context_lens
     return out
 
 
-_mq_ws_cache: dict = {}
+_prefill_ws_cache: dict = {}
 
 
-def _mq_workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
+def _prefill_workspace(nbytes: int, device, stream_handle: int) -> torch.Tensor:
     key = (str(device), stream_handle)
-    ws = _mq_ws_cache.get(key)
+    ws = _prefill_ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _mq_ws_cache[key] = ws
+        _prefill_ws_cache[key] = ws
     return ws
 
 

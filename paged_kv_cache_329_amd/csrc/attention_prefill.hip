@@ -59,6 +59,13 @@ constexpr int kXcds = 8;                    // MI355X: 8 XCDs, workgroups dealt 
 constexpr int kMaxTableBytes = 64 * 1024;   // block-table entries staged in LDS, at most
 constexpr int kTblPad = 8;                  // -1 entries after them (a step reads at most 7 past)
 
+// One workgroup slot of the tile path: which query tile of which (sequence, kv head) it
+// runs, with that sequence's clamped query range and length, and the steps the tile takes
+// (its work).  unit < 0 marks a slot with nothing to do.
+struct TileJob {
+  int unit, tile, q0, n, L, steps, pad0, pad1;
+};
+
 struct PrefillArgs {
   void* out;
   const void* q;
@@ -70,9 +77,54 @@ struct PrefillArgs {
   int B, Hkv, G, num_blocks, max_blocks, num_q_tokens;
   int tiles;            // query tiles per (sequence, kv head)
   int units_per_xcd;    // ceil(B * Hkv / kXcds)
+  int per_xcd;          // units_per_xcd * tiles: workgroup slots per XCD
+  int cols;             // (query, head) columns per tile
+  int step_tok;         // keys staged per step
   float qk_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
+  int64_t max_tok;      // max_blocks * block size: keys a table can reach
+  TileJob* plan;        // launch order, [kXcds][per_xcd], or null for the default order
 };
+
+// Sequence s's query range and length, clamped as the kernels read them.
+struct SeqSpan {
+  int q0, n, L;
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const PrefillArgs& a, int s) {
+  int q0 = a.query_start[s], q1 = a.query_start[s + 1];
+  q0 = std::min(std::max(q0, 0), a.num_q_tokens);
+  q1 = std::min(std::max(q1, q0), a.num_q_tokens);
+  int L = std::max(a.context_lens[s], 0);
+  if (int64_t(L) > a.max_tok) L = int(a.max_tok);
+  return SeqSpan{q0, q1 - q0, L};
+}
+
+// Query tiles of a unit with at least one query column: min(ceil(n G / cols), tiles).
+__device__ __forceinline__ int live_tiles(const PrefillArgs& a, const SeqSpan& sp) {
+  return int(std::min<int64_t>((int64_t(sp.n) * a.G + a.cols - 1) / a.cols, a.tiles));
+}
+
+// The record of tile `tile` (live) of unit `unit`, with the steps it takes.
+__device__ __forceinline__ TileJob make_job(const PrefillArgs& a, int unit, int tile, const SeqSpan& sp) {
+  const int col0 = tile * a.cols;
+  const int last_q = std::min(sp.n - 1, (col0 + a.cols - 1) / a.G);
+  const int ntok = std::max(sp.L - sp.n + last_q + 1, 0);
+  return TileJob{unit, tile, sp.q0, sp.n, sp.L, (ntok + a.step_tok - 1) / a.step_tok, 0, 0};
+}
+
+// Slot j of XCD xcd in the default order: the (sequence, kv head) units are dealt to the
+// XCDs round-robin (unit u on XCD u % kXcds), and every query tile of a unit goes to the
+// unit's XCD, so the unit's K/V stays in that XCD's L2 while its tiles run; a unit's tiles
+// follow each other, last (longest) tile first.
+__device__ __forceinline__ TileJob tile_job(const PrefillArgs& a, int xcd, int j) {
+  const int unit = xcd + kXcds * (j / a.tiles);
+  const int tile = a.tiles - 1 - j % a.tiles;
+  if (unit >= a.B * a.Hkv) return TileJob{-1, 0, 0, 0, 0, 0, 0, 0};
+  const SeqSpan sp = seq_span(a, unit / a.Hkv);
+  if (tile >= live_tiles(a, sp)) return TileJob{-1, 0, 0, 0, 0, 0, 0, 0};
+  return make_job(a, unit, tile, sp);
+}
 
 // Sub-tiles staged per step: 16 KiB of K plus 16 KiB of V, at most 8 sub-tiles.
 template <int KV, int D>
@@ -110,24 +162,15 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroup b runs on XCD b % kXcds.  The (sequence, kv head) units are dealt to the XCDs
-  // round-robin (unit u on XCD u % kXcds), and every query tile of a unit goes to the unit's
-  // XCD, last tile first, so the unit's K/V stays in that XCD's L2 while its tiles run.
+  // Workgroup b runs on XCD b % kXcds, as its slot b / kXcds there.  With a plan, the
+  // slots of an XCD hold its tiles longest first (the plan pass below); otherwise they follow
+  // the default order of tile_job.  Either way a tile's output is the same.
   const int xcd = int(blockIdx.x) % kXcds, j = int(blockIdx.x) / kXcds;
-  const int unit = xcd + kXcds * (j / a.tiles);
-  if (unit >= a.B * a.Hkv) return;
-  const int s = unit / a.Hkv, g = unit % a.Hkv;
-  const int tile = a.tiles - 1 - j % a.tiles;
-
-  int q0 = a.query_start[s], q1 = a.query_start[s + 1];
-  q0 = std::min(std::max(q0, 0), a.num_q_tokens);
-  q1 = std::min(std::max(q1, q0), a.num_q_tokens);
-  const int n = q1 - q0;
+  const TileJob job = a.plan ? a.plan[int64_t(xcd) * a.per_xcd + j] : tile_job(a, xcd, j);
+  if (job.unit < 0) return;
+  const int s = job.unit / a.Hkv, g = job.unit % a.Hkv;
+  const int tile = job.tile, q0 = job.q0, n = job.n, L = job.L;
   const int col0 = tile * COLS;
-  if (col0 >= n * a.G) return;
-  int L = a.context_lens[s];
-  L = std::max(L, 0);
-  if (int64_t(L) > int64_t(a.max_blocks) * BS) L = a.max_blocks * BS;
   const int last_q = std::min(n - 1, (col0 + COLS - 1) / a.G);
   const int ntok = std::max(L - n + last_q + 1, 0);      // keys the workgroup reads
   const int nsub = (ntok + 15) / 16;
@@ -465,6 +508,119 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
                        pack_bf16x2(acc[ct][nn][2] * inv, acc[ct][nn][3] * inv));
       }
     }
+  }
+}
+
+// ---- launch order of the query tiles ------------------------------------------------------
+//
+// A workgroup holds a CU for as long as its tile takes, and a tile's time grows with the keys
+// it reads.  In the default order an XCD runs its units in index order, so a long unit dealt
+// late leaves a few CUs busy after the rest have drained.  The plan pass orders each XCD's
+// units by the steps of their longest tile, longest first (a counting sort over step counts),
+// and gives each unit a run of consecutive slots holding its tiles, last (longest) tile
+// first; the slots of tiles with no query column go last.  Sorting whole units rather than
+// single tiles keeps the tiles that run together on one unit, whose K/V then stays in the
+// XCD's L2: an order of single tiles by length ran more units at once and lost more in L2
+// misses than it gained in balance on full prompts.  Units with equal step counts take the
+// order in which their atomic increments land, which changes the launch order but not what
+// any tile computes.
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 2048;   // step counts, shifted right by `shift` to fit
+constexpr int kPlanUnits = 2048;     // units per XCD the plan orders, at most
+constexpr int kPlanPerThread = kPlanUnits / kPlanThreads;
+static_assert(kPlanUnits % kPlanThreads == 0, "plan tiling");
+
+// In-place exclusive prefix sum of v[0..n) by the whole workgroup; returns the total.
+__device__ int plan_exclusive_scan(int* v, int n, int* wave_total) {
+  const int tid = int(threadIdx.x), lane = tid & 63;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int lo = std::min(n, tid * per), hi = std::min(n, lo + per);
+  int mine = 0;
+  for (int r = lo; r < hi; ++r) mine += v[r];
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_total[tid >> 6] = incl;
+  __syncthreads();
+  int run = incl - mine, total = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    if (w < (tid >> 6)) run += wave_total[w];
+    total += wave_total[w];
+  }
+  for (int r = lo; r < hi; ++r) {
+    const int c = v[r];
+    v[r] = run;
+    run += c;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void paged_attention_prefill_plan_kernel(PrefillArgs a, int shift) {
+  // Bucket r holds the units whose longest tile has the r-th largest step count; bucket
+  // kPlanBuckets the units with no live tile.
+  __shared__ int cursor[kPlanBuckets + 1];
+  __shared__ int wave_total[kPlanThreads / 64];
+  __shared__ int u_tiles[kPlanUnits];   // by unit (i: unit xcd + kXcds i): live tiles
+  __shared__ SeqSpan u_span[kPlanUnits];
+  __shared__ int r_unit[kPlanUnits];    // by place in the order: the unit
+  __shared__ int r_first[kPlanUnits];   // by place: the unit's live tiles, then its first slot
+  const int xcd = int(blockIdx.x), tid = int(threadIdx.x);
+  const int U = a.units_per_xcd;
+  for (int i = tid; i <= kPlanBuckets; i += kPlanThreads) cursor[i] = 0;
+  __syncthreads();
+  int bucket[kPlanPerThread];
+#pragma unroll
+  for (int k = 0; k < kPlanPerThread; ++k) {
+    const int i = tid + k * kPlanThreads, unit = xcd + kXcds * i;
+    bucket[k] = kPlanBuckets;
+    if (i >= U) continue;
+    int nt = 0;
+    SeqSpan sp{0, 0, 0};
+    if (unit < a.B * a.Hkv) {
+      sp = seq_span(a, unit / a.Hkv);
+      nt = live_tiles(a, sp);
+      if (nt > 0)
+        bucket[k] = kPlanBuckets - 1 - std::min(make_job(a, unit, nt - 1, sp).steps >> shift, kPlanBuckets - 1);
+    }
+    u_tiles[i] = nt;
+    u_span[i] = sp;
+    atomicAdd(&cursor[bucket[k]], 1);
+  }
+  __syncthreads();
+  plan_exclusive_scan(cursor, kPlanBuckets + 1, wave_total);
+#pragma unroll
+  for (int k = 0; k < kPlanPerThread; ++k) {
+    const int i = tid + k * kPlanThreads;
+    if (i >= U) continue;
+    const int r = atomicAdd(&cursor[bucket[k]], 1);
+    r_unit[r] = i;
+    r_first[r] = u_tiles[i];
+  }
+  __syncthreads();
+  const int live = plan_exclusive_scan(r_first, U, wave_total);
+
+  // Slots [0, live) hold the live tiles unit by unit in order, each unit's last tile first;
+  // [live, per_xcd) nothing.  Places with live tiles come first, with increasing first
+  // slots, so slot j's place is the last one whose first slot is <= j.
+  TileJob* out = a.plan + int64_t(xcd) * a.per_xcd;
+  for (int j = tid; j < a.per_xcd; j += kPlanThreads) {
+    TileJob t{-1, 0, 0, 0, 0, 0, 0, 0};
+    if (j < live) {
+      int lo = 0, hi = U;   // r_first[lo] <= j < r_first[hi] (r_first[U] read as live)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (r_first[mid] <= j) lo = mid;
+        else hi = mid;
+      }
+      const int i = r_unit[lo];
+      t = make_job(a, xcd + kXcds * i, u_tiles[i] - 1 - (j - r_first[lo]), u_span[i]);
+    }
+    out[j] = t;
   }
 }
 
@@ -1018,15 +1174,37 @@ PrefillFn prefill_fn() {
 }
 
 template <int KV>
-bool pick_prefill(int D, int bs, PrefillFn* fn, int* cols) {
+bool pick_prefill(int D, int bs, PrefillFn* fn, int* cols, int* step_tok) {
+  constexpr int CKV = KV == PKV_FP8_E4M3FN ? PKV_BF16 : KV;
   const int ct = KV == PKV_F32 ? 1 : 2;
   *cols = kWaves * 16 * ct;
+  *step_tok = 16 * (D == 64 ? step_subtiles<CKV, 64>() : step_subtiles<CKV, 128>());
   if (D == 64 && bs == 16) *fn = prefill_fn<KV, 64, 16>();
   else if (D == 64 && bs == 32) *fn = prefill_fn<KV, 64, 32>();
   else if (D == 128 && bs == 16) *fn = prefill_fn<KV, 128, 16>();
   else if (D == 128 && bs == 32) *fn = prefill_fn<KV, 128, 32>();
   else return false;
   return true;
+}
+
+bool pick_prefill_any(pkv_dtype kv, int D, int bs, PrefillFn* fn, int* cols, int* step_tok) {
+  return kv == PKV_F32    ? pick_prefill<PKV_F32>(D, bs, fn, cols, step_tok)
+         : kv == PKV_BF16 ? pick_prefill<PKV_BF16>(D, bs, fn, cols, step_tok)
+                          : pick_prefill<PKV_FP8_E4M3FN>(D, bs, fn, cols, step_tok);
+}
+
+// The tile path's grid: kXcds * units_per_xcd * tiles workgroup slots.
+bool tile_grid(int B, int Hkv, int G, int max_query_len, int cols, int64_t* tiles, int64_t* per_xcd) {
+  *tiles = (int64_t(max_query_len) * G + cols - 1) / cols;
+  *per_xcd = (int64_t(B) * Hkv + kXcds - 1) / kXcds * *tiles;
+  return *tiles <= int64_t(INT32_MAX) && *per_xcd <= int64_t(INT32_MAX) / kXcds;
+}
+
+// The plan's bytes, one TileJob per slot; 0 when an XCD has more units than the plan orders
+// (the tiles then run in the default order).
+size_t plan_bytes(int B, int Hkv, int64_t per_xcd) {
+  if ((int64_t(B) * Hkv + kXcds - 1) / kXcds > kPlanUnits) return 0;
+  return (size_t(kXcds) * per_xcd * sizeof(TileJob) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -1073,7 +1251,18 @@ extern "C" pkv_status pkv_paged_attention_prefill_workspace_size(int num_seqs, i
                                  block_size, q_dtype, kv_dtype);
   if (st != PKV_OK) return st;
   *bytes = 0;
-  if (!few_queries(max_query_len, num_q_heads / num_kv_heads)) return PKV_OK;
+  if (!few_queries(max_query_len, num_q_heads / num_kv_heads)) {
+    // The tile path's plan: optional, but the tiles then run longest first.
+    PrefillFn kfn = nullptr;
+    int cols = 0, step_tok = 0;
+    int64_t tiles = 0, per_xcd = 0;
+    if (!pick_prefill_any(kv_dtype, head_dim, block_size, &kfn, &cols, &step_tok))
+      return pkv::fail(PKV_UNSUPPORTED, "%s: no kernel for this shape", fn);
+    if (!tile_grid(num_seqs, num_kv_heads, num_q_heads / num_kv_heads, max_query_len, cols, &tiles, &per_xcd))
+      return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tiles", fn);
+    *bytes = plan_bytes(num_seqs, num_kv_heads, per_xcd);
+    return PKV_OK;
+  }
   MqPair kp;
   int splits = 0;
   if ((st = mq_splits(fn, kv_dtype, head_dim, block_size, num_splits, &kp, &splits)) != PKV_OK) return st;
@@ -1180,15 +1369,16 @@ extern "C" pkv_status pkv_paged_attention_prefill(
                      kMaxTableBytes / 4 - kTblPad);
 
   PrefillFn kfn = nullptr;
-  int cols = 0;
-  bool ok = kv_dtype == PKV_F32    ? pick_prefill<PKV_F32>(head_dim, block_size, &kfn, &cols)
-            : kv_dtype == PKV_BF16 ? pick_prefill<PKV_BF16>(head_dim, block_size, &kfn, &cols)
-                                   : pick_prefill<PKV_FP8_E4M3FN>(head_dim, block_size, &kfn, &cols);
-  if (!ok) return pkv::fail(PKV_UNSUPPORTED, "%s: no kernel for this shape", fn);
+  int cols = 0, step_tok = 0;
+  if (!pick_prefill_any(kv_dtype, head_dim, block_size, &kfn, &cols, &step_tok))
+    return pkv::fail(PKV_UNSUPPORTED, "%s: no kernel for this shape", fn);
   const int G = Hq / Hkv;
-  const int64_t tiles = (int64_t(max_query_len) * G + cols - 1) / cols;
-  if (tiles > int64_t(INT32_MAX))
+  int64_t tiles = 0, per_xcd = 0;
+  if (!tile_grid(B, Hkv, G, max_query_len, cols, &tiles, &per_xcd))
     return pkv::fail(PKV_UNSUPPORTED, "%s: too many query tiles", fn);
+  const size_t need = plan_bytes(B, Hkv, per_xcd);
+  if (workspace && workspace_bytes < need)
+    return pkv::fail(PKV_INVALID_ARG, "%s: workspace of %zu bytes < %zu required", fn, workspace_bytes, need);
 
   PrefillArgs a;
   a.out = out;
@@ -1208,10 +1398,23 @@ extern "C" pkv_status pkv_paged_attention_prefill(
   a.v_scale = v_scale;
   a.tiles = int(tiles);
   a.units_per_xcd = (B * Hkv + kXcds - 1) / kXcds;
-  const int64_t wgs = int64_t(kXcds) * a.units_per_xcd * tiles;
-  if (wgs > int64_t(UINT32_MAX))
-    return pkv::fail(PKV_UNSUPPORTED, "%s: too many workgroups", fn);
+  a.per_xcd = int(per_xcd);
+  a.cols = cols;
+  a.step_tok = step_tok;
+  a.max_tok = int64_t(max_blocks_per_seq) * block_size;
+  a.plan = need > 0 ? static_cast<TileJob*>(workspace) : nullptr;
+  const int64_t wgs = int64_t(kXcds) * per_xcd;
   const dim3 grid{unsigned(wgs)}, block{unsigned(kThreads)};
+  if (a.plan) {
+    // Step counts are bucketed exactly while the longest possible tile has fewer steps than
+    // there are buckets, and coarsened by powers of two beyond.
+    const int64_t max_steps = (a.max_tok + step_tok - 1) / step_tok;
+    int shift = 0;
+    while ((max_steps >> shift) >= kPlanBuckets) ++shift;
+    hipLaunchKernelGGL(paged_attention_prefill_plan_kernel, dim3(kXcds), dim3(kPlanThreads), 0, hs, a, shift);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pkv::fail(PKV_HIP_ERROR, "%s: plan launch: %s", fn, hipGetErrorString(e));
+  }
   const size_t lds = size_t(tbl_bytes);
   void *ev0 = nullptr, *ev1 = nullptr;
   if (pkv::take_launch_events(&ev0, &ev1)) {

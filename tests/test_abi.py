@@ -166,6 +166,29 @@ def test_prefill_tile_path_rejects_pool_too_large_for_staged_table():
     assert st == 2 and b"num_blocks * num_kv_heads" in lib.pkv_last_error()
 
 
+def test_prefill_tile_path_plan_workspace():
+    """On the tile path the workspace holds the launch plan: one 32-byte record per
+    workgroup slot, 8 XCDs x ceil(B * Hkv / 8) units x tiles of 256 (query, head) columns
+    (128 for f32), rounded up to 256 bytes, while an XCD has at most 2048 units.  A non-NULL
+    workspace smaller than that is refused on the host; NULL means the default launch order."""
+    lib = pkv.lib()
+    # 3 sequences x 8 kv heads: 3 units per XCD; 100 queries x G 4 = 400 columns: 2 tiles.
+    want = 8 * 3 * 2 * 32
+    assert pkv.paged_attention_prefill_workspace_size(3, 32, 8, 128, 16, pkv.BF16, pkv.BF16, 100) == want
+    assert pkv.paged_attention_prefill_workspace_size(3, 32, 8, 128, 16, pkv.BF16, pkv.FP8_E4M3FN, 100) == want
+    # f32: 128 columns per tile, so 4 tiles.
+    assert pkv.paged_attention_prefill_workspace_size(3, 32, 8, 128, 16, pkv.F32, pkv.F32, 100) == 2 * want
+    # 1 sequence x 2 kv heads: one unit slot per XCD, 1 tile, 256 bytes after rounding.
+    assert pkv.paged_attention_prefill_workspace_size(1, 4, 2, 64, 32, pkv.BF16, pkv.BF16, 40) == 256
+    # The plan orders at most 2048 units per XCD; beyond that there is none (default order).
+    assert pkv.paged_attention_prefill_workspace_size(2048, 32, 8, 128, 16, pkv.BF16, pkv.BF16, 100) == 8 * 2048 * 2 * 32
+    assert pkv.paged_attention_prefill_workspace_size(2049, 32, 8, 128, 16, pkv.BF16, pkv.BF16, 100) == 0
+    a = ctypes.c_void_p(256)
+    st = lib.pkv_paged_attention_prefill(a, a, a, a, a, a, a, 3, 300, 32, 8, 128, 16, 64, 8, 100,
+                                         0.125, 1.0, 1.0, pkv.BF16, pkv.BF16, 0, a, want - 1, None, None)
+    assert st == 1 and b"workspace" in lib.pkv_last_error()
+
+
 def test_noalloc_decode_rejects_a_workspace_beyond_its_scratch():
     """The entry point that allocates nothing refuses, on the host and before touching a
     device, a call whose workspace would exceed its fixed scratch."""

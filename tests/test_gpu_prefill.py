@@ -202,6 +202,60 @@ def test_few_query_path_many_short_sequences(splits):
     assert_close(got, oatt.prefill_case(case), wl.kv_dtype, f"few-query many short splits={splits}")
 
 
+ORDER_CASES = {
+    # Many (sequence, kv head) units per XCD with unequal lengths, several tiles each.
+    "prefill_bf16": WORKLOADS["prefill_llama3_8b_bf16"].scaled(batch=14, length_dist=("uniform", 1, 700)),
+    "chunk_bf16": WORKLOADS["chunked_prefill_llama3_8b_bf16"].scaled(
+        batch=12, length_dist=("uniform", 1, 900), query_dist=("fixed", 150)),
+    "prefill_fp8": WORKLOADS["prefill_fp8_kv"].scaled(batch=10, length_dist=("uniform", 1, 600)),
+    "f32_d128_bs32_g4": SMALL["f32_d128_bs32_g4"].scaled(batch=9, length_dist=("uniform", 1, 400)),
+}
+
+
+@pytest.mark.parametrize("name", list(ORDER_CASES))
+def test_tile_path_launch_order_leaves_the_bits(name):
+    """The tile path with a workspace first runs a plan pass that launches the query tiles
+    longest first; without one (NULL) they run in the default order.  Both give the oracle's
+    result and the same bytes, and the plan needs no initial workspace contents (it is
+    poisoned with 0xFF bytes first)."""
+    require_gpu()
+    import ctypes
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from gpu_helpers import to_dev
+    wl = ORDER_CASES[name]
+    case = make_prefill_case(wl, 6)
+    log(f"launch order {name} lengths={case.lengths.tolist()} q_lens={case.q_lens.tolist()}")
+    k, v = pack(case)
+    q = to_dev(case.q, wl.q_dtype)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).cuda()
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
+    qs = torch.from_numpy(case.query_start.astype(np.int32)).cuda()
+    max_q = int(case.q_lens.max())
+    G = wl.num_q_heads // wl.num_kv_heads
+    assert max_q * G > pkv.FEW_QUERY_COLUMNS                 # the tile path
+    qd = pkv.F32 if wl.q_dtype == "f32" else pkv.BF16
+    kd = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
+    nbytes = pkv.paged_attention_prefill_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                         wl.block_size, qd, kd, max_q, 0)
+    assert nbytes > 0
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    planned = torch.empty_like(q)
+    pkv.paged_attention_prefill(planned, q, k, v, tables, lens, qs, max_q, case.scale, float(case.k_scale),
+                                float(case.v_scale), workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, f"launch order {name}")
+    unordered = torch.empty_like(q)
+    st = pkv.lib().pkv_paged_attention_prefill(
+        unordered.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), tables.data_ptr(), lens.data_ptr(),
+        qs.data_ptr(), wl.batch, q.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+        k.shape[0], tables.shape[1], max_q, ctypes.c_float(case.scale), ctypes.c_float(float(case.k_scale)),
+        ctypes.c_float(float(case.v_scale)), qd, kd, 0, None, 0, None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, pkv.lib().pkv_last_error()
+    torch.cuda.synchronize()
+    assert raw_bytes(unordered) == raw_bytes(planned)
+
+
 def _prefill_splits(case, k, v, splits):
     import torch
     import paged_kv_cache_329_amd as pkv

@@ -256,6 +256,26 @@ def test_tile_path_launch_order_leaves_the_bits(name):
     assert raw_bytes(unordered) == raw_bytes(planned)
 
 
+def test_tile_path_without_a_plan_beyond_its_unit_limit():
+    """2,100 short prompts x 8 kv heads is 16,800 (sequence, kv head) units, past the 16,384
+    the launch plan orders: the workspace size is 0 and the tiles run in the default order.
+    Sampled query rows are checked against the oracle, and every row is finite."""
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    wl = WORKLOADS["prefill_llama3_8b_bf16"].scaled(batch=2100, length_dist=("uniform", 9, 16))
+    case = make_prefill_case(wl, 12)
+    max_q = int(case.q_lens.max())
+    assert max_q * wl.group_size > pkv.FEW_QUERY_COLUMNS
+    assert pkv.paged_attention_prefill_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                      wl.block_size, pkv.BF16, pkv.BF16, max_q) == 0
+    log(f"no-plan prefill: {wl.batch} sequences, {case.num_q_tokens} query rows")
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v))
+    assert np.all(np.isfinite(got))
+    rows = np.sort(np.random.default_rng(3).choice(case.num_q_tokens, size=400, replace=False))
+    assert_close(got[rows], oatt.prefill_case(case, rows), wl.kv_dtype, "no-plan prefill")
+
+
 def _prefill_splits(case, k, v, splits):
     import torch
     import paged_kv_cache_329_amd as pkv

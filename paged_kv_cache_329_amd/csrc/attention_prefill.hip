@@ -35,7 +35,8 @@
 //    position is skipped by that wave (it still stages its share of the loads).  V elements
 //    of slots at or past L_s are zeroed (an unwritten tail slot may hold NaN).
 //  * Order: all tiles of one (sequence, kv head) run on one XCD (sharing its L2), launched
-//    last tile first, so the tiles with the most keys start earliest.
+//    last tile first, so the tiles with the most keys start earliest.  Given a workspace, a
+//    plan pass first orders each XCD's (sequence, kv head) units longest first.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

@@ -256,6 +256,38 @@ def test_tile_path_launch_order_leaves_the_bits(name):
     assert raw_bytes(unordered) == raw_bytes(planned)
 
 
+def test_tile_path_plan_with_tables_at_the_width_limit():
+    """Tables padded to 16,376 entries (the tile path's limit) make the longest possible tile
+    4,094 steps, so the plan counts steps in coarser buckets (shifted right by one).  The
+    planned and the unplanned launch agree with the oracle and with each other bit for bit."""
+    require_gpu()
+    import ctypes
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    from gpu_helpers import to_dev
+    wl = ORDER_CASES["prefill_bf16"]
+    case = make_prefill_case(wl, 7)
+    width = 16376
+    tables_np = np.full((wl.batch, width), -1, np.int32)
+    tables_np[:, :case.block_tables.shape[1]] = case.block_tables
+    k, v = pack(case)
+    planned = prefill(case, k, v, tables=tables_np)
+    assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, "plan at the table width limit")
+    q = to_dev(case.q, wl.q_dtype)
+    tables = torch.from_numpy(tables_np).cuda()
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
+    qs = torch.from_numpy(case.query_start.astype(np.int32)).cuda()
+    unordered = torch.empty_like(q)
+    st = pkv.lib().pkv_paged_attention_prefill(
+        unordered.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), tables.data_ptr(), lens.data_ptr(),
+        qs.data_ptr(), wl.batch, q.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
+        k.shape[0], width, int(case.q_lens.max()), ctypes.c_float(case.scale), ctypes.c_float(1.0),
+        ctypes.c_float(1.0), pkv.BF16, pkv.BF16, 0, None, 0, None, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, pkv.lib().pkv_last_error()
+    torch.cuda.synchronize()
+    assert raw_bytes(unordered) == raw_bytes(planned)
+
+
 def test_tile_path_without_a_plan_beyond_its_unit_limit():
     """2,100 short prompts x 8 kv heads is 16,800 (sequence, kv head) units, past the 16,384
     the launch plan orders: the workspace size is 0 and the tiles run in the default order.

@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void paged_attention_prefill_kernel(Pr
   const uint8_t* vbase = a.v_cache + int64_t(g) * REGION;
   __syncthreads();   // s_tbl
 
-  // Chunk tid + 256*r of a step: K or V, sub-tile u, chunk w.  Sub-tiles past the keys the
+  // Chunk tid + kThreads*r of a step: K or V, sub-tile u, chunk w.  Sub-tiles past the keys the
   // workgroup reads and blocks outside [0, num_blocks) are read from block 0 (always in
   // bounds) and staged as zeros; zmask marks them (rare: the last step, or a bad table entry).
   //

@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import paged_kv_cache_329_amd as pkv
+from synth import Workload, make_decode_case
 
 TORCH_KV = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3fn": torch.float8_e4m3fn}
 INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8_e4m3fn": torch.uint8}
@@ -210,3 +211,23 @@ def check_all_sequences(got, case, name, chunk=8):
         seqs = list(range(c, min(B, c + chunk)))
         assert_close(got[seqs], oatt.decode_case(case, seqs), case.wl.kv_dtype, f"{name}, sequences {seqs}")
     log(f"{name}: all {B} sequences match the oracle")
+
+
+def random_decode_case(seed):
+    """A seeded random decode batch over every supported axis: head size, block size, cache
+    type, group size (up to 16, including sizes that leave merge lanes idle), kv heads
+    (including counts walked in groups of one and two), batch, and lengths with empty
+    sequences among them."""
+    rng = np.random.default_rng(2000 + seed)
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    kv = str(rng.choice(["f32", "bf16", "fp8_e4m3fn"]))
+    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    B = int(rng.integers(1, 21))
+    lengths = rng.integers(0, 1200, size=B)
+    lengths[rng.random(B) < 0.15] = 0
+    q_dtype = "f32" if kv == "f32" else "bf16"
+    wl = Workload(f"rand{seed}", B, Hkv * G, Hkv, D, bs, q_dtype, kv, ("uniform", 0, 1200))
+    splits = int(rng.choice([0, 1, 2, 7, 100, 1000, 3000]))
+    return make_decode_case(wl, seed, lengths=lengths), splits

@@ -11,7 +11,7 @@ import torch
 from oracle import attention as oatt
 from synth import WORKLOADS, Workload, bf16_bits_from_f32, make_decode_case
 
-from gpu_helpers import as_f64, assert_close, decode, log, pack, raw_bytes, require_gpu, to_dev
+from gpu_helpers import as_f64, assert_close, decode, log, pack, random_decode_case, raw_bytes, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,30 +47,10 @@ def test_parity_small(name, seed):
     assert_close(got, oatt.decode_case(case), wl.kv_dtype, name)
 
 
-def _random_decode_case(seed):
-    """A seeded random decode batch over every supported axis: head size, block size, cache
-    type, group size (up to 16, including sizes that leave merge lanes idle), kv heads
-    (including counts walked in groups of one and two), batch, and lengths with empty
-    sequences among them."""
-    rng = np.random.default_rng(2000 + seed)
-    D = int(rng.choice([64, 128]))
-    bs = int(rng.choice([16, 32]))
-    kv = str(rng.choice(["f32", "bf16", "fp8_e4m3fn"]))
-    G = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
-    Hkv = int(rng.choice([1, 2, 3, 4, 6, 8]))
-    B = int(rng.integers(1, 21))
-    lengths = rng.integers(0, 1200, size=B)
-    lengths[rng.random(B) < 0.15] = 0
-    q_dtype = "f32" if kv == "f32" else "bf16"
-    wl = Workload(f"rand{seed}", B, Hkv * G, Hkv, D, bs, q_dtype, kv, ("uniform", 0, 1200))
-    splits = int(rng.choice([0, 1, 2, 7, 100, 1000, 3000]))
-    return make_decode_case(wl, seed, lengths=lengths), splits
-
-
 @pytest.mark.parametrize("seed", range(8))
 def test_random_shapes(seed):
     require_gpu()
-    case, splits = _random_decode_case(seed)
+    case, splits = random_decode_case(seed)
     wl = case.wl
     log(f"random decode {seed}: D={wl.head_dim} bs={wl.block_size} kv={wl.kv_dtype} G={wl.group_size} "
         f"Hkv={wl.num_kv_heads} B={wl.batch} splits={splits} lengths={case.lengths.tolist()}")

@@ -18,7 +18,7 @@ from oracle import attention as oatt
 from synth import WORKLOADS, Workload, make_decode_case
 
 from gpu_helpers import (INT_VIEW, as_f64, assert_close, check_all_sequences, decode, kv_storage, log, pack, pool_pair,
-                         raw_bytes, require_gpu, to_dev)
+                         random_decode_case, raw_bytes, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,25 @@ def _assert_same_up_to_rounding(got, ref, kv_dtype):
     a, b = as_f64(got), as_f64(ref)
     bound = 1e-5 if kv_dtype == "f32" else 2.0 ** -6 * (1.0 + np.abs(b))
     assert np.all(np.abs(a - b) <= bound), float(np.max(np.abs(a - b)))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_step_random_shapes(seed):
+    """The decode test's seeded random shapes through the step with append, at each draw's
+    split count: oracle parity, the pool bit-identical to kv_cache_write's, and agreement
+    with write-then-decode up to rounding."""
+    require_gpu()
+    case, splits = random_decode_case(seed)
+    wl = case.wl
+    log(f"random decode step {seed}: D={wl.head_dim} bs={wl.block_size} kv={wl.kv_dtype} G={wl.group_size} "
+        f"Hkv={wl.num_kv_heads} B={wl.batch} splits={splits} lengths={case.lengths.tolist()}")
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn, num_splits=splits)
+    assert_close(as_f64(out), oatt.decode_case(case), wl.kv_dtype, f"random decode step {seed}")
+    k_ref, v_ref = pack(case)
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k_ref))
+    assert np.array_equal(_pool_bytes(v), _pool_bytes(v_ref))
+    _assert_same_up_to_rounding(out, decode(case, k_ref, v_ref, num_splits=splits), wl.kv_dtype)
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -362,6 +362,38 @@ def test_tile_path_without_a_plan_beyond_its_unit_limit():
     assert_close(got[rows], oatt.prefill_case(case, rows), wl.kv_dtype, "no-plan prefill")
 
 
+def _random_few_case(seed):
+    """A seeded random few-query batch: at most 32 (query, head) columns per (sequence, kv
+    head), over random head and block sizes, cache types, group and batch sizes."""
+    rng = np.random.default_rng(3000 + seed)
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    kv = str(rng.choice(["f32", "bf16", "fp8_e4m3fn"]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    B = int(rng.integers(1, 40))
+    lengths = rng.integers(0, 900, size=B)
+    q_lens = np.minimum(rng.integers(0, 32 // G + 1, size=B), np.maximum(lengths, 1))
+    q_dtype = "f32" if kv == "f32" else "bf16"
+    wl = Workload(f"few{seed}", B, Hkv * G, Hkv, D, bs, q_dtype, kv, ("uniform", 0, 900), query_dist=("all",))
+    splits = int(rng.choice([0, 1, 3, 50, 600]))
+    return make_prefill_case(wl, seed, lengths=np.maximum(lengths, q_lens), q_lens=q_lens), splits
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_few_query_path_random_shapes(seed):
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    case, splits = _random_few_case(seed)
+    wl = case.wl
+    assert int(case.q_lens.max()) * wl.group_size <= pkv.FEW_QUERY_COLUMNS
+    log(f"random few-query {seed}: D={wl.head_dim} bs={wl.block_size} kv={wl.kv_dtype} G={wl.group_size} "
+        f"Hkv={wl.num_kv_heads} B={wl.batch} splits={splits} q_lens={case.q_lens.tolist()}")
+    k, v = pack(case)
+    got = as_f64(prefill(case, k, v) if splits == 0 else _prefill_splits(case, k, v, splits))
+    assert_close(got, oatt.prefill_case(case), wl.kv_dtype, f"random few-query {seed}")
+
+
 def _prefill_splits(case, k, v, splits):
     import torch
     import paged_kv_cache_329_amd as pkv

@@ -187,6 +187,27 @@ def test_prefix_groups_other_shapes(name, num_splits):
     _check_bench_step(make_prefix_step_case(GROUP_SHAPES[name], 3), num_splits, prefix_groups=True)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_groups_random_shapes(seed):
+    """Seeded random shapes through the step with prefix groups: head and block size, group
+    size, kv heads, group size and prefix length (whole blocks), the batch's seed and the
+    split count; every sequence of every step against the oracle and the pools checked at
+    the end."""
+    require_gpu()
+    rng = np.random.default_rng(4000 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    group = int(rng.choice([2, 5, 8, 12]))
+    bs = int(rng.choice([16, 32]))
+    # The prefill of a group forks its members from a root whose prefix fills whole blocks.
+    wl = SMALL.scaled(head_dim=int(rng.choice([64, 128])), block_size=bs, num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                      prefix_group=group, prefix_len=bs * int(rng.integers(1, 5)), batch=group * int(rng.integers(1, 5)))
+    splits = int(rng.choice([0, 5, 17, 300]))
+    log(f"random prefix groups {seed}: D={wl.head_dim} bs={wl.block_size} G={G} Hkv={Hkv} "
+        f"group={wl.prefix_group} prefix={wl.prefix_len} B={wl.batch} splits={splits}")
+    _check_bench_step(make_prefix_step_case(wl, 10 + seed), splits, prefix_groups=True)
+
+
 @pytest.mark.parametrize("num_splits", [0, 17])
 def test_prefix_groups_fp8_cache(num_splits):
     """The step with prefix groups over an fp8 e4m3fn cache with 32-token blocks: the

@@ -650,7 +650,7 @@ def _vmm_bench(args):
                 pools[-1] = (vmm.k, vmm.v, torch.from_numpy(tables).to(dev), vmm, firsts)
                 mapped += vmm.mapped_bytes
         except pkv.PagedKVError as e:
-            # Record how far the mapping got: the driver caps the number of allocations.
+            # Record how far the mapping got: the GPU kernel driver caps the number of allocations.
             last = pools[-1][3] if pools else None
             if last is not None and pools[-1][2] is None:
                 n_pages += (last.mapped_bytes // last.page_bytes) - 2

@@ -213,6 +213,30 @@ def check_all_sequences(got, case, name, chunk=8):
     log(f"{name}: all {B} sequences match the oracle")
 
 
+def prefill_default_order(case, k, v, tables=None):
+    """The tile path of pkv_paged_attention_prefill called through the C ABI with a NULL
+    workspace, so that no launch plan is made and the query tiles run in the default order."""
+    import ctypes
+
+    wl = case.wl
+    tables = case.block_tables if tables is None else tables
+    qd = to_dev(case.q, wl.q_dtype)
+    t = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).cuda()
+    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
+    qs = torch.from_numpy(np.asarray(case.query_start, np.int32)).cuda()
+    codes = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}
+    out = torch.empty_like(qd)
+    st = pkv.lib().pkv_paged_attention_prefill(
+        out.data_ptr(), qd.data_ptr(), k.data_ptr(), v.data_ptr(), t.data_ptr(), lens.data_ptr(), qs.data_ptr(),
+        wl.batch, qd.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, k.shape[0], t.shape[1],
+        int(case.q_lens.max()), ctypes.c_float(case.scale), ctypes.c_float(float(case.k_scale)),
+        ctypes.c_float(float(case.v_scale)), codes[wl.q_dtype], codes[wl.kv_dtype], 0, None, 0, None,
+        torch.cuda.current_stream().cuda_stream)
+    assert st == 0, pkv.lib().pkv_last_error()
+    torch.cuda.synchronize()
+    return out
+
+
 def random_decode_case(seed):
     """A seeded random decode batch over every supported axis: head size, block size, cache
     type, group size (up to 16, including sizes that leave merge lanes idle), kv heads

@@ -12,7 +12,7 @@ import pytest
 from oracle import attention as oatt
 from synth import WORKLOADS, Workload, make_prefill_case
 
-from gpu_helpers import as_f64, assert_close, decode, log, pack, prefill, raw_bytes, require_gpu
+from gpu_helpers import as_f64, assert_close, decode, log, pack, prefill, prefill_default_order, raw_bytes, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -219,7 +219,6 @@ def test_tile_path_launch_order_leaves_the_bits(name):
     result and the same bytes, and the plan needs no initial workspace contents (it is
     poisoned with 0xFF bytes first)."""
     require_gpu()
-    import ctypes
     import torch
     import paged_kv_cache_329_amd as pkv
     from gpu_helpers import to_dev
@@ -245,15 +244,7 @@ def test_tile_path_launch_order_leaves_the_bits(name):
                                 float(case.v_scale), workspace=ws)
     torch.cuda.synchronize()
     assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, f"launch order {name}")
-    unordered = torch.empty_like(q)
-    st = pkv.lib().pkv_paged_attention_prefill(
-        unordered.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), tables.data_ptr(), lens.data_ptr(),
-        qs.data_ptr(), wl.batch, q.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-        k.shape[0], tables.shape[1], max_q, ctypes.c_float(case.scale), ctypes.c_float(float(case.k_scale)),
-        ctypes.c_float(float(case.v_scale)), qd, kd, 0, None, 0, None, torch.cuda.current_stream().cuda_stream)
-    assert st == 0, pkv.lib().pkv_last_error()
-    torch.cuda.synchronize()
-    assert raw_bytes(unordered) == raw_bytes(planned)
+    assert raw_bytes(prefill_default_order(case, k, v)) == raw_bytes(planned)
 
 
 def _random_tile_case(seed):
@@ -280,10 +271,7 @@ def test_tile_path_launch_plan_random_shapes(seed):
     the oracle's result on every row, and the same bytes as the default order (NULL
     workspace)."""
     require_gpu()
-    import ctypes
-    import torch
     import paged_kv_cache_329_amd as pkv
-    from gpu_helpers import to_dev
     case = _random_tile_case(seed)
     wl = case.wl
     max_q = int(case.q_lens.max())
@@ -293,21 +281,7 @@ def test_tile_path_launch_plan_random_shapes(seed):
     k, v = pack(case)
     planned = prefill(case, k, v)
     assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, f"random tile case {seed}")
-    q = to_dev(case.q, wl.q_dtype)
-    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).cuda()
-    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
-    qs = torch.from_numpy(case.query_start.astype(np.int32)).cuda()
-    qd = pkv.F32 if wl.q_dtype == "f32" else pkv.BF16
-    kd = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
-    unordered = torch.empty_like(q)
-    st = pkv.lib().pkv_paged_attention_prefill(
-        unordered.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), tables.data_ptr(), lens.data_ptr(),
-        qs.data_ptr(), wl.batch, q.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-        k.shape[0], tables.shape[1], max_q, ctypes.c_float(case.scale), ctypes.c_float(float(case.k_scale)),
-        ctypes.c_float(float(case.v_scale)), qd, kd, 0, None, 0, None, torch.cuda.current_stream().cuda_stream)
-    assert st == 0, pkv.lib().pkv_last_error()
-    torch.cuda.synchronize()
-    assert raw_bytes(unordered) == raw_bytes(planned)
+    assert raw_bytes(prefill_default_order(case, k, v)) == raw_bytes(planned)
 
 
 def test_tile_path_plan_with_tables_at_the_width_limit():
@@ -315,10 +289,6 @@ def test_tile_path_plan_with_tables_at_the_width_limit():
     4,094 steps, so the plan counts steps in coarser buckets (shifted right by one).  The
     planned and the unplanned launch agree with the oracle and with each other bit for bit."""
     require_gpu()
-    import ctypes
-    import torch
-    import paged_kv_cache_329_amd as pkv
-    from gpu_helpers import to_dev
     wl = ORDER_CASES["prefill_bf16"]
     case = make_prefill_case(wl, 7)
     width = 16376
@@ -327,19 +297,7 @@ def test_tile_path_plan_with_tables_at_the_width_limit():
     k, v = pack(case)
     planned = prefill(case, k, v, tables=tables_np)
     assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, "plan at the table width limit")
-    q = to_dev(case.q, wl.q_dtype)
-    tables = torch.from_numpy(tables_np).cuda()
-    lens = torch.from_numpy(case.lengths.astype(np.int32)).cuda()
-    qs = torch.from_numpy(case.query_start.astype(np.int32)).cuda()
-    unordered = torch.empty_like(q)
-    st = pkv.lib().pkv_paged_attention_prefill(
-        unordered.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(), tables.data_ptr(), lens.data_ptr(),
-        qs.data_ptr(), wl.batch, q.shape[0], wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size,
-        k.shape[0], width, int(case.q_lens.max()), ctypes.c_float(case.scale), ctypes.c_float(1.0),
-        ctypes.c_float(1.0), pkv.BF16, pkv.BF16, 0, None, 0, None, torch.cuda.current_stream().cuda_stream)
-    assert st == 0, pkv.lib().pkv_last_error()
-    torch.cuda.synchronize()
-    assert raw_bytes(unordered) == raw_bytes(planned)
+    assert raw_bytes(prefill_default_order(case, k, v, tables=tables_np)) == raw_bytes(planned)
 
 
 def test_tile_path_without_a_plan_beyond_its_unit_limit():

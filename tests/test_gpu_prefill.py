@@ -12,7 +12,8 @@ import pytest
 from oracle import attention as oatt
 from synth import WORKLOADS, Workload, make_prefill_case
 
-from gpu_helpers import as_f64, assert_close, decode, log, pack, prefill, prefill_default_order, raw_bytes, require_gpu
+from gpu_helpers import (as_f64, assert_close, decode, log, pack, prefill, prefill_default_order, raw_bytes,
+                         require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -170,7 +171,6 @@ def test_few_query_path_parity(name, splits):
     require_gpu()
     import torch
     import paged_kv_cache_329_amd as pkv
-    from gpu_helpers import to_dev
     wl = FEW[name]
     case = make_prefill_case(wl, 2)
     log(f"few-query {name} splits={splits} lengths={case.lengths.tolist()} q_lens={case.q_lens.tolist()}")
@@ -221,7 +221,6 @@ def test_tile_path_launch_order_leaves_the_bits(name):
     require_gpu()
     import torch
     import paged_kv_cache_329_amd as pkv
-    from gpu_helpers import to_dev
     wl = ORDER_CASES[name]
     case = make_prefill_case(wl, 6)
     log(f"launch order {name} lengths={case.lengths.tolist()} q_lens={case.q_lens.tolist()}")
@@ -282,6 +281,67 @@ def test_tile_path_launch_plan_random_shapes(seed):
     planned = prefill(case, k, v)
     assert_close(as_f64(planned), oatt.prefill_case(case), wl.kv_dtype, f"random tile case {seed}")
     assert raw_bytes(prefill_default_order(case, k, v)) == raw_bytes(planned)
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "chunk_bf16", "f32_d128_bs32_g4"])
+def test_launch_plan_records(name):
+    """The plan the tile path leaves in its workspace: one 32-byte record (unit, tile, q0, n,
+    L, steps, 0, 0) per workgroup slot, [8 XCDs][units per XCD x tiles].  On each XCD the
+    live slots hold exactly the live tiles of the units dealt to it (unit % 8), each unit's
+    tiles in one run, last tile first; the runs come in non-increasing order of their first
+    (longest) tile's steps; the remaining slots are empty (unit -1); and every record holds
+    its sequence's query range and length and its tile's step count."""
+    require_gpu()
+    import torch
+    import paged_kv_cache_329_amd as pkv
+    wl = ORDER_CASES[name]
+    case = make_prefill_case(wl, 8)
+    k, v = pack(case)
+    max_q = int(case.q_lens.max())
+    qd = pkv.F32 if wl.q_dtype == "f32" else pkv.BF16
+    kd = {"f32": pkv.F32, "bf16": pkv.BF16, "fp8_e4m3fn": pkv.FP8_E4M3FN}[wl.kv_dtype]
+    nbytes = pkv.paged_attention_prefill_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                                         wl.block_size, qd, kd, max_q)
+    ws = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(to_dev(case.q, wl.q_dtype))
+    pkv.paged_attention_prefill(out, to_dev(case.q, wl.q_dtype), k, v,
+                                torch.from_numpy(np.ascontiguousarray(case.block_tables, np.int32)).cuda(),
+                                torch.from_numpy(case.lengths.astype(np.int32)).cuda(),
+                                torch.from_numpy(case.query_start.astype(np.int32)).cuda(), max_q, case.scale,
+                                float(case.k_scale), float(case.v_scale), workspace=ws)
+    torch.cuda.synchronize()
+    # Expected geometry, from the documented tiling: 256 (query, head) columns per tile (128
+    # for f32), 16 * sub-tiles-per-step keys per step (16 KiB of K per step, at most 8 sub-tiles).
+    G, Hkv, B = wl.group_size, wl.num_kv_heads, wl.batch
+    cols = 128 if wl.kv_dtype == "f32" else 256
+    eb = 4 if wl.kv_dtype == "f32" else 2
+    step_tok = 16 * min(8, 16384 // (16 * wl.head_dim * eb))
+    tiles = -(-max_q * G // cols)
+    per_xcd = -(-B * Hkv // 8) * tiles
+    rec = ws[:8 * per_xcd * 32].cpu().numpy().view(np.int32).reshape(8, per_xcd, 8)
+    qs = case.query_start.astype(np.int64)
+    for x in range(8):
+        live = []
+        for u in range(x, B * Hkv, 8):
+            s_ = u // Hkv
+            n, L = int(qs[s_ + 1] - qs[s_]), int(case.lengths[s_])
+            for t in range(min(-(-n * G // cols), tiles)):
+                last_q = min(n - 1, (t * cols + cols - 1) // G)
+                live.append((u, t, int(qs[s_]), n, L, -(-max(L - n + last_q + 1, 0) // step_tok)))
+        got = [tuple(int(c) for c in r[:6]) for r in rec[x] if r[0] >= 0]
+        assert sorted(got) == sorted(live), f"XCD {x}: the live slots are not the live tiles"
+        assert np.all(rec[x][len(got):, 0] == -1) and np.all(rec[x][:len(got), 0] >= 0)
+        runs = []
+        for r in got:
+            if not runs or runs[-1][0][0] != r[0]:
+                runs.append([r])
+            else:
+                runs[-1].append(r)
+        assert len({r[0][0] for r in runs}) == len(runs), f"XCD {x}: a unit's tiles are split"
+        for run in runs:
+            assert [r[1] for r in run] == sorted((r[1] for r in run), reverse=True)
+        firsts = [run[0][5] for run in runs]
+        assert firsts == sorted(firsts, reverse=True), f"XCD {x}: units not longest first"
 
 
 def test_tile_path_plan_with_tables_at_the_width_limit():
@@ -355,7 +415,6 @@ def test_few_query_path_random_shapes(seed):
 def _prefill_splits(case, k, v, splits):
     import torch
     import paged_kv_cache_329_amd as pkv
-    from gpu_helpers import to_dev
     wl = case.wl
     q = to_dev(case.q, wl.q_dtype)
     out = torch.empty_like(q)

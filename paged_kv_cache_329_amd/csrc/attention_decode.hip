@@ -61,6 +61,10 @@ constexpr int kWavesPerWG = 4;
 constexpr int kXcds = 8;   // MI355X: workgroups are dealt to the 8 XCDs round-robin
 constexpr int kMaxGroup = 16;
 constexpr int kGroupCols = 32;   // (member, query head) columns of a group share: two 16-column tiles
+// Batches of up to kScanSeqs sequences: each workgroup of the prefix-group split pass scans
+// both work lists into LDS, kScanSeqs / (kWavesPerWG * 64) sequences per thread.
+constexpr int kScanSeqs = 512;
+constexpr int kScanPerThread = kScanSeqs / (kWavesPerWG * 64);
 
 // Work lists are cut by estimated cost, not by block count.  A unit (one sequence's blocks for
 // one head group) weighs kUnitW plus kBlockW per block: its q and table round trip and its
@@ -149,6 +153,10 @@ struct DecodeArgs {
   float* ws_gml;   // [splits * 2][kGroupCols][2]
   float* ws_fgacc; // [B * Hkv][kGroupCols][D]
   float* ws_fgml;  // [B * Hkv][kGroupCols][2]
+  // [B][8] int32, when the split pass scans the lists in LDS (B <= kScanSeqs): sequence s's
+  // member offset, its chunk's group offset, the chunk's blocks, s's group blocks, s's member
+  // blocks and its chunk's first sequence, for the merge.
+  int* ws_rec;
   int appending;   // 1 for the decode step with append (token L-1 is the appended one)
 };
 
@@ -228,6 +236,50 @@ __device__ int group_work(const DecodeArgs& a, int bs, int lane) {
     acc += s < a.B ? unit_span(chunk_blocks(a, s, bs), kGroupBlockW) : 0;
   }
   return wave_sum(acc) * head_groups(a);
+}
+
+// Per-unit spans of sequence s in the member list (unit_blocks<true>) and of the chunk that s
+// starts in the group list (chunk_blocks), from the same definitions, with every lookup
+// issued unconditionally (indices clamped into range, results selected): the sequence's own
+// entries, then its chunk's, then the chunk sources', three dependent round trips in all.
+struct SeqSpans {
+  int mspan, gspan;   // per-unit spans in the member and group lists
+  int skip;           // leading blocks the group pass reads for s (group_skip)
+  int f, P;           // s's chunk (its first sequence) and that chunk's blocks, when skip > 0
+};
+
+__device__ __forceinline__ SeqSpans seq_spans(const DecodeArgs& a, int s, int bs) {
+  const int M = kGroupCols / a.G;
+  const int Ls = seq_len(a, s, bs);
+  const int fs = a.chunk_first[s], gbs = a.group_blocks[s], srcs = a.chunk_src[s];
+  const bool f_ok = fs >= 0 && fs <= s && s - fs < M;
+  const int fc = f_ok ? fs : s;
+  const int cf_f = a.chunk_first[fc], src_f = a.chunk_src[fc];
+  const int sf = unsigned(src_f) < unsigned(a.B) ? src_f : 0;
+  const int ss = unsigned(srcs) < unsigned(a.B) ? srcs : 0;
+  const int cf_sf = a.chunk_first[sf], gb_sf = a.group_blocks[sf], L_sf = seq_len(a, sf, bs);
+  const int cf_ss = a.chunk_first[ss], gb_ss = a.group_blocks[ss], L_ss = seq_len(a, ss, bs);
+  auto full_blocks = [&](int L) { return (L - (a.appending && L > 0 ? 1 : 0)) / bs; };
+  const bool ok_f = cf_f == fc && src_f >= fc && src_f - fc < M && src_f < a.B && cf_sf == fc;
+  const int cb_f = ok_f ? min(max(gb_sf, 0), full_blocks(L_sf)) : 0;
+  const int skip = f_ok ? min(min(max(gbs, 0), cb_f), full_blocks(Ls)) : 0;
+  const bool ok_s = fs == s && srcs >= s && srcs - s < M && srcs < a.B && cf_ss == s;
+  const int cb_s = ok_s ? min(max(gb_ss, 0), full_blocks(L_ss)) : 0;
+  return SeqSpans{unit_span((Ls + bs - 1) / bs - skip, kBlockW), unit_span(cb_s, kGroupBlockW), skip, fc, cb_f};
+}
+
+// Largest s in [0, n) with hg * e[s] <= x, for e non-decreasing in LDS with e[0] = 0: each
+// step samples 64 evenly spaced entries of the remaining range.
+__device__ __forceinline__ int lds_search(const int* e, int n, int hg, int x, int lane) {
+  int lo = 0;
+  while (n > 1) {
+    const int step = (n + 63) / 64;
+    const bool le = lane * step < n && hg * e[lo + lane * step] <= x;
+    const int l = 63 - __builtin_clzll(__ballot(le));
+    lo += l * step;
+    n = std::min(step, n - l * step);
+  }
+  return lo;
 }
 
 // Sequence whose units contain work position x (0 <= x < W), and the weighted positions of
@@ -466,7 +518,8 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
 // hold / hold_ml: this wave's LDS rows for the partial of the share's first segment.
 template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG, bool GROUPED>
 __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin,
-                                           int c_end, f32x4 (*hold)[64], float2* hold_ml) {
+                                           int c_end, f32x4 (*hold)[64], float2* hold_ml,
+                                           const int* lds_off = nullptr, int s_start = 0, int off_start = 0) {
   static_assert(!(CONTIG && APPEND), "the contiguous placement has no decode step with append");
   static_assert(!(GROUPED && (MIX || CONTIG)), "prefix groups read shared blocks once, through tables");
   using F = Frag<KV, D>;
@@ -477,13 +530,27 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
   constexpr int64_t REGION = int64_t(BS) * D * T::EB;
 
   bool holding = false;
+  // lds_off (prefix groups, when the workgroup has scanned the list): exclusive prefix sums
+  // of the per-unit spans of the member list in LDS, and the share's first sequence and its
+  // offset, found there.  A unit's blocks then follow from its span.
   int s, seq_off;
-  locate<GROUPED>(a, BS, lane, c_begin, s, seq_off);
+  if (lds_off) {
+    s = s_start;
+    seq_off = off_start;
+  } else {
+    locate<GROUPED>(a, BS, lane, c_begin, s, seq_off);
+  }
   if (s >= a.B) return;
   int L = seq_len(a, s, BS);
-  int skip = GROUPED ? group_skip(a, s, BS) : 0;   // leading blocks the group pass reads
   int nbt = (L + BS - 1) / BS;                     // blocks of the sequence
-  int nb = nbt - skip;                             // blocks of each of its units in this list
+  int skip, nb;                                    // leading blocks the group pass reads; blocks
+  if (lds_off) {                                   // of each of its units in this list
+    nb = (lds_off[s + 1] - lds_off[s] - kUnitW) / kBlockW;
+    skip = nbt - nb;
+  } else {
+    skip = GROUPED ? group_skip(a, s, BS) : 0;
+    nb = nbt - skip;
+  }
   int span = unit_span(nb, kBlockW);
   int hg = (c_begin - seq_off) / span;
   int g = hg * a.coop + sub;
@@ -495,14 +562,25 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
     unit_off += span;
     if (++hg == head_groups(a)) {
       hg = 0;
-      do {
-        done = ++s >= a.B;
-      } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
+      if (lds_off) {
+        do {
+          done = ++s >= a.B;
+        } while (!done && lds_off[s + 1] == lds_off[s]);
+      } else {
+        do {
+          done = ++s >= a.B;
+        } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
+      }
       if (done) return false;
       L = seq_len(a, s, BS);
-      skip = GROUPED ? group_skip(a, s, BS) : 0;
       nbt = (L + BS - 1) / BS;
-      nb = nbt - skip;
+      if (lds_off) {
+        nb = (lds_off[s + 1] - lds_off[s] - kUnitW) / kBlockW;
+        skip = nbt - nb;
+      } else {
+        skip = GROUPED ? group_skip(a, s, BS) : 0;
+        nb = nbt - skip;
+      }
       span = unit_span(nb, kBlockW);
     }
     g = hg * a.coop + sub;
@@ -786,7 +864,8 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 // last segments as pieces (share * coop + sub) * 2 + slot.
 template <int KV, int D, int BS>
 __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin, int c_end,
-                                           f32x4 (*hold)[64], float2 (*hold_ml)[64]) {
+                                           f32x4 (*hold)[64], float2 (*hold_ml)[64], const int* lds_off = nullptr,
+                                           int f_start = 0, int off_start = 0) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;
@@ -798,10 +877,16 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
   const int row = lane >> 4;
   bool holding = false;
 
+  // lds_off: as in split_walk, over the group list's per-unit spans.
   int f, chunk_off;
-  locate<false, true>(a, BS, lane, c_begin, f, chunk_off);
+  if (lds_off) {
+    f = f_start;
+    chunk_off = off_start;
+  } else {
+    locate<false, true>(a, BS, lane, c_begin, f, chunk_off);
+  }
   if (f >= a.B) return;
-  int P = chunk_blocks(a, f, BS);
+  int P = lds_off ? (lds_off[f + 1] - lds_off[f] - kUnitW) / kGroupBlockW : chunk_blocks(a, f, BS);
   int span = unit_span(P, kGroupBlockW);
   int hg = (c_begin - chunk_off) / span;
   int g = hg * a.coop + sub;
@@ -813,11 +898,19 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
     unit_off += span;
     if (++hg == head_groups(a)) {
       hg = 0;
-      do {
-        ++f;
-      } while (f < a.B && chunk_blocks(a, f, BS) == 0);
-      if (f >= a.B) return false;
-      P = chunk_blocks(a, f, BS);
+      if (lds_off) {
+        do {
+          ++f;
+        } while (f < a.B && lds_off[f + 1] == lds_off[f]);
+        if (f >= a.B) return false;
+        P = (lds_off[f + 1] - lds_off[f] - kUnitW) / kGroupBlockW;
+      } else {
+        do {
+          ++f;
+        } while (f < a.B && chunk_blocks(a, f, BS) == 0);
+        if (f >= a.B) return false;
+        P = chunk_blocks(a, f, BS);
+      }
       span = unit_span(P, kGroupBlockW);
     }
     g = hg * a.coop + sub;
@@ -974,6 +1067,10 @@ __device__ __forceinline__ void grouped_shares(const DecodeArgs& a, int Wm, int 
 // floor(w nsg / S)), so that both kinds run on every XCD at once.  Header: member offsets
 // [B+1] (total at [B]), the split count, head-group width and B at [B+1..B+3], group offsets
 // [B+1] from [B+4] (total at [2B+4]), nsg at [2B+5].
+// Start-up: with at most kScanSeqs sequences, the workgroup's threads take the sequences
+// between them, each with its lookups in flight together, and scan both lists into LDS; a
+// wave then finds its share's first unit there and reads later units' block counts there,
+// instead of walking the sequences' entries 64 at a time through dependent loads.
 template <int KV, int D, int BS, int NSUB, bool APPEND>
 __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_kernel(DecodeArgs a) {
   using F = Frag<KV, D>;
@@ -982,13 +1079,86 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_k
   const int wave = logical_wave(wv);
   __shared__ f32x4 s_hold[kWavesPerWG][(kGroupCols / 16) * F::NT][64];
   __shared__ float2 s_hold_ml[kWavesPerWG][kGroupCols / 16][64];
-  const int Wm = total_work<true>(a, BS, lane);
-  const int Wg = group_work(a, BS, lane);
+  // Both work lists, scanned by the workgroup when the batch fits: exclusive prefix sums of
+  // the per-unit spans, [s] for sequence s and the total from [B] on.
+  __shared__ int s_moff[kScanSeqs + 1];
+  __shared__ int s_goff[kScanSeqs + 1];
+  __shared__ int s_wsum[2][kWavesPerWG];
+  const int hg = head_groups(a);
+  const bool lds_lists = a.B <= kScanSeqs;
+  int Wm, Wg;
+  if (lds_lists) {
+    const int tid = threadIdx.x;
+    SeqSpans sp[kScanPerThread];
+    int ms[kScanPerThread], gs[kScanPerThread];
+    int msum = 0, gsum = 0;
+#pragma unroll
+    for (int r = 0; r < kScanPerThread; ++r) {
+      const int sq = tid * kScanPerThread + r;
+      sp[r] = seq_spans(a, std::min(sq, a.B - 1), BS);
+      ms[r] = sq < a.B ? sp[r].mspan : 0;
+      gs[r] = sq < a.B ? sp[r].gspan : 0;
+      msum += ms[r];
+      gsum += gs[r];
+    }
+    const int mi = wave_incl_scan(msum, lane), gi = wave_incl_scan(gsum, lane);
+    if (lane == 63) {
+      s_wsum[0][wv] = mi;
+      s_wsum[1][wv] = gi;
+    }
+    __syncthreads();
+    int mb = mi - msum, gb = gi - gsum, mt = 0, gt = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWG; ++w) {
+      mb += w < wv ? s_wsum[0][w] : 0;
+      gb += w < wv ? s_wsum[1][w] : 0;
+      mt += s_wsum[0][w];
+      gt += s_wsum[1][w];
+    }
+#pragma unroll
+    for (int r = 0; r < kScanPerThread; ++r) {
+      s_moff[tid * kScanPerThread + r] = mb;
+      s_goff[tid * kScanPerThread + r] = gb;
+      mb += ms[r];
+      gb += gs[r];
+    }
+    if (tid == 0) {
+      s_moff[kScanSeqs] = mt;
+      s_goff[kScanSeqs] = gt;
+    }
+    __syncthreads();
+    Wm = mt * hg;
+    Wg = gt * hg;
+    if (blockIdx.x == 0) {
+#pragma unroll
+      for (int r = 0; r < kScanPerThread; ++r) {
+        const int sq = tid * kScanPerThread + r;
+        if (sq < a.B) {
+          const bool grp = sp[r].skip > 0;
+          int* rec = a.ws_rec + 8 * sq;
+          *reinterpret_cast<int4*>(rec) = make_int4(s_moff[sq] * hg, grp ? s_goff[sp[r].f] * hg : 0, grp ? sp[r].P : 0,
+                                                    sp[r].skip);
+          *reinterpret_cast<int4*>(rec + 4) =
+              make_int4(ms[r] > 0 ? (ms[r] - kUnitW) / kBlockW : 0, grp ? sp[r].f : 0, 0, 0);
+        }
+      }
+    }
+  } else {
+    Wm = total_work<true>(a, BS, lane);
+    Wg = group_work(a, BS, lane);
+  }
   int S, nsg;
   grouped_shares(a, Wm, Wg, S, nsg);
   if (wave == 0) {
-    write_offsets<true, false>(a, BS, lane, a.ws_seq);
-    write_offsets<false, true>(a, BS, lane, a.ws_seq + a.B + 4);
+    if (lds_lists) {
+      for (int sq = lane; sq <= a.B; sq += 64) {
+        a.ws_seq[sq] = s_moff[sq] * hg;
+        a.ws_seq[a.B + 4 + sq] = s_goff[sq] * hg;
+      }
+    } else {
+      write_offsets<true, false>(a, BS, lane, a.ws_seq);
+      write_offsets<false, true>(a, BS, lane, a.ws_seq + a.B + 4);
+    }
     if (lane == 0) {
       a.ws_seq[a.B + 1] = a.splits;
       a.ws_seq[a.B + 2] = a.coop;
@@ -999,15 +1169,25 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_k
   const int share = wave / a.coop;
   const int sub = wave % a.coop;
   if (share >= S) return;
+  // Group share gi of nsg over Wg, or member share mi of S - nsg over Wm.  The share's index
+  // and bounds are wave-uniform: kept in scalar registers.
   const int gi = int(int64_t(share) * nsg / S);
-  if (int64_t(share + 1) * nsg / S > gi) {
-    group_walk<KV, D, BS>(a, lane, gi, sub, int(share_begin(gi, Wg, nsg)), int(share_begin(gi + 1, Wg, nsg)),
-                          s_hold[wv], s_hold_ml[wv]);
+  const bool is_group = int64_t(share + 1) * nsg / S > gi;
+  const int idx = __builtin_amdgcn_readfirstlane(is_group ? gi : share - gi);
+  const int n = is_group ? nsg : S - nsg, Wl = is_group ? Wg : Wm;
+  const int c_begin = __builtin_amdgcn_readfirstlane(int(share_begin(idx, Wl, n)));
+  const int c_end = __builtin_amdgcn_readfirstlane(int(share_begin(idx + 1, Wl, n)));
+  const int* lds_off = lds_lists ? (is_group ? s_goff : s_moff) : nullptr;
+  int s0 = 0, off0 = 0;
+  if (lds_lists) {
+    s0 = __builtin_amdgcn_readfirstlane(lds_search(lds_off, a.B, hg, c_begin, lane));
+    off0 = lds_off[s0] * hg;
+  }
+  if (is_group) {
+    group_walk<KV, D, BS>(a, lane, idx, sub, c_begin, c_end, s_hold[wv], s_hold_ml[wv], lds_off, s0, off0);
   } else {
-    const int ms = share - gi, nsm = S - nsg;
-    split_walk<KV, D, BS, NSUB, APPEND, false, false, true>(a, lane, ms, sub, int(share_begin(ms, Wm, nsm)),
-                                                            int(share_begin(ms + 1, Wm, nsm)), s_hold[wv],
-                                                            s_hold_ml[wv][0]);
+    split_walk<KV, D, BS, NSUB, APPEND, false, false, true>(a, lane, idx, sub, c_begin, c_end, s_hold[wv],
+                                                            s_hold_ml[wv][0], lds_off, s0, off0);
   }
 }
 
@@ -1211,19 +1391,36 @@ __global__ __launch_bounds__(64) void paged_attention_grouped_merge_kernel(Decod
   grouped_shares(a, Wm, Wg, S, nsg_again);
   const int nsm = S - nsg;
 
-  const int skip = group_skip(a, s, BS);
-  const int nbm = seq_blocks(a, s, BS) - skip;
+  // s's group blocks, member blocks, chunk, the chunk's blocks and both offsets: from the
+  // split pass's record when it scanned the lists in LDS, else from their definitions.
+  int skip, nbm, f = 0, P = 0, moff, goff_f = 0;
+  if (a.B <= kScanSeqs) {
+    const int4 r0 = *reinterpret_cast<const int4*>(a.ws_rec + 8 * s);
+    const int4 r1 = *reinterpret_cast<const int4*>(a.ws_rec + 8 * s + 4);
+    moff = r0.x;
+    goff_f = r0.y;
+    P = r0.z;
+    skip = r0.w;
+    nbm = r1.x;
+    f = r1.y;
+  } else {
+    skip = group_skip(a, s, BS);
+    nbm = seq_blocks(a, s, BS) - skip;
+    moff = a.ws_seq[s];
+    if (skip > 0) {
+      f = a.chunk_first[s];
+      P = chunk_blocks(a, f, BS);
+      goff_f = goff[f];
+    }
+  }
   // Group pieces [0, ng) and member pieces [ng, ng + nm): where each lies.
   int ng = 0, nm = 0;
   int64_t g_first = 0, g_wf = 0, m_first = 0, m_wf = 0;
   bool g_slot = false, m_slot = false;
   int col = 0;
-  int f = 0;
   if (skip > 0) {
-    f = a.chunk_first[s];
     col = (s - f) * a.G + h;
-    const int P = chunk_blocks(a, f, BS);
-    const int off = goff[f] + hg * unit_span(P, kGroupBlockW);
+    const int off = goff_f + hg * unit_span(P, kGroupBlockW);
     const int64_t wf = share_of(off + kUnitW, Wg, nsg), wl = share_of(off + kUnitW + (P - 1) * kGroupBlockW, Wg, nsg);
     g_slot = wf == wl;
     ng = g_slot ? 1 : int(wl - wf + 1);
@@ -1231,7 +1428,7 @@ __global__ __launch_bounds__(64) void paged_attention_grouped_merge_kernel(Decod
     g_first = (wf * C + sub) * 2 + (share_begin(wf, Wg, nsg) >= off ? 0 : 1);
   }
   if (nbm > 0) {
-    const int off = a.ws_seq[s] + hg * unit_span(nbm, kBlockW);
+    const int off = moff + hg * unit_span(nbm, kBlockW);
     const int64_t wf = share_of(off + kUnitW, Wm, nsm), wl = share_of(off + kUnitW + (nbm - 1) * kBlockW, Wm, nsm);
     if (wf == wl && skip == 0) return;   // finished and written by the split pass
     m_slot = wf == wl;
@@ -1458,8 +1655,8 @@ size_t workspace_bytes_for(int splits, int B, int G, int D) {
 // finished inside a share [B * Hkv][G], the group pieces of shares [splits * 2][32], group
 // units finished inside a share [B * Hkv][32]; accumulators float32 [D] and (max, sum) pairs.
 struct GroupedLayout {
-  int64_t hdr, sacc, sml, macc, mml, gacc, gml, fgacc, fgml;
-  int64_t total() const { return hdr + sacc + sml + macc + mml + gacc + gml + fgacc + fgml; }
+  int64_t hdr, sacc, sml, macc, mml, gacc, gml, fgacc, fgml, rec;
+  int64_t total() const { return hdr + sacc + sml + macc + mml + gacc + gml + fgacc + fgml + rec; }
 };
 
 GroupedLayout grouped_layout(int splits, int B, int Hkv, int G, int D) {
@@ -1473,6 +1670,7 @@ GroupedLayout grouped_layout(int splits, int B, int Hkv, int G, int D) {
   l.gml = round256(int64_t(splits) * 2 * kGroupCols * 2 * 4);
   l.fgacc = round256(int64_t(B) * Hkv * kGroupCols * D * 4);
   l.fgml = round256(int64_t(B) * Hkv * kGroupCols * 2 * 4);
+  l.rec = round256(int64_t(B) * 8 * 4);
   return l;
 }
 
@@ -1597,6 +1795,7 @@ pkv_status run_decode(const char* fn, Phase phase, void* out, const void* q, con
     a.ws_gml = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc);
     a.ws_fgacc = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc + l.gml);
     a.ws_fgml = reinterpret_cast<float*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc + l.gml + l.fgacc);
+    a.ws_rec = reinterpret_cast<int*>(w + l.hdr + l.sacc + l.sml + l.macc + l.mml + l.gacc + l.gml + l.fgacc + l.fgml);
   }
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (phase != kMergeOnly) {

@@ -177,6 +177,10 @@ GROUP_SHAPES = {
     # kv heads walked in pairs (6 heads) and one at a time (3 heads).
     "hkv6": SMALL.scaled(num_q_heads=24, num_kv_heads=6),
     "hkv3": SMALL.scaled(num_q_heads=6, num_kv_heads=3),
+    # The split pass scans batches of up to 512 sequences in each workgroup, larger ones
+    # wave by wave: a batch at that limit and one past it.
+    "b512": SMALL.scaled(batch=512, length_dist=("lognormal", 40.0, 0.5, 120)),
+    "b520": SMALL.scaled(batch=520, length_dist=("lognormal", 40.0, 0.5, 120)),
 }
 
 

@@ -65,6 +65,11 @@ constexpr int kGroupCols = 32;   // (member, query head) columns of a group shar
 // both work lists into LDS, kScanSeqs / (kWavesPerWG * 64) sequences per thread.
 constexpr int kScanSeqs = 512;
 constexpr int kScanPerThread = kScanSeqs / (kWavesPerWG * 64);
+// LDS entry of a sequence's group columns in the prefix-group pass: (group blocks << 10) |
+// chunk first (kNoChunk when outside [0, num_seqs)); used while the table width is below
+// 2^21 blocks.
+constexpr int kNoChunk = 1023;
+constexpr int kGlimMaxBlocks = 1 << 21;
 
 // Work lists are cut by estimated cost, not by block count.  A unit (one sequence's blocks for
 // one head group) weighs kUnitW plus kBlockW per block: its q and table round trip and its
@@ -246,6 +251,8 @@ struct SeqSpans {
   int mspan, gspan;   // per-unit spans in the member and group lists
   int skip;           // leading blocks the group pass reads for s (group_skip)
   int f, P;           // s's chunk (its first sequence) and that chunk's blocks, when skip > 0
+  int L;              // s's clamped length
+  int cf;             // chunk_first[s] as stored
 };
 
 __device__ __forceinline__ SeqSpans seq_spans(const DecodeArgs& a, int s, int bs) {
@@ -265,7 +272,7 @@ __device__ __forceinline__ SeqSpans seq_spans(const DecodeArgs& a, int s, int bs
   const int skip = f_ok ? min(min(max(gbs, 0), cb_f), full_blocks(Ls)) : 0;
   const bool ok_s = fs == s && srcs >= s && srcs - s < M && srcs < a.B && cf_ss == s;
   const int cb_s = ok_s ? min(max(gb_ss, 0), full_blocks(L_ss)) : 0;
-  return SeqSpans{unit_span((Ls + bs - 1) / bs - skip, kBlockW), unit_span(cb_s, kGroupBlockW), skip, fc, cb_f};
+  return SeqSpans{unit_span((Ls + bs - 1) / bs - skip, kBlockW), unit_span(cb_s, kGroupBlockW), skip, fc, cb_f, Ls, fs};
 }
 
 // Largest s in [0, n) with hg * e[s] <= x, for e non-decreasing in LDS with e[0] = 0: each
@@ -519,7 +526,8 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t piece
 template <int KV, int D, int BS, int NSUB, bool APPEND, bool MIX, bool CONTIG, bool GROUPED>
 __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin,
                                            int c_end, f32x4 (*hold)[64], float2* hold_ml,
-                                           const int* lds_off = nullptr, int s_start = 0, int off_start = 0) {
+                                           const int* lds_off = nullptr, const int* lds_len = nullptr,
+                                           int s_start = 0, int off_start = 0) {
   static_assert(!(CONTIG && APPEND), "the contiguous placement has no decode step with append");
   static_assert(!(GROUPED && (MIX || CONTIG)), "prefix groups read shared blocks once, through tables");
   using F = Frag<KV, D>;
@@ -530,9 +538,9 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
   constexpr int64_t REGION = int64_t(BS) * D * T::EB;
 
   bool holding = false;
-  // lds_off (prefix groups, when the workgroup has scanned the list): exclusive prefix sums
-  // of the per-unit spans of the member list in LDS, and the share's first sequence and its
-  // offset, found there.  A unit's blocks then follow from its span.
+  // lds_off / lds_len (when the workgroup has scanned the list): exclusive prefix sums of the
+  // per-unit spans of the list and the sequences' clamped lengths, in LDS, and the share's
+  // first sequence and its offset, found there.  A unit's blocks then follow from its span.
   int s, seq_off;
   if (lds_off) {
     s = s_start;
@@ -541,7 +549,7 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
     locate<GROUPED>(a, BS, lane, c_begin, s, seq_off);
   }
   if (s >= a.B) return;
-  int L = seq_len(a, s, BS);
+  int L = lds_len ? lds_len[s] : seq_len(a, s, BS);
   int nbt = (L + BS - 1) / BS;                     // blocks of the sequence
   int skip, nb;                                    // leading blocks the group pass reads; blocks
   if (lds_off) {                                   // of each of its units in this list
@@ -572,7 +580,7 @@ __device__ __forceinline__ void split_walk(const DecodeArgs& a, int lane, int sh
         } while (!done && unit_blocks<GROUPED>(a, s, BS) == 0);
       }
       if (done) return false;
-      L = seq_len(a, s, BS);
+      L = lds_len ? lds_len[s] : seq_len(a, s, BS);
       nbt = (L + BS - 1) / BS;
       if (lds_off) {
         nb = (lds_off[s + 1] - lds_off[s] - kUnitW) / kBlockW;
@@ -836,9 +844,54 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
   // would hold up every load behind it.  Each lane reads back only what it wrote.
   __shared__ f32x4 s_hold[kWavesPerWG][F::NT][64];
   __shared__ float2 s_hold_ml[kWavesPerWG][64];
-  const int W = total_work(a, BS, lane);
+  // The work list, scanned by the workgroup when the batch fits (as in the prefix-group
+  // pass): exclusive prefix sums of the per-unit spans ([B] on: the total) and the clamped
+  // lengths.
+  __shared__ int s_off[kScanSeqs + 1];
+  __shared__ int s_len[kScanSeqs];
+  __shared__ int s_wsum[kWavesPerWG];
+  const int hg = head_groups(a);
+  const bool lds_lists = a.B <= kScanSeqs;
+  int W;
+  if (lds_lists) {
+    const int tid = threadIdx.x;
+    int len[kScanPerThread], sp[kScanPerThread], sum = 0;
+#pragma unroll
+    for (int r = 0; r < kScanPerThread; ++r) {
+      const int sq = tid * kScanPerThread + r;
+      const int L = seq_len(a, std::min(sq, a.B - 1), BS);
+      len[r] = sq < a.B ? L : 0;
+      sp[r] = unit_span((len[r] + BS - 1) / BS, kBlockW);
+      sum += sp[r];
+    }
+    const int incl = wave_incl_scan(sum, lane);
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int base = incl - sum, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWG; ++w) {
+      base += w < wv ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+#pragma unroll
+    for (int r = 0; r < kScanPerThread; ++r) {
+      const int sq = tid * kScanPerThread + r;
+      s_off[sq] = base;
+      s_len[sq] = len[r];
+      base += sp[r];
+    }
+    if (tid == 0) s_off[kScanSeqs] = total;
+    __syncthreads();
+    W = total * hg;
+  } else {
+    W = total_work(a, BS, lane);
+  }
   if (wave == 0) {
-    write_offsets<false, false>(a, BS, lane, a.ws_seq);
+    if (lds_lists) {
+      for (int sq = lane; sq <= a.B; sq += 64) a.ws_seq[sq] = s_off[sq] * hg;
+    } else {
+      write_offsets<false, false>(a, BS, lane, a.ws_seq);
+    }
     if (lane == 0) {
       a.ws_seq[a.B + 1] = a.splits;
       a.ws_seq[a.B + 2] = a.coop;
@@ -850,9 +903,16 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
   const int sub = wave % a.coop;
   const int nshare = list_shares(a.splits / a.coop, W, kBlockW);
   if (share >= nshare) return;
-  split_walk<KV, D, BS, NSUB, APPEND, MIX, CONTIG, false>(a, lane, share, sub, int(share_begin(share, W, nshare)),
-                                                          int(share_begin(share + 1, W, nshare)), s_hold[wv],
-                                                          s_hold_ml[wv]);
+  const int c_begin = __builtin_amdgcn_readfirstlane(int(share_begin(share, W, nshare)));
+  const int c_end = __builtin_amdgcn_readfirstlane(int(share_begin(share + 1, W, nshare)));
+  int s0 = 0, off0 = 0;
+  if (lds_lists) {
+    s0 = __builtin_amdgcn_readfirstlane(lds_search(s_off, a.B, hg, c_begin, lane));
+    off0 = s_off[s0] * hg;
+  }
+  split_walk<KV, D, BS, NSUB, APPEND, MIX, CONTIG, false>(a, lane, share, sub, c_begin, c_end, s_hold[wv],
+                                                          s_hold_ml[wv], lds_lists ? s_off : nullptr,
+                                                          lds_lists ? s_len : nullptr, s0, off0);
 }
 
 // One share of the group work list (chunk first sequence f, head group, block j < P_f):
@@ -865,7 +925,7 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_split_ker
 template <int KV, int D, int BS>
 __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int share, int sub, int c_begin, int c_end,
                                            f32x4 (*hold)[64], float2 (*hold_ml)[64], const int* lds_off = nullptr,
-                                           int f_start = 0, int off_start = 0) {
+                                           const int* lds_glim = nullptr, int f_start = 0, int off_start = 0) {
   using F = Frag<KV, D>;
   using T = KvTraits<KV>;
   constexpr int X = 16 / T::EB;
@@ -877,7 +937,8 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
   const int row = lane >> 4;
   bool holding = false;
 
-  // lds_off: as in split_walk, over the group list's per-unit spans.
+  // lds_off: as in split_walk, over the group list's per-unit spans; lds_glim: every
+  // sequence's chunk and group blocks (kNoChunk and the group blocks' entry layout above).
   int f, chunk_off;
   if (lds_off) {
     f = f_start;
@@ -935,8 +996,13 @@ __device__ __forceinline__ void group_walk(const DecodeArgs& a, int lane, int sh
     for (int ct = 0; ct < CT; ++ct) {
       const int c = 16 * ct + (lane & 15);
       const int m = c / a.G, hh = c % a.G, sq = f + m;
-      const bool member = m < M && sq < a.B && a.chunk_first[sq] == f;
-      lim[ct] = member ? group_skip(a, sq, BS) * BS : 0;
+      if (lds_glim) {
+        const int gl = m < M && sq < a.B ? lds_glim[sq] : kNoChunk;
+        lim[ct] = (gl & kNoChunk) == f ? (gl >> 10) * BS : 0;
+      } else {
+        const bool member = m < M && sq < a.B && a.chunk_first[sq] == f;
+        lim[ct] = member ? group_skip(a, sq, BS) * BS : 0;
+      }
       const uint8_t* qrow = static_cast<const uint8_t*>(a.q) +
                             ((int64_t(sq) * a.Hkv + g) * a.G + hh) * D * T::QB;
 #pragma unroll
@@ -1083,9 +1149,14 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_k
   // the per-unit spans, [s] for sequence s and the total from [B] on.
   __shared__ int s_moff[kScanSeqs + 1];
   __shared__ int s_goff[kScanSeqs + 1];
+  __shared__ int s_len[kScanSeqs];
+  __shared__ int s_glim[kScanSeqs];
   __shared__ int s_wsum[2][kWavesPerWG];
   const int hg = head_groups(a);
   const bool lds_lists = a.B <= kScanSeqs;
+  // (Neither these entries nor the LDS lengths for f32 caches, whose appending kernel has no
+  // registers to spare for them.)
+  const bool lds_glim = KV != PKV_F32 && lds_lists && a.max_blocks < kGlimMaxBlocks;
   int Wm, Wg;
   if (lds_lists) {
     const int tid = threadIdx.x;
@@ -1117,8 +1188,11 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_k
     }
 #pragma unroll
     for (int r = 0; r < kScanPerThread; ++r) {
-      s_moff[tid * kScanPerThread + r] = mb;
-      s_goff[tid * kScanPerThread + r] = gb;
+      const int sq = tid * kScanPerThread + r;
+      s_moff[sq] = mb;
+      s_goff[sq] = gb;
+      s_len[sq] = sp[r].L;
+      s_glim[sq] = int((unsigned(sp[r].skip) << 10) | (unsigned(sp[r].cf) < unsigned(a.B) ? sp[r].cf : kNoChunk));
       mb += ms[r];
       gb += gs[r];
     }
@@ -1184,10 +1258,12 @@ __global__ __launch_bounds__(kWavesPerWG * 64, 2) void paged_attention_grouped_k
     off0 = lds_off[s0] * hg;
   }
   if (is_group) {
-    group_walk<KV, D, BS>(a, lane, idx, sub, c_begin, c_end, s_hold[wv], s_hold_ml[wv], lds_off, s0, off0);
+    group_walk<KV, D, BS>(a, lane, idx, sub, c_begin, c_end, s_hold[wv], s_hold_ml[wv], lds_off,
+                          lds_glim ? s_glim : nullptr, s0, off0);
   } else {
     split_walk<KV, D, BS, NSUB, APPEND, false, false, true>(a, lane, idx, sub, c_begin, c_end, s_hold[wv],
-                                                            s_hold_ml[wv][0], lds_off, s0, off0);
+                                                            s_hold_ml[wv][0], lds_off,
+                                                            KV != PKV_F32 && lds_lists ? s_len : nullptr, s0, off0);
   }
 }
 

@@ -275,20 +275,6 @@ __device__ __forceinline__ SeqSpans seq_spans(const DecodeArgs& a, int s, int bs
   return SeqSpans{unit_span((Ls + bs - 1) / bs - skip, kBlockW), unit_span(cb_s, kGroupBlockW), skip, fc, cb_f, Ls, fs};
 }
 
-// Largest s in [0, n) with hg * e[s] <= x, for e non-decreasing in LDS with e[0] = 0: each
-// step samples 64 evenly spaced entries of the remaining range.
-__device__ __forceinline__ int lds_search(const int* e, int n, int hg, int x, int lane) {
-  int lo = 0;
-  while (n > 1) {
-    const int step = (n + 63) / 64;
-    const bool le = lane * step < n && hg * e[lo + lane * step] <= x;
-    const int l = 63 - __builtin_clzll(__ballot(le));
-    lo += l * step;
-    n = std::min(step, n - l * step);
-  }
-  return lo;
-}
-
 // Sequence whose units contain work position x (0 <= x < W), and the weighted positions of
 // the units before it.  GROUP: over the group work list (chunk first sequences and their
 // blocks).

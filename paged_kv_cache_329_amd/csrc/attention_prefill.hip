@@ -638,6 +638,10 @@ __global__ __launch_bounds__(kPlanThreads) void paged_attention_prefill_plan_ker
 
 constexpr int kMqWaves = 4;
 constexpr int kMqCols = 32;   // columns per (sequence, kv head) this path takes
+// Batches of up to kMqScanSeqs sequences: each workgroup of the few-query split pass scans
+// its work list into LDS, kMqScanSeqs / (kMqWaves * 64) sequences per thread.
+constexpr int kMqScanSeqs = 512;
+constexpr int kMqScanPerThread = kMqScanSeqs / (kMqWaves * 64);
 
 struct MqArgs {
   void* out;
@@ -780,17 +784,68 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
     hold_cols = 0;
   };
 
-  const int W = mq_total(a, BS, lane);
-  if (wave == 0) {
-    int base = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-      const int sq = b0 + lane;
-      const int w = sq < a.B ? mq_span((mq_len(a, sq, BS) + BS - 1) / BS) * (a.Hkv / a.coop) : 0;
-      const int incl = wave_incl_scan(w, lane);
-      if (sq < a.B) a.ws_seq[sq] = base + incl - w;
-      base += __builtin_amdgcn_readlane(incl, 63);
+  // The work list, scanned by the workgroup when the batch fits: exclusive prefix sums of the
+  // per-unit spans ([B] on: the total), the clamped lengths and the query ranges, in LDS; a
+  // wave then finds its share's first unit there and reads later units' entries there.
+  __shared__ int s_off[kMqScanSeqs + 1];
+  __shared__ int s_len[kMqScanSeqs];
+  __shared__ int s_q0[kMqScanSeqs];
+  __shared__ int s_qn[kMqScanSeqs];
+  __shared__ int s_wsum[kMqWaves];
+  const int hgs = a.Hkv / a.coop;
+  const bool lds_lists = a.B <= kMqScanSeqs;
+  int W;
+  if (lds_lists) {
+    const int tid = threadIdx.x;
+    int len[kMqScanPerThread], sp[kMqScanPerThread], sum = 0;
+#pragma unroll
+    for (int r = 0; r < kMqScanPerThread; ++r) {
+      const int sq = tid * kMqScanPerThread + r, sc = std::min(sq, a.B - 1);
+      const int L = mq_len(a, sc, BS);
+      int q0, n;
+      mq_queries(a, sc, q0, n);
+      len[r] = sq < a.B ? L : 0;
+      sp[r] = mq_span((len[r] + BS - 1) / BS);
+      sum += sp[r];
+      s_q0[sq] = q0;
+      s_qn[sq] = n;
     }
-    if (lane == 0) a.ws_seq[a.B] = base;
+    const int incl = wave_incl_scan(sum, lane);
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int base = incl - sum, total = 0;
+#pragma unroll
+    for (int w = 0; w < kMqWaves; ++w) {
+      base += w < wv ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+#pragma unroll
+    for (int r = 0; r < kMqScanPerThread; ++r) {
+      const int sq = tid * kMqScanPerThread + r;
+      s_off[sq] = base;
+      s_len[sq] = len[r];
+      base += sp[r];
+    }
+    if (tid == 0) s_off[kMqScanSeqs] = total;
+    __syncthreads();
+    W = total * hgs;
+  } else {
+    W = mq_total(a, BS, lane);
+  }
+  if (wave == 0) {
+    if (lds_lists) {
+      for (int sq = lane; sq <= a.B; sq += 64) a.ws_seq[sq] = s_off[sq] * hgs;
+    } else {
+      int base = 0;
+      for (int b0 = 0; b0 < a.B; b0 += 64) {
+        const int sq = b0 + lane;
+        const int w = sq < a.B ? mq_span((mq_len(a, sq, BS) + BS - 1) / BS) * hgs : 0;
+        const int incl = wave_incl_scan(w, lane);
+        if (sq < a.B) a.ws_seq[sq] = base + incl - w;
+        base += __builtin_amdgcn_readlane(incl, 63);
+      }
+      if (lane == 0) a.ws_seq[a.B] = base;
+    }
   }
   if (W == 0) return;
   // Share of this wave's group of `coop` consecutive waves, walked side by side on kv heads
@@ -802,13 +857,18 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
   // its last).
   const int nshare = std::min(a.splits / a.coop, W / kMqBlockW);
   if (share >= nshare) return;
-  const int c_begin = int(share_begin(share, W, nshare));
-  const int c_end = int(share_begin(share + 1, W, nshare));
+  const int c_begin = __builtin_amdgcn_readfirstlane(int(share_begin(share, W, nshare)));
+  const int c_end = __builtin_amdgcn_readfirstlane(int(share_begin(share + 1, W, nshare)));
 
   int s, seq_off;
-  mq_locate(a, BS, lane, c_begin, s, seq_off);
+  if (lds_lists) {
+    s = __builtin_amdgcn_readfirstlane(lds_search(s_off, a.B, hgs, c_begin, lane));
+    seq_off = s_off[s] * hgs;
+  } else {
+    mq_locate(a, BS, lane, c_begin, s, seq_off);
+  }
   if (s >= a.B) return;
-  int L = mq_len(a, s, BS);
+  int L = lds_lists ? s_len[s] : mq_len(a, s, BS);
   int nb = (L + BS - 1) / BS;
   int span = mq_span(nb);
   int hg = (c_begin - seq_off) / span;
@@ -831,7 +891,12 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       // Sub-tiles below ks lie in blocks shared with other sequences: cached loads.
       const int ks = MIX ? std::min(__builtin_amdgcn_readfirstlane(a.shared_prefix[s]), nb) * NSB : 0;
       int q0, n;
-      mq_queries(a, s, q0, n);
+      if (lds_lists) {
+        q0 = s_q0[s];
+        n = s_qn[s];
+      } else {
+        mq_queries(a, s, q0, n);
+      }
       // Column c = 16*ct + lane%16 is (query c / G, head c % G); query i sits at L - n + i.
       int posc[CT];
       uint4 qf[CT][F::NLOAD * F::QCH];
@@ -967,7 +1032,7 @@ __global__ __launch_bounds__(256, 2) void paged_attention_mq_split_kernel(MqArgs
       bool done;
       do {
         done = ++s >= a.B;
-      } while (!done && (L = mq_len(a, s, BS)) == 0);
+      } while (!done && (L = lds_lists ? s_len[s] : mq_len(a, s, BS)) == 0);
       if (done) break;
       nb = (L + BS - 1) / BS;
       span = mq_span(nb);

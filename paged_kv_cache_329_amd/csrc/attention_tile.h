@@ -15,6 +15,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "pagedkv.h"
@@ -131,6 +132,20 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     if (lane >= o) v += t;
   }
   return v;
+}
+
+// Largest s in [0, n) with hg * e[s] <= x, for e non-decreasing in LDS with e[0] = 0: each
+// step samples 64 evenly spaced entries of the remaining range.
+__device__ __forceinline__ int lds_search(const int* e, int n, int hg, int x, int lane) {
+  int lo = 0;
+  while (n > 1) {
+    const int step = (n + 63) / 64;
+    const bool le = lane * step < n && hg * e[lo + lane * step] <= x;
+    const int l = 63 - __builtin_clzll(__ballot(le));
+    lo += l * step;
+    n = std::min(step, n - l * step);
+  }
+  return lo;
 }
 
 // Equal shares of a work list of W positions cut into n: share w starts at w * W / n.

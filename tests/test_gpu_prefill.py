@@ -412,6 +412,23 @@ def test_few_query_path_random_shapes(seed):
     assert_close(got, oatt.prefill_case(case), wl.kv_dtype, f"random few-query {seed}")
 
 
+@pytest.mark.parametrize("B", [512, 520])
+def test_few_query_path_batch_sizes_around_the_scan_limit(B):
+    """The few-query split pass scans batches of up to 512 sequences into LDS in every
+    workgroup and walks larger ones wave by wave: a batch at the limit and one past it, with
+    empty sequences and sequences without queries among them, against the oracle."""
+    require_gpu()
+    import paged_kv_cache_329_amd as pkv
+    rng = np.random.default_rng(3100 + B)
+    lengths = rng.integers(0, 120, size=B)
+    q_lens = np.minimum(rng.integers(0, 9, size=B), lengths)
+    wl = Workload(f"few_b{B}", B, 32, 8, 128, 16, "bf16", "bf16", ("uniform", 0, 120), query_dist=("all",))
+    case = make_prefill_case(wl, 7, lengths=lengths, q_lens=q_lens)
+    assert int(case.q_lens.max()) * wl.group_size <= pkv.FEW_QUERY_COLUMNS
+    k, v = pack(case)
+    assert_close(as_f64(prefill(case, k, v)), oatt.prefill_case(case), "bf16", f"few-query batch {B}")
+
+
 def _prefill_splits(case, k, v, splits):
     import torch
     import paged_kv_cache_329_amd as pkv

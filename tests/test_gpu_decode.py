@@ -146,6 +146,22 @@ def test_many_short_sequences(name, num_splits):
     assert_close(got, oatt.decode_case(case), wl.kv_dtype, f"{name} splits={num_splits}")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_bf16", "tiny_fp32"])
+@pytest.mark.parametrize("batch", [512, 520])
+def test_batches_around_the_scan_limit(name, batch):
+    """The split pass scans batches of up to 512 sequences into LDS in every workgroup and
+    walks larger ones wave by wave: a batch at the limit and one past it, short sequences
+    with empty ones among them, against the oracle."""
+    require_gpu()
+    wl = SMALL[name].scaled(batch=batch, length_dist=("uniform", 0, 60), pool_blocks=None)
+    case = make_decode_case(wl, 13)
+    log(f"batch {batch} {name} sum L={int(case.lengths.sum())}")
+    k, v = pack(case)
+    got = as_f64(decode(case, k, v))
+    assert np.all(got[case.lengths == 0] == 0)
+    assert_close(got, oatt.decode_case(case), wl.kv_dtype, f"{name} batch {batch}")
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_bf16", "fp8_kv", "tiny_fp32"])
 @pytest.mark.parametrize("num_splits", [0, 5])
 def test_context_lengths_outside_the_table_are_clamped(name, num_splits):

@@ -141,6 +141,22 @@ def test_decode_step_edge_lengths(name):
     assert np.array_equal(_pool_bytes(v), _pool_bytes(v_ref))
 
 
+@pytest.mark.parametrize("batch", [512, 520])
+def test_decode_step_batches_around_the_scan_limit(batch):
+    """The step over a batch at the split pass's 512-sequence LDS scan limit and one past it
+    (short sequences, some with only the appended token): oracle parity and the pool
+    bit-identical to kv_cache_write's."""
+    require_gpu()
+    wl = CASES["llama3_8b_bf16"].scaled(batch=batch, length_dist=("uniform", 1, 60))
+    case = make_decode_case(wl, 14)
+    k, v, kn, vn = _withheld(case)
+    out = _step(case, k, v, kn, vn)
+    assert_close(as_f64(out), oatt.decode_case(case), wl.kv_dtype, f"step batch {batch}")
+    k_ref, v_ref = pack(case)
+    assert np.array_equal(_pool_bytes(k), _pool_bytes(k_ref))
+    assert np.array_equal(_pool_bytes(v), _pool_bytes(v_ref))
+
+
 @pytest.mark.parametrize("n", [1, 7, 1000])
 def test_decode_step_phases_and_split_counts(n):
     require_gpu()

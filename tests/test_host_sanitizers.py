@@ -49,7 +49,7 @@ def test_allocator_is_clean_under_address_and_undefined_behaviour_sanitizers():
     env.update({
         "PKV_LIBRARY": lib,
         "LD_PRELOAD": asan,
-        # Python and torch are not instrumented: their own allocations are not ours to judge.
+        # Python and torch are not instrumented: their own allocations are not ours to check.
         "ASAN_OPTIONS": "detect_leaks=0:alloc_dealloc_mismatch=0:abort_on_error=0:halt_on_error=1",
         "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1",
         "HYPOTHESIS_PROFILE": "default",
